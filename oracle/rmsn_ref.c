@@ -1,0 +1,195 @@
+/*
+ * rmsn_ref.c -- CPU oracle for the row-wise RMSNorm (test infrastructure only;
+ * see rmsn_ref.h for the definition it follows and who may call it).
+ *
+ * Plain C99, written step by step in the order of the definition so that it
+ * can be checked by eye. Build flags keep IEEE binary32 semantics:
+ * -O2 -ffp-contract=off, no -ffast-math; fmaf, sqrtf and '/' are the C
+ * library's correctly rounded operations (C11 F.10, IEEE 754-2008 5.4).
+ *
+ * Sources: Lecture 04 "Launch Geometry: Grids, Occupancy, and 327 Norms per
+ * Token", section 2.1 (the narrow sum of squares, the block sum, the inverse
+ * from ss/(float)n + eps, then the wide elementwise apply); Lecture 08
+ * "Graph-resident decode", section 8 (short sequential chains combined by a
+ * balanced tree).
+ */
+#include "rmsn_ref.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define LANES 256      /* R256 step 1: number of lane chains          */
+#define WAVE 64        /* R256 step 2: width of each halving tree     */
+#define WAVES (LANES / WAVE)
+
+float rmsn_ref_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;   /* exact: bf16 is the top half of binary32 */
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+uint16_t rmsn_ref_f32_to_bf16(float v)
+{
+    uint32_t u;
+    memcpy(&u, &v, sizeof u);
+    if (isnan(v))
+        return (uint16_t)(0x7FC0u | ((u >> 16) & 0x8000u));
+    /* Round to nearest, ties to even, on the 16 dropped bits. A carry out of
+     * the mantissa correctly moves to the next binade or to infinity. */
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/* Steps 1-3 given the row as binary32 values produced by `get`. */
+typedef float (*getter)(const void* row, int64_t d);
+
+static float get_f32(const void* row, int64_t d) { return ((const float*)row)[d]; }
+static float get_bf16(const void* row, int64_t d)
+{
+    return rmsn_ref_bf16_to_f32(((const uint16_t*)row)[d]);
+}
+
+static void lane_chains(const void* row, int64_t n, getter get, float p[LANES])
+{
+    /* Step 1: lane l accumulates x[l], x[l+256], ... in ascending order. */
+    for (int l = 0; l < LANES; ++l) {
+        float acc = 0.0f;
+        for (int64_t d = l; d < n; d += LANES) {
+            float xd = get(row, d);
+            acc = fmaf(xd, xd, acc);
+        }
+        p[l] = acc;
+    }
+}
+
+static void wave_trees(const float p[LANES], float W[WAVES])
+{
+    /* Step 2: each 64-lane group is reduced by descending halving. */
+    for (int w = 0; w < WAVES; ++w) {
+        float q[WAVE];
+        for (int j = 0; j < WAVE; ++j) q[j] = p[WAVE * w + j];
+        for (int s = WAVE / 2; s >= 1; s /= 2)
+            for (int j = 0; j < s; ++j) q[j] = q[j] + q[j + s];
+        W[w] = q[0];
+    }
+}
+
+static float block_tree(const float W[WAVES])
+{
+    /* Step 3: the same halving applied to the four group totals. */
+    float a = W[0] + W[2];
+    float b = W[1] + W[3];
+    return a + b;
+}
+
+static float sumsq(const void* row, int64_t n, getter get)
+{
+    float p[LANES], W[WAVES];
+    lane_chains(row, n, get, p);
+    wave_trees(p, W);
+    return block_tree(W);
+}
+
+float rmsn_ref_sumsq_f32(const float* x, int64_t n) { return sumsq(x, n, get_f32); }
+float rmsn_ref_sumsq_bf16(const uint16_t* x, int64_t n) { return sumsq(x, n, get_bf16); }
+
+void rmsn_ref_wave_totals_f32(const float* x, int64_t n, float out_w[4])
+{
+    float p[LANES];
+    lane_chains(x, n, get_f32, p);
+    wave_trees(p, out_w);
+}
+
+float rmsn_ref_inv(float ss, int64_t n, float eps)
+{
+    float m = ss / (float)n;   /* step 4: mean of squares, n exact in binary32 */
+    float t = m + eps;         /* step 5                                        */
+    float r = sqrtf(t);        /* step 6: correctly rounded square root         */
+    float inv = 1.0f / r;      /* step 7: correctly rounded reciprocal          */
+    return inv;
+}
+
+void rmsn_ref_row_f32(const float* x, const float* w, float* y, int64_t n, float eps)
+{
+    float inv = rmsn_ref_inv(rmsn_ref_sumsq_f32(x, n), n, eps);
+    for (int64_t d = 0; d < n; ++d) {
+        float a = x[d] * inv;  /* step 8, left to right */
+        y[d] = a * w[d];
+    }
+}
+
+void rmsn_ref_row_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, float eps)
+{
+    float inv = rmsn_ref_inv(rmsn_ref_sumsq_bf16(x, n), n, eps);
+    for (int64_t d = 0; d < n; ++d) {
+        float a = rmsn_ref_bf16_to_f32(x[d]) * inv;
+        float b = a * rmsn_ref_bf16_to_f32(w[d]);
+        y[d] = rmsn_ref_f32_to_bf16(b);
+    }
+}
+
+/* ---- many rows, optionally on several threads ---------------------------- */
+
+typedef struct {
+    int dtype;
+    const void* x; int64_t xs;
+    const void* w;
+    void* y; int64_t ys;
+    int64_t r0, r1, n;
+    float eps;
+} rows_job;
+
+static void run_rows(const rows_job* j)
+{
+    for (int64_t r = j->r0; r < j->r1; ++r) {
+        if (j->dtype == RMSN_REF_F32)
+            rmsn_ref_row_f32((const float*)j->x + r * j->xs, (const float*)j->w,
+                             (float*)j->y + r * j->ys, j->n, j->eps);
+        else
+            rmsn_ref_row_bf16((const uint16_t*)j->x + r * j->xs, (const uint16_t*)j->w,
+                              (uint16_t*)j->y + r * j->ys, j->n, j->eps);
+    }
+}
+
+static void* rows_thread(void* arg)
+{
+    run_rows((const rows_job*)arg);
+    return NULL;
+}
+
+int rmsn_ref_rows(int dtype, const void* x, int64_t x_stride, const void* w,
+                  void* y, int64_t y_stride, int64_t rows, int64_t n, float eps,
+                  int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if ((int64_t)nthreads > rows) nthreads = (int)(rows > 0 ? rows : 1);
+    rows_job base = {dtype, x, x_stride, w, y, y_stride, 0, rows, n, eps};
+    if (nthreads == 1) {
+        run_rows(&base);
+        return 1;
+    }
+    rows_job* jobs = (rows_job*)calloc((size_t)nthreads, sizeof *jobs);
+    pthread_t* tid = (pthread_t*)calloc((size_t)nthreads, sizeof *tid);
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = base;
+        jobs[t].r0 = rows * t / nthreads;
+        jobs[t].r1 = rows * (t + 1) / nthreads;
+        if (pthread_create(&tid[t], NULL, rows_thread, &jobs[t]) == 0) {
+            ++started;
+        } else {
+            run_rows(&jobs[t]);      /* no thread: do this block here */
+            tid[t] = 0;
+        }
+    }
+    for (int t = 0; t < nthreads; ++t)
+        if (tid[t]) pthread_join(tid[t], NULL);
+    free(jobs);
+    free(tid);
+    return started > 0 ? started : 1;
+}
