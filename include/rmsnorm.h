@@ -1,0 +1,194 @@
+/*
+ * rmsnorm.h -- C ABI of the MI355X (gfx950) row-wise RMSNorm library.
+ *
+ * Operation (Lecture 04 "Launch Geometry: Grids, Occupancy, and 327 Norms per
+ * Token", section 2 and 2.1): for each row of width n,
+ *     inv  = 1 / sqrt( (sum_d x[d]^2) / (float)n + eps )
+ *     y[d] = (x[d] * inv) * w[d]
+ * in IEEE binary32. The sum of squares uses one fixed association ("R256"),
+ * which is part of the result's bits (section 2.1: the reduction's width is
+ * part of the numerics, the elementwise apply's width is not):
+ *   1. 256 lane chains: lane l = fmaf(x[d], x[d], lane l) for d = l, l+256, ...
+ *      ascending, starting from +0;
+ *   2. each 64-lane group reduced by descending halving (j + 32, 16, 8, 4, 2, 1);
+ *   3. ss = (G0 + G2) + (G1 + G3);
+ *   4-7. m = ss / (float)n; t = m + eps; r = sqrtf(t); inv = 1.0f / r, every
+ *      operation correctly rounded (no approximate reciprocal square root);
+ *   8. y = (x * inv) * w, left to right; bf16 outputs are rounded once to
+ *      nearest even from the binary32 value.
+ * Every entry point and every internal code path (register-resident rows,
+ * streaming rows, any rows-per-workgroup, eager or graph replay, any pointer
+ * alignment) gives the same bits. Denormals are preserved, NaN/Inf propagate
+ * per IEEE (bf16 NaN outputs are quiet NaNs; payloads are not specified).
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or synchronises inside rmsnorm_f32, rmsnorm_bf16,
+ *    rmsnorm_batched_rows, rmsnorm_sequence_eager or
+ *    rmsnorm_sequence_graph_launch, so each of them may itself be captured
+ *    into a caller's HIP graph.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    asynchronously; the return value reports argument and launch errors
+ *    only. A fault inside a kernel surfaces at the caller's next
+ *    synchronisation.
+ *  - Return value: an rmsn_status. On failure nothing is enqueued and
+ *    rmsnorm_last_error() describes the reason (per calling thread).
+ *  - RMSN_EINVAL: a null pointer, n < 1 or n > 2^24 ((float)n must be exact),
+ *    rows < 1, a row stride < n, eps negative / NaN / infinite, a pointer not
+ *    aligned to its element size (4 B binary32, 2 B bf16), or overlapping
+ *    x / y ranges other than exact in-place use (y == x with equal strides),
+ *    or w overlapping y. No HIP call is made before these checks pass.
+ *  - In-place (y == x) is allowed: each row is read completely before any of
+ *    its outputs is written.
+ *  - bf16 values are passed as their 16-bit patterns (uint16_t).
+ */
+#ifndef RMSNORM_H
+#define RMSNORM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RMSN_OK = 0,
+    RMSN_EINVAL = 1,   /* invalid argument; nothing enqueued                        */
+    RMSN_EHIP = 2,     /* a HIP runtime call failed; message names the call and code */
+    RMSN_ECAPTURE = 3, /* graph capture failed; the handle replays eagerly instead   */
+    RMSN_ENOMEM = 4    /* host or device allocation in graph creation failed         */
+} rmsn_status;
+
+typedef enum { RMSN_F32 = 0, RMSN_BF16 = 1 } rmsn_dtype;
+
+#define RMSN_MAX_N (1 << 24)
+#define RMSN_MAX_SEQUENCE 65536
+
+/* One row of a sequence, stored in DEVICE memory (32 bytes, 8-byte aligned).
+ * x, w, y: device pointers with the element type of the sequence; n: width.
+ * Kernels read the descriptor when they run, so rewriting a table entry
+ * between graph replays changes what the next replay normalises
+ * (Lecture 08 "Graph-resident decode", section 2: values that vary per replay
+ * live in device memory and are read by the kernel). n is used only as a loop
+ * bound: any n in [1, 2^24] gives the exact result on replay, whatever width
+ * the node was captured with (only speed depends on it); n outside that range
+ * makes the node write nothing. Pointer alignment rules are as above. */
+typedef struct rmsn_desc {
+    const void* x;
+    const void* w;
+    void* y;
+    int64_t n;
+} rmsn_desc;
+
+/* Opaque handle of a captured sequence (host memory owned by the library). */
+typedef struct rmsn_graph rmsn_graph;
+
+/* One binary32 row: y[0..n) from x[0..n) and w[0..n). Lecture 04 section 2. */
+int rmsnorm_f32(const float* x, const float* w, float* y, int64_t n, float eps, void* stream);
+
+/* One bf16 row (bit patterns); binary32 arithmetic, one rounding at the store. */
+int rmsnorm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, float eps,
+                 void* stream);
+
+/* `rows` rows of width n sharing one weight row. Row r of x starts at
+ * x + r * x_row_stride elements, row r of y at y + r * y_row_stride.
+ * dtype is an rmsn_dtype. Many aligned rows run one row per 64-lane
+ * wavefront, several wavefronts per workgroup; few rows run one row per
+ * 256-thread workgroup so each row gets four wavefronts (Lecture 04 section 1:
+ * match the grid to the compute units; see rmsnorm_plan_query). */
+int rmsnorm_batched_rows(int dtype, const void* x, int64_t x_row_stride, const void* w, void* y,
+                         int64_t y_row_stride, int64_t rows, int64_t n, float eps, void* stream);
+
+/* The norms of a decode step, in order, issued as `count` dependent launches
+ * on `stream` (the eager arm). d_table: DEVICE array of count descriptors.
+ * h_widths: HOST array of count widths that size each launch (the same plan
+ * function sizes graph nodes, so both arms launch identical kernels). */
+int rmsnorm_sequence_eager(int dtype, const rmsn_desc* d_table, const int64_t* h_widths,
+                           int32_t count, float eps, void* stream);
+
+/* Capture the same `count` launches into one HIP graph and instantiate it
+ * (Lecture 08 "Graph-resident decode", sections 1-3). Every kernel variant is
+ * run once on a private scratch row before capture so that no lazy
+ * initialisation happens inside it. On success *out is a new handle and
+ * RMSN_OK is returned. If capture or instantiation fails, the partial graph is
+ * destroyed, *out is still a valid handle in eager-fallback mode (launch then
+ * issues the eager sequence: slower, same bits), and RMSN_ECAPTURE is
+ * returned. d_table must stay valid until the handle is destroyed; h_widths
+ * is copied. On RMSN_EINVAL / RMSN_ENOMEM / RMSN_EHIP, *out is NULL. */
+int rmsnorm_sequence_graph_create(int dtype, const rmsn_desc* d_table, const int64_t* h_widths,
+                                  int32_t count, float eps, rmsn_graph** out);
+
+/* Replay the whole sequence with one graph launch on `stream`. */
+int rmsnorm_sequence_graph_launch(rmsn_graph* g, void* stream);
+
+/* Release the graph and the handle. NULL is accepted. Does not synchronise:
+ * the caller makes sure no launch of it is still pending. */
+int rmsnorm_sequence_graph_destroy(rmsn_graph* g);
+
+/* Number of nodes in the captured graph (0 in eager-fallback mode). */
+int rmsnorm_graph_node_count(const rmsn_graph* g, int64_t* out);
+
+/* 1 if the handle replays eagerly because capture failed, else 0. */
+int rmsnorm_graph_is_fallback(const rmsn_graph* g, int* out);
+
+/* Human-readable reason for the last failure on this thread ("" if none). */
+const char* rmsnorm_last_error(void);
+
+/* ---- launch planning (host only, no HIP call) ---------------------------- */
+
+/* Code paths. All give identical bits; they differ in how rows are mapped to
+ * the hardware (Lecture 04 section 2.1: the apply may be laid out freely once
+ * the reduction's association is fixed).
+ *   RMSN_PATH_WAVE:   one 64-lane wavefront per row, the row held in
+ *                     registers, 16-byte (binary32) / 8-byte (bf16) loads;
+ *                     needs vector-aligned rows and n <= 8192.
+ *   RMSN_PATH_BLOCK:  one 256-thread workgroup per row, wavefront g holding
+ *                     the 64 lane chains of group g in registers; any element
+ *                     alignment, n <= 8192.
+ *   RMSN_PATH_STREAM: as BLOCK but streaming the row twice (sum, then apply)
+ *                     instead of holding it; any n up to 2^24. */
+enum { RMSN_PATH_WAVE = 0, RMSN_PATH_BLOCK = 1, RMSN_PATH_STREAM = 2 };
+
+typedef struct rmsn_plan_info {
+    int32_t path;            /* one of RMSN_PATH_*                                */
+    int32_t chunks;          /* 256-element chunks a lane's registers hold (0:
+                                streaming)                                        */
+    int32_t rows_per_block;  /* rows per workgroup                                */
+    int32_t block;           /* threads per workgroup                             */
+    int64_t grid;            /* workgroups                                        */
+} rmsn_plan_info;
+
+/* The launch the library would use for `rows` rows of width n whose row and
+ * weight pointers are (aligned != 0) or are not (aligned == 0) aligned to
+ * 16 B (binary32) / 8 B (bf16). Same function the launches use. Returns
+ * RMSN_EINVAL for an invalid dtype, rows or n. */
+int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int aligned, rmsn_plan_info* out);
+
+/* Process-wide overrides, for proving that code paths give identical bits
+ * (Lecture 04 section 6: one binary, switchable arms). Defaults come from the
+ * environment at first use (RMSN_PATH, RMSN_ROWS_PER_BLOCK), else automatic.
+ *   RMSN_OPT_PATH:           -1 automatic, or an RMSN_PATH_* value; a path a
+ *                            launch is not eligible for (WAVE on unaligned
+ *                            rows or n > 8192, BLOCK with n > 8192) falls
+ *                            back to the automatic choice
+ *   RMSN_OPT_ROWS_PER_BLOCK:  0 automatic, else 1, 2 or 4 (WAVE path only)
+ * Returns RMSN_EINVAL for an unknown key or value. Not synchronised with
+ * launches on other threads. */
+enum { RMSN_OPT_PATH = 1, RMSN_OPT_ROWS_PER_BLOCK = 2 };
+int rmsnorm_set_option(int key, int value);
+int rmsnorm_get_option(int key, int* value);
+
+/* ---- diagnostics ----------------------------------------------------------- */
+
+/* Runs the kernels' own steps 4-7 (the device functions every row kernel
+ * calls) on count consecutive binary32 bit patterns starting at first_bits,
+ * taken as ss, with the given n and eps: r_out[i] = sqrtf(ss/(float)n + eps),
+ * inv_out[i] = 1.0f / r_out[i]. Device output arrays of count floats. Used to
+ * check the device square root and division against a CPU exhaustively. */
+int rmsnorm_diag_inverse(uint32_t first_bits, int64_t count, int64_t n, float eps, float* r_out,
+                         float* inv_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RMSNORM_H */

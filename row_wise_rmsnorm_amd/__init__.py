@@ -1,0 +1,253 @@
+"""Python binding of the gfx950 row-wise RMSNorm library (librmsnorm_amd.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/rmsnorm.h. torch supplies device memory
+and the stream; nothing here computes a result, and there is no CPU fallback.
+Importing this module without the built library raises ImportError.
+
+Function names follow the C entry points:
+    rmsnorm_f32(x, w, eps, out=None)           one binary32 row
+    rmsnorm_bf16(x, w, eps, out=None)          one bf16 row
+    rmsnorm_batched_rows(x, w, eps, out=None)  2-D, rows share w
+    rmsnorm_sequence_eager(table, widths, eps, dtype)
+    SequenceGraph(table, widths, eps, dtype)   captured sequence (.launch())
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librmsnorm_amd.so")
+
+RMSN_OK, RMSN_EINVAL, RMSN_EHIP, RMSN_ECAPTURE, RMSN_ENOMEM = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM = -1, 0, 1, 2
+OPT_PATH, OPT_ROWS_PER_BLOCK = 1, 2
+MAX_N = 1 << 24
+DESC_BYTES = 32
+
+
+class RmsnormError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"rmsnorm status {status}: {message}")
+        self.status = status
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("chunks", ctypes.c_int32),
+                ("rows_per_block", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("grid", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"row_wise_rmsnorm_amd: {LIB_PATH} is not built "
+                          "(run __graft_entry__.build() or row_wise_rmsnorm_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_uint32
+    c_int = ctypes.c_int
+    sig = {
+        "rmsnorm_f32": [vp, vp, vp, i64, f, vp],
+        "rmsnorm_bf16": [vp, vp, vp, i64, f, vp],
+        "rmsnorm_batched_rows": [c_int, vp, i64, vp, vp, i64, i64, i64, f, vp],
+        "rmsnorm_sequence_eager": [c_int, vp, vp, i32, f, vp],
+        "rmsnorm_sequence_graph_create": [c_int, vp, vp, i32, f, ctypes.POINTER(vp)],
+        "rmsnorm_sequence_graph_launch": [vp, vp],
+        "rmsnorm_sequence_graph_destroy": [vp],
+        "rmsnorm_graph_node_count": [vp, ctypes.POINTER(i64)],
+        "rmsnorm_graph_is_fallback": [vp, ctypes.POINTER(c_int)],
+        "rmsnorm_plan_query": [c_int, i64, i64, c_int, ctypes.POINTER(_PlanInfo)],
+        "rmsnorm_set_option": [c_int, c_int],
+        "rmsnorm_get_option": [c_int, ctypes.POINTER(c_int)],
+        "rmsnorm_diag_inverse": [u32, i64, i64, f, vp, vp, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = c_int
+    lib.rmsnorm_last_error.argtypes = []
+    lib.rmsnorm_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+EXPORTED = ("rmsnorm_f32", "rmsnorm_bf16", "rmsnorm_batched_rows", "rmsnorm_sequence_eager",
+            "rmsnorm_sequence_graph_create", "rmsnorm_sequence_graph_launch",
+            "rmsnorm_sequence_graph_destroy", "rmsnorm_graph_node_count",
+            "rmsnorm_graph_is_fallback", "rmsnorm_last_error", "rmsnorm_plan_query",
+            "rmsnorm_set_option", "rmsnorm_get_option", "rmsnorm_diag_inverse")
+
+
+def lib():
+    """The ctypes handle of the loaded library."""
+    return _lib
+
+
+def last_error():
+    return (_lib.rmsnorm_last_error() or b"").decode()
+
+
+def _check(status):
+    if status != RMSN_OK:
+        raise RmsnormError(status, last_error())
+    return status
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"float32 or bfloat16 tensor expected, got {t.dtype}")
+
+
+def _device_tensor(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t
+
+
+def _out_like(x, out):
+    import torch
+    if out is None:
+        return torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or out.device != x.device:
+        raise ValueError("out must match x in shape, dtype and device")
+    return out
+
+
+def rmsnorm_f32(x, w, eps, out=None, stream=None):
+    """One binary32 row (1-D contiguous tensors)."""
+    _device_tensor(x, "x"), _device_tensor(w, "w")
+    if x.dim() != 1 or not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("1-D contiguous tensors expected")
+    y = _out_like(x, out)
+    _check(_lib.rmsnorm_f32(x.data_ptr(), w.data_ptr(), y.data_ptr(), x.numel(),
+                            float(eps), _stream_ptr(stream)))
+    return y
+
+
+def rmsnorm_bf16(x, w, eps, out=None, stream=None):
+    """One bf16 row (1-D contiguous tensors)."""
+    _device_tensor(x, "x"), _device_tensor(w, "w")
+    if x.dim() != 1 or not x.is_contiguous() or not w.is_contiguous():
+        raise ValueError("1-D contiguous tensors expected")
+    y = _out_like(x, out)
+    _check(_lib.rmsnorm_bf16(x.data_ptr(), w.data_ptr(), y.data_ptr(), x.numel(),
+                             float(eps), _stream_ptr(stream)))
+    return y
+
+
+def rmsnorm_batched_rows(x, w, eps, out=None, stream=None):
+    """Every row of a 2-D tensor (unit stride along a row) against w."""
+    _device_tensor(x, "x"), _device_tensor(w, "w")
+    if x.dim() != 2 or x.stride(1) != 1 or not w.is_contiguous():
+        raise ValueError("2-D tensor with unit stride along rows expected")
+    y = _out_like(x, out)
+    if y.stride(1) != 1:
+        raise ValueError("out must have unit stride along rows")
+    _check(_lib.rmsnorm_batched_rows(_dtype_code(x), x.data_ptr(), x.stride(0), w.data_ptr(),
+                                     y.data_ptr(), y.stride(0), x.shape[0], x.shape[1],
+                                     float(eps), _stream_ptr(stream)))
+    return y
+
+
+def make_table(rows, device=None):
+    """Device descriptor table from a list of (x, w, y) GPU tensors (each
+    1-D); returns (table tensor, host widths list)."""
+    import struct
+    import torch
+    buf = bytearray()
+    widths = []
+    for x, w, y in rows:
+        buf += struct.pack("<QQQq", x.data_ptr(), w.data_ptr(), y.data_ptr(), x.numel())
+        widths.append(int(x.numel()))
+    host = torch.frombuffer(bytes(buf), dtype=torch.uint8)
+    dev = device if device is not None else rows[0][0].device
+    return host.to(dev), widths
+
+
+def _widths_array(widths):
+    arr = (ctypes.c_int64 * len(widths))(*[int(v) for v in widths])
+    return arr
+
+
+def rmsnorm_sequence_eager(table, widths, eps, dtype, stream=None):
+    """Issue len(widths) dependent launches reading descriptors from `table`."""
+    arr = _widths_array(widths)
+    _check(_lib.rmsnorm_sequence_eager(int(dtype), ctypes.c_void_p(table.data_ptr()), arr,
+                                       len(widths), float(eps), _stream_ptr(stream)))
+
+
+class SequenceGraph:
+    """A decode step's norms captured as one HIP graph (or, if capture failed,
+    an eager replay with the same kernels). `status` is RMSN_OK or
+    RMSN_ECAPTURE."""
+
+    def __init__(self, table, widths, eps, dtype):
+        self._table = table  # keep the descriptor table alive with the graph
+        arr = _widths_array(widths)
+        h = ctypes.c_void_p()
+        st = _lib.rmsnorm_sequence_graph_create(int(dtype), ctypes.c_void_p(table.data_ptr()),
+                                                arr, len(widths), float(eps), ctypes.byref(h))
+        if st not in (RMSN_OK, RMSN_ECAPTURE):
+            raise RmsnormError(st, last_error())
+        self.status = st
+        self.capture_error = last_error() if st == RMSN_ECAPTURE else ""
+        self._h = h
+
+    def launch(self, stream=None):
+        _check(_lib.rmsnorm_sequence_graph_launch(self._h, _stream_ptr(stream)))
+
+    def node_count(self):
+        v = ctypes.c_int64()
+        _check(_lib.rmsnorm_graph_node_count(self._h, ctypes.byref(v)))
+        return v.value
+
+    def is_fallback(self):
+        v = ctypes.c_int()
+        _check(_lib.rmsnorm_graph_is_fallback(self._h, ctypes.byref(v)))
+        return bool(v.value)
+
+    def destroy(self):
+        if self._h:
+            _check(_lib.rmsnorm_sequence_graph_destroy(self._h))
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def plan_query(dtype, rows, n, aligned=True):
+    info = _PlanInfo()
+    _check(_lib.rmsnorm_plan_query(int(dtype), int(rows), int(n), 1 if aligned else 0,
+                                   ctypes.byref(info)))
+    return {"path": info.path, "chunks": info.chunks, "rows_per_block": info.rows_per_block,
+            "block": info.block, "grid": info.grid}
+
+
+def set_option(key, value):
+    _check(_lib.rmsnorm_set_option(int(key), int(value)))
+
+
+def get_option(key):
+    v = ctypes.c_int()
+    _check(_lib.rmsnorm_get_option(int(key), ctypes.byref(v)))
+    return v.value
+
+
+def diag_inverse(first_bits, count, n, eps, r_out, inv_out, stream=None):
+    """Steps 4-7 of the kernels over consecutive bit patterns (diagnostic)."""
+    _check(_lib.rmsnorm_diag_inverse(int(first_bits), int(count), int(n), float(eps),
+                                     ctypes.c_void_p(r_out.data_ptr()),
+                                     ctypes.c_void_p(inv_out.data_ptr()), _stream_ptr(stream)))

@@ -1,0 +1,42 @@
+"""Build the gfx950 HIP library in place: row_wise_rmsnorm_amd/librmsnorm_amd.so.
+
+hipcc cross-compiles for gfx950 without a GPU present. Floating point:
+contraction off (-ffp-contract=off), no fast-math, HIP's default correctly
+rounded binary32 division and square root; packed-FP32 instructions are
+disabled for the device code.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "librmsnorm_amd.so")
+SOURCES = [os.path.join(HERE, "csrc", f) for f in
+           ("rmsn_kernels.hip", "rmsn_api.hip", "rmsn_plan.cpp")]
+ARCH = os.environ.get("RMSN_OFFLOAD_ARCH", "gfx950")
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+    "-I", os.path.join(ROOT, "include"),
+    "-I", os.path.join(HERE, "csrc"),
+]
+
+
+def build(verbose=True):
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = LIB + ".tmp"
+    cmd = [hipcc, *FLAGS, "-o", tmp, *SOURCES]
+    if verbose:
+        print("[hip] " + " ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

@@ -1,0 +1,488 @@
+// rmsn_kernels.hip -- row-wise RMSNorm kernels for CDNA4 (gfx950).
+//
+// What is computed (Lecture 04 "Launch Geometry: Grids, Occupancy, and 327
+// Norms per Token", sections 2 and 2.1): per row, the sum of squares under
+// one fixed association, inv = 1/sqrt(ss/(float)n + eps), y = (x*inv)*w.
+// Section 2.1's rule decides the design: the association of the reduction is
+// part of the numerics and stays fixed; the elementwise apply is laid out
+// however the hardware likes. The association ("R256"):
+//   lane chains  p[l] = fmaf(x[d], x[d], p[l]), d = l, l+256, ... ascending
+//   group trees  four 64-lane groups, descending halving 32,16,8,4,2,1
+//   combine      ss = (G0 + G2) + (G1 + G3)
+// Every kernel below evaluates exactly these operations in this order; the
+// three row layouts only decide which hardware lane holds which chain.
+//
+// Layouts (all rows are independent; one row never spans workgroups):
+//   WAVE   one wavefront per row. Lane t holds elements 256k + 4t + {0..3}
+//          of every 256-element chunk k -- one 16-byte (binary32) or 8-byte
+//          (bf16) load per chunk -- so its four registers ARE the chains of
+//          lanes 4t..4t+3. Group g is lanes 16g..16g+15 of the wavefront; the
+//          halving steps 32/16/8/4 are DPP row shifts by 8/4/2/1 inside each
+//          16-lane row, steps 2/1 are adds between a lane's own registers, and
+//          the combine reads lanes 0/16/32/48. No LDS, no barrier; HBM is read
+//          once and the row lives in VGPRs between the reduction and the apply.
+//   BLOCK  four wavefronts (256 threads) per row. Thread l is chain l; wave g
+//          is group g and reduces it with two cross-row shuffles and four DPP
+//          row shifts; the four group totals meet in 16 bytes of LDS across
+//          one barrier. Element loads are 4/2 bytes, so any element-aligned
+//          pointer works; the row stays in VGPRs (n <= 256 * chunks).
+//   STREAM BLOCK's mapping, but the row is streamed twice (once for the sum,
+//          once for the apply) instead of being held: any n up to 2^24.
+//
+// Floating point: contraction is off for this file; the one fused operation
+// of the association is written as fmaf. '/' and sqrtf are the correctly
+// rounded sequences HIP generates by default for binary32 (no approximate
+// reciprocal square root); f32 denormals are preserved.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rmsn_launch.h"
+
+#pragma clang fp contract(off)
+
+namespace rmsn {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Element access. bf16 values are their 16-bit patterns; widening is exact.
+
+__device__ __forceinline__ float widen(float v) { return v; }
+__device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// binary32 -> bf16, round to nearest, ties to even on the 16 dropped bits;
+// NaN -> quiet NaN keeping the sign.
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void put(float* p, float v) { *p = v; }
+__device__ __forceinline__ void put(uint16_t* p, float v) { *p = (uint16_t)bf16_bits(v); }
+
+// Four consecutive elements ("a quad") as they sit in registers: binary32
+// quads are 16 bytes, bf16 quads stay packed in 8 bytes and are widened on use.
+template <typename T> struct Quad;
+
+template <> struct Quad<float> {
+    using raw = float4;
+    static __device__ __forceinline__ raw load(const float* p) {
+        return *reinterpret_cast<const float4*>(p);
+    }
+    static __device__ __forceinline__ raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    // Elements e..e+3 of a row of width n with e < n < e + 4 possible: the
+    // missing ones read as +0 (addresses are clamped into the row).
+    static __device__ __forceinline__ raw load_tail(const float* p, int e, int n) {
+        raw r;
+        r.x = e + 0 < n ? p[min(e + 0, n - 1)] : 0.f;
+        r.y = e + 1 < n ? p[min(e + 1, n - 1)] : 0.f;
+        r.z = e + 2 < n ? p[min(e + 2, n - 1)] : 0.f;
+        r.w = e + 3 < n ? p[min(e + 3, n - 1)] : 0.f;
+        return r;
+    }
+    static __device__ __forceinline__ void unpack(const raw& r, float v[4]) {
+        v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float v[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+template <> struct Quad<uint16_t> {
+    using raw = uint2;
+    static __device__ __forceinline__ raw load(const uint16_t* p) {
+        return *reinterpret_cast<const uint2*>(p);
+    }
+    static __device__ __forceinline__ raw zero() { return make_uint2(0u, 0u); }
+    static __device__ __forceinline__ raw load_tail(const uint16_t* p, int e, int n) {
+        const uint32_t b0 = e + 0 < n ? p[min(e + 0, n - 1)] : 0u;
+        const uint32_t b1 = e + 1 < n ? p[min(e + 1, n - 1)] : 0u;
+        const uint32_t b2 = e + 2 < n ? p[min(e + 2, n - 1)] : 0u;
+        const uint32_t b3 = e + 3 < n ? p[min(e + 3, n - 1)] : 0u;
+        return make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
+    static __device__ __forceinline__ void unpack(const raw& r, float v[4]) {
+        v[0] = __uint_as_float(r.x << 16);
+        v[1] = __uint_as_float(r.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(r.y << 16);
+        v[3] = __uint_as_float(r.y & 0xFFFF0000u);
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float v[4]) {
+        uint2 q;
+        q.x = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+        q.y = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+        *reinterpret_cast<uint2*>(p) = q;
+    }
+};
+
+// Make the compiler treat a quad's registers as rewritten (the asm is empty):
+// values derived from it before this point (the widened bf16 floats of the
+// reduction) cannot be reused after it, so they need not stay live.
+__device__ __forceinline__ void opaque(float4& r) {
+    asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w));
+}
+__device__ __forceinline__ void opaque(uint2& r) { asm volatile("" : "+v"(r.x), "+v"(r.y)); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane moves.
+
+// Lane i receives lane i+K of its 16-lane DPP row (lanes past the row's end
+// receive 0; the trees never use those lanes' results).
+template <int K>
+__device__ __forceinline__ float row_shl(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + K, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// ---------------------------------------------------------------------------
+// Steps 4-7 of the association: shared by every kernel and the diagnostic.
+
+__device__ __forceinline__ float mean_eps_root(float ss, int n, float eps) {
+    const float m = ss / (float)n;  // n <= 2^24: exact as binary32
+    const float t = m + eps;
+    return sqrtf(t);                // correctly rounded
+}
+__device__ __forceinline__ float reciprocal(float r) { return 1.0f / r; }  // correctly rounded
+__device__ __forceinline__ float inverse_rms(float ss, int n, float eps) {
+    return reciprocal(mean_eps_root(ss, n, eps));
+}
+
+// ---------------------------------------------------------------------------
+// WAVE layout: one wavefront per row, lane t holds chains 4t..4t+3.
+
+// Group trees and combine for the WAVE layout. On entry lane t's p[e] is the
+// finished chain of association lane 4t+e; group g = lanes 16g..16g+15, where
+// association lane 64g+j sits in wavefront lane 16g + j/4, register j%4.
+__device__ __forceinline__ float wave_sumsq(float p0, float p1, float p2, float p3) {
+    // halving s = 32, 16, 8, 4: partner j+s is s/4 wavefront lanes further
+    p0 += row_shl<8>(p0); p1 += row_shl<8>(p1); p2 += row_shl<8>(p2); p3 += row_shl<8>(p3);
+    p0 += row_shl<4>(p0); p1 += row_shl<4>(p1); p2 += row_shl<4>(p2); p3 += row_shl<4>(p3);
+    p0 += row_shl<2>(p0); p1 += row_shl<2>(p1); p2 += row_shl<2>(p2); p3 += row_shl<2>(p3);
+    p0 += row_shl<1>(p0); p1 += row_shl<1>(p1); p2 += row_shl<1>(p2); p3 += row_shl<1>(p3);
+    // halving s = 2 and 1 inside the lane
+    const float g = (p0 + p2) + (p1 + p3);
+    // group totals sit in lanes 0, 16, 32, 48
+    const float g0 = lane_value(g, 0), g1 = lane_value(g, 16);
+    const float g2 = lane_value(g, 32), g3 = lane_value(g, 48);
+    return (g0 + g2) + (g1 + g3);
+}
+
+// Chunks a kernel instance may assume complete: the plan picks the smallest
+// bucket holding the row, so a row using bucket NCH has more than
+// 256 * (previous bucket) elements.
+constexpr int prev_bucket(int nch) {
+    return nch <= 1 ? 0 : nch <= 2 ? 1 : nch <= 4 ? 2 : nch <= 6 ? 4 : nch <= 8 ? 6
+         : nch <= 12 ? 8 : nch <= 16 ? 12 : nch <= 20 ? 16 : nch <= 24 ? 20 : nch <= 28 ? 24 : 28;
+}
+
+// Chunks whose weights the WAVE apply phase loads at once.
+template <typename T>
+constexpr int wave_apply_group() { return sizeof(T) == 4 ? 1 : 2; }
+
+// Resident wavefronts per SIMD the WAVE kernels are compiled for: the row's
+// registers (4 values per chunk; bf16 packed two per VGPR), one weight group,
+// and a few for addresses and temporaries, out of 512 VGPRs per SIMD lane.
+template <typename T, int NCH>
+constexpr int wave_occupancy() {
+    constexpr int q = sizeof(T) == 4 ? 4 : 2;
+    constexpr int regs = (NCH + wave_apply_group<T>()) * q + (sizeof(T) == 4 ? 16 : 8);
+    constexpr int w = 512 / ((regs + 7) / 8 * 8);
+    return w > 8 ? 8 : (w < 1 ? 1 : w);
+}
+
+// Requires 256 * prev_bucket(NCH) < n <= 256 * NCH (guaranteed by the plan).
+template <typename T, int NCH>
+__device__ __forceinline__ void row_wave(const T* x, const T* __restrict__ w, T* y, int n,
+                                         float eps, int lane) {
+    using Q = Quad<T>;
+    constexpr int MINF = prev_bucket(NCH);
+    // Chunks [0, full) are complete; chunk `full` is the ragged tail when n is
+    // not a multiple of 256. `full` is wave-uniform: the tests are scalar.
+    const int full = n >> 8;
+    const int lo = lane << 2;
+    typename Q::raw xr[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k)
+        if (k < MINF || k < full) xr[k] = Q::load(x + (k << 8) + lo);
+    const int et = (full << 8) + lo;  // this lane's first element of the tail chunk
+    const typename Q::raw xt = (n & 255) ? Q::load_tail(x, et, n) : Q::zero();
+    // Lane chains in ascending chunk order; the tail chunk comes last and reads
+    // +0 past the row (fmaf(0, 0, p) == p for p >= +0).
+    float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+        if (k < MINF || k < full) {
+            float v[4];
+            Q::unpack(xr[k], v);
+            p0 = fmaf(v[0], v[0], p0);
+            p1 = fmaf(v[1], v[1], p1);
+            p2 = fmaf(v[2], v[2], p2);
+            p3 = fmaf(v[3], v[3], p3);
+        }
+    }
+    {
+        float v[4];
+        Q::unpack(xt, v);
+        p0 = fmaf(v[0], v[0], p0);
+        p1 = fmaf(v[1], v[1], p1);
+        p2 = fmaf(v[2], v[2], p2);
+        p3 = fmaf(v[3], v[3], p3);
+    }
+    const float inv = inverse_rms(wave_sumsq(p0, p1, p2, p3), n, eps);
+#pragma unroll
+    for (int k = 0; k < NCH; ++k)
+        if (k < MINF || k < full) opaque(xr[k]);
+    // Apply in groups of G chunks: the group's weight loads are issued
+    // together, then its outputs are stored. The scheduling barrier keeps the
+    // compiler from hoisting every weight load to the top, which would hold
+    // the whole weight row in registers and cut the resident wavefronts.
+    constexpr int G = wave_apply_group<T>();
+#pragma unroll
+    for (int k0 = 0; k0 < NCH; k0 += G) {
+        typename Q::raw wr[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int k = k0 + j;
+            if (k < NCH && (k < MINF || k < full)) wr[j] = Q::load(w + (k << 8) + lo);
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int k = k0 + j;
+            if (k < NCH && (k < MINF || k < full)) {
+                float v[4], wv[4], o[4];
+                Q::unpack(xr[k], v);
+                Q::unpack(wr[j], wv);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = (v[i] * inv) * wv[i];
+                Q::store(y + (k << 8) + lo, o);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (n & 255) {
+        float v[4];
+        Q::unpack(xt, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (et + i < n) put(y + et + i, (v[i] * inv) * widen(w[et + i]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// BLOCK / STREAM layout: 256 threads per row, thread l = chain l, wave g = group g.
+
+// Descending halving over the 64 lanes of this wavefront; the total lands in lane 0.
+__device__ __forceinline__ float group_tree(float v) {
+    v += __shfl_down(v, 32, 64);
+    v += __shfl_down(v, 16, 64);
+    v += row_shl<8>(v);
+    v += row_shl<4>(v);
+    v += row_shl<2>(v);
+    v += row_shl<1>(v);
+    return v;
+}
+
+// Group trees, the combine through LDS, and steps 4-7. Every thread of the
+// block calls this once per row with its finished chain p.
+__device__ __forceinline__ float block_inverse(float p, int n, float eps, float* lds4) {
+    const float g = group_tree(p);
+    if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = g;
+    __syncthreads();
+    const float ss = (lds4[0] + lds4[2]) + (lds4[1] + lds4[3]);
+    return inverse_rms(ss, n, eps);
+}
+
+// NCH > 0: rows with 256 * prev_bucket(NCH) < n <= 256 * NCH are held in
+// registers; any other n (possible for descriptor rows rewritten between graph
+// replays) is streamed. NCH == 0: always streamed.
+template <typename T, int NCH>
+__device__ __forceinline__ void row_block(const T* x, const T* __restrict__ w, T* y, int n,
+                                          float eps, float* lds4) {
+    constexpr int MINF = prev_bucket(NCH);
+    const int l = threadIdx.x;  // association lane 0..255
+    const int full = n >> 8;    // complete 256-element chunks (wave-uniform)
+    float p = 0.0f;
+    if (NCH > 0 && full >= MINF && full + ((n & 255) != 0) <= NCH) {
+        constexpr int R = NCH > 0 ? NCH : 1;
+        float xv[R], wv[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            if (k < MINF || k < full) xv[k] = widen(x[(k << 8) + l]);
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            if (k < MINF || k < full) wv[k] = widen(w[(k << 8) + l]);
+        // the ragged tail chunk: lanes past the row read +0 (clamped address)
+        const int dt = (full << 8) + l;
+        const bool tail = (n & 255) != 0;
+        const float xt = tail && dt < n ? widen(x[min(dt, n - 1)]) : 0.0f;
+        const float wt = tail && dt < n ? widen(w[min(dt, n - 1)]) : 0.0f;
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            if (k < MINF || k < full) p = fmaf(xv[k], xv[k], p);
+        p = fmaf(xt, xt, p);  // +0 past the row: no change
+        const float inv = block_inverse(p, n, eps, lds4);
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            if (k < MINF || k < full) put(y + (k << 8) + l, (xv[k] * inv) * wv[k]);
+        if (tail && dt < n) put(y + dt, (xt * inv) * wt);
+    } else {
+        for (int d = l; d < n; d += 256) {
+            const float v = widen(x[d]);
+            p = fmaf(v, v, p);
+        }
+        const float inv = block_inverse(p, n, eps, lds4);
+        for (int d = l; d < n; d += 256) put(y + d, (widen(x[d]) * inv) * widen(w[d]));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernels.
+
+template <typename T, int NCH, int RPB>
+__global__ __launch_bounds__(64 * RPB, (wave_occupancy<T, NCH>())) void k_rows_wave(const T* x, int64_t xs,
+                                                        const T* __restrict__ w, T* y,
+                                                        int64_t ys, int64_t rows, int n,
+                                                        float eps) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t r = (int64_t)blockIdx.x * RPB + wave;
+    if (r >= rows) return;
+    row_wave<T, NCH>(x + r * xs, w, y + r * ys, n, eps, threadIdx.x & 63);
+}
+
+template <typename T, int NCH>
+__global__ __launch_bounds__(256) void k_rows_block(const T* x, int64_t xs,
+                                                    const T* __restrict__ w, T* y, int64_t ys,
+                                                    int n, float eps) {
+    __shared__ float lds4[4];
+    const int64_t r = blockIdx.x;
+    row_block<T, NCH>(x + r * xs, w, y + r * ys, n, eps, lds4);
+}
+
+// One row whose pointers and width are read from device memory when the
+// kernel runs (Lecture 08 "Graph-resident decode", section 2: a value used
+// only as a loop bound can live in device memory; the launch geometry comes
+// from the capture-time width).
+template <typename T, int NCH>
+__global__ __launch_bounds__(256) void k_desc_block(const rmsn_desc* __restrict__ d, float eps) {
+    __shared__ float lds4[4];
+    const int64_t n = d->n;
+    if (n < 1 || n > RMSN_MAX_N) return;
+    row_block<T, NCH>(static_cast<const T*>(d->x), static_cast<const T*>(d->w),
+                      static_cast<T*>(d->y), (int)n, eps, lds4);
+}
+
+__global__ __launch_bounds__(256) void k_diag_inverse(uint32_t first, int64_t count, int n,
+                                                      float eps, float* r_out, float* inv_out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= count) return;
+    const float ss = __uint_as_float(first + (uint32_t)i);
+    const float r = mean_eps_root(ss, n, eps);
+    r_out[i] = r;
+    inv_out[i] = reciprocal(r);
+}
+
+// ---------------------------------------------------------------------------
+// Instance selection. The bucket list matches kChunkBuckets in rmsn_plan.h.
+
+#define RMSN_FOR_BUCKETS(X) X(1) X(2) X(4) X(6) X(8) X(12) X(16) X(20) X(24) X(28) X(32)
+
+template <typename T>
+hipError_t launch_wave_t(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
+                         int64_t ys, int64_t rows, int n, float eps, hipStream_t s) {
+    const T* xp = static_cast<const T*>(x);
+    const T* wp = static_cast<const T*>(w);
+    T* yp = static_cast<T*>(y);
+    const dim3 grid((unsigned)p.grid), block((unsigned)p.block);
+#define RMSN_CASE(C)                                                                        \
+    case C:                                                                                 \
+        if (p.rows_per_block == 4)                                                          \
+            hipLaunchKernelGGL((k_rows_wave<T, C, 4>), grid, block, 0, s, xp, xs, wp, yp,  \
+                               ys, rows, n, eps);                                           \
+        else if (p.rows_per_block == 2)                                                     \
+            hipLaunchKernelGGL((k_rows_wave<T, C, 2>), grid, block, 0, s, xp, xs, wp, yp,  \
+                               ys, rows, n, eps);                                           \
+        else                                                                                \
+            hipLaunchKernelGGL((k_rows_wave<T, C, 1>), grid, block, 0, s, xp, xs, wp, yp,  \
+                               ys, rows, n, eps);                                           \
+        break;
+    switch (p.chunks) {
+        RMSN_FOR_BUCKETS(RMSN_CASE)
+        default: return hipErrorInvalidValue;
+    }
+#undef RMSN_CASE
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_block_t(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
+                          int64_t ys, int n, float eps, hipStream_t s) {
+    const T* xp = static_cast<const T*>(x);
+    const T* wp = static_cast<const T*>(w);
+    T* yp = static_cast<T*>(y);
+    const dim3 grid((unsigned)p.grid), block(256);
+#define RMSN_CASE(C)                                                                          \
+    case C:                                                                                   \
+        hipLaunchKernelGGL((k_rows_block<T, C>), grid, block, 0, s, xp, xs, wp, yp, ys, n,   \
+                           eps);                                                              \
+        break;
+    switch (p.chunks) {
+        RMSN_CASE(0)
+        RMSN_FOR_BUCKETS(RMSN_CASE)
+        default: return hipErrorInvalidValue;
+    }
+#undef RMSN_CASE
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_desc_t(const Plan& p, const rmsn_desc* d, float eps, hipStream_t s) {
+#define RMSN_CASE(C)                                                                    \
+    case C:                                                                             \
+        hipLaunchKernelGGL((k_desc_block<T, C>), dim3(1), dim3(256), 0, s, d, eps);     \
+        break;
+    switch (p.chunks) {
+        RMSN_CASE(0)
+        RMSN_FOR_BUCKETS(RMSN_CASE)
+        default: return hipErrorInvalidValue;
+    }
+#undef RMSN_CASE
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
+                       int64_t ys, int64_t rows, int n, float eps, hipStream_t stream) {
+    if (p.grid < 1 || p.grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (p.path == RMSN_PATH_WAVE) {
+        // the WAVE kernels rely on the plan's bucket choice for this n
+        if (p.chunks != chunk_bucket(n)) return hipErrorInvalidValue;
+        return p.dtype == RMSN_F32
+                   ? launch_wave_t<float>(p, x, xs, w, y, ys, rows, n, eps, stream)
+                   : launch_wave_t<uint16_t>(p, x, xs, w, y, ys, rows, n, eps, stream);
+    }
+    return p.dtype == RMSN_F32 ? launch_block_t<float>(p, x, xs, w, y, ys, n, eps, stream)
+                               : launch_block_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
+}
+
+hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, hipStream_t stream) {
+    if (p.path == RMSN_PATH_WAVE) return hipErrorInvalidValue;  // descriptors use BLOCK/STREAM
+    return p.dtype == RMSN_F32 ? launch_desc_t<float>(p, d, eps, stream)
+                               : launch_desc_t<uint16_t>(p, d, eps, stream);
+}
+
+hipError_t launch_diag_inverse(uint32_t first_bits, int64_t count, int n, float eps, float* r_out,
+                               float* inv_out, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    const int64_t blocks = (count + 255) / 256;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_diag_inverse, dim3((unsigned)blocks), dim3(256), 0, stream, first_bits,
+                       count, n, eps, r_out, inv_out);
+    return hipGetLastError();
+}
+
+}  // namespace rmsn

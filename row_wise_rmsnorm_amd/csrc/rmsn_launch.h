@@ -1,0 +1,26 @@
+// rmsn_launch.h -- host-side launchers of the gfx950 kernels (rmsn_kernels.hip).
+// Each enqueues on `stream` and returns the launch's hipError_t; none
+// allocates or synchronises.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "rmsn_plan.h"
+#include "rmsnorm.h"
+
+namespace rmsn {
+
+// `rows` rows, one per wavefront, with the geometry of plan `p`.
+hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
+                       int64_t ys, int64_t rows, int n, float eps, hipStream_t stream);
+
+// One row described by the device-resident descriptor `d` (read when the
+// kernel runs); plan `p` was made for the capture-time width.
+hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, hipStream_t stream);
+
+// Steps 4-7 over consecutive bit patterns (diagnostic).
+hipError_t launch_diag_inverse(uint32_t first_bits, int64_t count, int n, float eps, float* r_out,
+                               float* inv_out, hipStream_t stream);
+
+}  // namespace rmsn

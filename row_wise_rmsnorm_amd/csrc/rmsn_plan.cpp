@@ -1,0 +1,258 @@
+// rmsn_plan.cpp -- launch planning, options and argument validation.
+// Pure host C++: nothing here touches the HIP runtime, so every check can run
+// (and is tested) on a machine without a GPU.
+#include "rmsn_plan.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+namespace rmsn {
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+std::atomic<int> g_path{-2};   // -2 = not yet read from the environment
+std::atomic<int> g_rpb{-2};
+
+int env_int(const char* name, int dflt) {
+    const char* s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    char* end = nullptr;
+    long v = std::strtol(s, &end, 10);
+    if (end == s) return dflt;
+    return (int)v;
+}
+
+bool valid_path(int v) {
+    return v == -1 || v == RMSN_PATH_WAVE || v == RMSN_PATH_BLOCK || v == RMSN_PATH_STREAM;
+}
+bool valid_rpb(int v) { return v == 0 || v == 1 || v == 2 || v == 4; }
+
+// Byte ranges [a, a+la) and [b, b+lb) intersect.
+bool overlaps(uintptr_t a, uint64_t la, uintptr_t b, uint64_t lb) {
+    return a < b + lb && b < a + la;
+}
+
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+}
+
+void clear_error() { g_err[0] = '\0'; }
+const char* last_error() { return g_err; }
+
+int option_path() {
+    int v = g_path.load(std::memory_order_relaxed);
+    if (v == -2) {
+        v = env_int("RMSN_PATH", -1);
+        if (!valid_path(v)) v = -1;
+        g_path.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+int option_rows_per_block() {
+    int v = g_rpb.load(std::memory_order_relaxed);
+    if (v == -2) {
+        v = env_int("RMSN_ROWS_PER_BLOCK", 0);
+        if (!valid_rpb(v)) v = 0;
+        g_rpb.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+int set_option(int key, int value) {
+    if (key == RMSN_OPT_PATH) {
+        if (!valid_path(value)) {
+            set_error("rmsnorm_set_option: path must be -1 (automatic), %d, %d or %d, got %d",
+                      RMSN_PATH_WAVE, RMSN_PATH_BLOCK, RMSN_PATH_STREAM, value);
+            return RMSN_EINVAL;
+        }
+        g_path.store(value, std::memory_order_relaxed);
+        return RMSN_OK;
+    }
+    if (key == RMSN_OPT_ROWS_PER_BLOCK) {
+        if (!valid_rpb(value)) {
+            set_error("rmsnorm_set_option: rows per block must be 0, 1, 2 or 4, got %d", value);
+            return RMSN_EINVAL;
+        }
+        g_rpb.store(value, std::memory_order_relaxed);
+        return RMSN_OK;
+    }
+    set_error("rmsnorm_set_option: unknown key %d", key);
+    return RMSN_EINVAL;
+}
+
+int get_option(int key, int* value) {
+    if (!value) {
+        set_error("rmsnorm_get_option: null output pointer");
+        return RMSN_EINVAL;
+    }
+    if (key == RMSN_OPT_PATH) { *value = option_path(); return RMSN_OK; }
+    if (key == RMSN_OPT_ROWS_PER_BLOCK) { *value = option_rows_per_block(); return RMSN_OK; }
+    set_error("rmsnorm_get_option: unknown key %d", key);
+    return RMSN_EINVAL;
+}
+
+int chunk_bucket(int64_t n) {
+    const int64_t need = (n + kLanes - 1) / kLanes;
+    for (int i = 0; i < kNumBuckets; ++i)
+        if (kChunkBuckets[i] >= need) return kChunkBuckets[i];
+    return 0;
+}
+
+int auto_rows_per_block(int64_t rows) {
+    // Four rows (wavefronts) per workgroup quarter the workgroups the
+    // dispatcher has to issue while every CU still holds many wavefronts.
+    return rows >= 4 * kWaveMinRows ? 4 : 1;
+}
+
+int make_plan(int dtype, int64_t rows, int64_t n, bool aligned, Plan* out) {
+    if (dtype != RMSN_F32 && dtype != RMSN_BF16) {
+        set_error("unknown dtype %d", dtype);
+        return RMSN_EINVAL;
+    }
+    if (rows < 1) {
+        set_error("rows must be >= 1, got %lld", (long long)rows);
+        return RMSN_EINVAL;
+    }
+    if (n < 1 || n > RMSN_MAX_N) {
+        set_error("n must be in [1, %d], got %lld", RMSN_MAX_N, (long long)n);
+        return RMSN_EINVAL;
+    }
+    const int bucket = chunk_bucket(n);
+    const bool can_wave = bucket != 0 && aligned;
+    const bool can_block = bucket != 0;
+    int path;
+    switch (option_path()) {
+        case RMSN_PATH_WAVE: path = can_wave ? RMSN_PATH_WAVE : -1; break;
+        case RMSN_PATH_BLOCK: path = can_block ? RMSN_PATH_BLOCK : -1; break;
+        case RMSN_PATH_STREAM: path = RMSN_PATH_STREAM; break;
+        default: path = -1; break;
+    }
+    if (path < 0) {
+        if (can_wave && rows >= kWaveMinRows) path = RMSN_PATH_WAVE;
+        else if (can_block) path = RMSN_PATH_BLOCK;
+        else path = RMSN_PATH_STREAM;
+    }
+    Plan p{};
+    p.dtype = dtype;
+    p.path = path;
+    if (path == RMSN_PATH_WAVE) {
+        int rpb = option_rows_per_block();
+        if (rpb == 0) rpb = auto_rows_per_block(rows);
+        p.chunks = bucket;
+        p.rows_per_block = rpb;
+        p.block = kWave * rpb;
+        p.grid = (rows + rpb - 1) / rpb;
+    } else {
+        p.chunks = path == RMSN_PATH_BLOCK ? bucket : 0;
+        p.rows_per_block = 1;
+        p.block = kBlockThreads;
+        p.grid = rows;
+    }
+    *out = p;
+    return RMSN_OK;
+}
+
+int check_eps(float eps) {
+    if (!std::isfinite(eps) || eps < 0.0f) {
+        set_error("eps must be finite and >= 0, got %g", (double)eps);
+        return RMSN_EINVAL;
+    }
+    return RMSN_OK;
+}
+
+int check_row_args(int dtype, const void* x, int64_t xs, const void* w, const void* y, int64_t ys,
+                   int64_t rows, int64_t n) {
+    if (dtype != RMSN_F32 && dtype != RMSN_BF16) {
+        set_error("unknown dtype %d", dtype);
+        return RMSN_EINVAL;
+    }
+    if (!x || !w || !y) {
+        set_error("null pointer (x=%p w=%p y=%p)", x, w, y);
+        return RMSN_EINVAL;
+    }
+    if (n < 1 || n > RMSN_MAX_N) {
+        set_error("n must be in [1, %d], got %lld", RMSN_MAX_N, (long long)n);
+        return RMSN_EINVAL;
+    }
+    if (rows < 1) {
+        set_error("rows must be >= 1, got %lld", (long long)rows);
+        return RMSN_EINVAL;
+    }
+    if (xs < n || ys < n) {
+        set_error("row strides must be >= n (x stride %lld, y stride %lld, n %lld)",
+                  (long long)xs, (long long)ys, (long long)n);
+        return RMSN_EINVAL;
+    }
+    const int64_t es = elem_bytes(dtype);
+    const int64_t lim = INT64_MAX / 4;
+    if ((rows - 1) > (lim - n) / xs || (rows - 1) > (lim - n) / ys) {
+        set_error("rows * stride overflows");
+        return RMSN_EINVAL;
+    }
+    const uintptr_t px = (uintptr_t)x, pw = (uintptr_t)w, py = (uintptr_t)y;
+    if ((px | pw | py) % (uintptr_t)es) {
+        set_error("pointers must be aligned to the %lld-byte element size (x=%p w=%p y=%p)",
+                  (long long)es, x, w, y);
+        return RMSN_EINVAL;
+    }
+    const uint64_t lx = (uint64_t)(((rows - 1) * xs + n) * es);
+    const uint64_t ly = (uint64_t)(((rows - 1) * ys + n) * es);
+    const uint64_t lw = (uint64_t)(n * es);
+    const bool in_place = px == py && xs == ys;
+    if (!in_place && overlaps(px, lx, py, ly)) {
+        set_error("x and y overlap without being the same rows (in-place needs y == x and equal strides)");
+        return RMSN_EINVAL;
+    }
+    if (overlaps(pw, lw, py, ly)) {
+        set_error("w overlaps y");
+        return RMSN_EINVAL;
+    }
+    return RMSN_OK;
+}
+
+}  // namespace rmsn
+
+namespace rmsn {
+
+int check_sequence_args(int dtype, const rmsn_desc* d_table, const int64_t* h_widths,
+                        int32_t count, float eps) {
+    if (dtype != RMSN_F32 && dtype != RMSN_BF16) {
+        set_error("unknown dtype %d", dtype);
+        return RMSN_EINVAL;
+    }
+    if (!d_table || !h_widths) {
+        set_error("null pointer (d_table=%p h_widths=%p)", (const void*)d_table,
+                  (const void*)h_widths);
+        return RMSN_EINVAL;
+    }
+    if ((uintptr_t)d_table % alignof(rmsn_desc)) {
+        set_error("d_table must be %d-byte aligned", (int)alignof(rmsn_desc));
+        return RMSN_EINVAL;
+    }
+    if (count < 1 || count > RMSN_MAX_SEQUENCE) {
+        set_error("count must be in [1, %d], got %d", RMSN_MAX_SEQUENCE, (int)count);
+        return RMSN_EINVAL;
+    }
+    for (int32_t i = 0; i < count; ++i) {
+        if (h_widths[i] < 1 || h_widths[i] > RMSN_MAX_N) {
+            set_error("width %d must be in [1, %d], got %lld", (int)i, RMSN_MAX_N,
+                      (long long)h_widths[i]);
+            return RMSN_EINVAL;
+        }
+    }
+    return check_eps(eps);
+}
+
+}  // namespace rmsn

@@ -1,0 +1,67 @@
+// rmsn_plan.h -- launch planning and argument validation (pure host C++, no
+// HIP). One function decides every launch, so an eager call, a graph capture
+// and a plan query can never disagree (Lecture 08 "Graph-resident decode",
+// section 2: the capture check and the launcher call the same plan function).
+#pragma once
+
+#include <stdint.h>
+
+#include "rmsnorm.h"
+
+namespace rmsn {
+
+constexpr int kLanes = 256;      // lane chains of the fixed association
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kBlockThreads = 256;
+constexpr int kMaxChunks = 32;   // largest row held in registers: 32 * 256 = 8192
+// Register-resident kernel instances: a lane keeps `chunks` values (BLOCK
+// path) or groups of four values (WAVE path), one per 256 elements of the row.
+constexpr int kChunkBuckets[] = {1, 2, 4, 6, 8, 12, 16, 20, 24, 28, 32};
+constexpr int kNumBuckets = sizeof(kChunkBuckets) / sizeof(kChunkBuckets[0]);
+// Row counts from which the WAVE path is chosen automatically: below it a row
+// gets a whole workgroup (four wavefronts) so its loads spread over four SIMDs.
+constexpr int64_t kWaveMinRows = 1024;
+
+struct Plan {
+    int dtype;           // RMSN_F32 / RMSN_BF16
+    int path;            // RMSN_PATH_WAVE / _BLOCK / _STREAM
+    int chunks;          // kernel instance: a bucket, or 0 for streaming
+    int rows_per_block;  // rows per workgroup
+    int block;           // threads per workgroup
+    int64_t grid;        // workgroups
+};
+
+inline int elem_bytes(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
+// Bytes one lane loads per 256-element chunk on the WAVE path: four elements.
+inline int vec_bytes(int dtype) { return 4 * elem_bytes(dtype); }
+
+// Smallest bucket holding ceil(n/256) chunks, or 0 if n needs more than kMaxChunks.
+int chunk_bucket(int64_t n);
+
+// Rows per workgroup on the WAVE path, chosen automatically.
+int auto_rows_per_block(int64_t rows);
+
+// Plan a launch of `rows` rows of width n. `aligned`: every row's x and y and
+// the weight start on a vec_bytes(dtype) boundary. Returns RMSN_OK or
+// RMSN_EINVAL (bad dtype, rows < 1, n outside [1, 2^24]).
+int make_plan(int dtype, int64_t rows, int64_t n, bool aligned, Plan* out);
+
+// Process-wide options (rmsnorm_set_option); read lazily from the environment.
+int option_path();            // -1 automatic, else an RMSN_PATH_* value
+int option_rows_per_block();  // 0 automatic, else 1/2/4
+int set_option(int key, int value);
+int get_option(int key, int* value);
+
+// Argument checks shared by the entry points. Each returns RMSN_OK or
+// RMSN_EINVAL and, on failure, sets the thread's last-error message.
+int check_eps(float eps);
+int check_row_args(int dtype, const void* x, int64_t xs, const void* w, const void* y, int64_t ys,
+                   int64_t rows, int64_t n);
+int check_sequence_args(int dtype, const rmsn_desc* d_table, const int64_t* h_widths,
+                        int32_t count, float eps);
+
+void set_error(const char* fmt, ...);
+void clear_error();
+const char* last_error();
+
+}  // namespace rmsn

@@ -1,0 +1,190 @@
+"""Host-side checks of the C ABI, runnable without a GPU.
+
+* the built library loads and exports every function include/rmsnorm.h declares
+* every invalid argument is rejected with RMSN_EINVAL before any HIP call
+  (on a machine without a GPU any HIP call would fail with RMSN_EHIP instead)
+* the launch plan: paths, register buckets, rows per workgroup, grid
+* process-wide options
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rmsnorm.h")
+
+
+@pytest.fixture(scope="module")
+def rn():
+    import row_wise_rmsnorm_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(rmsnorm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    fns = declared_functions()
+    for name in ("rmsnorm_f32", "rmsnorm_bf16", "rmsnorm_batched_rows",
+                 "rmsnorm_sequence_graph_create", "rmsnorm_sequence_graph_launch",
+                 "rmsnorm_sequence_graph_destroy", "rmsnorm_sequence_eager"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(rn):
+    lib = ctypes.CDLL(rn.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(rn.EXPORTED)
+
+
+def test_desc_layout_is_32_bytes():
+    text = open(HEADER).read()
+    assert re.search(r"const void\* x;\s*const void\* w;\s*void\* y;\s*int64_t n;", text)
+
+
+# ---- argument validation ------------------------------------------------------
+
+A16 = 0x10000          # fake, never dereferenced device addresses
+B16 = 0x20000
+C16 = 0x30000
+
+
+def call_rows(rn, dtype=0, x=A16, xs=64, w=B16, y=C16, ys=64, rows=2, n=64, eps=1e-6):
+    return rn.lib().rmsnorm_batched_rows(dtype, x, xs, w, y, ys, rows, n, eps, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=2), dict(dtype=-1),
+    dict(x=0), dict(w=0), dict(y=0),
+    dict(n=0), dict(n=-5), dict(n=(1 << 24) + 1),
+    dict(rows=0), dict(rows=-1),
+    dict(xs=63), dict(ys=10),
+    dict(eps=-1e-6), dict(eps=float("nan")), dict(eps=float("inf")),
+    dict(x=A16 + 2), dict(dtype=1, x=A16 + 1), dict(w=B16 + 1), dict(y=C16 + 3),
+    dict(y=A16 + 4),                        # partial x / y overlap
+    dict(y=A16, ys=128, xs=64),             # same base, different strides
+    dict(w=C16 + 8),                        # w inside y
+    dict(xs=1 << 62, rows=1 << 20),         # extent overflow
+])
+def test_batched_rows_rejects(rn, kw):
+    assert call_rows(rn, **kw) == rn.RMSN_EINVAL
+    assert rn.last_error() != ""
+
+
+def test_single_row_entry_points_reject(rn):
+    L = rn.lib()
+    assert L.rmsnorm_f32(0, B16, C16, 64, 1e-6, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_f32(A16, B16, C16, 0, 1e-6, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_f32(A16 + 1, B16, C16, 8, 1e-6, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_f32(A16, B16, C16, 8, -1.0, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_bf16(A16, B16, C16, 1 << 25, 1e-6, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_bf16(A16 + 1, B16, C16, 8, 1e-6, None) == rn.RMSN_EINVAL
+
+
+def test_in_place_is_accepted_by_validation(rn):
+    # y == x with equal strides passes validation; without a GPU the launch
+    # itself then fails with a HIP error, never with EINVAL.
+    st = call_rows(rn, y=A16, ys=64)
+    assert st != rn.RMSN_EINVAL
+
+
+def test_sequence_validation(rn):
+    L = rn.lib()
+    w3 = (ctypes.c_int64 * 3)(7168, 1536, 512)
+    bad = (ctypes.c_int64 * 3)(7168, 0, 512)
+    assert L.rmsnorm_sequence_eager(0, None, w3, 3, 1e-6, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_sequence_eager(0, A16, None, 3, 1e-6, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_sequence_eager(0, A16, w3, 0, 1e-6, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_sequence_eager(0, A16, bad, 3, 1e-6, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_sequence_eager(0, A16 + 4, w3, 3, 1e-6, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_sequence_eager(5, A16, w3, 3, 1e-6, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_sequence_eager(0, A16, w3, 3, float("nan"), None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_sequence_eager(0, A16, w3, 70000, 1e-6, None) == rn.RMSN_EINVAL
+    h = ctypes.c_void_p(1234)
+    assert L.rmsnorm_sequence_graph_create(0, A16, bad, 3, 1e-6, ctypes.byref(h)) == rn.RMSN_EINVAL
+    assert h.value is None
+    assert L.rmsnorm_sequence_graph_create(0, A16, w3, 3, 1e-6, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_sequence_graph_launch(None, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_sequence_graph_destroy(None) == rn.RMSN_OK
+    v = ctypes.c_int64()
+    assert L.rmsnorm_graph_node_count(None, ctypes.byref(v)) == rn.RMSN_EINVAL
+
+
+def test_diag_validation(rn):
+    L = rn.lib()
+    assert L.rmsnorm_diag_inverse(0xFFFFFFFF, 2, 1, 0.0, A16, B16, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_diag_inverse(0, 16, 0, 0.0, A16, B16, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_diag_inverse(0, 16, 1, -1.0, A16, B16, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_diag_inverse(0, 16, 1, 0.0, 0, B16, None) == rn.RMSN_EINVAL
+
+
+# ---- planning -------------------------------------------------------------------
+
+def test_plan_paths_and_buckets(rn):
+    # many aligned rows: one wavefront per row, four rows per workgroup
+    p = rn.plan_query(rn.BF16, 8192, 7168, aligned=True)
+    assert p == {"path": rn.PATH_WAVE, "chunks": 28, "rows_per_block": 4, "block": 256, "grid": 2048}
+    # few rows: a 256-thread workgroup per row
+    p = rn.plan_query(rn.BF16, 64, 7168, aligned=True)
+    assert p == {"path": rn.PATH_BLOCK, "chunks": 28, "rows_per_block": 1, "block": 256, "grid": 64}
+    # single rows of the decode step
+    assert rn.plan_query(rn.F32, 1, 7168)["chunks"] == 28
+    assert rn.plan_query(rn.F32, 1, 1536)["chunks"] == 6
+    assert rn.plan_query(rn.F32, 1, 512)["chunks"] == 2
+    # unaligned rows never take the WAVE path
+    assert rn.plan_query(rn.F32, 4096, 7168, aligned=False)["path"] == rn.PATH_BLOCK
+    # beyond 8192 elements: streamed
+    p = rn.plan_query(rn.F32, 3, 8193)
+    assert p["path"] == rn.PATH_STREAM and p["chunks"] == 0 and p["grid"] == 3
+    p = rn.plan_query(rn.F32, 1, 1 << 24)
+    assert p["path"] == rn.PATH_STREAM
+
+
+@pytest.mark.parametrize("n", [1, 255, 256, 257, 511, 512, 513, 1024, 1535, 1536, 2049, 3072,
+                               4096, 5000, 6144, 6145, 7167, 7168, 8191, 8192])
+def test_plan_bucket_holds_row_and_previous_does_not(rn, n):
+    buckets = [1, 2, 4, 6, 8, 12, 16, 20, 24, 28, 32]
+    c = rn.plan_query(rn.F32, 1, n)["chunks"]
+    assert c in buckets and 256 * c >= n
+    i = buckets.index(c)
+    if i > 0:
+        assert 256 * buckets[i - 1] < n
+
+
+def test_plan_rejects(rn):
+    for args in [(2, 1, 10), (0, 0, 10), (0, 1, 0), (0, 1, (1 << 24) + 1)]:
+        with pytest.raises(rn.RmsnormError):
+            rn.plan_query(*args)
+
+
+def test_options_roundtrip_and_force_paths(rn):
+    try:
+        rn.set_option(rn.OPT_PATH, rn.PATH_STREAM)
+        assert rn.get_option(rn.OPT_PATH) == rn.PATH_STREAM
+        assert rn.plan_query(rn.BF16, 8192, 7168)["path"] == rn.PATH_STREAM
+        rn.set_option(rn.OPT_PATH, rn.PATH_BLOCK)
+        assert rn.plan_query(rn.BF16, 8192, 7168)["path"] == rn.PATH_BLOCK
+        rn.set_option(rn.OPT_PATH, rn.PATH_WAVE)
+        assert rn.plan_query(rn.BF16, 3, 7168)["path"] == rn.PATH_WAVE
+        # ineligible: falls back to the automatic choice
+        assert rn.plan_query(rn.BF16, 3, 7168, aligned=False)["path"] == rn.PATH_BLOCK
+        assert rn.plan_query(rn.BF16, 3, 9000)["path"] == rn.PATH_STREAM
+        rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
+        rn.set_option(rn.OPT_ROWS_PER_BLOCK, 2)
+        p = rn.plan_query(rn.BF16, 8191, 7168)
+        assert p["rows_per_block"] == 2 and p["grid"] == 4096 and p["block"] == 128
+        with pytest.raises(rn.RmsnormError):
+            rn.set_option(rn.OPT_ROWS_PER_BLOCK, 3)
+        with pytest.raises(rn.RmsnormError):
+            rn.set_option(rn.OPT_PATH, 7)
+        with pytest.raises(rn.RmsnormError):
+            rn.set_option(99, 0)
+    finally:
+        rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
+        rn.set_option(rn.OPT_ROWS_PER_BLOCK, 0)

@@ -1,0 +1,277 @@
+"""The decode step's 327 norms, eager and as one captured HIP graph.
+
+Follows the testing discipline of Lecture 08 "Graph-resident decode":
+* section 4: one replay proves nothing -- several replays, each after the
+  descriptor table has been rewritten to point at different rows, each
+  compared byte for byte with the eager arm and the CPU oracle;
+* a negative control: the same check applied to a graph whose pointers were
+  frozen at capture (a plain by-value launch captured with torch) must fail
+  from the second replay, so the check can tell the difference;
+* section 5: A/A controls (eager vs eager, graph vs graph) before A/B;
+* section 2: widths are read from device memory, so a replay whose widths
+  differ from the capture-time widths is still exact;
+* section 3: a capture broken on purpose degrades to eager replay with the
+  same bits and reports it.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch  # imported at collection: the first import on a fresh machine is slow
+
+import oracle
+import workloads as wl
+from gpu_util import assert_bits_f32, dev, f32_host, say, to_dev_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rn():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import row_wise_rmsnorm_amd as m
+    m.set_option(m.OPT_PATH, m.PATH_AUTO)
+    m.set_option(m.OPT_ROWS_PER_BLOCK, 0)
+    return m
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+class Step:
+    """Device buffers for one decode step: `sets` alternative input sets per
+    norm, one output per norm, and a descriptor table pointing at set 0."""
+
+    def __init__(self, rn, rows, sets=3):
+        import torch
+        self.rn = rn
+        self.widths = [len(x) for x, _ in rows]
+        self.inputs = []  # inputs[s][i] = (x_host, w_host, x_dev, w_dev)
+        for s in range(sets):
+            cur = []
+            for i, (x, w) in enumerate(rows):
+                if s > 0:   # other sets: differently seeded rows of the same widths
+                    x, w = wl.misc_f32(900000 + 1000 * s + i, len(x))
+                cur.append((x, w, to_dev_f32(x), to_dev_f32(w)))
+            self.inputs.append(cur)
+        self.ys = [torch.empty(n, dtype=torch.float32, device=dev()) for n in self.widths]
+        self.table, _ = rn.make_table([(c[2], c[3], y) for c, y in zip(self.inputs[0], self.ys)])
+
+    def point_at(self, s, widths=None):
+        """Rewrite the table in place (same device buffer) to input set s,
+        optionally with other widths (prefixes of the same rows)."""
+        rows = []
+        for i, (c, y) in enumerate(zip(self.inputs[s], self.ys)):
+            n = self.widths[i] if widths is None else widths[i]
+            rows.append((c[2][:n], c[3][:n], y[:n]))
+        new, _ = self.rn.make_table(rows)
+        self.table.copy_(new)
+        sync()
+
+    def clear_outputs(self):
+        for y in self.ys:
+            y.fill_(float("nan"))
+        sync()
+
+    def outputs(self):
+        return [f32_host(y) for y in self.ys]
+
+    def expected(self, s, widths=None):
+        out = []
+        for i, (x, w, _, _) in enumerate(self.inputs[s]):
+            n = len(x) if widths is None else widths[i]
+            out.append(oracle.row_f32(x[:n], w[:n], wl.EPS))
+        return out
+
+
+def compare(got, want, what):
+    for i, (g, w) in enumerate(zip(got, want)):
+        n = len(w)
+        assert_bits_f32(g[:n], w, f"{what}: norm {i}")
+
+
+@pytest.fixture(scope="module")
+def step(rn):
+    say("building the 327-norm decode step")
+    return Step(rn, wl.decode())
+
+
+def test_eager_sequence_matches_oracle(rn, step):
+    say("eager sequence")
+    step.point_at(0)
+    step.clear_outputs()
+    rn.rmsnorm_sequence_eager(step.table, step.widths, wl.EPS, rn.F32)
+    sync()
+    compare(step.outputs(), step.expected(0), "eager")
+
+
+def test_aa_eager_vs_eager(rn, step):
+    say("A/A eager")
+    step.point_at(1)
+    runs = []
+    for _ in range(2):
+        step.clear_outputs()
+        rn.rmsnorm_sequence_eager(step.table, step.widths, wl.EPS, rn.F32)
+        sync()
+        runs.append(step.outputs())
+    compare(runs[0], runs[1], "A/A eager")
+
+
+def test_graph_replays_follow_the_table(rn, step):
+    say("graph capture")
+    step.point_at(0)
+    g = rn.SequenceGraph(step.table, step.widths, wl.EPS, rn.F32)
+    assert g.status == rn.RMSN_OK, g.capture_error
+    assert not g.is_fallback()
+    assert g.node_count() == len(step.widths) == 327
+    previous = None
+    for rep, s in enumerate([0, 1, 2, 0, 2, 1, 1]):
+        step.point_at(s)
+        step.clear_outputs()
+        g.launch()
+        sync()
+        got = step.outputs()
+        compare(got, step.expected(s), f"replay {rep} (set {s})")
+        # eager on the same table gives the same bytes
+        step.clear_outputs()
+        rn.rmsnorm_sequence_eager(step.table, step.widths, wl.EPS, rn.F32)
+        sync()
+        compare(got, step.outputs(), f"replay {rep} vs eager")
+        if previous is not None and previous[0] == s:
+            compare(got, previous[1], f"A/A graph replay {rep}")
+        previous = (s, got)
+    g.destroy()
+
+
+def test_graph_replay_with_changed_widths(rn, step):
+    """Widths are loop bounds read from the table: replays with other
+    (smaller) widths than the capture-time ones are exact and write nothing
+    past the new width; crossing below a register bucket streams the row."""
+    say("graph replay with changed widths")
+    step.point_at(0)
+    g = rn.SequenceGraph(step.table, step.widths, wl.EPS, rn.F32)
+    assert g.status == rn.RMSN_OK
+    gen = np.random.Generator(np.random.PCG64(4))
+    for rep in range(3):
+        widths = [int(gen.integers(1, n + 1)) for n in step.widths]
+        step.point_at(rep % 3, widths=widths)
+        step.clear_outputs()
+        g.launch()
+        sync()
+        got = step.outputs()
+        want = step.expected(rep % 3, widths=widths)
+        compare(got, want, f"changed widths replay {rep}")
+        for i, (y, n) in enumerate(zip(got, widths)):
+            assert np.isnan(y[n:]).all(), f"norm {i} wrote past its width"
+    step.point_at(0)
+    g.destroy()
+
+
+def test_graph_rows_can_be_wider_than_capture(rn):
+    """A node captured at width 512 replays a row of width 9000 exactly."""
+    import torch
+    say("replay wider than capture")
+    x, w = wl.misc_f32(77, 9000)
+    xd, wd = to_dev_f32(x), to_dev_f32(w)
+    y = torch.empty(9000, dtype=torch.float32, device=dev())
+    table, _ = rn.make_table([(xd[:512], wd[:512], y[:512])])
+    g = rn.SequenceGraph(table, [512], wl.EPS, rn.F32)
+    assert g.status == rn.RMSN_OK
+    new, _ = rn.make_table([(xd, wd, y)])
+    table.copy_(new)
+    y.fill_(float("nan"))
+    g.launch()
+    sync()
+    assert_bits_f32(f32_host(y), oracle.row_f32(x, w, wl.EPS), "wider than capture")
+    g.destroy()
+
+
+def test_negative_control_frozen_pointers(rn, step):
+    """A graph that froze its row pointers at capture (by-value launches
+    captured with torch) passes replay 1 and fails the same check once the
+    rows change -- the check has discriminating power."""
+    import torch
+    say("negative control: frozen pointers")
+    k = 6
+    step.point_at(0)
+    ys = step.ys[:k]
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s_cap):
+        # warm up outside capture, then capture by-value launches of set 0
+        for i in range(k):
+            c = step.inputs[0][i]
+            rn.rmsnorm_f32(c[2], c[3], wl.EPS, out=ys[i])
+        torch.cuda.current_stream().synchronize()
+        with torch.cuda.graph(graph, stream=s_cap):
+            for i in range(k):
+                c = step.inputs[0][i]
+                rn.rmsnorm_f32(c[2], c[3], wl.EPS, out=ys[i])
+    torch.cuda.current_stream().wait_stream(s_cap)
+    sync()
+    failures = []
+    for rep, s in enumerate([0, 1, 2]):
+        for y in ys:
+            y.fill_(float("nan"))
+        sync()
+        graph.replay()
+        sync()
+        want = step.expected(s)[:k]
+        ok = all(np.array_equal(f32_host(y).view(np.uint32), w.view(np.uint32))
+                 for y, w in zip(ys, want))
+        failures.append(not ok)
+    assert failures == [False, True, True], failures
+
+
+def test_forced_capture_failure_falls_back_to_eager(rn, step):
+    say("forced capture failure")
+    step.point_at(2)
+    os.environ["RMSN_TEST_BREAK_CAPTURE"] = "1"
+    try:
+        g = rn.SequenceGraph(step.table, step.widths, wl.EPS, rn.F32)
+    finally:
+        del os.environ["RMSN_TEST_BREAK_CAPTURE"]
+    assert g.status == rn.RMSN_ECAPTURE
+    assert "capture" in g.capture_error.lower()
+    assert g.is_fallback()
+    assert g.node_count() == 0
+    for rep in range(3):
+        step.point_at((2 + rep) % 3)
+        step.clear_outputs()
+        g.launch()
+        sync()
+        compare(step.outputs(), step.expected((2 + rep) % 3), f"fallback replay {rep}")
+    g.destroy()
+    # the library still captures normally afterwards
+    g2 = rn.SequenceGraph(step.table, step.widths, wl.EPS, rn.F32)
+    assert g2.status == rn.RMSN_OK
+    g2.destroy()
+    step.point_at(0)
+
+
+def test_graph_of_bf16_rows(rn):
+    import torch
+    from gpu_util import assert_bits_bf16, bf16_host, to_dev_bf16
+    say("bf16 sequence graph")
+    rows = []
+    for i, n in enumerate([7168, 1536, 512, 100, 7168]):
+        x, w = wl.misc_f32(300 + i, n)
+        rows.append((wl.to_bf16_bits(x), wl.to_bf16_bits(w)))
+    xs = [to_dev_bf16(x) for x, _ in rows]
+    ws = [to_dev_bf16(w) for _, w in rows]
+    ys = [torch.empty_like(t) for t in xs]
+    table, widths = rn.make_table(list(zip(xs, ws, ys)))
+    g = rn.SequenceGraph(table, widths, wl.EPS, rn.BF16)
+    assert g.status == rn.RMSN_OK
+    for rep in range(3):
+        for y in ys:
+            y.zero_()
+        g.launch()
+        sync()
+        for (x, w), y in zip(rows, ys):
+            assert_bits_bf16(bf16_host(y), oracle.row_bf16(x, w, wl.EPS), f"bf16 replay {rep}")
+    g.destroy()
