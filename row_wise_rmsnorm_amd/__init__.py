@@ -153,9 +153,12 @@ def rmsnorm_batched_rows(x, w, eps, out=None, stream=None):
     y = _out_like(x, out)
     if y.stride(1) != 1:
         raise ValueError("out must have unit stride along rows")
-    _check(_lib.rmsnorm_batched_rows(_dtype_code(x), x.data_ptr(), x.stride(0), w.data_ptr(),
-                                     y.data_ptr(), y.stride(0), x.shape[0], x.shape[1],
-                                     float(eps), _stream_ptr(stream)))
+    rows, n = x.shape
+    # a single row's stride is never used; torch may report 0 for a size-1 axis
+    xs = x.stride(0) if rows > 1 else n
+    ys = y.stride(0) if rows > 1 else n
+    _check(_lib.rmsnorm_batched_rows(_dtype_code(x), x.data_ptr(), xs, w.data_ptr(),
+                                     y.data_ptr(), ys, rows, n, float(eps), _stream_ptr(stream)))
     return y
 
 
@@ -169,7 +172,7 @@ def make_table(rows, device=None):
     for x, w, y in rows:
         buf += struct.pack("<QQQq", x.data_ptr(), w.data_ptr(), y.data_ptr(), x.numel())
         widths.append(int(x.numel()))
-    host = torch.frombuffer(bytes(buf), dtype=torch.uint8)
+    host = torch.frombuffer(buf, dtype=torch.uint8)
     dev = device if device is not None else rows[0][0].device
     return host.to(dev), widths
 
