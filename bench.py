@@ -112,9 +112,20 @@ def bench_prefill(rn, torch, np, wl, steps, warmup):
     reps = []
     for _ in range(5):
         reps.append(1000.0 * elapsed_ms(step, steps) / steps)
-    # warm arm: one buffer set, so the last-level cache may hold part of it
+    # warm arms: one buffer set, so the last-level cache may hold part of it;
+    # with the automatic (streaming) plan and with default caching forced
     warm = 1000.0 * elapsed_ms(lambda i: rn.rmsnorm_batched_rows(xs[0], w, eps, out=ys[0]),
                                steps) / steps
+    rn.set_option(rn.OPT_STREAMING, 0)
+    try:
+        warm_cached = 1000.0 * elapsed_ms(
+            lambda i: rn.rmsnorm_batched_rows(xs[0], w, eps, out=ys[0]), steps) / steps
+        rot_cached = 1000.0 * elapsed_ms(step, steps) / steps
+    finally:
+        rn.set_option(rn.OPT_STREAMING, -1)
+    # a plain device copy of the same bytes (x read, y written), rotated the
+    # same way: the practical bandwidth ceiling of this traffic pattern
+    copy_us = 1000.0 * elapsed_ms(lambda i: ys[i % ROTATE].copy_(xs[i % ROTATE]), steps) / steps
     # spot parity of the timed output against the oracle (first/last rows)
     import oracle
     torch.cuda.synchronize()
@@ -127,9 +138,32 @@ def bench_prefill(rn, torch, np, wl, steps, warmup):
         "gbs": algo_bytes / (us * 1e-6) / 1e9,
         "reps_us": stats(reps), "warm_us": warm,
         "warm_gbs": algo_bytes / (warm * 1e-6) / 1e9,
+        "warm_cached_us": warm_cached, "rotated_cached_us": rot_cached,
+        "copy_us": copy_us, "copy_gbs": (rows * n * 4) / (copy_us * 1e-6) / 1e9,
         "rows_per_s": rows / (us * 1e-6), "spot_parity": parity,
         "host": (xb, wb),
     }
+
+
+def bench_prefill_only(rn, torch, np, wl, steps, warmup):
+    """Only the rotated, timed prefill launches (for kernel-trace and counter
+    runs, so the profiler's average covers exactly the launches timed here)."""
+    rows, n = wl.PREFILL_SHAPE
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    xs = [torch.randn(rows, n, device=dev, generator=g).to(torch.bfloat16) for _ in range(ROTATE)]
+    w = (1.0 + 0.1 * torch.randn(n, device=dev, generator=g)).to(torch.bfloat16)
+    ys = [torch.empty_like(xs[0]) for _ in range(ROTATE)]
+    eps = float(wl.EPS)
+    step = lambda i: rn.rmsnorm_batched_rows(xs[i % ROTATE], w, eps, out=ys[i % ROTATE])
+    for i in range(warmup):
+        step(i)
+    us = 1000.0 * elapsed_ms(step, steps) / steps
+    algo = rows * n * 4 + n * 2
+    return {"prefill_only": True, "launches_timed": steps, "warmup_launches": warmup,
+            "us_per_launch": us, "gbs": algo / (us * 1e-6) / 1e9,
+            "plan": rn.plan_query(rn.BF16, rows, n)}
 
 
 def bench_single(rn, torch, np, wl):
@@ -300,6 +334,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true")
+    ap.add_argument("--sections", default="prefill,single,batch64,decode",
+                    help="comma list of prefill,single,batch64,decode (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
@@ -318,10 +354,27 @@ def main():
         profile_kernels(rn, torch, np, wl)
         return
 
+    sections = set(args.sections.split(","))
+    if "prefill" in sections and sections != {"prefill", "single", "batch64", "decode"}:
+        # a profiling run of the prefill kernel alone: only the timed launches
+        pre = bench_prefill_only(rn, torch, np, wl, args.steps, args.warmup)
+        print(json.dumps(pre), flush=True)
+        return
+    if sections != {"prefill", "single", "batch64", "decode"}:
+        out = {}
+        if "single" in sections:
+            out["single_norm"] = bench_single(rn, torch, np, wl)
+        if "batch64" in sections:
+            out["batch64"] = bench_batch64(rn, torch, np, wl)
+        if "decode" in sections:
+            out["decode_step"] = bench_decode(rn, torch, np, wl, args.decode_steps)
+        print(json.dumps(out), flush=True)
+        return
     torch.cuda.synchronize()
     t_start = time.time()
     pre = bench_prefill(rn, torch, np, wl, args.steps, args.warmup)
-    log(f"prefill {pre['us_per_launch']:.2f} us  {pre['gbs']:.0f} GB/s")
+    log(f"prefill {pre['us_per_launch']:.2f} us  {pre['gbs']:.0f} GB/s "
+        f"(copy of the same bytes {pre['copy_us']:.2f} us)")
     single = bench_single(rn, torch, np, wl)
     log(f"single {single['us_back_to_back']:.2f} us back-to-back")
     b64 = bench_batch64(rn, torch, np, wl)
@@ -368,6 +421,11 @@ def main():
         "prefill": {
             "us_reps": pre["reps_us"], "warm_us": round(pre["warm_us"], 3),
             "warm_gbs": round(pre["warm_gbs"], 1), "rows_per_s": pre["rows_per_s"],
+            "warm_cached_us": round(pre["warm_cached_us"], 3),
+            "rotated_cached_us": round(pre["rotated_cached_us"], 3),
+            "copy_reference_us": round(pre["copy_us"], 3),
+            "copy_reference_gbs": round(pre["copy_gbs"], 1),
+            "fraction_of_copy": round(pre["copy_us"] / pre["us_per_launch"], 4),
             "spot_parity_vs_oracle": pre["spot_parity"],
         },
         "single_norm": single,

@@ -153,9 +153,11 @@ typedef struct rmsn_plan_info {
     int32_t path;            /* one of RMSN_PATH_*                                */
     int32_t chunks;          /* 256-element chunks a lane's registers hold (0:
                                 streaming)                                        */
-    int32_t rows_per_block;  /* rows per workgroup                                */
+    int32_t rows_per_block;  /* rows (wavefronts) per workgroup on WAVE, else 1   */
     int32_t block;           /* threads per workgroup                             */
     int64_t grid;            /* workgroups                                        */
+    int32_t streaming;       /* WAVE: 1 = non-temporal loads of x / stores of y   */
+    int32_t reserved;
 } rmsn_plan_info;
 
 /* The launch the library would use for `rows` rows of width n whose row and
@@ -166,15 +168,20 @@ int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int aligned, rmsn_pla
 
 /* Process-wide overrides, for proving that code paths give identical bits
  * (Lecture 04 section 6: one binary, switchable arms). Defaults come from the
- * environment at first use (RMSN_PATH, RMSN_ROWS_PER_BLOCK), else automatic.
+ * environment at first use, else automatic.
  *   RMSN_OPT_PATH:           -1 automatic, or an RMSN_PATH_* value; a path a
  *                            launch is not eligible for (WAVE on unaligned
  *                            rows or n > 8192, BLOCK with n > 8192) falls
  *                            back to the automatic choice
- *   RMSN_OPT_ROWS_PER_BLOCK:  0 automatic, else 1, 2 or 4 (WAVE path only)
+ *   RMSN_OPT_ROWS_PER_BLOCK:  0 automatic, else 4 or 8 rows (wavefronts) per
+ *                            workgroup sharing one LDS copy of w (WAVE path)
+ *   RMSN_OPT_STREAMING:      -1 automatic (on when x + y of the launch reach
+ *                            64 MiB), 0 off, 1 on: non-temporal loads of x and
+ *                            stores of y (WAVE path)
  * Returns RMSN_EINVAL for an unknown key or value. Not synchronised with
- * launches on other threads. */
-enum { RMSN_OPT_PATH = 1, RMSN_OPT_ROWS_PER_BLOCK = 2 };
+ * launches on other threads. Environment: RMSN_PATH, RMSN_ROWS_PER_BLOCK,
+ * RMSN_STREAMING. */
+enum { RMSN_OPT_PATH = 1, RMSN_OPT_ROWS_PER_BLOCK = 2, RMSN_OPT_STREAMING = 3 };
 int rmsnorm_set_option(int key, int value);
 int rmsnorm_get_option(int key, int* value);
 

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "librmsnorm_amd.so")
 RMSN_OK, RMSN_EINVAL, RMSN_EHIP, RMSN_ECAPTURE, RMSN_ENOMEM = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM = -1, 0, 1, 2
-OPT_PATH, OPT_ROWS_PER_BLOCK = 1, 2
+OPT_PATH, OPT_ROWS_PER_BLOCK, OPT_STREAMING = 1, 2, 3
 MAX_N = 1 << 24
 DESC_BYTES = 32
 
@@ -35,7 +35,8 @@ class RmsnormError(RuntimeError):
 class _PlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("chunks", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("block", ctypes.c_int32),
-                ("grid", ctypes.c_int64)]
+                ("grid", ctypes.c_int64), ("streaming", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 def _load():
@@ -236,7 +237,7 @@ def plan_query(dtype, rows, n, aligned=True):
     _check(_lib.rmsnorm_plan_query(int(dtype), int(rows), int(n), 1 if aligned else 0,
                                    ctypes.byref(info)))
     return {"path": info.path, "chunks": info.chunks, "rows_per_block": info.rows_per_block,
-            "block": info.block, "grid": info.grid}
+            "streaming": info.streaming, "block": info.block, "grid": info.grid}
 
 
 def set_option(key, value):

@@ -311,6 +311,8 @@ int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int aligned, rmsn_pla
     out->rows_per_block = p.rows_per_block;
     out->block = p.block;
     out->grid = p.grid;
+    out->streaming = p.streaming;
+    out->reserved = 0;
     return RMSN_OK;
 }
 

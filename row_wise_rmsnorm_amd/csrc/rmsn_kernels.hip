@@ -43,6 +43,23 @@
 namespace rmsn {
 namespace {
 
+// Global-memory (address space 1) byte pointers. A wave-uniform one held in
+// scalar registers becomes the scalar base of a load's address.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) char* gptr_c;
+typedef __attribute__((address_space(1))) char* gptr;
+
+__device__ __forceinline__ gptr_c scalar_gptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (gptr_c)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ gptr scalar_gptr(void* p) {
+    return (gptr)scalar_gptr(static_cast<const void*>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Element access. bf16 values are their 16-bit patterns; widening is exact.
 
@@ -66,6 +83,20 @@ template <typename T> struct Quad;
 
 template <> struct Quad<float> {
     using raw = float4;
+    template <bool NT>
+    static __device__ __forceinline__ raw gload(gptr_c p) {
+        auto* a = reinterpret_cast<const __attribute__((address_space(1))) f32x4*>(p);
+        const f32x4 v = NT ? __builtin_nontemporal_load(a) : *a;
+        return make_float4(v.x, v.y, v.z, v.w);
+    }
+    template <bool NT>
+    static __device__ __forceinline__ void gstore(gptr p, const float v[4]) {
+        f32x4 q;
+        q.x = v[0]; q.y = v[1]; q.z = v[2]; q.w = v[3];
+        auto* a = reinterpret_cast<__attribute__((address_space(1))) f32x4*>(p);
+        if (NT) __builtin_nontemporal_store(q, a);
+        else *a = q;
+    }
     static __device__ __forceinline__ raw load(const float* p) {
         return *reinterpret_cast<const float4*>(p);
     }
@@ -90,6 +121,21 @@ template <> struct Quad<float> {
 
 template <> struct Quad<uint16_t> {
     using raw = uint2;
+    template <bool NT>
+    static __device__ __forceinline__ raw gload(gptr_c p) {
+        auto* a = reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(p);
+        const u32x2 v = NT ? __builtin_nontemporal_load(a) : *a;
+        return make_uint2(v.x, v.y);
+    }
+    template <bool NT>
+    static __device__ __forceinline__ void gstore(gptr p, const float v[4]) {
+        u32x2 q;
+        q.x = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
+        q.y = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+        auto* a = reinterpret_cast<__attribute__((address_space(1))) u32x2*>(p);
+        if (NT) __builtin_nontemporal_store(q, a);
+        else *a = q;
+    }
     static __device__ __forceinline__ raw load(const uint16_t* p) {
         return *reinterpret_cast<const uint2*>(p);
     }
@@ -179,98 +225,125 @@ constexpr int prev_bucket(int nch) {
          : nch <= 12 ? 8 : nch <= 16 ? 12 : nch <= 20 ? 16 : nch <= 24 ? 20 : nch <= 28 ? 24 : 28;
 }
 
-// Chunks whose weights the WAVE apply phase loads at once.
-template <typename T>
-constexpr int wave_apply_group() { return sizeof(T) == 4 ? 1 : 2; }
-
 // Resident wavefronts per SIMD the WAVE kernels are compiled for: the row's
-// registers (4 values per chunk; bf16 packed two per VGPR), one weight group,
-// and a few for addresses and temporaries, out of 512 VGPRs per SIMD lane.
-template <typename T, int NCH>
+// registers (4 values per chunk; bf16 packed two per VGPR), the ragged-tail
+// chunk unless the width is exactly 256 * NCH, and a few for chains,
+// addresses and temporaries, out of 512 VGPRs per SIMD lane.
+template <typename T, int NCH, bool EXACT>
 constexpr int wave_occupancy() {
     constexpr int q = sizeof(T) == 4 ? 4 : 2;
-    constexpr int regs = (NCH + wave_apply_group<T>()) * q + (sizeof(T) == 4 ? 16 : 8);
+    constexpr int regs = NCH * q + (EXACT ? 0 : q) + 16 + (sizeof(T) == 4 ? 8 : 0);
     constexpr int w = 512 / ((regs + 7) / 8 * 8);
     return w > 8 ? 8 : (w < 1 ? 1 : w);
 }
 
-// Requires 256 * prev_bucket(NCH) < n <= 256 * NCH (guaranteed by the plan).
-template <typename T, int NCH>
-__device__ __forceinline__ void row_wave(const T* x, const T* __restrict__ w, T* y, int n,
-                                         float eps, int lane) {
+// One row held by one wavefront: load() issues every load of the row, finish()
+// reduces, normalises and stores it. NT: non-temporal (streaming) hints on the
+// row's loads and stores, for batches too large for the caches to help.
+// Requires 256 * prev_bucket(NCH) < n <= 256 * NCH, and n == 256 * NCH when
+// EXACT (both guaranteed by the plan).
+template <typename T, int NCH, bool EXACT, bool NT>
+struct WaveRow {
     using Q = Quad<T>;
-    constexpr int MINF = prev_bucket(NCH);
-    // Chunks [0, full) are complete; chunk `full` is the ragged tail when n is
-    // not a multiple of 256. `full` is wave-uniform: the tests are scalar.
-    const int full = n >> 8;
-    const int lo = lane << 2;
+    static constexpr int MINF = EXACT ? NCH : prev_bucket(NCH);
+    // Addresses are a scalar base per 4 KB of the row (the reach of the
+    // instruction's immediate offset) plus an unsigned per-lane byte offset, so
+    // every load and store uses the scalar-base addressing mode instead of a
+    // 64-bit address pair per lane.
+    static constexpr uint32_t chunk_bytes = 256u * sizeof(T);
+    static constexpr int per_base = 4096 / chunk_bytes;
+
     typename Q::raw xr[NCH];
+    typename Q::raw xt;
+
+    // Chunks [0, full) are complete; chunk `full` is the ragged tail when n is
+    // not a multiple of 256. `full` is wave-uniform, so the tests are scalar
+    // branches; chunks below MINF need none (none at all when EXACT).
+    static __device__ __forceinline__ int full_chunks(int n) { return EXACT ? NCH : (n >> 8); }
+
+    __device__ __forceinline__ void load(const T* x, int n, int lane) {
+        const int full = full_chunks(n);
+        const uint32_t lane_bytes = (uint32_t)lane * (uint32_t)(4 * sizeof(T));
 #pragma unroll
-    for (int k = 0; k < NCH; ++k)
-        if (k < MINF || k < full) xr[k] = Q::load(x + (k << 8) + lo);
-    const int et = (full << 8) + lo;  // this lane's first element of the tail chunk
-    const typename Q::raw xt = (n & 255) ? Q::load_tail(x, et, n) : Q::zero();
-    // Lane chains in ascending chunk order; the tail chunk comes last and reads
-    // +0 past the row (fmaf(0, 0, p) == p for p >= +0).
-    float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
+        for (int k = 0; k < NCH; ++k) {
+            if (k < MINF || k < full) {
+                gptr_c base =
+                    scalar_gptr(reinterpret_cast<const char*>(x) + (k / per_base) * 4096);
+                xr[k] = Q::template gload<NT>(base + lane_bytes +
+                                              (uint32_t)(k % per_base) * chunk_bytes);
+            }
+        }
+        xt = Q::zero();
+        if (!EXACT && (n & 255)) xt = Q::load_tail(x, (full << 8) + (lane << 2), n);
+    }
+
+    // wl: the weight row staged in LDS as quads (quad q = elements 4q..4q+3);
+    // w: the same row in global memory, read only for the ragged tail.
+    __device__ __forceinline__ void finish(const T* __restrict__ w,
+                                           const typename Q::raw* wl, T* y, int n, float eps,
+                                           int lane) {
+        const int full = full_chunks(n);
+        const uint32_t lane_bytes = (uint32_t)lane * (uint32_t)(4 * sizeof(T));
+        // Lane chains in ascending chunk order; the tail chunk comes last and
+        // reads +0 past the row (fmaf(0, 0, p) == p for p >= +0). The per-chunk
+        // scheduling barriers keep each chunk's widening next to its four fmas,
+        // so widened copies of later chunks are never live with the packed row.
+        __builtin_amdgcn_sched_barrier(0);
+        float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-        if (k < MINF || k < full) {
+        for (int k = 0; k < NCH; ++k) {
+            if (k < MINF || k < full) {
+                float v[4];
+                Q::unpack(xr[k], v);
+                p0 = fmaf(v[0], v[0], p0);
+                p1 = fmaf(v[1], v[1], p1);
+                p2 = fmaf(v[2], v[2], p2);
+                p3 = fmaf(v[3], v[3], p3);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!EXACT) {
             float v[4];
-            Q::unpack(xr[k], v);
+            Q::unpack(xt, v);
             p0 = fmaf(v[0], v[0], p0);
             p1 = fmaf(v[1], v[1], p1);
             p2 = fmaf(v[2], v[2], p2);
             p3 = fmaf(v[3], v[3], p3);
         }
-    }
-    {
-        float v[4];
-        Q::unpack(xt, v);
-        p0 = fmaf(v[0], v[0], p0);
-        p1 = fmaf(v[1], v[1], p1);
-        p2 = fmaf(v[2], v[2], p2);
-        p3 = fmaf(v[3], v[3], p3);
-    }
-    const float inv = inverse_rms(wave_sumsq(p0, p1, p2, p3), n, eps);
+        const float inv = inverse_rms(wave_sumsq(p0, p1, p2, p3), n, eps);
 #pragma unroll
-    for (int k = 0; k < NCH; ++k)
-        if (k < MINF || k < full) opaque(xr[k]);
-    // Apply in groups of G chunks: the group's weight loads are issued
-    // together, then its outputs are stored. The scheduling barrier keeps the
-    // compiler from hoisting every weight load to the top, which would hold
-    // the whole weight row in registers and cut the resident wavefronts.
-    constexpr int G = wave_apply_group<T>();
+        for (int k = 0; k < NCH; ++k)
+            if (k < MINF || k < full) opaque(xr[k]);
+        // Apply two chunks at a time. The scheduling barrier stops the compiler
+        // from hoisting every LDS weight read to the top (LDS cannot alias the
+        // global stores), which would hold the whole weight row in registers.
 #pragma unroll
-    for (int k0 = 0; k0 < NCH; k0 += G) {
-        typename Q::raw wr[G];
+        for (int k0 = 0; k0 < NCH; k0 += 2) {
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int k = k0 + j;
-            if (k < NCH && (k < MINF || k < full)) wr[j] = Q::load(w + (k << 8) + lo);
-        }
+            for (int k = k0; k < k0 + 2 && k < NCH; ++k) {
+                if (k < MINF || k < full) {
+                    float v[4], wv[4], o[4];
+                    Q::unpack(xr[k], v);
+                    Q::unpack(wl[(k << 6) + lane], wv);
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int k = k0 + j;
-            if (k < NCH && (k < MINF || k < full)) {
-                float v[4], wv[4], o[4];
-                Q::unpack(xr[k], v);
-                Q::unpack(wr[j], wv);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = (v[i] * inv) * wv[i];
-                Q::store(y + (k << 8) + lo, o);
+                    for (int i = 0; i < 4; ++i) o[i] = (v[i] * inv) * wv[i];
+                    gptr base = scalar_gptr(reinterpret_cast<char*>(y) + (k / per_base) * 4096);
+                    Q::template gstore<NT>(base + lane_bytes +
+                                               (uint32_t)(k % per_base) * chunk_bytes, o);
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if (n & 255) {
-        float v[4];
-        Q::unpack(xt, v);
+        if (!EXACT && (n & 255)) {
+            const int et = (full << 8) + (lane << 2);
+            float v[4];
+            Q::unpack(xt, v);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (et + i < n) put(y + et + i, (v[i] * inv) * widen(w[et + i]));
+            for (int i = 0; i < 4; ++i)
+                if (et + i < n) put(y + et + i, (v[i] * inv) * widen(w[et + i]));
+        }
     }
-}
+};
 
 // ---------------------------------------------------------------------------
 // BLOCK / STREAM layout: 256 threads per row, thread l = chain l, wave g = group g.
@@ -342,15 +415,28 @@ __device__ __forceinline__ void row_block(const T* x, const T* __restrict__ w, T
 // ---------------------------------------------------------------------------
 // Kernels.
 
-template <typename T, int NCH, int RPB>
-__global__ __launch_bounds__(64 * RPB, (wave_occupancy<T, NCH>())) void k_rows_wave(const T* x, int64_t xs,
-                                                        const T* __restrict__ w, T* y,
-                                                        int64_t ys, int64_t rows, int n,
-                                                        float eps) {
+// WAVE layout: RPB rows per workgroup, one per wavefront (EXACT: n is exactly
+// 256 * NCH, so no chunk is partial; NT: streaming hints). The workgroup first
+// stages the shared weight row in LDS (dynamic LDS of (n/4) quads), so each
+// row reads x from HBM and w from LDS instead of every row re-reading w
+// through L2.
+template <typename T, int NCH, int RPB, bool EXACT, bool NT>
+__global__ __launch_bounds__(64 * RPB, (wave_occupancy<T, NCH, EXACT>())) void k_rows_wave(
+    const T* x, int64_t xs, const T* __restrict__ w, T* y, int64_t ys, int64_t rows, int n,
+    float eps) {
+    using Q = Quad<T>;
+    extern __shared__ __align__(16) unsigned char wave_smem[];
+    typename Q::raw* wl = reinterpret_cast<typename Q::raw*>(wave_smem);
+    const int nq = n >> 2;  // complete quads of the weight row
+    for (int q = threadIdx.x; q < nq; q += 64 * RPB) wl[q] = Q::load(w + (q << 2));
+    __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t r = (int64_t)blockIdx.x * RPB + wave;
     if (r >= rows) return;
-    row_wave<T, NCH>(x + r * xs, w, y + r * ys, n, eps, threadIdx.x & 63);
+    const int lane = threadIdx.x & 63;
+    WaveRow<T, NCH, EXACT, NT> row;
+    row.load(x + r * xs, n, lane);
+    row.finish(w, wl, y + r * ys, n, eps, lane);
 }
 
 template <typename T, int NCH>
@@ -397,23 +483,35 @@ hipError_t launch_wave_t(const Plan& p, const void* x, int64_t xs, const void* w
     const T* wp = static_cast<const T*>(w);
     T* yp = static_cast<T*>(y);
     const dim3 grid((unsigned)p.grid), block((unsigned)p.block);
-#define RMSN_CASE(C)                                                                        \
-    case C:                                                                                 \
-        if (p.rows_per_block == 4)                                                          \
-            hipLaunchKernelGGL((k_rows_wave<T, C, 4>), grid, block, 0, s, xp, xs, wp, yp,  \
-                               ys, rows, n, eps);                                           \
-        else if (p.rows_per_block == 2)                                                     \
-            hipLaunchKernelGGL((k_rows_wave<T, C, 2>), grid, block, 0, s, xp, xs, wp, yp,  \
-                               ys, rows, n, eps);                                           \
-        else                                                                                \
-            hipLaunchKernelGGL((k_rows_wave<T, C, 1>), grid, block, 0, s, xp, xs, wp, yp,  \
-                               ys, rows, n, eps);                                           \
+    const size_t lds = (size_t)(n >> 2) * sizeof(typename Quad<T>::raw);
+    const bool exact = n == 256 * p.chunks;
+#define RMSN_RPB(C, R)                                                                        \
+    if (exact && p.streaming)                                                                 \
+        hipLaunchKernelGGL((k_rows_wave<T, C, R, true, true>), grid, block, lds, s, xp, xs,   \
+                           wp, yp, ys, rows, n, eps);                                         \
+    else if (exact)                                                                           \
+        hipLaunchKernelGGL((k_rows_wave<T, C, R, true, false>), grid, block, lds, s, xp, xs,  \
+                           wp, yp, ys, rows, n, eps);                                         \
+    else if (p.streaming)                                                                     \
+        hipLaunchKernelGGL((k_rows_wave<T, C, R, false, true>), grid, block, lds, s, xp, xs,  \
+                           wp, yp, ys, rows, n, eps);                                         \
+    else                                                                                      \
+        hipLaunchKernelGGL((k_rows_wave<T, C, R, false, false>), grid, block, lds, s, xp, xs, \
+                           wp, yp, ys, rows, n, eps)
+#define RMSN_CASE(C)                                                   \
+    case C:                                                            \
+        switch (p.rows_per_block) {                                    \
+            case 8: RMSN_RPB(C, 8); break;                             \
+            case 4: RMSN_RPB(C, 4); break;                             \
+            default: return hipErrorInvalidValue;                      \
+        }                                                              \
         break;
     switch (p.chunks) {
         RMSN_FOR_BUCKETS(RMSN_CASE)
         default: return hipErrorInvalidValue;
     }
 #undef RMSN_CASE
+#undef RMSN_RPB
     return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ thread_local char g_err[512] = "";
 
 std::atomic<int> g_path{-2};   // -2 = not yet read from the environment
 std::atomic<int> g_rpb{-2};
+std::atomic<int> g_stream{-2};
 
 int env_int(const char* name, int dflt) {
     const char* s = std::getenv(name);
@@ -31,7 +32,8 @@ int env_int(const char* name, int dflt) {
 bool valid_path(int v) {
     return v == -1 || v == RMSN_PATH_WAVE || v == RMSN_PATH_BLOCK || v == RMSN_PATH_STREAM;
 }
-bool valid_rpb(int v) { return v == 0 || v == 1 || v == 2 || v == 4; }
+bool valid_rpb(int v) { return v == 0 || v == 4 || v == 8; }
+bool valid_streaming(int v) { return v == -1 || v == 0 || v == 1; }
 
 // Byte ranges [a, a+la) and [b, b+lb) intersect.
 bool overlaps(uintptr_t a, uint64_t la, uintptr_t b, uint64_t lb) {
@@ -70,6 +72,16 @@ int option_rows_per_block() {
     return v;
 }
 
+int option_streaming() {
+    int v = g_stream.load(std::memory_order_relaxed);
+    if (v == -2) {
+        v = env_int("RMSN_STREAMING", -1);
+        if (!valid_streaming(v)) v = -1;
+        g_stream.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 int set_option(int key, int value) {
     if (key == RMSN_OPT_PATH) {
         if (!valid_path(value)) {
@@ -82,10 +94,18 @@ int set_option(int key, int value) {
     }
     if (key == RMSN_OPT_ROWS_PER_BLOCK) {
         if (!valid_rpb(value)) {
-            set_error("rmsnorm_set_option: rows per block must be 0, 1, 2 or 4, got %d", value);
+            set_error("rmsnorm_set_option: rows per block must be 0, 4 or 8, got %d", value);
             return RMSN_EINVAL;
         }
         g_rpb.store(value, std::memory_order_relaxed);
+        return RMSN_OK;
+    }
+    if (key == RMSN_OPT_STREAMING) {
+        if (!valid_streaming(value)) {
+            set_error("rmsnorm_set_option: streaming must be -1, 0 or 1, got %d", value);
+            return RMSN_EINVAL;
+        }
+        g_stream.store(value, std::memory_order_relaxed);
         return RMSN_OK;
     }
     set_error("rmsnorm_set_option: unknown key %d", key);
@@ -99,6 +119,7 @@ int get_option(int key, int* value) {
     }
     if (key == RMSN_OPT_PATH) { *value = option_path(); return RMSN_OK; }
     if (key == RMSN_OPT_ROWS_PER_BLOCK) { *value = option_rows_per_block(); return RMSN_OK; }
+    if (key == RMSN_OPT_STREAMING) { *value = option_streaming(); return RMSN_OK; }
     set_error("rmsnorm_get_option: unknown key %d", key);
     return RMSN_EINVAL;
 }
@@ -111,9 +132,14 @@ int chunk_bucket(int64_t n) {
 }
 
 int auto_rows_per_block(int64_t rows) {
-    // Four rows (wavefronts) per workgroup quarter the workgroups the
-    // dispatcher has to issue while every CU still holds many wavefronts.
-    return rows >= 4 * kWaveMinRows ? 4 : 1;
+    // The workgroup's wavefronts share one LDS copy of the weight row: eight
+    // for large batches, four while eight would leave CUs without a
+    // workgroup (fewer than 256 * 8 rows).
+    return rows >= 8 * 256 ? 8 : 4;
+}
+
+bool auto_streaming(int dtype, int64_t rows, int64_t n) {
+    return rows * n * 2 * elem_bytes(dtype) >= kStreamBytes;
 }
 
 int make_plan(int dtype, int64_t rows, int64_t n, bool aligned, Plan* out) {
@@ -150,13 +176,16 @@ int make_plan(int dtype, int64_t rows, int64_t n, bool aligned, Plan* out) {
     if (path == RMSN_PATH_WAVE) {
         int rpb = option_rows_per_block();
         if (rpb == 0) rpb = auto_rows_per_block(rows);
+        const int st = option_streaming();
         p.chunks = bucket;
         p.rows_per_block = rpb;
+        p.streaming = st < 0 ? (auto_streaming(dtype, rows, n) ? 1 : 0) : st;
         p.block = kWave * rpb;
         p.grid = (rows + rpb - 1) / rpb;
     } else {
         p.chunks = path == RMSN_PATH_BLOCK ? bucket : 0;
         p.rows_per_block = 1;
+        p.streaming = 0;
         p.block = kBlockThreads;
         p.grid = rows;
     }

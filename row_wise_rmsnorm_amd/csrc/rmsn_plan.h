@@ -21,12 +21,17 @@ constexpr int kNumBuckets = sizeof(kChunkBuckets) / sizeof(kChunkBuckets[0]);
 // Row counts from which the WAVE path is chosen automatically: below it a row
 // gets a whole workgroup (four wavefronts) so its loads spread over four SIMDs.
 constexpr int64_t kWaveMinRows = 1024;
+// Launch footprints (x read + y written) from which the WAVE path streams with
+// non-temporal hints: far beyond the 32 MB of L2 and a large share of the
+// 256 MB last-level cache, where keeping the rows cached cannot pay.
+constexpr int64_t kStreamBytes = 64ll << 20;
 
 struct Plan {
     int dtype;           // RMSN_F32 / RMSN_BF16
     int path;            // RMSN_PATH_WAVE / _BLOCK / _STREAM
     int chunks;          // kernel instance: a bucket, or 0 for streaming
-    int rows_per_block;  // rows per workgroup
+    int rows_per_block;  // wavefronts (= rows) per workgroup on the WAVE path, else 1
+    int streaming;       // WAVE path: non-temporal loads of x and stores of y
     int block;           // threads per workgroup
     int64_t grid;        // workgroups
 };
@@ -38,8 +43,9 @@ inline int vec_bytes(int dtype) { return 4 * elem_bytes(dtype); }
 // Smallest bucket holding ceil(n/256) chunks, or 0 if n needs more than kMaxChunks.
 int chunk_bucket(int64_t n);
 
-// Rows per workgroup on the WAVE path, chosen automatically.
+// Rows per workgroup and the streaming choice on the WAVE path, automatic.
 int auto_rows_per_block(int64_t rows);
+bool auto_streaming(int dtype, int64_t rows, int64_t n);
 
 // Plan a launch of `rows` rows of width n. `aligned`: every row's x and y and
 // the weight start on a vec_bytes(dtype) boundary. Returns RMSN_OK or
@@ -48,7 +54,8 @@ int make_plan(int dtype, int64_t rows, int64_t n, bool aligned, Plan* out);
 
 // Process-wide options (rmsnorm_set_option); read lazily from the environment.
 int option_path();            // -1 automatic, else an RMSN_PATH_* value
-int option_rows_per_block();  // 0 automatic, else 1/2/4
+int option_rows_per_block();  // 0 automatic, else 4 or 8
+int option_streaming();       // -1 automatic, 0 off, 1 on
 int set_option(int key, int value);
 int get_option(int key, int* value);
 

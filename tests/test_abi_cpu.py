@@ -127,12 +127,18 @@ def test_diag_validation(rn):
 # ---- planning -------------------------------------------------------------------
 
 def test_plan_paths_and_buckets(rn):
-    # many aligned rows: one wavefront per row, four rows per workgroup
+    # many aligned rows: one wavefront per row, eight rows per workgroup
+    # sharing one LDS copy of w; a 235 MB launch streams (non-temporal)
     p = rn.plan_query(rn.BF16, 8192, 7168, aligned=True)
-    assert p == {"path": rn.PATH_WAVE, "chunks": 28, "rows_per_block": 4, "block": 256, "grid": 2048}
+    assert p == {"path": rn.PATH_WAVE, "chunks": 28, "rows_per_block": 8, "streaming": 1,
+                 "block": 512, "grid": 1024}
+    # a 29 MB launch keeps the default cache policy; fewer than 2048 rows: 4 per workgroup
+    p = rn.plan_query(rn.BF16, 1024, 7168, aligned=True)
+    assert p["streaming"] == 0 and p["rows_per_block"] == 4 and p["grid"] == 256
     # few rows: a 256-thread workgroup per row
     p = rn.plan_query(rn.BF16, 64, 7168, aligned=True)
-    assert p == {"path": rn.PATH_BLOCK, "chunks": 28, "rows_per_block": 1, "block": 256, "grid": 64}
+    assert p == {"path": rn.PATH_BLOCK, "chunks": 28, "rows_per_block": 1, "streaming": 0,
+                 "block": 256, "grid": 64}
     # single rows of the decode step
     assert rn.plan_query(rn.F32, 1, 7168)["chunks"] == 28
     assert rn.plan_query(rn.F32, 1, 1536)["chunks"] == 6
@@ -176,11 +182,18 @@ def test_options_roundtrip_and_force_paths(rn):
         assert rn.plan_query(rn.BF16, 3, 7168, aligned=False)["path"] == rn.PATH_BLOCK
         assert rn.plan_query(rn.BF16, 3, 9000)["path"] == rn.PATH_STREAM
         rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
-        rn.set_option(rn.OPT_ROWS_PER_BLOCK, 2)
+        rn.set_option(rn.OPT_ROWS_PER_BLOCK, 4)
         p = rn.plan_query(rn.BF16, 8191, 7168)
-        assert p["rows_per_block"] == 2 and p["grid"] == 4096 and p["block"] == 128
-        with pytest.raises(rn.RmsnormError):
-            rn.set_option(rn.OPT_ROWS_PER_BLOCK, 3)
+        assert p["rows_per_block"] == 4 and p["grid"] == 2048 and p["block"] == 256
+        rn.set_option(rn.OPT_STREAMING, 0)
+        assert rn.plan_query(rn.BF16, 8191, 7168)["streaming"] == 0
+        rn.set_option(rn.OPT_STREAMING, 1)
+        assert rn.plan_query(rn.BF16, 1024, 256)["streaming"] == 1
+        assert rn.get_option(rn.OPT_STREAMING) == 1
+        for bad in ((rn.OPT_ROWS_PER_BLOCK, 3), (rn.OPT_ROWS_PER_BLOCK, 1),
+                    (rn.OPT_STREAMING, 2), (rn.OPT_STREAMING, -2)):
+            with pytest.raises(rn.RmsnormError):
+                rn.set_option(*bad)
         with pytest.raises(rn.RmsnormError):
             rn.set_option(rn.OPT_PATH, 7)
         with pytest.raises(rn.RmsnormError):
@@ -188,3 +201,4 @@ def test_options_roundtrip_and_force_paths(rn):
     finally:
         rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
         rn.set_option(rn.OPT_ROWS_PER_BLOCK, 0)
+        rn.set_option(rn.OPT_STREAMING, -1)

@@ -26,6 +26,7 @@ def rn():
     import row_wise_rmsnorm_amd as m
     m.set_option(m.OPT_PATH, m.PATH_AUTO)
     m.set_option(m.OPT_ROWS_PER_BLOCK, 0)
+    m.set_option(m.OPT_STREAMING, -1)
     return m
 
 
@@ -123,7 +124,13 @@ def test_prefill_bf16_full(rn):
     say(f"bf16 8192 x 7168 plan {plan}")
     got = gpu_rows(rn, xb, wb, wl.EPS, rn.BF16)
     say("bf16 8192 x 7168 oracle")
-    assert_bits_bf16(got, oracle_rows(xb, wb, wl.EPS), "prefill")
+    want = oracle_rows(xb, wb, wl.EPS)
+    assert_bits_bf16(got, want, "prefill")
+    try:
+        rn.set_option(rn.OPT_STREAMING, 0)
+        assert_bits_bf16(gpu_rows(rn, xb, wb, wl.EPS, rn.BF16), want, "prefill, cached loads")
+    finally:
+        rn.set_option(rn.OPT_STREAMING, -1)
 
 
 # ---- every code path gives the same bits ---------------------------------------------
@@ -131,7 +138,8 @@ def test_prefill_bf16_full(rn):
 PATH_CASES = [
     (8, 7168, "f32"), (33, 1000, "bf16"), (40, 257, "bf16"), (5, 8192, "f32"),
     (6, 8192, "bf16"), (3, 9000, "f32"), (17, 1536, "f32"), (9, 512, "bf16"), (4, 1, "f32"),
-    (12, 255, "f32"), (7, 7167, "bf16"),
+    (12, 255, "f32"), (7, 7167, "bf16"), (19, 7168, "bf16"), (21, 2048, "bf16"),
+    (13, 3072, "f32"),
 ]
 
 
@@ -152,14 +160,17 @@ def test_paths_and_rows_per_block_identical(rn, rows, n, kind):
     want = oracle_rows(x, w, wl.EPS)
     try:
         for path in (rn.PATH_AUTO, rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM):
-            for rpb in ((0, 1, 2, 4) if path == rn.PATH_WAVE else (0,)):
-                rn.set_option(rn.OPT_PATH, path)
-                rn.set_option(rn.OPT_ROWS_PER_BLOCK, rpb)
-                got = gpu_rows(rn, x, w, wl.EPS, dtype)
-                assert_rows(rn, got, want, dtype, f"path {path} rpb {rpb}")
+            for rpb in ((0, 4, 8) if path == rn.PATH_WAVE else (0,)):
+                for st in ((-1, 0, 1) if path == rn.PATH_WAVE else (-1,)):
+                    rn.set_option(rn.OPT_PATH, path)
+                    rn.set_option(rn.OPT_ROWS_PER_BLOCK, rpb)
+                    rn.set_option(rn.OPT_STREAMING, st)
+                    got = gpu_rows(rn, x, w, wl.EPS, dtype)
+                    assert_rows(rn, got, want, dtype, f"path {path} rpb {rpb} streaming {st}")
     finally:
         rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
         rn.set_option(rn.OPT_ROWS_PER_BLOCK, 0)
+        rn.set_option(rn.OPT_STREAMING, -1)
 
 
 def test_single_row_entry_equals_batched(rn):
