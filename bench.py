@@ -126,8 +126,10 @@ def bench_prefill(rn, torch, np, wl, steps, warmup):
     # a plain device copy of the same bytes (x read, y written), rotated the
     # same way: the practical bandwidth ceiling of this traffic pattern
     copy_us = 1000.0 * elapsed_ms(lambda i: ys[i % ROTATE].copy_(xs[i % ROTATE]), steps) / steps
-    # spot parity of the timed output against the oracle (first/last rows)
+    # spot parity of the kernel's output (automatic plan) against the oracle;
+    # the copy above overwrote the output buffers, so run it once more first
     import oracle
+    rn.rmsnorm_batched_rows(xs[0], w, eps, out=ys[0])
     torch.cuda.synchronize()
     ids = [0, 1, 4095, rows - 1]
     got = ys[0].view(torch.int16)[ids].cpu().numpy().view(np.uint16)
