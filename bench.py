@@ -168,6 +168,29 @@ def bench_prefill_only(rn, torch, np, wl, steps, warmup):
             "plan": rn.plan_query(rn.BF16, rows, n)}
 
 
+def graph_us_per_launch(torch, fn, per_graph=100, replays=20, reps=5):
+    """Per-launch device time of `fn` (one launch on the given stream) with no
+    host in the loop: `per_graph` launches captured in one graph, replayed
+    `replays` times, HIP events around the replays; `reps` repetitions. Each
+    launch still pays the graph's per-node dispatch cost."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(per_graph):
+            fn(s)
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        out.append(1000.0 * elapsed_ms(lambda i: g.replay(), replays) / (per_graph * replays))
+    del g
+    return stats(out)
+
+
 def bench_single(rn, torch, np, wl):
     x, w = wl.single()
     dev = torch.device("cuda", 0)
@@ -177,12 +200,16 @@ def bench_single(rn, torch, np, wl):
     f = lambda i: rn.rmsnorm_f32(xd, wd, eps, out=yd)
     for i in range(50):
         f(i)
-    one = [1000.0 * elapsed_ms(f, 1) for _ in range(30)]          # one call per event pair
-    burst = 1000.0 * elapsed_ms(f, 1000) / 1000                     # back-to-back
+    dev_us = graph_us_per_launch(torch, lambda s: rn.rmsnorm_f32(xd, wd, eps, out=yd, stream=s))
+    one = [1000.0 * elapsed_ms(f, 1) for _ in range(30)]          # host call -> completion
+    burst = 1000.0 * elapsed_ms(f, 1000) / 1000                     # back-to-back host calls
     algo = 7168 * 4 * 3
-    return {"us_isolated": stats(one), "us_back_to_back": burst,
-            "gbs_back_to_back": algo / (burst * 1e-6) / 1e9,
-            "plan": rn.plan_query(rn.F32, 1, 7168)}
+    return {"us_per_norm_device": dev_us,
+            "gbs_device": algo / (dev_us["mean"] * 1e-6) / 1e9,
+            "us_isolated_host_call": stats(one), "us_back_to_back_host_calls": burst,
+            "plan": rn.plan_query(rn.F32, 1, 7168),
+            "note": ("us_per_norm_device: 100 launches captured in one graph, so no host work "
+                     "between launches; the host-call figures include Python and launch overhead")}
 
 
 def bench_batch64(rn, torch, np, wl):
@@ -195,11 +222,12 @@ def bench_batch64(rn, torch, np, wl):
     f = lambda i: rn.rmsnorm_batched_rows(x, w, eps, out=y)
     for i in range(50):
         f(i)
-    reps = [1000.0 * elapsed_ms(f, 200) / 200 for _ in range(5)]
-    us = statistics.fmean(reps)
+    dev_us = graph_us_per_launch(torch, lambda s: rn.rmsnorm_batched_rows(x, w, eps, out=y, stream=s))
+    host = [1000.0 * elapsed_ms(f, 200) / 200 for _ in range(3)]
     algo = 64 * 7168 * 4 + 7168 * 2
     plan = rn.plan_query(rn.BF16, 64, 7168)
-    return {"us": stats(reps), "gbs": algo / (us * 1e-6) / 1e9, "plan": plan,
+    return {"us_device": dev_us, "gbs_device": algo / (dev_us["mean"] * 1e-6) / 1e9,
+            "us_back_to_back_host_calls": stats(host), "plan": plan,
             "workgroups_per_cu": plan["grid"] / 256.0}
 
 
@@ -378,9 +406,9 @@ def main():
     log(f"prefill {pre['us_per_launch']:.2f} us  {pre['gbs']:.0f} GB/s "
         f"(copy of the same bytes {pre['copy_us']:.2f} us)")
     single = bench_single(rn, torch, np, wl)
-    log(f"single {single['us_back_to_back']:.2f} us back-to-back")
+    log(f"single {single['us_per_norm_device']['mean']:.2f} us per norm (graph-captured)")
     b64 = bench_batch64(rn, torch, np, wl)
-    log(f"batch64 {b64['us']['mean']:.2f} us")
+    log(f"batch64 {b64['us_device']['mean']:.2f} us (graph-captured)")
     dec = bench_decode(rn, torch, np, wl, args.decode_steps)
     log(f"decode eager {dec['eager_us_per_step']['mean']:.1f} us  "
         f"graph {dec['graph_us_per_step']['mean']:.1f} us")

@@ -59,6 +59,12 @@ __device__ __forceinline__ gptr_c scalar_gptr(const void* p) {
 __device__ __forceinline__ gptr scalar_gptr(void* p) {
     return (gptr)scalar_gptr(static_cast<const void*>(p));
 }
+__device__ __forceinline__ gptr_c scalar_gptr(gptr_c p) {
+    return scalar_gptr(reinterpret_cast<const void*>(reinterpret_cast<uint64_t>(p)));
+}
+__device__ __forceinline__ gptr scalar_gptr(gptr p) {
+    return (gptr)scalar_gptr(reinterpret_cast<const void*>(reinterpret_cast<uint64_t>(p)));
+}
 
 // ---------------------------------------------------------------------------
 // Element access. bf16 values are their 16-bit patterns; widening is exact.
@@ -369,46 +375,111 @@ __device__ __forceinline__ float block_inverse(float p, int n, float eps, float*
     return inverse_rms(ss, n, eps);
 }
 
+// Element access for the BLOCK layout, where lane l of a wavefront touches
+// element 64g + l of each chunk: consecutive lanes, consecutive elements.
+// Addresses are global (address space 1) byte offsets from the row base.
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    // raw()/value() split a load from its use so that every load of a row can
+    // be issued before any result is consumed.
+    using raw_t = float;
+    static __device__ __forceinline__ raw_t raw(gptr_c row, uint32_t d) {
+        return *reinterpret_cast<const __attribute__((address_space(1))) float*>(row + 4u * d);
+    }
+    static __device__ __forceinline__ float value(raw_t r) { return r; }
+    static __device__ __forceinline__ float load(gptr_c row, uint32_t d) { return raw(row, d); }
+    static __device__ __forceinline__ void store(gptr row, uint32_t d, float v) {
+        *reinterpret_cast<__attribute__((address_space(1))) float*>(row + 4u * d) = v;
+    }
+};
+
+template <> struct Elem<uint16_t> {
+    // 16-bit loads and stores: measured faster here than loading the dword
+    // that holds the element or pairing neighbour lanes into dword stores.
+    using raw_t = uint32_t;
+    static __device__ __forceinline__ raw_t raw(gptr_c row, uint32_t d) {
+        return *reinterpret_cast<const __attribute__((address_space(1))) uint16_t*>(row + 2u * d);
+    }
+    static __device__ __forceinline__ float value(raw_t b) { return __uint_as_float(b << 16); }
+    static __device__ __forceinline__ float load(gptr_c row, uint32_t d) { return value(raw(row, d)); }
+    static __device__ __forceinline__ void store(gptr row, uint32_t d, float v) {
+        *reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(row + 2u * d) =
+            (uint16_t)bf16_bits(v);
+    }
+};
+
 // NCH > 0: rows with 256 * prev_bucket(NCH) < n <= 256 * NCH are held in
 // registers; any other n (possible for descriptor rows rewritten between graph
-// replays) is streamed. NCH == 0: always streamed.
+// replays) is streamed. NCH == 0: always streamed. x, w, y are global memory.
 template <typename T, int NCH>
 __device__ __forceinline__ void row_block(const T* x, const T* __restrict__ w, T* y, int n,
                                           float eps, float* lds4) {
+    using E = Elem<T>;
     constexpr int MINF = prev_bucket(NCH);
-    const int l = threadIdx.x;  // association lane 0..255
-    const int full = n >> 8;    // complete 256-element chunks (wave-uniform)
+    const uint32_t l = threadIdx.x;  // association lane 0..255
+    const int full = n >> 8;         // complete 256-element chunks (wave-uniform)
+    gptr_c xg = scalar_gptr(x);
+    gptr_c wg = scalar_gptr(w);
+    gptr yg = scalar_gptr(y);
     float p = 0.0f;
     if (NCH > 0 && full >= MINF && full + ((n & 255) != 0) <= NCH) {
         constexpr int R = NCH > 0 ? NCH : 1;
+        // a scalar base per 4 KB of the row keeps every chunk's offset in the
+        // instruction's immediate field
+        constexpr uint32_t per_base = 4096 / (256 * sizeof(T));
+        // Chunks below MINF are complete. The others (the bucket's top chunks:
+        // complete, ragged or past the row) are loaded from a clamped, in-row
+        // index without branches and masked to +0 past the row only after every
+        // load of x and w has been issued (the scheduling barrier keeps the
+        // compiler from waiting for x before issuing w).
+        typename E::raw_t xr[R], wr[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const uint32_t kb = (uint32_t)(k / per_base) * 4096u;
+            const uint32_t d = (uint32_t)(k % per_base) * 256u + l;
+            if (k < MINF)
+                xr[k] = E::raw(scalar_gptr(xg + kb), d);
+            else
+                xr[k] = E::raw(xg, min(((uint32_t)k << 8) + l, (uint32_t)n - 1u));
+        }
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const uint32_t kb = (uint32_t)(k / per_base) * 4096u;
+            const uint32_t d = (uint32_t)(k % per_base) * 256u + l;
+            if (k < MINF)
+                wr[k] = E::raw(scalar_gptr(wg + kb), d);
+            else
+                wr[k] = E::raw(wg, min(((uint32_t)k << 8) + l, (uint32_t)n - 1u));
+        }
+        __builtin_amdgcn_sched_barrier(0);
         float xv[R], wv[R];
 #pragma unroll
-        for (int k = 0; k < R; ++k)
-            if (k < MINF || k < full) xv[k] = widen(x[(k << 8) + l]);
-#pragma unroll
-        for (int k = 0; k < R; ++k)
-            if (k < MINF || k < full) wv[k] = widen(w[(k << 8) + l]);
-        // the ragged tail chunk: lanes past the row read +0 (clamped address)
-        const int dt = (full << 8) + l;
-        const bool tail = (n & 255) != 0;
-        const float xt = tail && dt < n ? widen(x[min(dt, n - 1)]) : 0.0f;
-        const float wt = tail && dt < n ? widen(w[min(dt, n - 1)]) : 0.0f;
-#pragma unroll
-        for (int k = 0; k < R; ++k)
-            if (k < MINF || k < full) p = fmaf(xv[k], xv[k], p);
-        p = fmaf(xt, xt, p);  // +0 past the row: no change
+        for (int k = 0; k < R; ++k) {
+            xv[k] = E::value(xr[k]);
+            wv[k] = E::value(wr[k]);
+            if (k >= MINF && ((uint32_t)k << 8) + l >= (uint32_t)n) xv[k] = 0.0f;
+            p = fmaf(xv[k], xv[k], p);  // +0 past the row: no change
+        }
         const float inv = block_inverse(p, n, eps, lds4);
 #pragma unroll
-        for (int k = 0; k < R; ++k)
-            if (k < MINF || k < full) put(y + (k << 8) + l, (xv[k] * inv) * wv[k]);
-        if (tail && dt < n) put(y + dt, (xt * inv) * wt);
+        for (int k = 0; k < R; ++k) {
+            const float v = (xv[k] * inv) * wv[k];
+            if (k < MINF) {
+                const uint32_t kb = (uint32_t)(k / per_base) * 4096u;
+                E::store(scalar_gptr(yg + kb), (uint32_t)(k % per_base) * 256u + l, v);
+            } else if (((uint32_t)k << 8) + l < (uint32_t)n) {
+                E::store(yg, ((uint32_t)k << 8) + l, v);
+            }
+        }
     } else {
-        for (int d = l; d < n; d += 256) {
-            const float v = widen(x[d]);
+        for (uint32_t d = l; d < (uint32_t)n; d += 256) {
+            const float v = E::load(xg, d);
             p = fmaf(v, v, p);
         }
         const float inv = block_inverse(p, n, eps, lds4);
-        for (int d = l; d < n; d += 256) put(y + d, (widen(x[d]) * inv) * widen(w[d]));
+        for (uint32_t d = l; d < (uint32_t)n; d += 256)
+            E::store(yg, d, (E::load(xg, d) * inv) * E::load(wg, d));
     }
 }
 

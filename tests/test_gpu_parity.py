@@ -109,6 +109,30 @@ def test_sweep_independent_offsets(rn):
             assert_bits_f32(f32_host(by[oy:oy + n]), want, f"n={n} offsets {ox},{ow},{oy}")
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 64, 129, 255, 256, 1000, 4097, 7167, 7168, 9000])
+def test_bf16_independent_offsets(rn, n):
+    """bf16 rows whose x, w, y start 0..3 elements (0/2/4/6 bytes) past a
+    256-byte boundary, independently: exercises the dword loads of
+    2-byte-misaligned rows and both the paired and the 16-bit stores."""
+    import torch
+    say(f"bf16 offsets n={n}")
+    x, w = wl.misc_f32(70000 + n, n, sigma=3.0)
+    xb, wb = wl.to_bf16_bits(x), wl.to_bf16_bits(w)
+    want = oracle.row_bf16(xb, wb, wl.EPS)
+    for ox, ow, oy in ((0, 0, 0), (1, 1, 1), (1, 0, 3), (2, 3, 1), (3, 2, 0), (0, 1, 2)):
+        bx = torch.zeros(n + 8, dtype=torch.bfloat16, device=dev())
+        bw = torch.zeros(n + 8, dtype=torch.bfloat16, device=dev())
+        by = torch.zeros(n + 8, dtype=torch.bfloat16, device=dev())
+        bx[ox:ox + n].copy_(to_dev_bf16(xb))
+        bw[ow:ow + n].copy_(to_dev_bf16(wb))
+        rn.rmsnorm_bf16(bx[ox:ox + n], bw[ow:ow + n], wl.EPS, out=by[oy:oy + n])
+        sync()
+        got = bf16_host(by)
+        assert_bits_bf16(got[oy:oy + n], want, f"n={n} offsets {ox},{ow},{oy}")
+        # the neighbours of the row are untouched (paired stores stay inside it)
+        assert (got[:oy] == 0).all() and (got[oy + n:] == 0).all(), f"n={n} wrote outside"
+
+
 def test_batch64_bf16(rn):
     say("bf16 64 x 7168")
     xb, wb = wl.batch64()
@@ -292,7 +316,8 @@ def test_strided_rows(rn):
     say("strided rows")
     import torch
     for kind, rows, n, sx, sy in (("f32", 2000, 1000, 1030, 1001), ("bf16", 50, 7168, 7200, 7296),
-                                  ("bf16", 3000, 512, 520, 516)):
+                                  ("bf16", 3000, 512, 520, 516), ("bf16", 100, 1000, 1001, 1003),
+                                  ("bf16", 33, 7168, 7169, 7171)):
         x, w = _rows_input(rows, n, kind, sx)
         want = oracle_rows(x, w, wl.EPS)
         if kind == "f32":
