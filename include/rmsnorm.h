@@ -92,10 +92,10 @@ int rmsnorm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, f
 
 /* `rows` rows of width n sharing one weight row. Row r of x starts at
  * x + r * x_row_stride elements, row r of y at y + r * y_row_stride.
- * dtype is an rmsn_dtype. Many aligned rows run one row per 64-lane
- * wavefront, several wavefronts per workgroup; few rows run one row per
- * 256-thread workgroup so each row gets four wavefronts (Lecture 04 section 1:
- * match the grid to the compute units; see rmsnorm_plan_query). */
+ * dtype is an rmsn_dtype. Many 16-byte aligned rows run one row per
+ * workgroup of several wavefronts with 16-byte loads (RMSN_PATH_SPLIT); few
+ * rows run one row per 256-thread workgroup (Lecture 04 section 1: match the
+ * grid to the compute units; see rmsnorm_plan_query). */
 int rmsnorm_batched_rows(int dtype, const void* x, int64_t x_row_stride, const void* w, void* y,
                          int64_t y_row_stride, int64_t rows, int64_t n, float eps, void* stream);
 
@@ -146,42 +146,63 @@ const char* rmsnorm_last_error(void);
  *                     the 64 lane chains of group g in registers; any element
  *                     alignment, n <= 8192.
  *   RMSN_PATH_STREAM: as BLOCK but streaming the row twice (sum, then apply)
- *                     instead of holding it; any n up to 2^24. */
-enum { RMSN_PATH_WAVE = 0, RMSN_PATH_BLOCK = 1, RMSN_PATH_STREAM = 2 };
+ *                     instead of holding it; any n up to 2^24.
+ *   RMSN_PATH_SPLIT:  one workgroup of up to 16 wavefronts per row (Lecture 04
+ *                     section 1.1: widen the block until the row's width is
+ *                     the parallelism). The row is cut into 1 KB slices, one
+ *                     16-byte load per lane; each wavefront holds `loads`
+ *                     consecutive slices and continues the 256 lane chains
+ *                     where the previous wavefront left them (handed over
+ *                     through LDS), so the association is unchanged. Needs
+ *                     16-byte aligned rows and w, n * element size a multiple
+ *                     of 16, and rows of at most 128 KB. */
+enum { RMSN_PATH_WAVE = 0, RMSN_PATH_BLOCK = 1, RMSN_PATH_STREAM = 2, RMSN_PATH_SPLIT = 3 };
 
 typedef struct rmsn_plan_info {
     int32_t path;            /* one of RMSN_PATH_*                                */
     int32_t chunks;          /* 256-element chunks a lane's registers hold (0:
-                                streaming)                                        */
+                                streaming); SPLIT: chunks one wavefront holds     */
     int32_t rows_per_block;  /* rows (wavefronts) per workgroup on WAVE, else 1   */
     int32_t block;           /* threads per workgroup                             */
     int64_t grid;            /* workgroups                                        */
-    int32_t streaming;       /* WAVE: 1 = non-temporal loads of x / stores of y   */
-    int32_t reserved;
+    int32_t streaming;       /* WAVE / SPLIT: 1 = non-temporal loads of x and
+                                stores of y                                       */
+    int32_t loads;           /* SPLIT: 16-byte loads per lane (1 KB slices per
+                                wavefront), else 0                                */
 } rmsn_plan_info;
 
-/* The launch the library would use for `rows` rows of width n whose row and
- * weight pointers are (aligned != 0) or are not (aligned == 0) aligned to
- * 16 B (binary32) / 8 B (bf16). Same function the launches use. Returns
+/* The launch the library would use for `rows` rows of width n whose row starts
+ * (x and y) and weight all share the byte alignment `align` (the largest power
+ * of two dividing it counts, up to 16; 0 or anything below the element size
+ * means element alignment only). Same function the launches use. Returns
  * RMSN_EINVAL for an invalid dtype, rows or n. */
-int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int aligned, rmsn_plan_info* out);
+int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_info* out);
 
 /* Process-wide overrides, for proving that code paths give identical bits
  * (Lecture 04 section 6: one binary, switchable arms). Defaults come from the
  * environment at first use, else automatic.
  *   RMSN_OPT_PATH:           -1 automatic, or an RMSN_PATH_* value; a path a
  *                            launch is not eligible for (WAVE on unaligned
- *                            rows or n > 8192, BLOCK with n > 8192) falls
- *                            back to the automatic choice
+ *                            rows or n > 8192, BLOCK with n > 8192, SPLIT
+ *                            outside its conditions above) falls back to the
+ *                            automatic choice
  *   RMSN_OPT_ROWS_PER_BLOCK:  0 automatic, else 4 or 8 rows (wavefronts) per
  *                            workgroup sharing one LDS copy of w (WAVE path)
  *   RMSN_OPT_STREAMING:      -1 automatic (on when x + y of the launch reach
  *                            64 MiB), 0 off, 1 on: non-temporal loads of x and
- *                            stores of y (WAVE path)
+ *                            stores of y (WAVE and SPLIT paths)
+ *   RMSN_OPT_SPLIT_LOADS:     0 automatic, else 1, 2, 4 or 8 slices per
+ *                            wavefront (SPLIT path; a value that would need
+ *                            more than 16 wavefronts falls back to automatic)
  * Returns RMSN_EINVAL for an unknown key or value. Not synchronised with
  * launches on other threads. Environment: RMSN_PATH, RMSN_ROWS_PER_BLOCK,
- * RMSN_STREAMING. */
-enum { RMSN_OPT_PATH = 1, RMSN_OPT_ROWS_PER_BLOCK = 2, RMSN_OPT_STREAMING = 3 };
+ * RMSN_STREAMING, RMSN_SPLIT_LOADS. */
+enum {
+    RMSN_OPT_PATH = 1,
+    RMSN_OPT_ROWS_PER_BLOCK = 2,
+    RMSN_OPT_STREAMING = 3,
+    RMSN_OPT_SPLIT_LOADS = 4
+};
 int rmsnorm_set_option(int key, int value);
 int rmsnorm_get_option(int key, int* value);
 

@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_HERE, "librmsnorm_amd.so")
 
 RMSN_OK, RMSN_EINVAL, RMSN_EHIP, RMSN_ECAPTURE, RMSN_ENOMEM = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
-PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM = -1, 0, 1, 2
-OPT_PATH, OPT_ROWS_PER_BLOCK, OPT_STREAMING = 1, 2, 3
+PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM, PATH_SPLIT = -1, 0, 1, 2, 3
+OPT_PATH, OPT_ROWS_PER_BLOCK, OPT_STREAMING, OPT_SPLIT_LOADS = 1, 2, 3, 4
 MAX_N = 1 << 24
 DESC_BYTES = 32
 
@@ -36,7 +36,7 @@ class _PlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("chunks", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("streaming", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("loads", ctypes.c_int32)]
 
 
 def _load():
@@ -232,12 +232,17 @@ class SequenceGraph:
             pass
 
 
-def plan_query(dtype, rows, n, aligned=True):
+def plan_query(dtype, rows, n, aligned=True, align=None):
+    """The launch plan for `rows` rows of width n. `align`: byte alignment
+    shared by the row starts and w (default 16 if `aligned`, else element
+    alignment only)."""
+    if align is None:
+        align = 16 if aligned else 0
     info = _PlanInfo()
-    _check(_lib.rmsnorm_plan_query(int(dtype), int(rows), int(n), 1 if aligned else 0,
-                                   ctypes.byref(info)))
+    _check(_lib.rmsnorm_plan_query(int(dtype), int(rows), int(n), int(align), ctypes.byref(info)))
     return {"path": info.path, "chunks": info.chunks, "rows_per_block": info.rows_per_block,
-            "streaming": info.streaming, "block": info.block, "grid": info.grid}
+            "streaming": info.streaming, "block": info.block, "grid": info.grid,
+            "loads": info.loads}
 
 
 def set_option(key, value):

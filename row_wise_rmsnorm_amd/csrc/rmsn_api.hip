@@ -40,12 +40,14 @@ int hip_fail(const char* what, hipError_t e) {
     return RMSN_EHIP;
 }
 
-bool rows_vec_aligned(int dtype, const void* x, int64_t xs, const void* w, const void* y,
-                      int64_t ys) {
-    const uintptr_t vb = (uintptr_t)vec_bytes(dtype);
-    const int64_t es = elem_bytes(dtype);
-    return (uintptr_t)x % vb == 0 && (uintptr_t)w % vb == 0 && (uintptr_t)y % vb == 0 &&
-           (uint64_t)(xs * es) % vb == 0 && (uint64_t)(ys * es) % vb == 0;
+// The byte alignment (a power of two, at most 16) shared by every row start of
+// x and y and by w.
+int rows_alignment(int dtype, const void* x, int64_t xs, const void* w, const void* y,
+                   int64_t ys) {
+    const uint64_t es = (uint64_t)elem_bytes(dtype);
+    const uint64_t bits = (uint64_t)(uintptr_t)x | (uint64_t)(uintptr_t)w |
+                          (uint64_t)(uintptr_t)y | ((uint64_t)xs * es) | ((uint64_t)ys * es) | 16u;
+    return (int)(bits & (~bits + 1));  // lowest set bit
 }
 
 int run_rows(int dtype, const void* x, int64_t xs, const void* w, void* y, int64_t ys,
@@ -55,7 +57,7 @@ int run_rows(int dtype, const void* x, int64_t xs, const void* w, void* y, int64
     if (st != RMSN_OK) return st;
     if ((st = check_eps(eps)) != RMSN_OK) return st;
     Plan p;
-    st = make_plan(dtype, rows, n, rows_vec_aligned(dtype, x, xs, w, y, ys), &p);
+    st = make_plan(dtype, rows, n, rows_alignment(dtype, x, xs, w, y, ys), &p);
     if (st != RMSN_OK) return st;
     const hipError_t e =
         launch_rows(p, x, xs, w, y, ys, rows, (int)n, eps, static_cast<hipStream_t>(stream));
@@ -65,8 +67,8 @@ int run_rows(int dtype, const void* x, int64_t xs, const void* w, void* y, int64
 int plan_sequence(int dtype, const int64_t* widths, int32_t count, std::vector<Plan>* plans) {
     plans->resize((size_t)count);
     for (int32_t i = 0; i < count; ++i) {
-        // Descriptor rows may have any element alignment: never the WAVE path.
-        const int st = make_plan(dtype, 1, widths[i], false, &(*plans)[(size_t)i]);
+        // Descriptor rows may have any element alignment: BLOCK or STREAM only.
+        const int st = make_plan(dtype, 1, widths[i], 0, &(*plans)[(size_t)i]);
         if (st != RMSN_OK) return st;
     }
     return RMSN_OK;
@@ -297,14 +299,14 @@ int rmsnorm_graph_is_fallback(const rmsn_graph* g, int* out) {
 
 const char* rmsnorm_last_error(void) { return last_error(); }
 
-int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int aligned, rmsn_plan_info* out) {
+int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_info* out) {
     clear_error();
     if (!out) {
         set_error("null output pointer");
         return RMSN_EINVAL;
     }
     Plan p;
-    const int st = make_plan(dtype, rows, n, aligned != 0, &p);
+    const int st = make_plan(dtype, rows, n, align, &p);
     if (st != RMSN_OK) return st;
     out->path = p.path;
     out->chunks = p.chunks;
@@ -312,7 +314,7 @@ int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int aligned, rmsn_pla
     out->block = p.block;
     out->grid = p.grid;
     out->streaming = p.streaming;
-    out->reserved = 0;
+    out->loads = p.loads;
     return RMSN_OK;
 }
 

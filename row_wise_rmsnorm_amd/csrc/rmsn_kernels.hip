@@ -28,6 +28,12 @@
 //          pointer works; the row stays in VGPRs (n <= 256 * chunks).
 //   STREAM BLOCK's mapping, but the row is streamed twice (once for the sum,
 //          once for the apply) instead of being held: any n up to 2^24.
+//   SPLIT  one workgroup of S wavefronts per row, the row cut into 1 KB slices
+//          (one 16-byte load per lane). Wavefront s holds U consecutive
+//          slices; it continues the 256 lane chains from where wavefront s-1
+//          left them (1 KB of LDS, one barrier per hand-off), and the last
+//          wavefront runs the group trees. Every wavefront issues all of its
+//          loads at once, so the whole row is in flight from the start.
 //
 // Floating point: contraction is off for this file; the one fused operation
 // of the association is written as fmaf. '/' and sqrtf are the correctly
@@ -352,6 +358,183 @@ struct WaveRow {
 };
 
 // ---------------------------------------------------------------------------
+// SPLIT layout: a row is a sequence of 1 KB slices; lane t of a wavefront
+// loads bytes 16t..16t+15 of a slice. A binary32 slice is one 256-element
+// chunk and lane t's four values are the chains 4t..4t+3, as on the WAVE
+// path. A bf16 slice is two chunks: lane t < 32 loads elements 8t..8t+7 of
+// the first, lane t + 32 the same elements of the second. One 32-lane swap
+// per register pair regroups them so that every lane holds the same four
+// chains of both chunks: lane t < 32 chains 8t..8t+3, lane t + 32 chains
+// 8t+4..8t+7.
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4 gload16(gptr_c p) {
+    auto* a = reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(p);
+    return NT ? __builtin_nontemporal_load(a) : *a;
+}
+template <bool NT>
+__device__ __forceinline__ void gstore16(gptr p, u32x4 v) {
+    auto* a = reinterpret_cast<__attribute__((address_space(1))) u32x4*>(p);
+    if (NT) __builtin_nontemporal_store(v, a);
+    else *a = v;
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+// Lanes 0..31 keep their own a and receive b's upper half; lanes 32..63 keep
+// their own b and receive a's lower half -- as (r.first, r.second):
+//   lane i < 32:  first = a[i],      second = a[i + 32]
+//   lane i >= 32: first = b[i - 32], second = b[i]
+struct SwapPair { uint32_t first, second; };
+__device__ __forceinline__ SwapPair swap32(uint32_t a, uint32_t b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    return {r[0], r[1]};
+}
+
+__device__ __forceinline__ void chain4(float p[4], float v0, float v1, float v2, float v3) {
+    p[0] = fmaf(v0, v0, p[0]);
+    p[1] = fmaf(v1, v1, p[1]);
+    p[2] = fmaf(v2, v2, p[2]);
+    p[3] = fmaf(v3, v3, p[3]);
+}
+
+// One slice into the lane chains, chunks in ascending order.
+__device__ __forceinline__ void slice_chains(float p[4], u32x4 v, float) {
+    chain4(p, __uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+           __uint_as_float(v.w));
+}
+__device__ __forceinline__ void slice_chains(float p[4], u32x4 v, uint16_t) {
+    // first chunk: dwords x, y of the lower half-wave; second chunk: the same
+    // dwords of the upper half-wave (see swap32)
+    const SwapPair a = swap32(v.x, v.z);
+    const SwapPair b = swap32(v.y, v.w);
+    chain4(p, lo_bf16(a.first), hi_bf16(a.first), lo_bf16(b.first), hi_bf16(b.first));
+    chain4(p, lo_bf16(a.second), hi_bf16(a.second), lo_bf16(b.second), hi_bf16(b.second));
+}
+
+// Group trees and combine for the SPLIT layout.
+__device__ __forceinline__ float split_sumsq(const float p[4], int, float) {
+    return wave_sumsq(p[0], p[1], p[2], p[3]);  // binary32: the WAVE layout
+}
+// bf16: group g is lanes 8g..8g+7 and 8g+32..8g+39; association lane 64g+j
+// sits in lane 8g + (j/8) + 32*((j/4)&1), register j%4.
+__device__ __forceinline__ float split_sumsq(const float p[4], int lane, uint16_t) {
+    float q[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // halving s = 32, 16, 8: partner j+s is s/8 lanes further
+        q[e] = p[e] + row_shl<4>(p[e]);
+        q[e] = q[e] + row_shl<2>(q[e]);
+        q[e] = q[e] + row_shl<1>(q[e]);
+    }
+    // j = e sits in lane 8g, j = 4+e in lane 8g+32. Halving s = 4 pairs the
+    // two: the lower lane adds registers 0 and 2, the upper lane 1 and 3.
+    const SwapPair s01 = swap32(__float_as_uint(q[0]), __float_as_uint(q[1]));
+    const SwapPair s23 = swap32(__float_as_uint(q[2]), __float_as_uint(q[3]));
+    const bool low = lane < 32;
+    const float a0 = low ? q[0] : __uint_as_float(s01.first);   // j = e (e = 0 or 1)
+    const float a4 = low ? __uint_as_float(s01.second) : q[1];  // j = e + 4
+    const float c0 = low ? q[2] : __uint_as_float(s23.first);   // j = e + 2
+    const float c4 = low ? __uint_as_float(s23.second) : q[3];  // j = e + 6
+    // s = 2 in the lane; s = 1 between lane 8g (e = 0) and lane 8g+32 (e = 1)
+    const float t = (a0 + a4) + (c0 + c4);
+    const float g0 = lane_value(t, 0) + lane_value(t, 32);
+    const float g1 = lane_value(t, 8) + lane_value(t, 40);
+    const float g2 = lane_value(t, 16) + lane_value(t, 48);
+    const float g3 = lane_value(t, 24) + lane_value(t, 56);
+    return (g0 + g2) + (g1 + g3);
+}
+
+// y = (x * inv) * w for one slice, packed back into 16 bytes.
+__device__ __forceinline__ u32x4 slice_apply(u32x4 x, u32x4 w, float inv, float) {
+    u32x4 o;
+    o.x = __float_as_uint((__uint_as_float(x.x) * inv) * __uint_as_float(w.x));
+    o.y = __float_as_uint((__uint_as_float(x.y) * inv) * __uint_as_float(w.y));
+    o.z = __float_as_uint((__uint_as_float(x.z) * inv) * __uint_as_float(w.z));
+    o.w = __float_as_uint((__uint_as_float(x.w) * inv) * __uint_as_float(w.w));
+    return o;
+}
+__device__ __forceinline__ uint32_t apply_pair(uint32_t x, uint32_t w, float inv) {
+    const float lo = (lo_bf16(x) * inv) * lo_bf16(w);
+    const float hi = (hi_bf16(x) * inv) * hi_bf16(w);
+    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ u32x4 slice_apply(u32x4 x, u32x4 w, float inv, uint16_t) {
+    u32x4 o;
+    o.x = apply_pair(x.x, w.x, inv);
+    o.y = apply_pair(x.y, w.y, inv);
+    o.z = apply_pair(x.z, w.z, inv);
+    o.w = apply_pair(x.w, w.w, inv);
+    return o;
+}
+
+// The U slices wavefront s of a row owns: slices s*U .. s*U+U-1. nvec is the
+// row's length in 16-byte vectors (the plan makes n * sizeof(T) a multiple of
+// 16); vector v*64 + lane of the row is this lane's part of slice v. EXACT:
+// every slice of every wavefront is complete (nvec == 64 * U * wavefronts).
+// Otherwise vectors past the row are loaded from the row's last vector (an
+// in-row address, so no load needs a branch), count as +0 in the chains and
+// are not stored.
+template <typename T, int U, bool EXACT, bool NT>
+struct SplitPart {
+    u32x4 xr[U], wr[U];
+    uint32_t vi0;  // this lane's vector index in its first slice
+
+    // A scalar base per 4 slices keeps each load's offset in the immediate field.
+    static __device__ __forceinline__ uint32_t base_bytes(int s, int u) {
+        return (uint32_t)(s * U + (u & ~3)) * 1024u;
+    }
+    static __device__ __forceinline__ uint32_t lane_bytes(int lane, int u) {
+        return (uint32_t)lane * 16u + (uint32_t)(u & 3) * 1024u;
+    }
+    __device__ __forceinline__ bool in_row(int u, uint32_t nvec) const {
+        return EXACT || vi0 + 64u * (uint32_t)u < nvec;
+    }
+
+    __device__ __forceinline__ void load(gptr_c x, gptr_c w, int s, int lane, uint32_t nvec) {
+        vi0 = (uint32_t)(s * U) * 64u + (uint32_t)lane;
+        if (EXACT) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                xr[u] = gload16<NT>(scalar_gptr(x + base_bytes(s, u)) + lane_bytes(lane, u));
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                wr[u] = gload16<false>(scalar_gptr(w + base_bytes(s, u)) + lane_bytes(lane, u));
+        } else {
+            const uint32_t last = nvec - 1u;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                xr[u] = gload16<NT>(x + min(vi0 + 64u * (uint32_t)u, last) * 16u);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                wr[u] = gload16<false>(w + min(vi0 + 64u * (uint32_t)u, last) * 16u);
+        }
+    }
+
+    __device__ __forceinline__ void chains(float p[4], uint32_t nvec) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const u32x4 v = in_row(u, nvec) ? xr[u] : u32x4{0u, 0u, 0u, 0u};
+            slice_chains(p, v, T());
+        }
+    }
+
+    __device__ __forceinline__ void apply(float inv, gptr y, int s, int lane, uint32_t nvec) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const u32x4 o = slice_apply(xr[u], wr[u], inv, T());
+            if (EXACT)
+                gstore16<NT>(scalar_gptr(y + base_bytes(s, u)) + lane_bytes(lane, u), o);
+            else if (in_row(u, nvec))
+                gstore16<NT>(y + (vi0 + 64u * (uint32_t)u) * 16u, o);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
 // BLOCK / STREAM layout: 256 threads per row, thread l = chain l, wave g = group g.
 
 // Descending halving over the 64 lanes of this wavefront; the total lands in lane 0.
@@ -510,6 +693,46 @@ __global__ __launch_bounds__(64 * RPB, (wave_occupancy<T, NCH, EXACT>())) void k
     row.finish(w, wl, y + r * ys, n, eps, lane);
 }
 
+// SPLIT layout: one row per workgroup of blockDim.x / 64 wavefronts, U slices
+// each (EXACT: the row is exactly 64 * U * wavefronts vectors). Wavefront s waits for its turn (barrier s), takes the lane chains
+// from LDS, extends them over its slices and passes them on; the last
+// wavefront finishes the sum and publishes inv for the apply.
+template <typename T, int U, bool EXACT, bool NT>
+__global__ __launch_bounds__(1024) void k_rows_split(const T* x, int64_t xs,
+                                                     const T* __restrict__ w, T* y, int64_t ys,
+                                                     int n, float eps) {
+    __shared__ f32x4 hand[64];
+    __shared__ float inv_shared;
+    const int waves = blockDim.x >> 6;
+    const int s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t r = blockIdx.x;
+    const uint32_t nvec = (uint32_t)n * (uint32_t)sizeof(T) / 16u;
+    SplitPart<T, U, EXACT, NT> part;
+    part.load(scalar_gptr(reinterpret_cast<const char*>(x + r * xs)),
+              scalar_gptr(reinterpret_cast<const char*>(w)), s, lane, nvec);
+    for (int h = 0; h < waves; ++h) {
+        if (h == s) {
+            float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (s > 0) {
+                const f32x4 q = hand[lane];
+                p[0] = q.x; p[1] = q.y; p[2] = q.z; p[3] = q.w;
+            }
+            part.chains(p, nvec);
+            if (s + 1 < waves) {
+                f32x4 q;
+                q.x = p[0]; q.y = p[1]; q.z = p[2]; q.w = p[3];
+                hand[lane] = q;
+            } else {
+                const float inv = inverse_rms(split_sumsq(p, lane, T()), n, eps);
+                if (lane == 0) inv_shared = inv;
+            }
+        }
+        __syncthreads();
+    }
+    part.apply(inv_shared, scalar_gptr(reinterpret_cast<char*>(y + r * ys)), s, lane, nvec);
+}
+
 template <typename T, int NCH>
 __global__ __launch_bounds__(256) void k_rows_block(const T* x, int64_t xs,
                                                     const T* __restrict__ w, T* y, int64_t ys,
@@ -587,6 +810,35 @@ hipError_t launch_wave_t(const Plan& p, const void* x, int64_t xs, const void* w
 }
 
 template <typename T>
+hipError_t launch_split_t(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
+                          int64_t ys, int n, float eps, hipStream_t s) {
+    const T* xp = static_cast<const T*>(x);
+    const T* wp = static_cast<const T*>(w);
+    T* yp = static_cast<T*>(y);
+    const dim3 grid((unsigned)p.grid), block((unsigned)p.block);
+    const bool exact = (int64_t)n * (int64_t)sizeof(T) == (int64_t)p.loads * p.block * 16;
+#define RMSN_LAUNCH(U, E, NT)                                                                  \
+    hipLaunchKernelGGL((k_rows_split<T, U, E, NT>), grid, block, 0, s, xp, xs, wp, yp, ys, n, eps)
+#define RMSN_CASE(U)                                                                           \
+    case U:                                                                                    \
+        if (exact && p.streaming) RMSN_LAUNCH(U, true, true);                                  \
+        else if (exact) RMSN_LAUNCH(U, true, false);                                           \
+        else if (p.streaming) RMSN_LAUNCH(U, false, true);                                     \
+        else RMSN_LAUNCH(U, false, false);                                                     \
+        break;
+    switch (p.loads) {
+        RMSN_CASE(1)
+        RMSN_CASE(2)
+        RMSN_CASE(4)
+        RMSN_CASE(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef RMSN_CASE
+#undef RMSN_LAUNCH
+    return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_block_t(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
                           int64_t ys, int n, float eps, hipStream_t s) {
     const T* xp = static_cast<const T*>(x);
@@ -634,12 +886,24 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
                    ? launch_wave_t<float>(p, x, xs, w, y, ys, rows, n, eps, stream)
                    : launch_wave_t<uint16_t>(p, x, xs, w, y, ys, rows, n, eps, stream);
     }
+    if (p.path == RMSN_PATH_SPLIT) {
+        // the SPLIT kernel relies on the plan's geometry for this n: whole
+        // 16-byte vectors, one wavefront per `loads` slices
+        const int64_t waves = (split_slices(p.dtype, n) + p.loads - 1) / (p.loads > 0 ? p.loads : 1);
+        if (p.loads < 1 || ((int64_t)n * elem_bytes(p.dtype)) % 16 != 0 ||
+            waves > kMaxSplitWaves || p.block != kWave * waves || p.grid != rows)
+            return hipErrorInvalidValue;
+        return p.dtype == RMSN_F32
+                   ? launch_split_t<float>(p, x, xs, w, y, ys, n, eps, stream)
+                   : launch_split_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
+    }
     return p.dtype == RMSN_F32 ? launch_block_t<float>(p, x, xs, w, y, ys, n, eps, stream)
                                : launch_block_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
 }
 
 hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, hipStream_t stream) {
-    if (p.path == RMSN_PATH_WAVE) return hipErrorInvalidValue;  // descriptors use BLOCK/STREAM
+    if (p.path == RMSN_PATH_WAVE || p.path == RMSN_PATH_SPLIT)
+        return hipErrorInvalidValue;  // descriptors use BLOCK/STREAM
     return p.dtype == RMSN_F32 ? launch_desc_t<float>(p, d, eps, stream)
                                : launch_desc_t<uint16_t>(p, d, eps, stream);
 }

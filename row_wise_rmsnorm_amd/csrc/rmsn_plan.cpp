@@ -19,6 +19,7 @@ thread_local char g_err[512] = "";
 std::atomic<int> g_path{-2};   // -2 = not yet read from the environment
 std::atomic<int> g_rpb{-2};
 std::atomic<int> g_stream{-2};
+std::atomic<int> g_split{-2};
 
 int env_int(const char* name, int dflt) {
     const char* s = std::getenv(name);
@@ -30,8 +31,10 @@ int env_int(const char* name, int dflt) {
 }
 
 bool valid_path(int v) {
-    return v == -1 || v == RMSN_PATH_WAVE || v == RMSN_PATH_BLOCK || v == RMSN_PATH_STREAM;
+    return v == -1 || v == RMSN_PATH_WAVE || v == RMSN_PATH_BLOCK || v == RMSN_PATH_STREAM ||
+           v == RMSN_PATH_SPLIT;
 }
+bool valid_split_loads(int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8; }
 bool valid_rpb(int v) { return v == 0 || v == 4 || v == 8; }
 bool valid_streaming(int v) { return v == -1 || v == 0 || v == 1; }
 
@@ -82,11 +85,21 @@ int option_streaming() {
     return v;
 }
 
+int option_split_loads() {
+    int v = g_split.load(std::memory_order_relaxed);
+    if (v == -2) {
+        v = env_int("RMSN_SPLIT_LOADS", 0);
+        if (!valid_split_loads(v)) v = 0;
+        g_split.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 int set_option(int key, int value) {
     if (key == RMSN_OPT_PATH) {
         if (!valid_path(value)) {
-            set_error("rmsnorm_set_option: path must be -1 (automatic), %d, %d or %d, got %d",
-                      RMSN_PATH_WAVE, RMSN_PATH_BLOCK, RMSN_PATH_STREAM, value);
+            set_error("rmsnorm_set_option: path must be -1 (automatic), %d, %d, %d or %d, got %d",
+                      RMSN_PATH_WAVE, RMSN_PATH_BLOCK, RMSN_PATH_STREAM, RMSN_PATH_SPLIT, value);
             return RMSN_EINVAL;
         }
         g_path.store(value, std::memory_order_relaxed);
@@ -108,6 +121,14 @@ int set_option(int key, int value) {
         g_stream.store(value, std::memory_order_relaxed);
         return RMSN_OK;
     }
+    if (key == RMSN_OPT_SPLIT_LOADS) {
+        if (!valid_split_loads(value)) {
+            set_error("rmsnorm_set_option: split loads must be 0, 1, 2, 4 or 8, got %d", value);
+            return RMSN_EINVAL;
+        }
+        g_split.store(value, std::memory_order_relaxed);
+        return RMSN_OK;
+    }
     set_error("rmsnorm_set_option: unknown key %d", key);
     return RMSN_EINVAL;
 }
@@ -120,6 +141,7 @@ int get_option(int key, int* value) {
     if (key == RMSN_OPT_PATH) { *value = option_path(); return RMSN_OK; }
     if (key == RMSN_OPT_ROWS_PER_BLOCK) { *value = option_rows_per_block(); return RMSN_OK; }
     if (key == RMSN_OPT_STREAMING) { *value = option_streaming(); return RMSN_OK; }
+    if (key == RMSN_OPT_SPLIT_LOADS) { *value = option_split_loads(); return RMSN_OK; }
     set_error("rmsnorm_get_option: unknown key %d", key);
     return RMSN_EINVAL;
 }
@@ -142,7 +164,17 @@ bool auto_streaming(int dtype, int64_t rows, int64_t n) {
     return rows * n * 2 * elem_bytes(dtype) >= kStreamBytes;
 }
 
-int make_plan(int dtype, int64_t rows, int64_t n, bool aligned, Plan* out) {
+int auto_split_loads(int64_t slices) {
+    // fewest slices per wavefront that keep the row within kSplitTargetWaves
+    // wavefronts (fewer chain hand-offs), else within kMaxSplitWaves
+    for (int i = 0; i < kNumSplitLoads; ++i)
+        if ((slices + kSplitLoads[i] - 1) / kSplitLoads[i] <= kSplitTargetWaves) return kSplitLoads[i];
+    for (int i = 0; i < kNumSplitLoads; ++i)
+        if ((slices + kSplitLoads[i] - 1) / kSplitLoads[i] <= kMaxSplitWaves) return kSplitLoads[i];
+    return 0;
+}
+
+int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
     if (dtype != RMSN_F32 && dtype != RMSN_BF16) {
         set_error("unknown dtype %d", dtype);
         return RMSN_EINVAL;
@@ -155,33 +187,52 @@ int make_plan(int dtype, int64_t rows, int64_t n, bool aligned, Plan* out) {
         set_error("n must be in [1, %d], got %lld", RMSN_MAX_N, (long long)n);
         return RMSN_EINVAL;
     }
+    // the power of two (at most 16) that `align` guarantees
+    int a = 16;
+    while (a > 1 && (align <= 0 || align % a)) a >>= 1;
+    const int es = elem_bytes(dtype);
     const int bucket = chunk_bucket(n);
-    const bool can_wave = bucket != 0 && aligned;
+    const int64_t slices = split_slices(dtype, n);
+    const int split_auto = auto_split_loads(slices);
+    const bool can_split = a >= 16 && (n * es) % 16 == 0 && split_auto != 0;
+    const bool can_wave = bucket != 0 && a >= vec_bytes(dtype);
     const bool can_block = bucket != 0;
     int path;
     switch (option_path()) {
         case RMSN_PATH_WAVE: path = can_wave ? RMSN_PATH_WAVE : -1; break;
         case RMSN_PATH_BLOCK: path = can_block ? RMSN_PATH_BLOCK : -1; break;
         case RMSN_PATH_STREAM: path = RMSN_PATH_STREAM; break;
+        case RMSN_PATH_SPLIT: path = can_split ? RMSN_PATH_SPLIT : -1; break;
         default: path = -1; break;
     }
     if (path < 0) {
-        if (can_wave && rows >= kWaveMinRows) path = RMSN_PATH_WAVE;
+        if (can_split && rows >= kWaveMinRows) path = RMSN_PATH_SPLIT;
+        else if (can_wave && rows >= kWaveMinRows) path = RMSN_PATH_WAVE;
         else if (can_block) path = RMSN_PATH_BLOCK;
+        else if (can_split) path = RMSN_PATH_SPLIT;
         else path = RMSN_PATH_STREAM;
     }
     Plan p{};
     p.dtype = dtype;
     p.path = path;
+    const int st = option_streaming();
     if (path == RMSN_PATH_WAVE) {
         int rpb = option_rows_per_block();
         if (rpb == 0) rpb = auto_rows_per_block(rows);
-        const int st = option_streaming();
         p.chunks = bucket;
         p.rows_per_block = rpb;
         p.streaming = st < 0 ? (auto_streaming(dtype, rows, n) ? 1 : 0) : st;
         p.block = kWave * rpb;
         p.grid = (rows + rpb - 1) / rpb;
+    } else if (path == RMSN_PATH_SPLIT) {
+        int u = option_split_loads();
+        if (u == 0 || (slices + u - 1) / u > kMaxSplitWaves) u = split_auto;
+        p.loads = u;
+        p.chunks = u * (kSliceBytes / (kLanes * es));
+        p.rows_per_block = 1;
+        p.streaming = st < 0 ? (auto_streaming(dtype, rows, n) ? 1 : 0) : st;
+        p.block = kWave * (int)((slices + u - 1) / u);
+        p.grid = rows;
     } else {
         p.chunks = path == RMSN_PATH_BLOCK ? bucket : 0;
         p.rows_per_block = 1;

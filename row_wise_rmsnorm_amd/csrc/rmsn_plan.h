@@ -25,20 +25,36 @@ constexpr int64_t kWaveMinRows = 1024;
 // non-temporal hints: far beyond the 32 MB of L2 and a large share of the
 // 256 MB last-level cache, where keeping the rows cached cannot pay.
 constexpr int64_t kStreamBytes = 64ll << 20;
+// SPLIT path: a row is cut into 1 KB slices (one 16-byte load per lane of a
+// wavefront); a workgroup of up to 16 wavefronts holds one row, each
+// wavefront `loads` consecutive slices. Rows up to 128 slices (128 KB).
+constexpr int kSliceBytes = 1024;
+constexpr int kMaxSplitWaves = 16;
+constexpr int kSplitLoads[] = {1, 2, 4, 8};
+constexpr int kNumSplitLoads = sizeof(kSplitLoads) / sizeof(kSplitLoads[0]);
+// The automatic choice keeps a row to at most this many wavefronts: each one
+// more is one more hand-off of the lane chains through LDS.
+constexpr int kSplitTargetWaves = 8;
 
 struct Plan {
     int dtype;           // RMSN_F32 / RMSN_BF16
-    int path;            // RMSN_PATH_WAVE / _BLOCK / _STREAM
-    int chunks;          // kernel instance: a bucket, or 0 for streaming
+    int path;            // RMSN_PATH_WAVE / _BLOCK / _STREAM / _SPLIT
+    int chunks;          // kernel instance: a bucket, or 0 for streaming; SPLIT:
+                         // 256-element chunks one wavefront holds
     int rows_per_block;  // wavefronts (= rows) per workgroup on the WAVE path, else 1
-    int streaming;       // WAVE path: non-temporal loads of x and stores of y
+    int streaming;       // WAVE / SPLIT: non-temporal loads of x and stores of y
     int block;           // threads per workgroup
     int64_t grid;        // workgroups
+    int loads;           // SPLIT: 16-byte loads per lane (slices per wavefront), else 0
 };
 
 inline int elem_bytes(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
 // Bytes one lane loads per 256-element chunk on the WAVE path: four elements.
 inline int vec_bytes(int dtype) { return 4 * elem_bytes(dtype); }
+// 1 KB slices of a row of width n (the last one may be partial).
+inline int64_t split_slices(int dtype, int64_t n) {
+    return (n * elem_bytes(dtype) + kSliceBytes - 1) / kSliceBytes;
+}
 
 // Smallest bucket holding ceil(n/256) chunks, or 0 if n needs more than kMaxChunks.
 int chunk_bucket(int64_t n);
@@ -46,16 +62,21 @@ int chunk_bucket(int64_t n);
 // Rows per workgroup and the streaming choice on the WAVE path, automatic.
 int auto_rows_per_block(int64_t rows);
 bool auto_streaming(int dtype, int64_t rows, int64_t n);
+// Slices per wavefront on the SPLIT path for a row of `slices` slices (0 if
+// the row is too long for kMaxSplitWaves wavefronts).
+int auto_split_loads(int64_t slices);
 
-// Plan a launch of `rows` rows of width n. `aligned`: every row's x and y and
-// the weight start on a vec_bytes(dtype) boundary. Returns RMSN_OK or
-// RMSN_EINVAL (bad dtype, rows < 1, n outside [1, 2^24]).
-int make_plan(int dtype, int64_t rows, int64_t n, bool aligned, Plan* out);
+// Plan a launch of `rows` rows of width n. `align`: a byte alignment shared by
+// every row start of x and y and by w (the largest power of two dividing it
+// counts, up to 16; values below the element size mean element alignment).
+// Returns RMSN_OK or RMSN_EINVAL (bad dtype, rows < 1, n outside [1, 2^24]).
+int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out);
 
 // Process-wide options (rmsnorm_set_option); read lazily from the environment.
 int option_path();            // -1 automatic, else an RMSN_PATH_* value
 int option_rows_per_block();  // 0 automatic, else 4 or 8
 int option_streaming();       // -1 automatic, 0 off, 1 on
+int option_split_loads();     // 0 automatic, else 1, 2, 4 or 8
 int set_option(int key, int value);
 int get_option(int key, int* value);
 

@@ -127,29 +127,76 @@ def test_diag_validation(rn):
 # ---- planning -------------------------------------------------------------------
 
 def test_plan_paths_and_buckets(rn):
-    # many aligned rows: one wavefront per row, eight rows per workgroup
-    # sharing one LDS copy of w; a 235 MB launch streams (non-temporal)
+    # many 16-byte aligned rows: a workgroup of 7 wavefronts per row, two 1 KB
+    # slices (16-byte loads) per wavefront; a 235 MB launch streams (non-temporal)
     p = rn.plan_query(rn.BF16, 8192, 7168, aligned=True)
+    assert p == {"path": rn.PATH_SPLIT, "chunks": 4, "rows_per_block": 1, "streaming": 1,
+                 "block": 448, "grid": 8192, "loads": 2}
+    # binary32: 28 slices, four per wavefront
+    p = rn.plan_query(rn.F32, 8192, 7168)
+    assert (p["path"], p["loads"], p["block"], p["chunks"]) == (rn.PATH_SPLIT, 4, 448, 4)
+    # a 29 MB launch keeps the default cache policy
+    assert rn.plan_query(rn.BF16, 1024, 7168)["streaming"] == 0
+    # rows aligned to 8 bytes only: one wavefront per row, eight rows per
+    # workgroup sharing one LDS copy of w
+    p = rn.plan_query(rn.BF16, 8192, 7168, align=8)
     assert p == {"path": rn.PATH_WAVE, "chunks": 28, "rows_per_block": 8, "streaming": 1,
-                 "block": 512, "grid": 1024}
-    # a 29 MB launch keeps the default cache policy; fewer than 2048 rows: 4 per workgroup
-    p = rn.plan_query(rn.BF16, 1024, 7168, aligned=True)
-    assert p["streaming"] == 0 and p["rows_per_block"] == 4 and p["grid"] == 256
+                 "block": 512, "grid": 1024, "loads": 0}
+    # fewer than 2048 rows: 4 per workgroup
+    p = rn.plan_query(rn.BF16, 1024, 7168, align=8)
+    assert p["path"] == rn.PATH_WAVE and p["rows_per_block"] == 4 and p["grid"] == 256
+    # a width that is not a whole number of 16-byte vectors: WAVE
+    assert rn.plan_query(rn.BF16, 4096, 7164)["path"] == rn.PATH_WAVE
     # few rows: a 256-thread workgroup per row
     p = rn.plan_query(rn.BF16, 64, 7168, aligned=True)
     assert p == {"path": rn.PATH_BLOCK, "chunks": 28, "rows_per_block": 1, "streaming": 0,
-                 "block": 256, "grid": 64}
+                 "block": 256, "grid": 64, "loads": 0}
     # single rows of the decode step
     assert rn.plan_query(rn.F32, 1, 7168)["chunks"] == 28
     assert rn.plan_query(rn.F32, 1, 1536)["chunks"] == 6
     assert rn.plan_query(rn.F32, 1, 512)["chunks"] == 2
-    # unaligned rows never take the WAVE path
+    # unaligned rows never take the WAVE or SPLIT path
     assert rn.plan_query(rn.F32, 4096, 7168, aligned=False)["path"] == rn.PATH_BLOCK
-    # beyond 8192 elements: streamed
+    assert rn.plan_query(rn.F32, 4096, 7168, align=4)["path"] == rn.PATH_BLOCK
+    assert rn.plan_query(rn.F32, 4096, 7168, align=24)["path"] == rn.PATH_BLOCK  # 8 B
+    assert rn.plan_query(rn.BF16, 4096, 7168, align=24)["path"] == rn.PATH_WAVE
+    # beyond 8192 elements: SPLIT up to 128 KB rows of whole vectors, else streamed
     p = rn.plan_query(rn.F32, 3, 8193)
     assert p["path"] == rn.PATH_STREAM and p["chunks"] == 0 and p["grid"] == 3
+    p = rn.plan_query(rn.F32, 3, 8196)
+    assert p["path"] == rn.PATH_SPLIT and p["loads"] == 8 and p["block"] == 320
+    p = rn.plan_query(rn.BF16, 2, 65536)
+    assert p["path"] == rn.PATH_SPLIT and p["loads"] == 8 and p["block"] == 1024
+    assert rn.plan_query(rn.BF16, 2, 65544)["path"] == rn.PATH_STREAM
     p = rn.plan_query(rn.F32, 1, 1 << 24)
     assert p["path"] == rn.PATH_STREAM
+
+
+@pytest.mark.parametrize("n,es", [(4, 4), (8, 2), (256, 4), (1000, 2), (2056, 2), (7168, 2),
+                                  (7168, 4), (8196, 4), (12000, 4), (20000, 2), (32768, 4),
+                                  (65536, 2)])
+def test_split_geometry(rn, n, es):
+    """Every SPLIT plan: the fewest slices per wavefront keeping a row within 8
+    wavefronts (else 16), and a forced slice count honoured when it fits."""
+    dtype = rn.F32 if es == 4 else rn.BF16
+    slices = -(-n * es // 1024)
+    try:
+        rn.set_option(rn.OPT_PATH, rn.PATH_SPLIT)
+        p = rn.plan_query(dtype, 5, n)
+        assert p["path"] == rn.PATH_SPLIT
+        fits8 = [u for u in (1, 2, 4, 8) if -(-slices // u) <= 8]
+        fits16 = [u for u in (1, 2, 4, 8) if -(-slices // u) <= 16]
+        assert p["loads"] == (fits8[0] if fits8 else fits16[0])
+        assert p["block"] == 64 * -(-slices // p["loads"])
+        assert p["chunks"] == p["loads"] * 1024 // (256 * es)
+        for u in (1, 2, 4, 8):
+            rn.set_option(rn.OPT_SPLIT_LOADS, u)
+            q = rn.plan_query(dtype, 5, n)
+            want = u if -(-slices // u) <= 16 else p["loads"]
+            assert q["loads"] == want and q["block"] == 64 * -(-slices // want)
+    finally:
+        rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
+        rn.set_option(rn.OPT_SPLIT_LOADS, 0)
 
 
 @pytest.mark.parametrize("n", [1, 255, 256, 257, 511, 512, 513, 1024, 1535, 1536, 2049, 3072,
@@ -178,27 +225,42 @@ def test_options_roundtrip_and_force_paths(rn):
         assert rn.plan_query(rn.BF16, 8192, 7168)["path"] == rn.PATH_BLOCK
         rn.set_option(rn.OPT_PATH, rn.PATH_WAVE)
         assert rn.plan_query(rn.BF16, 3, 7168)["path"] == rn.PATH_WAVE
+        assert rn.plan_query(rn.BF16, 8192, 7168)["path"] == rn.PATH_WAVE
         # ineligible: falls back to the automatic choice
         assert rn.plan_query(rn.BF16, 3, 7168, aligned=False)["path"] == rn.PATH_BLOCK
-        assert rn.plan_query(rn.BF16, 3, 9000)["path"] == rn.PATH_STREAM
+        assert rn.plan_query(rn.BF16, 3, 9000)["path"] == rn.PATH_SPLIT
+        assert rn.plan_query(rn.BF16, 3, 9001)["path"] == rn.PATH_STREAM
+        rn.set_option(rn.OPT_PATH, rn.PATH_SPLIT)
+        assert rn.plan_query(rn.BF16, 3, 7168)["path"] == rn.PATH_SPLIT
+        assert rn.plan_query(rn.BF16, 3, 7167)["path"] == rn.PATH_BLOCK
+        assert rn.plan_query(rn.BF16, 3, 7168, align=8)["path"] == rn.PATH_BLOCK
         rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
         rn.set_option(rn.OPT_ROWS_PER_BLOCK, 4)
-        p = rn.plan_query(rn.BF16, 8191, 7168)
+        p = rn.plan_query(rn.BF16, 8191, 7168, align=8)
         assert p["rows_per_block"] == 4 and p["grid"] == 2048 and p["block"] == 256
         rn.set_option(rn.OPT_STREAMING, 0)
         assert rn.plan_query(rn.BF16, 8191, 7168)["streaming"] == 0
+        assert rn.plan_query(rn.BF16, 8191, 7168, align=8)["streaming"] == 0
         rn.set_option(rn.OPT_STREAMING, 1)
         assert rn.plan_query(rn.BF16, 1024, 256)["streaming"] == 1
         assert rn.get_option(rn.OPT_STREAMING) == 1
+        rn.set_option(rn.OPT_SPLIT_LOADS, 4)
+        assert rn.get_option(rn.OPT_SPLIT_LOADS) == 4
+        p = rn.plan_query(rn.BF16, 8192, 7168)
+        assert p["loads"] == 4 and p["block"] == 256
         for bad in ((rn.OPT_ROWS_PER_BLOCK, 3), (rn.OPT_ROWS_PER_BLOCK, 1),
-                    (rn.OPT_STREAMING, 2), (rn.OPT_STREAMING, -2)):
+                    (rn.OPT_STREAMING, 2), (rn.OPT_STREAMING, -2),
+                    (rn.OPT_SPLIT_LOADS, 3), (rn.OPT_SPLIT_LOADS, 16), (rn.OPT_SPLIT_LOADS, -1)):
             with pytest.raises(rn.RmsnormError):
                 rn.set_option(*bad)
         with pytest.raises(rn.RmsnormError):
             rn.set_option(rn.OPT_PATH, 7)
+        with pytest.raises(rn.RmsnormError):
+            rn.set_option(rn.OPT_PATH, 4)
         with pytest.raises(rn.RmsnormError):
             rn.set_option(99, 0)
     finally:
         rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
         rn.set_option(rn.OPT_ROWS_PER_BLOCK, 0)
         rn.set_option(rn.OPT_STREAMING, -1)
+        rn.set_option(rn.OPT_SPLIT_LOADS, 0)

@@ -27,6 +27,7 @@ def rn():
     m.set_option(m.OPT_PATH, m.PATH_AUTO)
     m.set_option(m.OPT_ROWS_PER_BLOCK, 0)
     m.set_option(m.OPT_STREAMING, -1)
+    m.set_option(m.OPT_SPLIT_LOADS, 0)
     return m
 
 
@@ -144,7 +145,7 @@ def test_prefill_bf16_full(rn):
     say("bf16 8192 x 7168 (generating inputs)")
     xb, wb = wl.prefill()
     plan = rn.plan_query(rn.BF16, 8192, 7168)
-    assert plan["path"] == rn.PATH_WAVE
+    assert plan["path"] == rn.PATH_SPLIT
     say(f"bf16 8192 x 7168 plan {plan}")
     got = gpu_rows(rn, xb, wb, wl.EPS, rn.BF16)
     say("bf16 8192 x 7168 oracle")
@@ -153,8 +154,12 @@ def test_prefill_bf16_full(rn):
     try:
         rn.set_option(rn.OPT_STREAMING, 0)
         assert_bits_bf16(gpu_rows(rn, xb, wb, wl.EPS, rn.BF16), want, "prefill, cached loads")
+        rn.set_option(rn.OPT_STREAMING, -1)
+        rn.set_option(rn.OPT_PATH, rn.PATH_WAVE)
+        assert_bits_bf16(gpu_rows(rn, xb, wb, wl.EPS, rn.BF16), want, "prefill, WAVE path")
     finally:
         rn.set_option(rn.OPT_STREAMING, -1)
+        rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
 
 
 # ---- every code path gives the same bits ---------------------------------------------
@@ -164,7 +169,19 @@ PATH_CASES = [
     (6, 8192, "bf16"), (3, 9000, "f32"), (17, 1536, "f32"), (9, 512, "bf16"), (4, 1, "f32"),
     (12, 255, "f32"), (7, 7167, "bf16"), (19, 7168, "bf16"), (21, 2048, "bf16"),
     (13, 3072, "f32"),
+    # SPLIT shapes: rows of one partial slice, a last slice of one vector,
+    # partial last wavefronts, and rows of 64 and 128 KB (8 and 16 wavefronts)
+    (5, 24, "f32"), (4, 8, "bf16"), (6, 2056, "bf16"), (3, 12000, "f32"),
+    (3, 16384, "f32"), (2, 20000, "bf16"), (2, 32768, "bf16"), (2, 65536, "bf16"),
 ]
+
+# (path, rows per block, streaming, split loads) settings every case runs under
+PATH_SETTINGS = (
+    [(-1, 0, -1, 0)]
+    + [(0, rpb, st, 0) for rpb in (0, 4, 8) for st in (-1, 0, 1)]
+    + [(1, 0, -1, 0), (2, 0, -1, 0)]
+    + [(3, 0, st, u) for u in (0, 1, 2, 4, 8) for st in (-1, 0, 1)]
+)
 
 
 def _rows_input(rows, n, kind, item):
@@ -176,6 +193,13 @@ def _rows_input(rows, n, kind, item):
     return x, w
 
 
+def _reset_options(rn):
+    rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
+    rn.set_option(rn.OPT_ROWS_PER_BLOCK, 0)
+    rn.set_option(rn.OPT_STREAMING, -1)
+    rn.set_option(rn.OPT_SPLIT_LOADS, 0)
+
+
 @pytest.mark.parametrize("rows,n,kind", PATH_CASES)
 def test_paths_and_rows_per_block_identical(rn, rows, n, kind):
     say(f"paths: {rows} x {n} {kind}")
@@ -183,18 +207,37 @@ def test_paths_and_rows_per_block_identical(rn, rows, n, kind):
     x, w = _rows_input(rows, n, kind, n)
     want = oracle_rows(x, w, wl.EPS)
     try:
-        for path in (rn.PATH_AUTO, rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM):
-            for rpb in ((0, 4, 8) if path == rn.PATH_WAVE else (0,)):
-                for st in ((-1, 0, 1) if path == rn.PATH_WAVE else (-1,)):
-                    rn.set_option(rn.OPT_PATH, path)
-                    rn.set_option(rn.OPT_ROWS_PER_BLOCK, rpb)
-                    rn.set_option(rn.OPT_STREAMING, st)
-                    got = gpu_rows(rn, x, w, wl.EPS, dtype)
-                    assert_rows(rn, got, want, dtype, f"path {path} rpb {rpb} streaming {st}")
+        for path, rpb, st, u in PATH_SETTINGS:
+            rn.set_option(rn.OPT_PATH, path)
+            rn.set_option(rn.OPT_ROWS_PER_BLOCK, rpb)
+            rn.set_option(rn.OPT_STREAMING, st)
+            rn.set_option(rn.OPT_SPLIT_LOADS, u)
+            got = gpu_rows(rn, x, w, wl.EPS, dtype)
+            assert_rows(rn, got, want, dtype,
+                        f"path {path} rpb {rpb} streaming {st} split loads {u}")
     finally:
-        rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
-        rn.set_option(rn.OPT_ROWS_PER_BLOCK, 0)
-        rn.set_option(rn.OPT_STREAMING, -1)
+        _reset_options(rn)
+
+
+def test_split_plans_cover_their_shapes(rn):
+    """The SPLIT cases above really take the SPLIT path, with the geometry the
+    kernel assumes (a check of the test itself, host only)."""
+    for rows, n, kind in PATH_CASES:
+        dtype = rn.F32 if kind == "f32" else rn.BF16
+        es = 4 if kind == "f32" else 2
+        if (n * es) % 16:
+            continue
+        p = rn.plan_query(dtype, rows, n, align=16)
+        slices = -(-n * es // 1024)
+        if p["path"] != rn.PATH_SPLIT:
+            assert p["path"] == rn.PATH_BLOCK and n <= 8192, (rows, n, kind, p)
+            try:
+                rn.set_option(rn.OPT_PATH, rn.PATH_SPLIT)
+                p = rn.plan_query(dtype, rows, n, align=16)
+            finally:
+                _reset_options(rn)
+        assert p["path"] == rn.PATH_SPLIT, (rows, n, kind, p)
+        assert p["block"] == 64 * -(-slices // p["loads"]) and p["block"] <= 1024
 
 
 def test_single_row_entry_equals_batched(rn):
@@ -251,7 +294,7 @@ def test_association_probes(rn):
     for i, x in enumerate(_probe_rows()):
         w = np.ones_like(x)
         want = oracle.row_f32(x, w, np.float32(0))
-        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM):
+        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT):
             try:
                 rn.set_option(rn.OPT_PATH, path)
                 xr = np.repeat(x[None, :], 2, axis=0)
@@ -262,9 +305,31 @@ def test_association_probes(rn):
             assert_bits_f32(got[1], want, f"probe {i} path {path}")
 
 
-def test_special_values(rn):
-    say("special values")
-    n = 777
+def test_association_probes_bf16(rn):
+    """The same probes in bf16 (every probe value is a bf16 number): the bf16
+    layouts place association lanes differently from the binary32 ones."""
+    say("association probes, bf16")
+    for i, x in enumerate(_probe_rows()):
+        xb = wl.to_bf16_bits(x)
+        wb = wl.to_bf16_bits(np.ones_like(x))
+        assert np.array_equal(oracle.bf16_to_f32(xb), x)
+        want = oracle.row_bf16(xb, wb, np.float32(0))
+        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT):
+            for u in ((0, 1, 2, 4) if path == rn.PATH_SPLIT else (0,)):
+                try:
+                    rn.set_option(rn.OPT_PATH, path)
+                    rn.set_option(rn.OPT_SPLIT_LOADS, u)
+                    got = gpu_rows(rn, np.repeat(xb[None, :], 2, axis=0), wb, np.float32(0),
+                                   rn.BF16)
+                finally:
+                    _reset_options(rn)
+                assert_bits_bf16(got[0], want, f"bf16 probe {i} path {path} loads {u}")
+                assert_bits_bf16(got[1], want, f"bf16 probe {i} path {path} loads {u}")
+
+
+@pytest.mark.parametrize("n", [777, 1000])
+def test_special_values(rn, n):
+    say(f"special values n={n}")
     g = np.random.Generator(np.random.PCG64(123))
     cases = []
     cases.append((np.zeros(n, np.float32), np.float32(0)))               # 0 * inf = NaN
@@ -280,7 +345,7 @@ def test_special_values(rn):
     w = (1.0 + 0.1 * g.standard_normal(n)).astype(np.float32)
     for i, (x, eps) in enumerate(cases):
         want = oracle.row_f32(x, w, eps)
-        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM):
+        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT):
             try:
                 rn.set_option(rn.OPT_PATH, path)
                 got = gpu_rows(rn, np.repeat(x[None, :], 2, axis=0), w, eps, rn.F32)
@@ -289,8 +354,14 @@ def test_special_values(rn):
             assert_bits_f32(got[1], want, f"case {i} path {path}")
         # bf16 with the same values rounded to bf16
         xb, wb = wl.to_bf16_bits(x), wl.to_bf16_bits(w)
-        assert_bits_bf16(gpu_rows(rn, xb[None, :], wb, eps, rn.BF16)[0],
-                         oracle.row_bf16(xb, wb, eps), f"bf16 case {i}")
+        want_b = oracle.row_bf16(xb, wb, eps)
+        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT):
+            try:
+                rn.set_option(rn.OPT_PATH, path)
+                got = gpu_rows(rn, np.repeat(xb[None, :], 2, axis=0), wb, eps, rn.BF16)
+            finally:
+                rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
+            assert_bits_bf16(got[1], want_b, f"bf16 case {i} path {path}")
 
 
 def test_in_place(rn):
