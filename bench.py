@@ -12,6 +12,7 @@ cache defeated by rotating over 4 buffer sets (940 MB). Also reported:
   graph replay (Lecture 08 section 1), A/A then ABBA x 3 with per-rep
   numbers and standard errors (Lecture 04 section 6.1);
 * roofline: the prefill kernel against the 8 TB/s HBM peak;
+* prefill.wave_path_us: the same launches on the one-wavefront-per-row layout;
 * cpu_baseline: the CPU oracle timed on this host (a reported baseline only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D]
@@ -123,6 +124,13 @@ def bench_prefill(rn, torch, np, wl, steps, warmup):
         rot_cached = 1000.0 * elapsed_ms(step, steps) / steps
     finally:
         rn.set_option(rn.OPT_STREAMING, -1)
+    # the one-wavefront-per-row layout on the same rotated launches, for comparison
+    rn.set_option(rn.OPT_PATH, rn.PATH_WAVE)
+    try:
+        wave_plan = rn.plan_query(rn.BF16, rows, n, aligned=True)
+        wave_us = 1000.0 * elapsed_ms(step, steps) / steps
+    finally:
+        rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
     # a plain device copy of the same bytes (x read, y written), rotated the
     # same way: the practical bandwidth ceiling of this traffic pattern
     copy_us = 1000.0 * elapsed_ms(lambda i: ys[i % ROTATE].copy_(xs[i % ROTATE]), steps) / steps
@@ -142,6 +150,7 @@ def bench_prefill(rn, torch, np, wl, steps, warmup):
         "warm_gbs": algo_bytes / (warm * 1e-6) / 1e9,
         "warm_cached_us": warm_cached, "rotated_cached_us": rot_cached,
         "copy_us": copy_us, "copy_gbs": (rows * n * 4) / (copy_us * 1e-6) / 1e9,
+        "wave_path_us": wave_us, "wave_path_plan": wave_plan,
         "rows_per_s": rows / (us * 1e-6), "spot_parity": parity,
         "host": (xb, wb),
     }
@@ -360,7 +369,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed prefill launches first (the first ~300 launches after a "
+                         "cold start run slower while the clocks settle)")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true")
@@ -453,6 +464,9 @@ def main():
             "warm_gbs": round(pre["warm_gbs"], 1), "rows_per_s": pre["rows_per_s"],
             "warm_cached_us": round(pre["warm_cached_us"], 3),
             "rotated_cached_us": round(pre["rotated_cached_us"], 3),
+            "wave_path_us": round(pre["wave_path_us"], 3),
+            "wave_path_gbs": round(pre["algo_bytes"] / (pre["wave_path_us"] * 1e-6) / 1e9, 1),
+            "wave_path_plan": pre["wave_path_plan"],
             "copy_reference_us": round(pre["copy_us"], 3),
             "copy_reference_gbs": round(pre["copy_gbs"], 1),
             "fraction_of_copy": round(pre["copy_us"] / pre["us_per_launch"], 4),

@@ -713,6 +713,9 @@ __global__ __launch_bounds__(1024) void k_rows_split(const T* x, int64_t xs,
               scalar_gptr(reinterpret_cast<const char*>(w)), s, lane, nvec);
     for (int h = 0; h < waves; ++h) {
         if (h == s) {
+            // the turn is the row's critical path: let this wavefront's
+            // instructions go first on its SIMD
+            __builtin_amdgcn_s_setprio(3);
             float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if (s > 0) {
                 const f32x4 q = hand[lane];
@@ -727,6 +730,7 @@ __global__ __launch_bounds__(1024) void k_rows_split(const T* x, int64_t xs,
                 const float inv = inverse_rms(split_sumsq(p, lane, T()), n, eps);
                 if (lane == 0) inv_shared = inv;
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         __syncthreads();
     }
