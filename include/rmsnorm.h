@@ -155,8 +155,20 @@ const char* rmsnorm_last_error(void);
  *                     where the previous wavefront left them (handed over
  *                     through LDS), so the association is unchanged. Needs
  *                     16-byte aligned rows and w, n * element size a multiple
- *                     of 16, and rows of at most 128 KB. */
-enum { RMSN_PATH_WAVE = 0, RMSN_PATH_BLOCK = 1, RMSN_PATH_STREAM = 2, RMSN_PATH_SPLIT = 3 };
+ *                     of 16, and rows of at most 128 KB.
+ *   RMSN_PATH_GROUP:  BLOCK's chains-to-threads mapping, but wavefront g reads
+ *                     its group's 64 elements of four consecutive 256-element
+ *                     chunks with one 16-byte (binary32) / 8-byte (bf16) load
+ *                     per lane and transposes them in registers: a quarter of
+ *                     BLOCK's load instructions. Needs quad-aligned pointers
+ *                     (16 B / 8 B), n a multiple of 4 and n <= 8192. */
+enum {
+    RMSN_PATH_WAVE = 0,
+    RMSN_PATH_BLOCK = 1,
+    RMSN_PATH_STREAM = 2,
+    RMSN_PATH_SPLIT = 3,
+    RMSN_PATH_GROUP = 4
+};
 
 typedef struct rmsn_plan_info {
     int32_t path;            /* one of RMSN_PATH_*                                */
@@ -168,14 +180,16 @@ typedef struct rmsn_plan_info {
     int32_t streaming;       /* WAVE / SPLIT: 1 = non-temporal loads of x and
                                 stores of y                                       */
     int32_t loads;           /* SPLIT: 16-byte loads per lane (1 KB slices per
-                                wavefront), else 0                                */
+                                wavefront); GROUP: loads per lane (1024-element
+                                blocks); else 0                                   */
 } rmsn_plan_info;
 
 /* The launch the library would use for `rows` rows of width n whose row starts
  * (x and y) and weight all share the byte alignment `align` (the largest power
  * of two dividing it counts, up to 16; 0 or anything below the element size
- * means element alignment only). Same function the launches use. Returns
- * RMSN_EINVAL for an invalid dtype, rows or n. */
+ * means element alignment only; -1 plans a descriptor row of a sequence,
+ * whose pointers the kernel checks when it runs). Same function the launches
+ * use. Returns RMSN_EINVAL for an invalid dtype, rows or n. */
 int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_info* out);
 
 /* Process-wide overrides, for proving that code paths give identical bits
@@ -183,9 +197,9 @@ int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_
  * environment at first use, else automatic.
  *   RMSN_OPT_PATH:           -1 automatic, or an RMSN_PATH_* value; a path a
  *                            launch is not eligible for (WAVE on unaligned
- *                            rows or n > 8192, BLOCK with n > 8192, SPLIT
- *                            outside its conditions above) falls back to the
- *                            automatic choice
+ *                            rows or n > 8192, BLOCK with n > 8192, SPLIT or
+ *                            GROUP outside their conditions above) falls back
+ *                            to the automatic choice
  *   RMSN_OPT_ROWS_PER_BLOCK:  0 automatic, else 4 or 8 rows (wavefronts) per
  *                            workgroup sharing one LDS copy of w (WAVE path)
  *   RMSN_OPT_STREAMING:      -1 automatic (on when x + y of the launch reach
@@ -215,6 +229,14 @@ int rmsnorm_get_option(int key, int* value);
  * check the device square root and division against a CPU exhaustively. */
 int rmsnorm_diag_inverse(uint32_t first_bits, int64_t count, int64_t n, float eps, float* r_out,
                          float* inv_out, void* stream);
+
+/* Runs the kernels' own binary32 -> bf16 narrowing of step 8 (the device
+ * function every bf16 store calls) on count consecutive bit patterns starting
+ * at first_bits: out[i] = bf16(pattern first_bits + i), a DEVICE array of count
+ * uint16. Used to check the hardware conversion against a CPU for every
+ * binary32 pattern. RMSN_EINVAL if the range leaves 32 bits or out is null or
+ * odd. */
+int rmsnorm_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -53,6 +53,8 @@ def _load():
     lib.rmsn_ref_bf16_to_f32.restype = c_f
     lib.rmsn_ref_f32_to_bf16.argtypes = [c_f]
     lib.rmsn_ref_f32_to_bf16.restype = ctypes.c_uint16
+    lib.rmsn_ref_f32_to_bf16_range.argtypes = [ctypes.c_uint32, c_i64, c_vp]
+    lib.rmsn_ref_f32_to_bf16_range.restype = None
     _lib = lib
     return lib
 
@@ -134,6 +136,16 @@ def bf16_to_f32(bits):
 
 def f32_to_bf16_scalar(v):
     return int(_load().rmsn_ref_f32_to_bf16(float(np.float32(v))))
+
+
+def f32_to_bf16_range(first_bits, count, out=None):
+    """Step 8's narrowing of the binary32 bit patterns first_bits,
+    first_bits + 1, ... (count of them), as a uint16 array."""
+    if out is None:
+        out = np.empty(int(count), dtype=np.uint16)
+    assert out.dtype == np.uint16 and out.flags.c_contiguous and out.size >= count
+    _load().rmsn_ref_f32_to_bf16_range(int(first_bits), int(count), _ptr(out))
+    return out[:count]
 
 
 def float64_reference(x, w, eps):

@@ -45,6 +45,16 @@ uint16_t rmsn_ref_f32_to_bf16(float v)
     return (uint16_t)(u >> 16);
 }
 
+void rmsn_ref_f32_to_bf16_range(uint32_t first_bits, int64_t count, uint16_t* out)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        const uint32_t u = first_bits + (uint32_t)i;
+        float v;
+        memcpy(&v, &u, sizeof v);
+        out[i] = rmsn_ref_f32_to_bf16(v);
+    }
+}
+
 /* Steps 1-3 given the row as binary32 values produced by `get`. */
 typedef float (*getter)(const void* row, int64_t d);
 

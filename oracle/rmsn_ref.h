@@ -64,6 +64,9 @@ int rmsn_ref_rows(int dtype, const void* x, int64_t x_stride, const void* w,
 /* Exact bf16 widening and the round-to-nearest-even narrowing of step 8. */
 float rmsn_ref_bf16_to_f32(uint16_t b);
 uint16_t rmsn_ref_f32_to_bf16(float v);
+/* The narrowing over `count` consecutive binary32 bit patterns from
+ * first_bits: out[i] = rmsn_ref_f32_to_bf16(bits first_bits + i). */
+void rmsn_ref_f32_to_bf16_range(uint32_t first_bits, int64_t count, uint16_t* out);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "librmsnorm_amd.so")
 
 RMSN_OK, RMSN_EINVAL, RMSN_EHIP, RMSN_ECAPTURE, RMSN_ENOMEM = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
-PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM, PATH_SPLIT = -1, 0, 1, 2, 3
+PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM, PATH_SPLIT, PATH_GROUP = -1, 0, 1, 2, 3, 4
 OPT_PATH, OPT_ROWS_PER_BLOCK, OPT_STREAMING, OPT_SPLIT_LOADS = 1, 2, 3, 4
 MAX_N = 1 << 24
 DESC_BYTES = 32
@@ -60,6 +60,7 @@ def _load():
         "rmsnorm_set_option": [c_int, c_int],
         "rmsnorm_get_option": [c_int, ctypes.POINTER(c_int)],
         "rmsnorm_diag_inverse": [u32, i64, i64, f, vp, vp, vp],
+        "rmsnorm_diag_bf16": [u32, i64, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -76,7 +77,8 @@ EXPORTED = ("rmsnorm_f32", "rmsnorm_bf16", "rmsnorm_batched_rows", "rmsnorm_sequ
             "rmsnorm_sequence_graph_create", "rmsnorm_sequence_graph_launch",
             "rmsnorm_sequence_graph_destroy", "rmsnorm_graph_node_count",
             "rmsnorm_graph_is_fallback", "rmsnorm_last_error", "rmsnorm_plan_query",
-            "rmsnorm_set_option", "rmsnorm_get_option", "rmsnorm_diag_inverse")
+            "rmsnorm_set_option", "rmsnorm_get_option", "rmsnorm_diag_inverse",
+            "rmsnorm_diag_bf16")
 
 
 def lib():
@@ -253,6 +255,13 @@ def get_option(key):
     v = ctypes.c_int()
     _check(_lib.rmsnorm_get_option(int(key), ctypes.byref(v)))
     return v.value
+
+
+def diag_bf16(first_bits, count, out, stream=None):
+    """Step 8's bf16 narrowing of the kernels over consecutive bit patterns
+    (diagnostic); `out`: a device tensor of at least `count` 2-byte elements."""
+    _check(_lib.rmsnorm_diag_bf16(int(first_bits), int(count), ctypes.c_void_p(out.data_ptr()),
+                                  _stream_ptr(stream)))
 
 
 def diag_inverse(first_bits, count, n, eps, r_out, inv_out, stream=None):

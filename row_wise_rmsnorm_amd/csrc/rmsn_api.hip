@@ -67,8 +67,9 @@ int run_rows(int dtype, const void* x, int64_t xs, const void* w, void* y, int64
 int plan_sequence(int dtype, const int64_t* widths, int32_t count, std::vector<Plan>* plans) {
     plans->resize((size_t)count);
     for (int32_t i = 0; i < count; ++i) {
-        // Descriptor rows may have any element alignment: BLOCK or STREAM only.
-        const int st = make_plan(dtype, 1, widths[i], 0, &(*plans)[(size_t)i]);
+        // Descriptor rows may have any element alignment: GROUP (whose kernel
+        // checks the pointers it reads), BLOCK or STREAM.
+        const int st = make_plan(dtype, 1, widths[i], kAlignAtRunTime, &(*plans)[(size_t)i]);
         if (st != RMSN_OK) return st;
     }
     return RMSN_OK;
@@ -101,12 +102,13 @@ int prewarm(const std::vector<Plan>& plans, int dtype, float eps, hipStream_t s)
         (e = hipMemcpyAsync(base + 128, one, es, hipMemcpyHostToDevice, s)) != hipSuccess) {
         st = hip_fail("hipMemcpyAsync (pre-warm row)", e);
     }
-    std::vector<int> seen;
+    std::vector<int> seen;  // kernel variants already run: path * 256 + chunks
     for (size_t i = 0; st == RMSN_OK && i < plans.size(); ++i) {
+        const int key = plans[i].path * 256 + plans[i].chunks;
         bool dup = false;
-        for (int c : seen) dup = dup || c == plans[i].chunks;
+        for (int c : seen) dup = dup || c == key;
         if (dup) continue;
-        seen.push_back(plans[i].chunks);
+        seen.push_back(key);
         e = launch_desc(plans[i], reinterpret_cast<const rmsn_desc*>(base), eps, s);
         if (e != hipSuccess) st = hip_fail("pre-warm launch", e);
     }
@@ -326,6 +328,25 @@ int rmsnorm_set_option(int key, int value) {
 int rmsnorm_get_option(int key, int* value) {
     clear_error();
     return get_option(key, value);
+}
+
+int rmsnorm_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out, void* stream) {
+    clear_error();
+    if (!out) {
+        set_error("null output pointer");
+        return RMSN_EINVAL;
+    }
+    if (count < 0 || (uint64_t)first_bits + (uint64_t)count > 0x100000000ull) {
+        set_error("bit-pattern range [%u, %u + %lld) leaves 32 bits", first_bits, first_bits,
+                  (long long)count);
+        return RMSN_EINVAL;
+    }
+    if ((uintptr_t)out % 2) {
+        set_error("output must be 2-byte aligned");
+        return RMSN_EINVAL;
+    }
+    const hipError_t e = launch_diag_bf16(first_bits, count, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? RMSN_OK : hip_fail("diagnostic launch", e);
 }
 
 int rmsnorm_diag_inverse(uint32_t first_bits, int64_t count, int64_t n, float eps, float* r_out,

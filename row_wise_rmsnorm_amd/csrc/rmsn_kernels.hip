@@ -28,6 +28,11 @@
 //          pointer works; the row stays in VGPRs (n <= 256 * chunks).
 //   STREAM BLOCK's mapping, but the row is streamed twice (once for the sum,
 //          once for the apply) instead of being held: any n up to 2^24.
+//   GROUP  BLOCK's mapping of chains to threads, but wavefront g reads its
+//          group's 64 elements of four chunks with one 16-byte (binary32) /
+//          8-byte (bf16) load per lane and a 4x4 register transpose (32- and
+//          16-lane swaps) gives each lane one chain over those four chunks:
+//          a quarter of the load instructions of BLOCK.
 //   SPLIT  one workgroup of S wavefronts per row, the row cut into 1 KB slices
 //          (one 16-byte load per lane). Wavefront s holds U consecutive
 //          slices; it continues the 256 lane chains from where wavefront s-1
@@ -78,12 +83,18 @@ __device__ __forceinline__ gptr scalar_gptr(gptr p) {
 __device__ __forceinline__ float widen(float v) { return v; }
 __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// binary32 -> bf16, round to nearest, ties to even on the 16 dropped bits;
-// NaN -> quiet NaN keeping the sign.
+// binary32 -> bf16, round to nearest, ties to even (the MODE register's
+// default rounding), denormals kept, NaN -> a quiet NaN: one
+// v_cvt_pk_bf16_f32 per pair of values. Checked against the CPU narrowing for
+// every binary32 bit pattern through rmsnorm_diag_bf16.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) & 0x8000u) | 0x7FC0u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ void put(float* p, float v) { *p = v; }
@@ -142,8 +153,8 @@ template <> struct Quad<uint16_t> {
     template <bool NT>
     static __device__ __forceinline__ void gstore(gptr p, const float v[4]) {
         u32x2 q;
-        q.x = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-        q.y = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+        q.x = bf16_pair(v[0], v[1]);
+        q.y = bf16_pair(v[2], v[3]);
         auto* a = reinterpret_cast<__attribute__((address_space(1))) u32x2*>(p);
         if (NT) __builtin_nontemporal_store(q, a);
         else *a = q;
@@ -167,8 +178,8 @@ template <> struct Quad<uint16_t> {
     }
     static __device__ __forceinline__ void store(uint16_t* p, const float v[4]) {
         uint2 q;
-        q.x = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-        q.y = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
+        q.x = bf16_pair(v[0], v[1]);
+        q.y = bf16_pair(v[2], v[3]);
         *reinterpret_cast<uint2*>(p) = q;
     }
 };
@@ -460,7 +471,7 @@ __device__ __forceinline__ u32x4 slice_apply(u32x4 x, u32x4 w, float inv, float)
 __device__ __forceinline__ uint32_t apply_pair(uint32_t x, uint32_t w, float inv) {
     const float lo = (lo_bf16(x) * inv) * lo_bf16(w);
     const float hi = (hi_bf16(x) * inv) * hi_bf16(w);
-    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+    return bf16_pair(lo, hi);
 }
 __device__ __forceinline__ u32x4 slice_apply(u32x4 x, u32x4 w, float inv, uint16_t) {
     u32x4 o;
@@ -533,6 +544,108 @@ struct SplitPart {
         }
     }
 };
+
+// ---------------------------------------------------------------------------
+// GROUP layout: 256 threads per row; wavefront g owns association group g.
+// One load per lane covers the group's 64 elements in four consecutive
+// 256-element chunks: lane 16q + t reads elements 256(4m+q) + 64g + 4t + {0..3}
+// of block m (1024 elements). A 4x4 transpose between the lane's 16-lane row
+// q and its register index then leaves lane 16q + t holding chain
+// 64g + 4t + q for chunks 4m .. 4m+3, in order.
+
+// Lanes 0..15 / 32..47 keep their own a and receive b's rows 0 / 2; lanes
+// 16..31 / 48..63 keep their own b and receive a's rows 1 / 3:
+//   first  = a with its odd 16-lane rows replaced by b's even rows
+//   second = b with its even 16-lane rows replaced by a's odd rows
+__device__ __forceinline__ SwapPair swap16(uint32_t a, uint32_t b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    return {r[0], r[1]};
+}
+
+// v[e] of lane 16q + t is X[q][e] (row q, register e); afterwards v[k] of that
+// lane is X[k][q].
+__device__ __forceinline__ void transpose4(float v[4]) {
+    const SwapPair a = swap32(__float_as_uint(v[0]), __float_as_uint(v[2]));
+    const SwapPair b = swap32(__float_as_uint(v[1]), __float_as_uint(v[3]));
+    // rows 0,1 of registers 2,3 moved to rows 2,3 of registers 0,1 and back
+    const SwapPair c = swap16(a.first, b.first);
+    const SwapPair d = swap16(a.second, b.second);
+    v[0] = __uint_as_float(c.first);
+    v[1] = __uint_as_float(c.second);
+    v[2] = __uint_as_float(d.first);
+    v[3] = __uint_as_float(d.second);
+}
+
+// Group tree of the GROUP layout: association lane 64g + 4t + q sits in lane
+// 16q + t. Halving 32/16/8/4 moves t by 8/4/2/1 (DPP row shifts); halving 2
+// and 1 move q by 2 and 1, i.e. lanes 0/32 and 16/48.
+__device__ __forceinline__ float group_sumsq(float p) {
+    p += row_shl<8>(p);
+    p += row_shl<4>(p);
+    p += row_shl<2>(p);
+    p += row_shl<1>(p);
+    return (lane_value(p, 0) + lane_value(p, 32)) + (lane_value(p, 16) + lane_value(p, 48));
+}
+
+// One row on the GROUP layout, Q blocks of 1024 elements: requires
+// 1024 (Q-1) < n <= 1024 Q, n a multiple of 4 and x, w, y aligned to a quad
+// (16 B binary32, 8 B bf16). Blocks below Q-1 are complete; in the last one,
+// quads past the row are loaded from the row's last quad (an in-row address)
+// and masked to +0 after every load has been issued.
+template <typename T, int Q>
+__device__ __forceinline__ void row_group(const T* x, const T* __restrict__ w, T* y, int n,
+                                          float eps, float* lds4) {
+    using QD = Quad<T>;
+    constexpr uint32_t es = sizeof(T);
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const uint32_t off = (uint32_t)((lane >> 4) * 256 + g * 64 + (lane & 15) * 4);  // elements
+    const uint32_t last = (uint32_t)n - 4u;
+    const bool exact = n == 1024 * Q;
+    typename QD::raw xr[Q], wr[Q];
+    gptr_c xg = scalar_gptr(reinterpret_cast<const char*>(x));
+    gptr_c wg = scalar_gptr(reinterpret_cast<const char*>(w));
+#pragma unroll
+    for (int m = 0; m < Q; ++m) {
+        const uint32_t e = m + 1 < Q || exact ? 1024u * m + off : min(1024u * m + off, last);
+        xr[m] = QD::template gload<false>(xg + e * es);
+    }
+#pragma unroll
+    for (int m = 0; m < Q; ++m) {
+        const uint32_t e = m + 1 < Q || exact ? 1024u * m + off : min(1024u * m + off, last);
+        wr[m] = QD::template gload<false>(wg + e * es);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool tail_in = exact || 1024u * (Q - 1) + off < (uint32_t)n;
+    float p = 0.0f;
+#pragma unroll
+    for (int m = 0; m < Q; ++m) {
+        float v[4];
+        QD::unpack(xr[m], v);
+        if (m + 1 == Q && !tail_in) v[0] = v[1] = v[2] = v[3] = 0.0f;
+        transpose4(v);
+        p = fmaf(v[0], v[0], p);  // chunks 4m, 4m+1, 4m+2, 4m+3 of chain 64g + 4t + q
+        p = fmaf(v[1], v[1], p);
+        p = fmaf(v[2], v[2], p);
+        p = fmaf(v[3], v[3], p);
+    }
+    const float gt = group_sumsq(p);
+    if (lane == 0) lds4[g] = gt;
+    __syncthreads();
+    const float inv = inverse_rms((lds4[0] + lds4[2]) + (lds4[1] + lds4[3]), n, eps);
+    gptr yg = scalar_gptr(reinterpret_cast<char*>(y));
+#pragma unroll
+    for (int m = 0; m < Q; ++m) {
+        if (m + 1 == Q && !tail_in) continue;
+        float v[4], wv[4], o[4];
+        QD::unpack(xr[m], v);
+        QD::unpack(wr[m], wv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (v[i] * inv) * wv[i];
+        QD::template gstore<false>(yg + (1024u * m + off) * es, o);
+    }
+}
+
 
 // ---------------------------------------------------------------------------
 // BLOCK / STREAM layout: 256 threads per row, thread l = chain l, wave g = group g.
@@ -737,6 +850,35 @@ __global__ __launch_bounds__(1024) void k_rows_split(const T* x, int64_t xs,
     part.apply(inv_shared, scalar_gptr(reinterpret_cast<char*>(y + r * ys)), s, lane, nvec);
 }
 
+template <typename T, int Q>
+__global__ __launch_bounds__(256) void k_rows_group(const T* x, int64_t xs,
+                                                    const T* __restrict__ w, T* y, int64_t ys,
+                                                    int n, float eps) {
+    __shared__ float lds4[4];
+    const int64_t r = blockIdx.x;
+    row_group<T, Q>(x + r * xs, w, y + r * ys, n, eps, lds4);
+}
+
+// GROUP-layout descriptor row: the captured instance Q is used when the row
+// read at run time fits it (width in (1024 (Q-1), 1024 Q], a multiple of 4,
+// quad-aligned pointers); any other row is streamed with BLOCK's mapping.
+template <typename T, int Q>
+__global__ __launch_bounds__(256) void k_desc_group(const rmsn_desc* __restrict__ d, float eps) {
+    __shared__ float lds4[4];
+    const int64_t n = d->n;
+    if (n < 1 || n > RMSN_MAX_N) return;
+    const T* x = static_cast<const T*>(d->x);
+    const T* w = static_cast<const T*>(d->w);
+    T* y = static_cast<T*>(d->y);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) |
+                        reinterpret_cast<uintptr_t>(y);
+    if ((n & 3) == 0 && n > 1024 * (Q - 1) && n <= 1024 * Q && a % (4 * sizeof(T)) == 0)
+        row_group<T, Q>(x, w, y, (int)n, eps, lds4);
+    else
+        row_block<T, 0>(x, w, y, (int)n, eps, lds4);
+}
+
+
 template <typename T, int NCH>
 __global__ __launch_bounds__(256) void k_rows_block(const T* x, int64_t xs,
                                                     const T* __restrict__ w, T* y, int64_t ys,
@@ -757,6 +899,21 @@ __global__ __launch_bounds__(256) void k_desc_block(const rmsn_desc* __restrict_
     if (n < 1 || n > RMSN_MAX_N) return;
     row_block<T, NCH>(static_cast<const T*>(d->x), static_cast<const T*>(d->w),
                       static_cast<T*>(d->y), (int)n, eps, lds4);
+}
+
+// The bf16 narrowing of the row kernels over consecutive bit patterns, two per
+// thread through the packed conversion the stores use.
+__global__ __launch_bounds__(256) void k_diag_bf16(uint32_t first, int64_t count, uint16_t* out) {
+    const int64_t i = 2 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+    if (i >= count) return;
+    const float a = __uint_as_float(first + (uint32_t)i);
+    if (i + 1 < count) {
+        const uint32_t p = bf16_pair(a, __uint_as_float(first + (uint32_t)i + 1u));
+        out[i] = (uint16_t)p;
+        out[i + 1] = (uint16_t)(p >> 16);
+    } else {
+        out[i] = (uint16_t)bf16_bits(a);
+    }
 }
 
 __global__ __launch_bounds__(256) void k_diag_inverse(uint32_t first, int64_t count, int n,
@@ -842,6 +999,28 @@ hipError_t launch_split_t(const Plan& p, const void* x, int64_t xs, const void* 
     return hipGetLastError();
 }
 
+#define RMSN_FOR_GROUP_BLOCKS(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
+
+template <typename T>
+hipError_t launch_group_t(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
+                          int64_t ys, int n, float eps, hipStream_t s) {
+    const T* xp = static_cast<const T*>(x);
+    const T* wp = static_cast<const T*>(w);
+    T* yp = static_cast<T*>(y);
+    const dim3 grid((unsigned)p.grid), block(256);
+#define RMSN_CASE(Q)                                                                          \
+    case Q:                                                                                   \
+        hipLaunchKernelGGL((k_rows_group<T, Q>), grid, block, 0, s, xp, xs, wp, yp, ys, n,   \
+                           eps);                                                              \
+        break;
+    switch (p.loads) {
+        RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)
+        default: return hipErrorInvalidValue;
+    }
+#undef RMSN_CASE
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_block_t(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
                           int64_t ys, int n, float eps, hipStream_t s) {
@@ -865,6 +1044,18 @@ hipError_t launch_block_t(const Plan& p, const void* x, int64_t xs, const void* 
 
 template <typename T>
 hipError_t launch_desc_t(const Plan& p, const rmsn_desc* d, float eps, hipStream_t s) {
+    if (p.path == RMSN_PATH_GROUP) {
+#define RMSN_CASE(Q)                                                                    \
+    case Q:                                                                             \
+        hipLaunchKernelGGL((k_desc_group<T, Q>), dim3(1), dim3(256), 0, s, d, eps);     \
+        break;
+        switch (p.loads) {
+            RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)
+            default: return hipErrorInvalidValue;
+        }
+#undef RMSN_CASE
+        return hipGetLastError();
+    }
 #define RMSN_CASE(C)                                                                    \
     case C:                                                                             \
         hipLaunchKernelGGL((k_desc_block<T, C>), dim3(1), dim3(256), 0, s, d, eps);     \
@@ -901,15 +1092,33 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
                    ? launch_split_t<float>(p, x, xs, w, y, ys, n, eps, stream)
                    : launch_split_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
     }
+    if (p.path == RMSN_PATH_GROUP) {
+        // the GROUP kernels rely on the plan's block count and a width of whole quads
+        if ((n & 3) != 0 || p.loads != (n + 1023) / 1024 || p.block != kBlockThreads ||
+            p.grid != rows)
+            return hipErrorInvalidValue;
+        return p.dtype == RMSN_F32 ? launch_group_t<float>(p, x, xs, w, y, ys, n, eps, stream)
+                                   : launch_group_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
+    }
     return p.dtype == RMSN_F32 ? launch_block_t<float>(p, x, xs, w, y, ys, n, eps, stream)
                                : launch_block_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
 }
 
 hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, hipStream_t stream) {
     if (p.path == RMSN_PATH_WAVE || p.path == RMSN_PATH_SPLIT)
-        return hipErrorInvalidValue;  // descriptors use BLOCK/STREAM
+        return hipErrorInvalidValue;  // descriptors use GROUP, BLOCK or STREAM
     return p.dtype == RMSN_F32 ? launch_desc_t<float>(p, d, eps, stream)
                                : launch_desc_t<uint16_t>(p, d, eps, stream);
+}
+
+hipError_t launch_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out,
+                            hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    const int64_t blocks = (count + 511) / 512;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_diag_bf16, dim3((unsigned)blocks), dim3(256), 0, stream, first_bits, count,
+                       out);
+    return hipGetLastError();
 }
 
 hipError_t launch_diag_inverse(uint32_t first_bits, int64_t count, int n, float eps, float* r_out,

@@ -19,6 +19,10 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
 // kernel runs); plan `p` was made for the capture-time width.
 hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, hipStream_t stream);
 
+// Step 8's bf16 narrowing over consecutive bit patterns (diagnostic).
+hipError_t launch_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out,
+                            hipStream_t stream);
+
 // Steps 4-7 over consecutive bit patterns (diagnostic).
 hipError_t launch_diag_inverse(uint32_t first_bits, int64_t count, int n, float eps, float* r_out,
                                float* inv_out, hipStream_t stream);

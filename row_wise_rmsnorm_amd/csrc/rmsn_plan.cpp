@@ -32,7 +32,7 @@ int env_int(const char* name, int dflt) {
 
 bool valid_path(int v) {
     return v == -1 || v == RMSN_PATH_WAVE || v == RMSN_PATH_BLOCK || v == RMSN_PATH_STREAM ||
-           v == RMSN_PATH_SPLIT;
+           v == RMSN_PATH_SPLIT || v == RMSN_PATH_GROUP;
 }
 bool valid_split_loads(int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8; }
 bool valid_rpb(int v) { return v == 0 || v == 4 || v == 8; }
@@ -98,8 +98,7 @@ int option_split_loads() {
 int set_option(int key, int value) {
     if (key == RMSN_OPT_PATH) {
         if (!valid_path(value)) {
-            set_error("rmsnorm_set_option: path must be -1 (automatic), %d, %d, %d or %d, got %d",
-                      RMSN_PATH_WAVE, RMSN_PATH_BLOCK, RMSN_PATH_STREAM, RMSN_PATH_SPLIT, value);
+            set_error("rmsnorm_set_option: path must be -1 (automatic) or 0..4, got %d", value);
             return RMSN_EINVAL;
         }
         g_path.store(value, std::memory_order_relaxed);
@@ -188,6 +187,7 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
         return RMSN_EINVAL;
     }
     // the power of two (at most 16) that `align` guarantees
+    const bool run_time = align == kAlignAtRunTime;
     int a = 16;
     while (a > 1 && (align <= 0 || align % a)) a >>= 1;
     const int es = elem_bytes(dtype);
@@ -197,17 +197,22 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
     const bool can_split = a >= 16 && (n * es) % 16 == 0 && split_auto != 0;
     const bool can_wave = bucket != 0 && a >= vec_bytes(dtype);
     const bool can_block = bucket != 0;
+    const bool can_group = bucket != 0 && n % 4 == 0 && (run_time || a >= vec_bytes(dtype));
     int path;
     switch (option_path()) {
         case RMSN_PATH_WAVE: path = can_wave ? RMSN_PATH_WAVE : -1; break;
         case RMSN_PATH_BLOCK: path = can_block ? RMSN_PATH_BLOCK : -1; break;
         case RMSN_PATH_STREAM: path = RMSN_PATH_STREAM; break;
         case RMSN_PATH_SPLIT: path = can_split ? RMSN_PATH_SPLIT : -1; break;
+        case RMSN_PATH_GROUP: path = can_group ? RMSN_PATH_GROUP : -1; break;
         default: path = -1; break;
     }
     if (path < 0) {
+        // Descriptor rows keep BLOCK: the GROUP descriptor kernel, which also
+        // carries the streaming fallback, measured slower in the decode step.
         if (can_split && rows >= kWaveMinRows) path = RMSN_PATH_SPLIT;
         else if (can_wave && rows >= kWaveMinRows) path = RMSN_PATH_WAVE;
+        else if (can_group && !run_time) path = RMSN_PATH_GROUP;
         else if (can_block) path = RMSN_PATH_BLOCK;
         else if (can_split) path = RMSN_PATH_SPLIT;
         else path = RMSN_PATH_STREAM;
@@ -232,6 +237,13 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
         p.rows_per_block = 1;
         p.streaming = st < 0 ? (auto_streaming(dtype, rows, n) ? 1 : 0) : st;
         p.block = kWave * (int)((slices + u - 1) / u);
+        p.grid = rows;
+    } else if (path == RMSN_PATH_GROUP) {
+        p.loads = (int)((n + 1023) / 1024);
+        p.chunks = 4 * p.loads;
+        p.rows_per_block = 1;
+        p.streaming = 0;
+        p.block = kBlockThreads;
         p.grid = rows;
     } else {
         p.chunks = path == RMSN_PATH_BLOCK ? bucket : 0;

@@ -38,14 +38,15 @@ constexpr int kSplitTargetWaves = 8;
 
 struct Plan {
     int dtype;           // RMSN_F32 / RMSN_BF16
-    int path;            // RMSN_PATH_WAVE / _BLOCK / _STREAM / _SPLIT
+    int path;            // RMSN_PATH_WAVE / _BLOCK / _STREAM / _SPLIT / _GROUP
     int chunks;          // kernel instance: a bucket, or 0 for streaming; SPLIT:
                          // 256-element chunks one wavefront holds
     int rows_per_block;  // wavefronts (= rows) per workgroup on the WAVE path, else 1
     int streaming;       // WAVE / SPLIT: non-temporal loads of x and stores of y
     int block;           // threads per workgroup
     int64_t grid;        // workgroups
-    int loads;           // SPLIT: 16-byte loads per lane (slices per wavefront), else 0
+    int loads;           // SPLIT: 16-byte loads per lane (slices per wavefront);
+                         // GROUP: loads per lane (1024-element blocks); else 0
 };
 
 inline int elem_bytes(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
@@ -68,8 +69,12 @@ int auto_split_loads(int64_t slices);
 
 // Plan a launch of `rows` rows of width n. `align`: a byte alignment shared by
 // every row start of x and y and by w (the largest power of two dividing it
-// counts, up to 16; values below the element size mean element alignment).
-// Returns RMSN_OK or RMSN_EINVAL (bad dtype, rows < 1, n outside [1, 2^24]).
+// counts, up to 16; values 0 .. element size mean element alignment), or
+// kAlignAtRunTime for descriptor rows, whose kernels check the pointers they
+// read (only the GROUP path does, falling back to streaming when they do not
+// fit). Returns RMSN_OK or RMSN_EINVAL (bad dtype, rows < 1, n outside
+// [1, 2^24]).
+constexpr int kAlignAtRunTime = -1;
 int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out);
 
 // Process-wide options (rmsnorm_set_option); read lazily from the environment.

@@ -118,6 +118,10 @@ def test_sequence_validation(rn):
 
 def test_diag_validation(rn):
     L = rn.lib()
+    assert L.rmsnorm_diag_bf16(0xFFFFFFFF, 2, A16, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_diag_bf16(0, 16, 0, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_diag_bf16(0, 16, A16 + 1, None) == rn.RMSN_EINVAL
+    assert L.rmsnorm_diag_bf16(0, -1, A16, None) == rn.RMSN_EINVAL
     assert L.rmsnorm_diag_inverse(0xFFFFFFFF, 2, 1, 0.0, A16, B16, None) == rn.RMSN_EINVAL
     assert L.rmsnorm_diag_inverse(0, 16, 0, 0.0, A16, B16, None) == rn.RMSN_EINVAL
     assert L.rmsnorm_diag_inverse(0, 16, 1, -1.0, A16, B16, None) == rn.RMSN_EINVAL
@@ -147,15 +151,28 @@ def test_plan_paths_and_buckets(rn):
     assert p["path"] == rn.PATH_WAVE and p["rows_per_block"] == 4 and p["grid"] == 256
     # a width that is not a whole number of 16-byte vectors: WAVE
     assert rn.plan_query(rn.BF16, 4096, 7164)["path"] == rn.PATH_WAVE
-    # few rows: a 256-thread workgroup per row
+    # few rows: a 256-thread workgroup per row, group segments read with
+    # vector loads (GROUP); element loads (BLOCK) when the rows are not
+    # quad-aligned or the width is not a whole number of quads
     p = rn.plan_query(rn.BF16, 64, 7168, aligned=True)
+    assert p == {"path": rn.PATH_GROUP, "chunks": 28, "rows_per_block": 1, "streaming": 0,
+                 "block": 256, "grid": 64, "loads": 7}
+    p = rn.plan_query(rn.BF16, 64, 7168, aligned=False)
     assert p == {"path": rn.PATH_BLOCK, "chunks": 28, "rows_per_block": 1, "streaming": 0,
                  "block": 256, "grid": 64, "loads": 0}
-    # single rows of the decode step
-    assert rn.plan_query(rn.F32, 1, 7168)["chunks"] == 28
-    assert rn.plan_query(rn.F32, 1, 1536)["chunks"] == 6
-    assert rn.plan_query(rn.F32, 1, 512)["chunks"] == 2
-    # unaligned rows never take the WAVE or SPLIT path
+    assert rn.plan_query(rn.BF16, 64, 7166)["path"] == rn.PATH_BLOCK
+    # single rows
+    assert rn.plan_query(rn.F32, 1, 7168)["path"] == rn.PATH_GROUP
+    assert rn.plan_query(rn.F32, 1, 7168, align=0)["chunks"] == 28
+    assert rn.plan_query(rn.F32, 1, 1536, align=0)["chunks"] == 6
+    assert rn.plan_query(rn.F32, 1, 512, align=0)["chunks"] == 2
+    # descriptor rows of the decode step: BLOCK instances by width
+    assert rn.plan_query(rn.F32, 1, 7168, align=-1) == {
+        "path": rn.PATH_BLOCK, "chunks": 28, "rows_per_block": 1, "streaming": 0,
+        "block": 256, "grid": 1, "loads": 0}
+    assert rn.plan_query(rn.F32, 1, 1536, align=-1)["chunks"] == 6
+    assert rn.plan_query(rn.F32, 1, 512, align=-1)["chunks"] == 2
+    # unaligned rows never take the WAVE, SPLIT or GROUP path
     assert rn.plan_query(rn.F32, 4096, 7168, aligned=False)["path"] == rn.PATH_BLOCK
     assert rn.plan_query(rn.F32, 4096, 7168, align=4)["path"] == rn.PATH_BLOCK
     assert rn.plan_query(rn.F32, 4096, 7168, align=24)["path"] == rn.PATH_BLOCK  # 8 B
@@ -203,7 +220,7 @@ def test_split_geometry(rn, n, es):
                                4096, 5000, 6144, 6145, 7167, 7168, 8191, 8192])
 def test_plan_bucket_holds_row_and_previous_does_not(rn, n):
     buckets = [1, 2, 4, 6, 8, 12, 16, 20, 24, 28, 32]
-    c = rn.plan_query(rn.F32, 1, n)["chunks"]
+    c = rn.plan_query(rn.F32, 1, n, align=0)["chunks"]
     assert c in buckets and 256 * c >= n
     i = buckets.index(c)
     if i > 0:
@@ -228,12 +245,25 @@ def test_options_roundtrip_and_force_paths(rn):
         assert rn.plan_query(rn.BF16, 8192, 7168)["path"] == rn.PATH_WAVE
         # ineligible: falls back to the automatic choice
         assert rn.plan_query(rn.BF16, 3, 7168, aligned=False)["path"] == rn.PATH_BLOCK
+        assert rn.plan_query(rn.BF16, 3, 7168, align=4)["path"] == rn.PATH_BLOCK
         assert rn.plan_query(rn.BF16, 3, 9000)["path"] == rn.PATH_SPLIT
         assert rn.plan_query(rn.BF16, 3, 9001)["path"] == rn.PATH_STREAM
         rn.set_option(rn.OPT_PATH, rn.PATH_SPLIT)
         assert rn.plan_query(rn.BF16, 3, 7168)["path"] == rn.PATH_SPLIT
         assert rn.plan_query(rn.BF16, 3, 7167)["path"] == rn.PATH_BLOCK
-        assert rn.plan_query(rn.BF16, 3, 7168, align=8)["path"] == rn.PATH_BLOCK
+        assert rn.plan_query(rn.BF16, 3, 7168, align=8)["path"] == rn.PATH_GROUP
+        rn.set_option(rn.OPT_PATH, rn.PATH_GROUP)
+        p = rn.plan_query(rn.BF16, 64, 7168, align=8)
+        assert p == {"path": rn.PATH_GROUP, "chunks": 28, "rows_per_block": 1, "streaming": 0,
+                     "block": 256, "grid": 64, "loads": 7}
+        assert rn.plan_query(rn.F32, 1, 1536)["loads"] == 2
+        assert rn.plan_query(rn.F32, 1, 4)["loads"] == 1
+        assert rn.plan_query(rn.F32, 1, 1025, align=16)["path"] == rn.PATH_BLOCK   # not whole quads
+        assert rn.plan_query(rn.F32, 1, 1024, align=8)["path"] == rn.PATH_BLOCK    # f32 quads need 16 B
+        assert rn.plan_query(rn.F32, 1, 8196)["path"] != rn.PATH_GROUP             # > 8192
+        # descriptor rows (alignment checked by the kernel when it runs)
+        assert rn.plan_query(rn.F32, 1, 1536, align=-1)["path"] == rn.PATH_GROUP
+        assert rn.plan_query(rn.F32, 1, 1537, align=-1)["path"] == rn.PATH_BLOCK
         rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
         rn.set_option(rn.OPT_ROWS_PER_BLOCK, 4)
         p = rn.plan_query(rn.BF16, 8191, 7168, align=8)
@@ -256,7 +286,7 @@ def test_options_roundtrip_and_force_paths(rn):
         with pytest.raises(rn.RmsnormError):
             rn.set_option(rn.OPT_PATH, 7)
         with pytest.raises(rn.RmsnormError):
-            rn.set_option(rn.OPT_PATH, 4)
+            rn.set_option(rn.OPT_PATH, 5)
         with pytest.raises(rn.RmsnormError):
             rn.set_option(99, 0)
     finally:

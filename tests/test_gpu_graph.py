@@ -99,8 +99,18 @@ def step(rn):
     return Step(rn, wl.decode())
 
 
-def test_eager_sequence_matches_oracle(rn, step):
-    say("eager sequence")
+@pytest.fixture(params=["auto", "block", "group"])
+def desc_path(rn, request):
+    """Plan the captured nodes (and the eager arm) with the automatic choice,
+    or force the BLOCK or GROUP descriptor kernels."""
+    path = {"auto": rn.PATH_AUTO, "block": rn.PATH_BLOCK, "group": rn.PATH_GROUP}[request.param]
+    rn.set_option(rn.OPT_PATH, path)
+    yield request.param
+    rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
+
+
+def test_eager_sequence_matches_oracle(rn, step, desc_path):
+    say(f"eager sequence ({desc_path})")
     step.point_at(0)
     step.clear_outputs()
     rn.rmsnorm_sequence_eager(step.table, step.widths, wl.EPS, rn.F32)
@@ -120,8 +130,8 @@ def test_aa_eager_vs_eager(rn, step):
     compare(runs[0], runs[1], "A/A eager")
 
 
-def test_graph_replays_follow_the_table(rn, step):
-    say("graph capture")
+def test_graph_replays_follow_the_table(rn, step, desc_path):
+    say(f"graph capture ({desc_path})")
     step.point_at(0)
     g = rn.SequenceGraph(step.table, step.widths, wl.EPS, rn.F32)
     assert g.status == rn.RMSN_OK, g.capture_error
@@ -146,11 +156,11 @@ def test_graph_replays_follow_the_table(rn, step):
     g.destroy()
 
 
-def test_graph_replay_with_changed_widths(rn, step):
+def test_graph_replay_with_changed_widths(rn, step, desc_path):
     """Widths are loop bounds read from the table: replays with other
     (smaller) widths than the capture-time ones are exact and write nothing
     past the new width; crossing below a register bucket streams the row."""
-    say("graph replay with changed widths")
+    say(f"graph replay with changed widths ({desc_path})")
     step.point_at(0)
     g = rn.SequenceGraph(step.table, step.widths, wl.EPS, rn.F32)
     assert g.status == rn.RMSN_OK
@@ -170,7 +180,7 @@ def test_graph_replay_with_changed_widths(rn, step):
     g.destroy()
 
 
-def test_graph_rows_can_be_wider_than_capture(rn):
+def test_graph_rows_can_be_wider_than_capture(rn, desc_path):
     """A node captured at width 512 replays a row of width 9000 exactly."""
     import torch
     say("replay wider than capture")
@@ -253,10 +263,10 @@ def test_forced_capture_failure_falls_back_to_eager(rn, step):
     step.point_at(0)
 
 
-def test_graph_of_bf16_rows(rn):
+def test_graph_of_bf16_rows(rn, desc_path):
     import torch
     from gpu_util import assert_bits_bf16, bf16_host, to_dev_bf16
-    say("bf16 sequence graph")
+    say(f"bf16 sequence graph ({desc_path})")
     rows = []
     for i, n in enumerate([7168, 1536, 512, 100, 7168]):
         x, w = wl.misc_f32(300 + i, n)
@@ -275,3 +285,42 @@ def test_graph_of_bf16_rows(rn):
         for (x, w), y in zip(rows, ys):
             assert_bits_bf16(bf16_host(y), oracle.row_bf16(x, w, wl.EPS), f"bf16 replay {rep}")
     g.destroy()
+
+
+def test_graph_rows_rewritten_to_misaligned_pointers(rn, step, desc_path):
+    """Descriptor rows may move to any element alignment between replays: a
+    node captured for aligned rows streams a misaligned one with the same bits."""
+    import torch
+    say(f"replay on misaligned rows ({desc_path})")
+    step.point_at(0)
+    g = rn.SequenceGraph(step.table, step.widths, wl.EPS, rn.F32)
+    assert g.status == rn.RMSN_OK
+    k = 12
+    bufs = []
+    rows = []
+    for i in range(k):
+        x, w, _, _ = step.inputs[1][i]
+        n = len(x)
+        o = 1 + i % 3                                     # 4, 8 or 12 bytes past 16-byte alignment
+        bx = torch.zeros(n + 4, dtype=torch.float32, device=dev())
+        bw = torch.zeros(n + 4, dtype=torch.float32, device=dev())
+        by = torch.full((n + 4,), float("nan"), dtype=torch.float32, device=dev())
+        bx[o:o + n].copy_(to_dev_f32(x))
+        bw[o:o + n].copy_(to_dev_f32(w))
+        bufs.append((bx, bw, by, o, n))
+        rows.append((bx[o:o + n], bw[o:o + n], by[o:o + n]))
+    for i in range(k, len(step.widths)):
+        c = step.inputs[1][i]
+        rows.append((c[2], c[3], step.ys[i]))
+    new, _ = rn.make_table(rows)
+    step.table.copy_(new)
+    sync()
+    g.launch()
+    sync()
+    for i, (bx, bw, by, o, n) in enumerate(bufs):
+        x, w, _, _ = step.inputs[1][i]
+        got = f32_host(by)
+        assert_bits_f32(got[o:o + n], oracle.row_f32(x, w, wl.EPS), f"misaligned norm {i}")
+        assert np.isnan(got[:o]).all() and np.isnan(got[o + n:]).all()
+    g.destroy()
+    step.point_at(0)

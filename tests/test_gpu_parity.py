@@ -173,13 +173,15 @@ PATH_CASES = [
     # partial last wavefronts, and rows of 64 and 128 KB (8 and 16 wavefronts)
     (5, 24, "f32"), (4, 8, "bf16"), (6, 2056, "bf16"), (3, 12000, "f32"),
     (3, 16384, "f32"), (2, 20000, "bf16"), (2, 32768, "bf16"), (2, 65536, "bf16"),
+    # GROUP shapes: one quad, a last block of one quad, exact blocks
+    (3, 4, "bf16"), (3, 1028, "f32"), (2, 4096, "f32"), (5, 5124, "bf16"),
 ]
 
 # (path, rows per block, streaming, split loads) settings every case runs under
 PATH_SETTINGS = (
     [(-1, 0, -1, 0)]
     + [(0, rpb, st, 0) for rpb in (0, 4, 8) for st in (-1, 0, 1)]
-    + [(1, 0, -1, 0), (2, 0, -1, 0)]
+    + [(1, 0, -1, 0), (2, 0, -1, 0), (4, 0, -1, 0)]
     + [(3, 0, st, u) for u in (0, 1, 2, 4, 8) for st in (-1, 0, 1)]
 )
 
@@ -230,7 +232,7 @@ def test_split_plans_cover_their_shapes(rn):
         p = rn.plan_query(dtype, rows, n, align=16)
         slices = -(-n * es // 1024)
         if p["path"] != rn.PATH_SPLIT:
-            assert p["path"] == rn.PATH_BLOCK and n <= 8192, (rows, n, kind, p)
+            assert p["path"] in (rn.PATH_BLOCK, rn.PATH_GROUP) and n <= 8192, (rows, n, kind, p)
             try:
                 rn.set_option(rn.OPT_PATH, rn.PATH_SPLIT)
                 p = rn.plan_query(dtype, rows, n, align=16)
@@ -294,7 +296,7 @@ def test_association_probes(rn):
     for i, x in enumerate(_probe_rows()):
         w = np.ones_like(x)
         want = oracle.row_f32(x, w, np.float32(0))
-        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT):
+        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT, rn.PATH_GROUP):
             try:
                 rn.set_option(rn.OPT_PATH, path)
                 xr = np.repeat(x[None, :], 2, axis=0)
@@ -314,7 +316,7 @@ def test_association_probes_bf16(rn):
         wb = wl.to_bf16_bits(np.ones_like(x))
         assert np.array_equal(oracle.bf16_to_f32(xb), x)
         want = oracle.row_bf16(xb, wb, np.float32(0))
-        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT):
+        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT, rn.PATH_GROUP):
             for u in ((0, 1, 2, 4) if path == rn.PATH_SPLIT else (0,)):
                 try:
                     rn.set_option(rn.OPT_PATH, path)
@@ -345,7 +347,7 @@ def test_special_values(rn, n):
     w = (1.0 + 0.1 * g.standard_normal(n)).astype(np.float32)
     for i, (x, eps) in enumerate(cases):
         want = oracle.row_f32(x, w, eps)
-        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT):
+        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT, rn.PATH_GROUP):
             try:
                 rn.set_option(rn.OPT_PATH, path)
                 got = gpu_rows(rn, np.repeat(x[None, :], 2, axis=0), w, eps, rn.F32)
@@ -355,7 +357,7 @@ def test_special_values(rn, n):
         # bf16 with the same values rounded to bf16
         xb, wb = wl.to_bf16_bits(x), wl.to_bf16_bits(w)
         want_b = oracle.row_bf16(xb, wb, eps)
-        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT):
+        for path in (rn.PATH_WAVE, rn.PATH_BLOCK, rn.PATH_STREAM, rn.PATH_SPLIT, rn.PATH_GROUP):
             try:
                 rn.set_option(rn.OPT_PATH, path)
                 got = gpu_rows(rn, np.repeat(xb[None, :], 2, axis=0), wb, eps, rn.BF16)
@@ -473,6 +475,32 @@ def test_sqrt_and_reciprocal_exhaustive(rn):
             say(f"sqrt/recip exhaustive: {start:#010x}")
         start += cnt
         k += 1
+
+
+@pytest.mark.timeout(600)
+def test_bf16_narrowing_exhaustive(rn):
+    """The kernels' binary32 -> bf16 narrowing (the hardware conversion every
+    bf16 store uses) equals the oracle's round-to-nearest-even for every one
+    of the 2^32 binary32 patterns; NaN stays NaN with its sign."""
+    import torch
+    chunk = 1 << 28
+    out_d = torch.empty(chunk, dtype=torch.int16, device=dev())
+    out_h = torch.empty(chunk, dtype=torch.int16).pin_memory()
+    want = np.empty(chunk, dtype=np.uint16)
+    for k, start in enumerate(range(0, 1 << 32, chunk)):
+        rn.diag_bf16(start, chunk, out_d)
+        out_h.copy_(out_d, non_blocking=True)
+        oracle.f32_to_bf16_range(start, chunk, out=want)
+        sync()
+        got = out_h.numpy().view(np.uint16)
+        bits = (np.arange(chunk, dtype=np.uint64) + start).astype(np.uint32)
+        nan = (bits & 0x7FFFFFFF) > 0x7F800000
+        assert np.array_equal(got[~nan], want[~nan]), f"bf16 narrowing differs in chunk at {start:#x}"
+        gn = got[nan]
+        assert np.all((gn & 0x7FFF) > 0x7F80), f"NaN not kept in chunk at {start:#x}"
+        assert np.array_equal(gn & 0x8000, (bits[nan] >> 16).astype(np.uint16) & 0x8000)
+        if k % 4 == 0:
+            say(f"bf16 narrowing exhaustive: {start:#010x}")
 
 
 def test_mean_division_sampled(rn):

@@ -386,6 +386,22 @@ def test_bf16_rounding_matches_torch_rne(oracle_mod):
             assert got == int(ref[k]), hex(int(allp[k]))
 
 
+def test_bf16_range_narrowing_matches_torch_rne(oracle_mod):
+    """The oracle's narrowing over a run of consecutive bit patterns (the form
+    the device's conversion is checked against) equals torch's RNE cast on
+    every non-NaN pattern of three 2^20-pattern windows: around 1.0, across the
+    largest finite values into infinity and NaN, and over the subnormals."""
+    import torch
+    for first in (0x3F780000, 0x7F700000, 0x00000000, 0x807F0000):
+        got = oracle_mod.f32_to_bf16_range(first, 1 << 20)
+        pats = (np.arange(1 << 20, dtype=np.uint64) + first).astype(np.uint32)
+        v = pats.view(np.float32)
+        ref = torch.from_numpy(v.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = np.isnan(v)
+        assert np.array_equal(got[~nan], ref[~nan]), hex(first)
+        assert np.all(got[nan] == (0x7FC0 | ((pats[nan] >> 16) & 0x8000)))
+
+
 def test_bf16_row_is_f32_row_rounded(oracle_mod):
     """The bf16 path equals the binary32 path on widened inputs, rounded once
     (torch's cast), i.e. no intermediate bf16 rounding."""
