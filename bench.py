@@ -11,6 +11,9 @@ cache defeated by rotating over 4 buffer sets (940 MB). Also reported:
 * decode_step: the 327-norm decode step, eager launches vs one captured
   graph replay (Lecture 08 section 1), A/A then ABBA x 3 with per-rep
   numbers and standard errors (Lecture 04 section 6.1);
+* decode_step_positioned: the same step walking a ring of rows through a
+  device-resident position that the step itself advances (Lecture 08
+  section 2), eager vs graph;
 * roofline: the prefill kernel against the 8 TB/s HBM peak;
 * prefill.wave_path_us: the same launches on the one-wavefront-per-row layout;
 * cpu_baseline: the CPU oracle timed on this host (a reported baseline only).
@@ -299,6 +302,81 @@ def bench_decode(rn, torch, np, wl, decode_steps):
     }
 
 
+def bench_decode_positioned(rn, torch, np, wl, decode_steps, period=4):
+    """The decode step as a positioned sequence: every norm owns a ring of
+    `period` rows (one 7168-element slot each, shorter rows use its start),
+    the descriptor table points at slot 0, and the step's last launch advances
+    a device-resident position -- so consecutive replays normalise the next
+    token's rows with no host work between them (Lecture 08 section 2)."""
+    rows = wl.decode()
+    dev = torch.device("cuda", 0)
+    slot = 7168
+    xs, ws, ys, hosts = [], [], [], []
+    for i, (x, w) in enumerate(rows):
+        n = len(x)
+        ring = np.zeros((period, slot), np.float32)
+        ring[0, :n] = x
+        for p in range(1, period):
+            ring[p, :n] = wl.misc_f32(600000 + period * i + p, n)[0]
+        hosts.append((ring, w))
+        xs.append(torch.from_numpy(ring).to(dev))
+        ws.append(torch.from_numpy(w).to(dev))
+        ys.append(torch.full((period, slot), float("nan"), dtype=torch.float32, device=dev))
+    n_of = [len(x) for x, _ in rows]
+    table, widths = rn.make_table([(xs[i][0, :n_of[i]], ws[i], ys[i][0, :n_of[i]])
+                                   for i in range(len(rows))])
+    d_pos = torch.zeros(1, dtype=torch.int64, device=dev)
+    pos = (d_pos, slot * 4, slot * 4, period)
+    eps = float(wl.EPS)
+    g = rn.SequenceGraph(table, widths, eps, rn.F32, position=pos)
+    if g.status != rn.RMSN_OK:
+        raise RuntimeError(f"positioned capture failed: {g.capture_error}")
+    eager = lambda i: rn.rmsnorm_sequence_eager(table, widths, eps, rn.F32, position=pos)
+    graph = lambda i: g.launch()
+    # correctness: one full cycle of the ring on the graph, every norm and position
+    import oracle
+    d_pos.zero_()
+    torch.cuda.synchronize()
+    for _ in range(period):
+        g.launch()
+    torch.cuda.synchronize()
+    ok = int(d_pos.item()) == 0          # the update wraps the position: a full cycle
+    for i, ((ring, w), y) in enumerate(zip(hosts, ys)):
+        got = y.cpu().numpy()
+        for p in range(period):
+            want = oracle.row_f32(ring[p, :n_of[i]], w, wl.EPS)
+            ok = ok and np.array_equal(got[p, :n_of[i]].view(np.uint32), want.view(np.uint32))
+    for i in range(20):
+        eager(i)
+        graph(i)
+    # the same kernels and update node on a ring of one position: every step
+    # re-reads the same rows, as the plain decode-step arms do
+    pos1 = (d_pos, slot * 4, slot * 4, 1)
+    g1 = rn.SequenceGraph(table, widths, eps, rn.F32, position=pos1)
+    if g1.status != rn.RMSN_OK:
+        raise RuntimeError(f"positioned capture failed: {g1.capture_error}")
+    graph1 = lambda i: g1.launch()
+    for i in range(20):
+        eager(i)
+        graph(i)
+        graph1(i)
+    res = {"A": [], "B": [], "C": []}
+    for a in ["A", "B", "C", "C", "B", "A"] * 2:
+        fn = {"A": eager, "B": graph, "C": graph1}[a]
+        res[a].append(1000.0 * elapsed_ms(fn, decode_steps) / decode_steps)
+    nodes = g.node_count()
+    g.destroy()
+    g1.destroy()
+    e, gr, g1s = stats(res["A"]), stats(res["B"]), stats(res["C"])
+    return {"eager_us_per_step": e, "graph_us_per_step": gr,
+            "graph_period1_us_per_step": g1s,
+            "speedup_graph_over_eager": e["mean"] / gr["mean"], "graph_nodes": nodes,
+            "period": period, "bit_exact_one_cycle_vs_oracle": bool(ok),
+            "note": ("327 norm nodes + 1 position-update node; each replay normalises the next "
+                     "position's rows, no host work between replays; graph_period1: the same "
+                     "graph on a ring of one position (same rows every step); ABCCBA x 2")}
+
+
 def cpu_baseline(np, wl, host):
     """The oracle as it stands, on this host's cores, over a bounded sample of
     the prefill workload; same algorithmic-byte accounting as the GPU."""
@@ -376,7 +454,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true")
     ap.add_argument("--sections", default="prefill,single,batch64,decode",
-                    help="comma list of prefill,single,batch64,decode (for profiling runs)")
+                    help="comma list of prefill,single,batch64,decode,positioned (for "
+                         "profiling runs; the default runs them all)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
@@ -396,12 +475,13 @@ def main():
         return
 
     sections = set(args.sections.split(","))
-    if "prefill" in sections and sections != {"prefill", "single", "batch64", "decode"}:
+    full = {"prefill", "single", "batch64", "decode"}
+    if "prefill" in sections and sections != full:
         # a profiling run of the prefill kernel alone: only the timed launches
         pre = bench_prefill_only(rn, torch, np, wl, args.steps, args.warmup)
         print(json.dumps(pre), flush=True)
         return
-    if sections != {"prefill", "single", "batch64", "decode"}:
+    if sections != full:
         out = {}
         if "single" in sections:
             out["single_norm"] = bench_single(rn, torch, np, wl)
@@ -409,6 +489,9 @@ def main():
             out["batch64"] = bench_batch64(rn, torch, np, wl)
         if "decode" in sections:
             out["decode_step"] = bench_decode(rn, torch, np, wl, args.decode_steps)
+        if "positioned" in sections:
+            out["decode_step_positioned"] = bench_decode_positioned(rn, torch, np, wl,
+                                                                    args.decode_steps)
         print(json.dumps(out), flush=True)
         return
     torch.cuda.synchronize()
@@ -423,6 +506,9 @@ def main():
     dec = bench_decode(rn, torch, np, wl, args.decode_steps)
     log(f"decode eager {dec['eager_us_per_step']['mean']:.1f} us  "
         f"graph {dec['graph_us_per_step']['mean']:.1f} us")
+    decp = bench_decode_positioned(rn, torch, np, wl, args.decode_steps)
+    log(f"decode positioned eager {decp['eager_us_per_step']['mean']:.1f} us  "
+        f"graph {decp['graph_us_per_step']['mean']:.1f} us")
     traffic, traffic_rec = measured_traffic()
     gpu_s = time.time() - t_start
     cpu = None
@@ -475,6 +561,7 @@ def main():
         "single_norm": single,
         "batch64": b64,
         "decode_step": dec,
+        "decode_step_positioned": decp,
         "traffic_record": traffic_rec,
         "gpu_section_s": round(gpu_s, 1),
     }

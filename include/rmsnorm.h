@@ -125,6 +125,62 @@ int rmsnorm_sequence_graph_launch(rmsn_graph* g, void* stream);
  * the caller makes sure no launch of it is still pending. */
 int rmsnorm_sequence_graph_destroy(rmsn_graph* g);
 
+/* ---- positioned sequences: the step's state update inside the graph ------ */
+
+/* A decode step is replayed once per token, and each token's rows differ.
+ * Lecture 08 "Graph-resident decode", section 2: promote the varying value to
+ * device memory, compute the address on the device, and run the state update
+ * itself inside the captured region. A positioned sequence does exactly that:
+ * its kernels read the device-resident position *d_pos when they run and take
+ * entry i's rows at
+ *     x_i + p * x_pitch,  y_i + p * y_pitch   (bytes),  p = (*d_pos) mod period,
+ * (w_i does not move), and its last launch stores (p + 1) mod period in
+ * *d_pos (so after the first step *d_pos stays in [0, period) and the kernels
+ * need no division). Replaying it walks `period` rows per norm, one per
+ * replay, with no host work between replays. */
+typedef struct rmsn_position {
+    int64_t* d_pos;   /* DEVICE int64, >= 0, 8-byte aligned, caller-owned; must
+                         outlive the handle and hold no other data           */
+    int64_t x_pitch;  /* bytes between consecutive positions' x rows, >= 0, a
+                         multiple of the element size                         */
+    int64_t y_pitch;  /* the same for y                                       */
+    int64_t period;   /* positions before p wraps to 0, >= 1                  */
+} rmsn_position;
+
+/* The eager arm of a positioned sequence: count norm launches at the current
+ * position, then the position update, all on `stream`. Arguments as for
+ * rmsnorm_sequence_eager; RMSN_EINVAL also for a null position, d_pos null or
+ * not 8-byte aligned, period < 1, negative or misaligned pitches, or
+ * period * pitch overflowing. */
+int rmsnorm_sequence_eager_positioned(int dtype, const rmsn_desc* d_table,
+                                      const int64_t* h_widths, int32_t count, float eps,
+                                      const rmsn_position* pos, void* stream);
+
+/* Capture a positioned sequence: count norm nodes and a last node that moves
+ * *d_pos to the next position (count + 1 nodes). Pre-warm runs every kernel variant, the
+ * update included, on a private row and a private position: neither the
+ * caller's rows nor *d_pos change before the first launch. Otherwise as
+ * rmsnorm_sequence_graph_create (a capture failure leaves *d_pos untouched
+ * and the handle replays eagerly, position update included). */
+int rmsnorm_sequence_graph_create_positioned(int dtype, const rmsn_desc* d_table,
+                                             const int64_t* h_widths, int32_t count, float eps,
+                                             const rmsn_position* pos, rmsn_graph** out);
+
+/* New capture-time widths for an existing handle (count must equal the
+ * handle's). Widths are a capture key only through the launch plan
+ * (Lecture 08 section 2: a value that decides the grid or the kernel cannot
+ * be promoted to device memory; re-capture when the plan moves, with the
+ * check and the launcher calling the same plan function). The sequence is
+ * planned again with the function every launch uses; if each node's launch
+ * (kernel instance, block, grid) is unchanged the executable graph is kept,
+ * else the sequence is pre-warmed and captured again and the old graph is
+ * released. *recaptured (may be NULL) is 1 if a new graph (or, on capture
+ * failure, the eager fallback with the new plans: RMSN_ECAPTURE) replaced the
+ * old one, else 0. On RMSN_EINVAL / RMSN_EHIP the handle is unchanged. Must not
+ * overlap a pending launch of the handle. */
+int rmsnorm_sequence_graph_update(rmsn_graph* g, const int64_t* h_widths, int32_t count,
+                                  int* recaptured);
+
 /* Number of nodes in the captured graph (0 in eager-fallback mode). */
 int rmsnorm_graph_node_count(const rmsn_graph* g, int64_t* out);
 

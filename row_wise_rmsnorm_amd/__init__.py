@@ -39,6 +39,17 @@ class _PlanInfo(ctypes.Structure):
                 ("loads", ctypes.c_int32)]
 
 
+class _Position(ctypes.Structure):
+    _fields_ = [("d_pos", ctypes.c_void_p), ("x_pitch", ctypes.c_int64),
+                ("y_pitch", ctypes.c_int64), ("period", ctypes.c_int64)]
+
+
+def _position(position):
+    """(d_pos int64 device tensor, x_pitch bytes, y_pitch bytes, period) -> struct."""
+    d_pos, x_pitch, y_pitch, period = position
+    return _Position(ctypes.c_void_p(d_pos.data_ptr()), int(x_pitch), int(y_pitch), int(period))
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"row_wise_rmsnorm_amd: {LIB_PATH} is not built "
@@ -61,6 +72,10 @@ def _load():
         "rmsnorm_get_option": [c_int, ctypes.POINTER(c_int)],
         "rmsnorm_diag_inverse": [u32, i64, i64, f, vp, vp, vp],
         "rmsnorm_diag_bf16": [u32, i64, vp, vp],
+        "rmsnorm_sequence_eager_positioned": [c_int, vp, vp, i32, f, ctypes.POINTER(_Position), vp],
+        "rmsnorm_sequence_graph_create_positioned": [c_int, vp, vp, i32, f,
+                                                     ctypes.POINTER(_Position), ctypes.POINTER(vp)],
+        "rmsnorm_sequence_graph_update": [vp, vp, i32, ctypes.POINTER(c_int)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -78,7 +93,8 @@ EXPORTED = ("rmsnorm_f32", "rmsnorm_bf16", "rmsnorm_batched_rows", "rmsnorm_sequ
             "rmsnorm_sequence_graph_destroy", "rmsnorm_graph_node_count",
             "rmsnorm_graph_is_fallback", "rmsnorm_last_error", "rmsnorm_plan_query",
             "rmsnorm_set_option", "rmsnorm_get_option", "rmsnorm_diag_inverse",
-            "rmsnorm_diag_bf16")
+            "rmsnorm_diag_bf16", "rmsnorm_sequence_eager_positioned",
+            "rmsnorm_sequence_graph_create_positioned", "rmsnorm_sequence_graph_update")
 
 
 def lib():
@@ -185,11 +201,20 @@ def _widths_array(widths):
     return arr
 
 
-def rmsnorm_sequence_eager(table, widths, eps, dtype, stream=None):
-    """Issue len(widths) dependent launches reading descriptors from `table`."""
+def rmsnorm_sequence_eager(table, widths, eps, dtype, stream=None, position=None):
+    """Issue len(widths) dependent launches reading descriptors from `table`.
+    position: None, or (d_pos tensor, x_pitch bytes, y_pitch bytes, period)
+    for a positioned sequence (rows taken at the device-resident position,
+    which the sequence then advances by one)."""
     arr = _widths_array(widths)
-    _check(_lib.rmsnorm_sequence_eager(int(dtype), ctypes.c_void_p(table.data_ptr()), arr,
-                                       len(widths), float(eps), _stream_ptr(stream)))
+    if position is None:
+        _check(_lib.rmsnorm_sequence_eager(int(dtype), ctypes.c_void_p(table.data_ptr()), arr,
+                                           len(widths), float(eps), _stream_ptr(stream)))
+    else:
+        pos = _position(position)
+        _check(_lib.rmsnorm_sequence_eager_positioned(
+            int(dtype), ctypes.c_void_p(table.data_ptr()), arr, len(widths), float(eps),
+            ctypes.byref(pos), _stream_ptr(stream)))
 
 
 class SequenceGraph:
@@ -197,12 +222,19 @@ class SequenceGraph:
     an eager replay with the same kernels). `status` is RMSN_OK or
     RMSN_ECAPTURE."""
 
-    def __init__(self, table, widths, eps, dtype):
+    def __init__(self, table, widths, eps, dtype, position=None):
         self._table = table  # keep the descriptor table alive with the graph
+        self._position = position
         arr = _widths_array(widths)
         h = ctypes.c_void_p()
-        st = _lib.rmsnorm_sequence_graph_create(int(dtype), ctypes.c_void_p(table.data_ptr()),
-                                                arr, len(widths), float(eps), ctypes.byref(h))
+        if position is None:
+            st = _lib.rmsnorm_sequence_graph_create(int(dtype), ctypes.c_void_p(table.data_ptr()),
+                                                    arr, len(widths), float(eps), ctypes.byref(h))
+        else:
+            pos = _position(position)
+            st = _lib.rmsnorm_sequence_graph_create_positioned(
+                int(dtype), ctypes.c_void_p(table.data_ptr()), arr, len(widths), float(eps),
+                ctypes.byref(pos), ctypes.byref(h))
         if st not in (RMSN_OK, RMSN_ECAPTURE):
             raise RmsnormError(st, last_error())
         self.status = st
@@ -211,6 +243,15 @@ class SequenceGraph:
 
     def launch(self, stream=None):
         _check(_lib.rmsnorm_sequence_graph_launch(self._h, _stream_ptr(stream)))
+
+    def update(self, widths):
+        """New capture-time widths; returns (status, recaptured)."""
+        arr = _widths_array(widths)
+        rec = ctypes.c_int()
+        st = _lib.rmsnorm_sequence_graph_update(self._h, arr, len(widths), ctypes.byref(rec))
+        if st not in (RMSN_OK, RMSN_ECAPTURE):
+            raise RmsnormError(st, last_error())
+        return st, bool(rec.value)
 
     def node_count(self):
         v = ctypes.c_int64()

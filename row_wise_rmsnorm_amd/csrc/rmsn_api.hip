@@ -7,7 +7,11 @@
 // decided by the same plan function the eager path uses (section 2); every
 // kernel variant runs once before capture so nothing initialises lazily inside
 // it, and a failed capture degrades to eager replay instead of failing
-// (section 3).
+// (section 3). A positioned sequence also carries its state update: a
+// device-resident position the kernels read, advanced by the sequence's last
+// launch, so the captured graph walks rows on its own (section 2); widths that
+// change the launch plan are a capture key and trigger a re-capture through
+// the same plan function (section 2).
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -27,6 +31,8 @@ struct rmsn_graph {
     float eps = 0.0f;
     const rmsn_desc* table = nullptr;
     std::vector<Plan> plans;
+    bool positioned = false;
+    PosArgs pos{nullptr, 0, 0, 1};
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
     int64_t nodes = 0;
@@ -75,23 +81,63 @@ int plan_sequence(int dtype, const int64_t* widths, int32_t count, std::vector<P
     return RMSN_OK;
 }
 
+// The sequence's launches on `s`; a positioned sequence ends with its
+// position update.
 int enqueue_sequence(const std::vector<Plan>& plans, const rmsn_desc* table, float eps,
-                     hipStream_t s) {
+                     const PosArgs* pos, hipStream_t s) {
     for (size_t i = 0; i < plans.size(); ++i) {
-        const hipError_t e = launch_desc(plans[i], table + i, eps, s);
+        const hipError_t e = launch_desc(plans[i], table + i, eps, pos, s);
         if (e != hipSuccess) return hip_fail("sequence kernel launch", e);
+    }
+    if (pos) {
+        const hipError_t e = launch_advance(const_cast<int64_t*>(pos->d_pos), pos->period, s);
+        if (e != hipSuccess) return hip_fail("position update launch", e);
     }
     return RMSN_OK;
 }
 
+int check_position(int dtype, const rmsn_position* pos, PosArgs* out) {
+    if (!pos || !pos->d_pos) {
+        set_error("null position (pos=%p)", (const void*)pos);
+        return RMSN_EINVAL;
+    }
+    if ((uintptr_t)pos->d_pos % 8) {
+        set_error("d_pos must be 8-byte aligned");
+        return RMSN_EINVAL;
+    }
+    const int64_t es = elem_bytes(dtype);
+    if (pos->period < 1 || pos->x_pitch < 0 || pos->y_pitch < 0 || pos->x_pitch % es ||
+        pos->y_pitch % es) {
+        set_error("position: period must be >= 1 and pitches >= 0 multiples of %lld bytes "
+                  "(period %lld, x_pitch %lld, y_pitch %lld)",
+                  (long long)es, (long long)pos->period, (long long)pos->x_pitch,
+                  (long long)pos->y_pitch);
+        return RMSN_EINVAL;
+    }
+    const int64_t lim = INT64_MAX / 4;
+    if ((pos->x_pitch && pos->period - 1 > lim / pos->x_pitch) ||
+        (pos->y_pitch && pos->period - 1 > lim / pos->y_pitch)) {
+        set_error("position: period * pitch overflows");
+        return RMSN_EINVAL;
+    }
+    *out = PosArgs{pos->d_pos, pos->x_pitch, pos->y_pitch, pos->period};
+    return RMSN_OK;
+}
+
 // Run every distinct kernel variant of the sequence once on a private 1-element
-// row, so module loading and any other first-use work happen before capture.
-int prewarm(const std::vector<Plan>& plans, int dtype, float eps, hipStream_t s) {
+// row (and, for a positioned sequence, a private position), so module loading
+// and any other first-use work happen before capture. The caller's rows and
+// position are not touched.
+int prewarm(const std::vector<Plan>& plans, int dtype, float eps, bool positioned,
+            hipStream_t s) {
     void* scratch = nullptr;
     hipError_t e = hipMalloc(&scratch, 256);
     if (e != hipSuccess) return hip_fail("hipMalloc (pre-warm row)", e);
     char* base = static_cast<char*>(scratch);
     rmsn_desc h{base + 64, base + 128, base + 192, 1};
+    int64_t* own_pos = reinterpret_cast<int64_t*>(base + 224);
+    const PosArgs own{own_pos, 0, 0, 1};
+    const int64_t zero = 0;
     int st = RMSN_OK;
     const uint32_t one_f32 = 0x3F800000u;
     const uint16_t one_bf16 = 0x3F80u;
@@ -99,7 +145,8 @@ int prewarm(const std::vector<Plan>& plans, int dtype, float eps, hipStream_t s)
     const size_t es = (size_t)elem_bytes(dtype);
     if ((e = hipMemcpyAsync(base, &h, sizeof h, hipMemcpyHostToDevice, s)) != hipSuccess ||
         (e = hipMemcpyAsync(base + 64, one, es, hipMemcpyHostToDevice, s)) != hipSuccess ||
-        (e = hipMemcpyAsync(base + 128, one, es, hipMemcpyHostToDevice, s)) != hipSuccess) {
+        (e = hipMemcpyAsync(base + 128, one, es, hipMemcpyHostToDevice, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(own_pos, &zero, sizeof zero, hipMemcpyHostToDevice, s)) != hipSuccess) {
         st = hip_fail("hipMemcpyAsync (pre-warm row)", e);
     }
     std::vector<int> seen;  // kernel variants already run: path * 256 + chunks
@@ -109,7 +156,12 @@ int prewarm(const std::vector<Plan>& plans, int dtype, float eps, hipStream_t s)
         for (int c : seen) dup = dup || c == key;
         if (dup) continue;
         seen.push_back(key);
-        e = launch_desc(plans[i], reinterpret_cast<const rmsn_desc*>(base), eps, s);
+        e = launch_desc(plans[i], reinterpret_cast<const rmsn_desc*>(base), eps,
+                        positioned ? &own : nullptr, s);
+        if (e != hipSuccess) st = hip_fail("pre-warm launch", e);
+    }
+    if (st == RMSN_OK && positioned) {
+        e = launch_advance(own_pos, 1, s);
         if (e != hipSuccess) st = hip_fail("pre-warm launch", e);
     }
     e = hipStreamSynchronize(s);
@@ -131,8 +183,9 @@ int capture(rmsn_graph* g, hipStream_t s) {
     hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) return hip_fail("hipStreamBeginCapture", e);
     int st = RMSN_OK;
+    const PosArgs* pos = g->positioned ? &g->pos : nullptr;
     for (size_t i = 0; i < g->plans.size() && st == RMSN_OK; ++i) {
-        e = launch_desc(g->plans[i], g->table + i, g->eps, s);
+        e = launch_desc(g->plans[i], g->table + i, g->eps, pos, s);
         if (e != hipSuccess) st = hip_fail("captured launch", e);
         // Test hook: a synchronisation is not allowed while capturing, which
         // makes the capture fail the way a forgotten lazy initialisation would.
@@ -141,6 +194,10 @@ int capture(rmsn_graph* g, hipStream_t s) {
             st = hip_fail("hipStreamSynchronize inside capture (RMSN_TEST_BREAK_CAPTURE)",
                           e == hipSuccess ? hipErrorStreamCaptureUnsupported : e);
         }
+    }
+    if (st == RMSN_OK && pos) {
+        e = launch_advance(const_cast<int64_t*>(pos->d_pos), pos->period, s);
+        if (e != hipSuccess) st = hip_fail("captured position update", e);
     }
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(s, &graph);
@@ -174,6 +231,86 @@ int capture(rmsn_graph* g, hipStream_t s) {
     return RMSN_OK;
 }
 
+// Pre-warm and capture g's sequence on a private stream. On success g holds
+// the new graph and is not in fallback mode. On a capture failure the
+// partial graph is gone, g->fallback is set (launches replay eagerly with the
+// same kernels), the reason is logged when RMSN_LOG=1, and RMSN_ECAPTURE is
+// returned. Other failures return their status with g unchanged.
+int build_graph(rmsn_graph* g) {
+    hipStream_t s = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail("hipStreamCreateWithFlags", e);
+    int st = prewarm(g->plans, g->dtype, g->eps, g->positioned, s);
+    if (st != RMSN_OK) {
+        (void)hipStreamDestroy(s);
+        return st;
+    }
+    st = capture(g, s);
+    (void)hipStreamDestroy(s);
+    if (st != RMSN_OK) {
+        // Graceful downgrade: the handle stays usable and replays eagerly.
+        // Capture executes nothing, so no device state needs restoring.
+        g->fallback = true;
+        g->graph = nullptr;
+        g->exec = nullptr;
+        g->nodes = 0;
+        if (env_flag("RMSN_LOG"))
+            std::fprintf(stderr, "[rmsnorm] graph capture failed, eager fallback: %s\n",
+                         last_error());
+        return RMSN_ECAPTURE;
+    }
+    g->fallback = false;
+    return RMSN_OK;
+}
+
+bool same_launches(const std::vector<Plan>& a, const std::vector<Plan>& b) {
+    if (a.size() != b.size()) return false;
+    for (size_t i = 0; i < a.size(); ++i) {
+        const Plan& p = a[i];
+        const Plan& q = b[i];
+        if (p.path != q.path || p.chunks != q.chunks || p.loads != q.loads ||
+            p.block != q.block || p.grid != q.grid || p.rows_per_block != q.rows_per_block ||
+            p.streaming != q.streaming)
+            return false;
+    }
+    return true;
+}
+
+int create_graph(int dtype, const rmsn_desc* d_table, const int64_t* h_widths, int32_t count,
+                 float eps, const rmsn_position* position, rmsn_graph** out) {
+    clear_error();
+    if (!out) {
+        set_error("null output handle pointer");
+        return RMSN_EINVAL;
+    }
+    *out = nullptr;
+    int st = check_sequence_args(dtype, d_table, h_widths, count, eps);
+    if (st != RMSN_OK) return st;
+    PosArgs pos{nullptr, 0, 0, 1};
+    if (position && (st = check_position(dtype, position, &pos)) != RMSN_OK) return st;
+    rmsn_graph* g = new (std::nothrow) rmsn_graph;
+    if (!g) {
+        set_error("out of host memory for the graph handle");
+        return RMSN_ENOMEM;
+    }
+    g->dtype = dtype;
+    g->eps = eps;
+    g->table = d_table;
+    g->positioned = position != nullptr;
+    g->pos = pos;
+    if ((st = plan_sequence(dtype, h_widths, count, &g->plans)) != RMSN_OK) {
+        delete g;
+        return st;
+    }
+    st = build_graph(g);
+    if (st != RMSN_OK && st != RMSN_ECAPTURE) {
+        delete g;
+        return st;
+    }
+    *out = g;
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -199,56 +336,71 @@ int rmsnorm_sequence_eager(int dtype, const rmsn_desc* d_table, const int64_t* h
     if (st != RMSN_OK) return st;
     std::vector<Plan> plans;
     if ((st = plan_sequence(dtype, h_widths, count, &plans)) != RMSN_OK) return st;
-    return enqueue_sequence(plans, d_table, eps, static_cast<hipStream_t>(stream));
+    return enqueue_sequence(plans, d_table, eps, nullptr, static_cast<hipStream_t>(stream));
+}
+
+int rmsnorm_sequence_eager_positioned(int dtype, const rmsn_desc* d_table,
+                                      const int64_t* h_widths, int32_t count, float eps,
+                                      const rmsn_position* position, void* stream) {
+    clear_error();
+    int st = check_sequence_args(dtype, d_table, h_widths, count, eps);
+    if (st != RMSN_OK) return st;
+    PosArgs pos;
+    if ((st = check_position(dtype, position, &pos)) != RMSN_OK) return st;
+    std::vector<Plan> plans;
+    if ((st = plan_sequence(dtype, h_widths, count, &plans)) != RMSN_OK) return st;
+    return enqueue_sequence(plans, d_table, eps, &pos, static_cast<hipStream_t>(stream));
 }
 
 int rmsnorm_sequence_graph_create(int dtype, const rmsn_desc* d_table, const int64_t* h_widths,
                                   int32_t count, float eps, rmsn_graph** out) {
-    clear_error();
-    if (!out) {
-        set_error("null output handle pointer");
+    return create_graph(dtype, d_table, h_widths, count, eps, nullptr, out);
+}
+
+int rmsnorm_sequence_graph_create_positioned(int dtype, const rmsn_desc* d_table,
+                                             const int64_t* h_widths, int32_t count, float eps,
+                                             const rmsn_position* position, rmsn_graph** out) {
+    if (!position) {
+        clear_error();
+        if (out) *out = nullptr;
+        set_error("null position");
         return RMSN_EINVAL;
     }
-    *out = nullptr;
-    int st = check_sequence_args(dtype, d_table, h_widths, count, eps);
-    if (st != RMSN_OK) return st;
-    rmsn_graph* g = new (std::nothrow) rmsn_graph;
+    return create_graph(dtype, d_table, h_widths, count, eps, position, out);
+}
+
+int rmsnorm_sequence_graph_update(rmsn_graph* g, const int64_t* h_widths, int32_t count,
+                                  int* recaptured) {
+    clear_error();
+    if (recaptured) *recaptured = 0;
     if (!g) {
-        set_error("out of host memory for the graph handle");
-        return RMSN_ENOMEM;
+        set_error("null graph handle");
+        return RMSN_EINVAL;
     }
-    g->dtype = dtype;
-    g->eps = eps;
-    g->table = d_table;
-    if ((st = plan_sequence(dtype, h_widths, count, &g->plans)) != RMSN_OK) {
-        delete g;
-        return st;
+    if ((size_t)count != g->plans.size()) {
+        set_error("count %d differs from the handle's %d norms", (int)count, (int)g->plans.size());
+        return RMSN_EINVAL;
     }
-    hipStream_t s = nullptr;
-    hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
-    if (e != hipSuccess) {
-        delete g;
-        return hip_fail("hipStreamCreateWithFlags", e);
-    }
-    st = prewarm(g->plans, dtype, eps, s);
-    if (st != RMSN_OK) {
-        (void)hipStreamDestroy(s);
-        delete g;
-        return st;
-    }
-    st = capture(g, s);
-    (void)hipStreamDestroy(s);
-    if (st != RMSN_OK) {
-        // Graceful downgrade: the handle stays usable and replays eagerly.
-        g->fallback = true;
-        if (env_flag("RMSN_LOG"))
-            std::fprintf(stderr, "[rmsnorm] graph capture failed, eager fallback: %s\n",
-                         last_error());
-        *out = g;
-        return RMSN_ECAPTURE;
-    }
-    *out = g;
-    return RMSN_OK;
+    int st = check_sequence_args(g->dtype, g->table, h_widths, count, g->eps);
+    if (st != RMSN_OK) return st;
+    std::vector<Plan> plans;
+    if ((st = plan_sequence(g->dtype, h_widths, count, &plans)) != RMSN_OK) return st;
+    // Same launches: the captured graph already runs exactly these kernels
+    // (widths are loop bounds read from the table when they run).
+    if (same_launches(plans, g->plans) && !g->fallback) return RMSN_OK;
+    rmsn_graph next = *g;
+    next.plans = plans;
+    next.graph = nullptr;
+    next.exec = nullptr;
+    next.nodes = 0;
+    st = build_graph(&next);
+    if (st != RMSN_OK && st != RMSN_ECAPTURE) return st;  // g unchanged
+    // Swap in the new graph (or the eager fallback with the new plans).
+    if (g->exec) (void)hipGraphExecDestroy(g->exec);
+    if (g->graph) (void)hipGraphDestroy(g->graph);
+    *g = next;
+    if (recaptured) *recaptured = 1;
+    return st;
 }
 
 int rmsnorm_sequence_graph_launch(rmsn_graph* g, void* stream) {
@@ -258,7 +410,8 @@ int rmsnorm_sequence_graph_launch(rmsn_graph* g, void* stream) {
         return RMSN_EINVAL;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (g->fallback) return enqueue_sequence(g->plans, g->table, g->eps, s);
+    if (g->fallback)
+        return enqueue_sequence(g->plans, g->table, g->eps, g->positioned ? &g->pos : nullptr, s);
     const hipError_t e = hipGraphLaunch(g->exec, s);
     return e == hipSuccess ? RMSN_OK : hip_fail("hipGraphLaunch", e);
 }

@@ -859,17 +859,64 @@ __global__ __launch_bounds__(256) void k_rows_group(const T* x, int64_t xs,
     row_group<T, Q>(x + r * xs, w, y + r * ys, n, eps, lds4);
 }
 
+// A descriptor row's x and y at the sequence's device-resident position when
+// POS (Lecture 08 "Graph-resident decode", section 2: the varying value lives
+// in device memory and the address is computed on the device): row pointers
+// move by p * pitch bytes, p = position mod period; w does not move.
+// The descriptor (one 32-byte load) and, when POS, the position are read
+// together at kernel start: both are needed before any row address exists,
+// so neither load may wait behind the other or behind the width check.
+template <bool POS>
+__device__ __forceinline__ rmsn_desc desc_load(const rmsn_desc* d, const PosArgs& pa,
+                                               uint64_t* pos) {
+    const rmsn_desc v = *d;
+    uint64_t x = reinterpret_cast<uint64_t>(v.x), w = reinterpret_cast<uint64_t>(v.w);
+    uint64_t y = reinterpret_cast<uint64_t>(v.y), n = (uint64_t)v.n;
+    uint64_t p = POS ? (uint64_t)*pa.d_pos : 0u;
+    // An empty asm that takes every loaded value: the compiler cannot sink
+    // either load below the width check, so both are in flight at once.
+    asm volatile("" : "+s"(x), "+s"(w), "+s"(y), "+s"(n), "+s"(p));
+    *pos = p;
+    rmsn_desc r;
+    r.x = reinterpret_cast<const void*>(x);
+    r.w = reinterpret_cast<const void*>(w);
+    r.y = reinterpret_cast<void*>(y);
+    r.n = (int64_t)n;
+    return r;
+}
+
+template <typename T, bool POS>
+__device__ __forceinline__ void desc_row(const rmsn_desc& d, uint64_t pos, const PosArgs& pa,
+                                         const T*& x, T*& y) {
+    const char* xb = static_cast<const char*>(d.x);
+    char* yb = static_cast<char*>(d.y);
+    if (POS) {
+        // the update keeps the position in [0, period); a caller-set larger
+        // one is reduced here (a 64-bit division, off the common path)
+        const uint64_t period = (uint64_t)pa.period;
+        const int64_t p = (int64_t)(pos < period ? pos : pos % period);
+        xb += p * pa.x_pitch;
+        yb += p * pa.y_pitch;
+    }
+    x = reinterpret_cast<const T*>(xb);
+    y = reinterpret_cast<T*>(yb);
+}
+
 // GROUP-layout descriptor row: the captured instance Q is used when the row
 // read at run time fits it (width in (1024 (Q-1), 1024 Q], a multiple of 4,
 // quad-aligned pointers); any other row is streamed with BLOCK's mapping.
-template <typename T, int Q>
-__global__ __launch_bounds__(256) void k_desc_group(const rmsn_desc* __restrict__ d, float eps) {
+template <typename T, int Q, bool POS>
+__global__ __launch_bounds__(256) void k_desc_group(const rmsn_desc* __restrict__ d, float eps,
+                                                    PosArgs pa) {
     __shared__ float lds4[4];
-    const int64_t n = d->n;
+    uint64_t pos;
+    const rmsn_desc dd = desc_load<POS>(d, pa, &pos);
+    const int64_t n = dd.n;
     if (n < 1 || n > RMSN_MAX_N) return;
-    const T* x = static_cast<const T*>(d->x);
-    const T* w = static_cast<const T*>(d->w);
-    T* y = static_cast<T*>(d->y);
+    const T* x;
+    T* y;
+    desc_row<T, POS>(dd, pos, pa, x, y);
+    const T* w = static_cast<const T*>(dd.w);
     const uintptr_t a = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) |
                         reinterpret_cast<uintptr_t>(y);
     if ((n & 3) == 0 && n > 1024 * (Q - 1) && n <= 1024 * Q && a % (4 * sizeof(T)) == 0)
@@ -892,13 +939,30 @@ __global__ __launch_bounds__(256) void k_rows_block(const T* x, int64_t xs,
 // kernel runs (Lecture 08 "Graph-resident decode", section 2: a value used
 // only as a loop bound can live in device memory; the launch geometry comes
 // from the capture-time width).
-template <typename T, int NCH>
-__global__ __launch_bounds__(256) void k_desc_block(const rmsn_desc* __restrict__ d, float eps) {
+template <typename T, int NCH, bool POS>
+__global__ __launch_bounds__(256) void k_desc_block(const rmsn_desc* __restrict__ d, float eps,
+                                                    PosArgs pa) {
     __shared__ float lds4[4];
-    const int64_t n = d->n;
+    uint64_t pos;
+    const rmsn_desc dd = desc_load<POS>(d, pa, &pos);
+    const int64_t n = dd.n;
     if (n < 1 || n > RMSN_MAX_N) return;
-    row_block<T, NCH>(static_cast<const T*>(d->x), static_cast<const T*>(d->w),
-                      static_cast<T*>(d->y), (int)n, eps, lds4);
+    const T* x;
+    T* y;
+    desc_row<T, POS>(dd, pos, pa, x, y);
+    row_block<T, NCH>(x, static_cast<const T*>(dd.w), y, (int)n, eps, lds4);
+}
+
+// The state update of a positioned sequence, its last launch (captured as
+// the graph's last node): the next launch of the sequence normalises the rows
+// of the next position, p + 1 wrapped to [0, period). One thread, a
+// vector-memory read-modify-write.
+__global__ __launch_bounds__(64) void k_advance(int64_t* d_pos, int64_t period) {
+    if (threadIdx.x != 0) return;
+    const uint64_t pos = (uint64_t)d_pos[0];
+    const uint64_t per = (uint64_t)period;
+    const uint64_t p = pos < per ? pos : pos % per;
+    d_pos[0] = (int64_t)(p + 1 == per ? 0 : p + 1);
 }
 
 // The bf16 narrowing of the row kernels over consecutive bit patterns, two per
@@ -1042,12 +1106,13 @@ hipError_t launch_block_t(const Plan& p, const void* x, int64_t xs, const void* 
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_desc_t(const Plan& p, const rmsn_desc* d, float eps, hipStream_t s) {
+template <typename T, bool POS>
+hipError_t launch_desc_t(const Plan& p, const rmsn_desc* d, float eps, const PosArgs& pa,
+                         hipStream_t s) {
     if (p.path == RMSN_PATH_GROUP) {
-#define RMSN_CASE(Q)                                                                    \
-    case Q:                                                                             \
-        hipLaunchKernelGGL((k_desc_group<T, Q>), dim3(1), dim3(256), 0, s, d, eps);     \
+#define RMSN_CASE(Q)                                                                          \
+    case Q:                                                                                   \
+        hipLaunchKernelGGL((k_desc_group<T, Q, POS>), dim3(1), dim3(256), 0, s, d, eps, pa);  \
         break;
         switch (p.loads) {
             RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)
@@ -1056,9 +1121,9 @@ hipError_t launch_desc_t(const Plan& p, const rmsn_desc* d, float eps, hipStream
 #undef RMSN_CASE
         return hipGetLastError();
     }
-#define RMSN_CASE(C)                                                                    \
-    case C:                                                                             \
-        hipLaunchKernelGGL((k_desc_block<T, C>), dim3(1), dim3(256), 0, s, d, eps);     \
+#define RMSN_CASE(C)                                                                          \
+    case C:                                                                                   \
+        hipLaunchKernelGGL((k_desc_block<T, C, POS>), dim3(1), dim3(256), 0, s, d, eps, pa);  \
         break;
     switch (p.chunks) {
         RMSN_CASE(0)
@@ -1104,11 +1169,21 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
                                : launch_block_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
 }
 
-hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, hipStream_t stream) {
+hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
+                       hipStream_t stream) {
     if (p.path == RMSN_PATH_WAVE || p.path == RMSN_PATH_SPLIT)
         return hipErrorInvalidValue;  // descriptors use GROUP, BLOCK or STREAM
-    return p.dtype == RMSN_F32 ? launch_desc_t<float>(p, d, eps, stream)
-                               : launch_desc_t<uint16_t>(p, d, eps, stream);
+    if (pos)
+        return p.dtype == RMSN_F32 ? launch_desc_t<float, true>(p, d, eps, *pos, stream)
+                                   : launch_desc_t<uint16_t, true>(p, d, eps, *pos, stream);
+    const PosArgs none{nullptr, 0, 0, 1};
+    return p.dtype == RMSN_F32 ? launch_desc_t<float, false>(p, d, eps, none, stream)
+                               : launch_desc_t<uint16_t, false>(p, d, eps, none, stream);
+}
+
+hipError_t launch_advance(int64_t* d_pos, int64_t period, hipStream_t stream) {
+    hipLaunchKernelGGL(k_advance, dim3(1), dim3(64), 0, stream, d_pos, period);
+    return hipGetLastError();
 }
 
 hipError_t launch_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out,

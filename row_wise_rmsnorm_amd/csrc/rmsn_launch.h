@@ -15,9 +15,24 @@ namespace rmsn {
 hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
                        int64_t ys, int64_t rows, int n, float eps, hipStream_t stream);
 
+// The position of a positioned sequence, passed by value to its kernels: the
+// position itself is device memory, read when the kernels run.
+struct PosArgs {
+    const int64_t* d_pos;
+    int64_t x_pitch;  // bytes
+    int64_t y_pitch;  // bytes
+    int64_t period;   // >= 1
+};
+
 // One row described by the device-resident descriptor `d` (read when the
-// kernel runs); plan `p` was made for the capture-time width.
-hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, hipStream_t stream);
+// kernel runs); plan `p` was made for the capture-time width. pos: NULL, or
+// the row is taken at the sequence's device-resident position.
+hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
+                       hipStream_t stream);
+
+// *d_pos = (*d_pos mod period + 1) mod period on the device (the state
+// update of a positioned sequence).
+hipError_t launch_advance(int64_t* d_pos, int64_t period, hipStream_t stream);
 
 // Step 8's bf16 narrowing over consecutive bit patterns (diagnostic).
 hipError_t launch_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out,

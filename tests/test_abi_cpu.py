@@ -116,6 +116,35 @@ def test_sequence_validation(rn):
     assert L.rmsnorm_graph_node_count(None, ctypes.byref(v)) == rn.RMSN_EINVAL
 
 
+def test_positioned_sequence_validation(rn):
+    import ctypes
+    L = rn.lib()
+    w3 = (ctypes.c_int64 * 3)(7168, 1536, 512)
+    P = rn._Position
+
+    def pos(d=C16 + 0x1000, xp=4096, yp=4096, period=4):
+        return ctypes.byref(P(ctypes.c_void_p(d), xp, yp, period))
+
+    eager = L.rmsnorm_sequence_eager_positioned
+    assert eager(0, A16, w3, 3, 1e-6, None, None) == rn.RMSN_EINVAL       # no position
+    for bad in (dict(d=0), dict(d=C16 + 4), dict(period=0), dict(period=-3), dict(xp=-4),
+                dict(xp=6), dict(yp=2), dict(xp=1 << 61, period=1 << 20)):
+        assert eager(0, A16, w3, 3, 1e-6, pos(**bad), None) == rn.RMSN_EINVAL, bad
+        assert rn.last_error() != ""
+    assert eager(1, A16, w3, 3, 1e-6, pos(xp=2, yp=6), None) != rn.RMSN_EINVAL  # bf16: 2-byte pitches
+    bad = (ctypes.c_int64 * 3)(7168, 0, 512)
+    assert eager(0, A16, bad, 3, 1e-6, pos(), None) == rn.RMSN_EINVAL
+    h = ctypes.c_void_p(1234)
+    create = L.rmsnorm_sequence_graph_create_positioned
+    assert create(0, A16, w3, 3, 1e-6, None, ctypes.byref(h)) == rn.RMSN_EINVAL
+    assert h.value is None
+    assert create(0, A16, w3, 3, 1e-6, pos(period=0), ctypes.byref(h)) == rn.RMSN_EINVAL
+    assert create(0, A16, w3, 3, 1e-6, pos(), None) == rn.RMSN_EINVAL
+    rec = ctypes.c_int(7)
+    assert L.rmsnorm_sequence_graph_update(None, w3, 3, ctypes.byref(rec)) == rn.RMSN_EINVAL
+    assert rec.value == 0
+
+
 def test_diag_validation(rn):
     L = rn.lib()
     assert L.rmsnorm_diag_bf16(0xFFFFFFFF, 2, A16, None) == rn.RMSN_EINVAL

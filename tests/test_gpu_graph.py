@@ -324,3 +324,204 @@ def test_graph_rows_rewritten_to_misaligned_pointers(rn, step, desc_path):
         assert np.isnan(got[:o]).all() and np.isnan(got[o + n:]).all()
     g.destroy()
     step.point_at(0)
+
+
+# ---- positioned sequences: the state update inside the graph ----------------------
+
+class Ring:
+    """`period` positions of every norm's x and y rows, packed per norm with a
+    pitch of the row's width (rows of one norm are consecutive), one w per
+    norm, and the descriptor table pointing at position 0."""
+
+    def __init__(self, rn, widths, period, kind="f32"):
+        import torch
+        self.rn, self.widths, self.period = rn, widths, period
+        self.kind = kind
+        self.x, self.w, self.xd, self.wd, self.yd = [], [], [], [], []
+        for i, n in enumerate(widths):
+            xs = np.empty((period, n), np.float32)
+            for p in range(period):
+                xs[p], w = wl.misc_f32(700000 + 97 * i + p, n, sigma=float(10.0 ** ((p % 5) - 2)))
+            _, w = wl.misc_f32(800000 + i, n)
+            if kind == "bf16":
+                xs, w = wl.to_bf16_bits(xs), wl.to_bf16_bits(w)
+                from gpu_util import to_dev_bf16
+                xd, wd = to_dev_bf16(xs), to_dev_bf16(w)
+            else:
+                xd, wd = to_dev_f32(xs), to_dev_f32(w)
+            self.x.append(xs)
+            self.w.append(w)
+            self.xd.append(xd)
+            self.wd.append(wd)
+            self.yd.append(torch.full_like(xd, float("nan")))
+        self.table, _ = rn.make_table([(self.xd[i][0], self.wd[i], self.yd[i][0])
+                                       for i in range(len(widths))])
+        self.d_pos = torch.zeros(1, dtype=torch.int64, device=dev())
+
+    def position(self, n):
+        # the rings used here give every norm the same width n, so one pitch
+        # (one row of n elements) serves every entry of the table
+        es = 4 if self.kind == "f32" else 2
+        return (self.d_pos, n * es, n * es, self.period)
+
+    def expected(self, i, p):
+        if self.kind == "f32":
+            return oracle.row_f32(self.x[i][p], self.w[i], wl.EPS)
+        return oracle.row_bf16(self.x[i][p], self.w[i], wl.EPS)
+
+    def got(self, i, p):
+        if self.kind == "f32":
+            return f32_host(self.yd[i][p])
+        from gpu_util import bf16_host
+        return bf16_host(self.yd[i][p])
+
+
+def _check_ring(ring, positions_done):
+    from gpu_util import assert_bits_bf16
+    for i in range(len(ring.widths)):
+        for p in range(ring.period):
+            got = ring.got(i, p)
+            if p in positions_done:
+                if ring.kind == "f32":
+                    assert_bits_f32(got, ring.expected(i, p), f"norm {i} position {p}")
+                else:
+                    assert_bits_bf16(got, ring.expected(i, p), f"norm {i} position {p}")
+            elif ring.kind == "f32":
+                assert np.isnan(got).all(), f"norm {i} position {p} written too early"
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_positioned_graph_walks_the_ring(rn, kind):
+    """A graph replayed with no host work between replays: each replay
+    normalises the next position's rows, the position lives in device memory
+    and is advanced by the graph's last node; 7 replays over a ring of 5."""
+    say(f"positioned graph ({kind})")
+    n = 1536
+    ring = Ring(rn, [n] * 24, period=5, kind=kind)
+    dt = rn.F32 if kind == "f32" else rn.BF16
+    g = rn.SequenceGraph(ring.table, ring.widths, wl.EPS, dt, position=ring.position(n))
+    assert g.status == rn.RMSN_OK, g.capture_error
+    assert g.node_count() == 24 + 1
+    assert int(ring.d_pos.item()) == 0, "pre-warm or capture moved the caller's position"
+    for rep in range(7):
+        g.launch()
+        sync()
+        assert int(ring.d_pos.item()) == (rep + 1) % 5   # the update wraps the position
+        if rep < 5:
+            _check_ring(ring, set(range(rep + 1)))
+    # replays 5 and 6 wrapped to positions 0 and 1 and rewrote them identically
+    _check_ring(ring, set(range(5)))
+    g.destroy()
+
+
+def test_positioned_eager_equals_graph(rn):
+    """Eager and graph arms of a positioned sequence: the same rows, the same
+    bits, the same position updates (A/B after an A/A of the eager arm)."""
+    say("positioned eager vs graph")
+    n = 7168
+    ring = Ring(rn, [n] * 6, period=3)
+    pos = ring.position(n)
+    runs = {}
+    for arm in ("eager", "eager2", "graph"):
+        for y in ring.yd:
+            y.fill_(float("nan"))
+        ring.d_pos.fill_(1)
+        if arm.startswith("eager"):
+            for _ in range(3):
+                rn.rmsnorm_sequence_eager(ring.table, ring.widths, wl.EPS, rn.F32, position=pos)
+        else:
+            g = rn.SequenceGraph(ring.table, ring.widths, wl.EPS, rn.F32, position=pos)
+            assert g.status == rn.RMSN_OK
+            for _ in range(3):
+                g.launch()
+            sync()
+            g.destroy()
+        sync()
+        assert int(ring.d_pos.item()) == (1 + 3) % 3
+        runs[arm] = [f32_host(y) for y in ring.yd]
+        _check_ring(ring, {0, 1, 2})
+    for a in ("eager2", "graph"):
+        for i, (u, v) in enumerate(zip(runs["eager"], runs[a])):
+            assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), f"{a} norm {i}"
+
+
+def test_positioned_capture_failure_keeps_position(rn):
+    """A capture broken on purpose leaves the caller's position untouched and
+    replays eagerly, position update included."""
+    say("positioned capture failure")
+    n = 512
+    ring = Ring(rn, [n] * 5, period=4)
+    ring.d_pos.fill_(2)
+    os.environ["RMSN_TEST_BREAK_CAPTURE"] = "1"
+    try:
+        g = rn.SequenceGraph(ring.table, ring.widths, wl.EPS, rn.F32, position=ring.position(n))
+    finally:
+        del os.environ["RMSN_TEST_BREAK_CAPTURE"]
+    assert g.status == rn.RMSN_ECAPTURE and g.is_fallback()
+    sync()
+    assert int(ring.d_pos.item()) == 2
+    for rep in range(4):
+        g.launch()
+        sync()
+        assert int(ring.d_pos.item()) == (3 + rep) % 4
+    _check_ring(ring, {0, 1, 2, 3})
+    g.destroy()
+
+
+def test_positioned_caller_position_beyond_period(rn):
+    """A position the caller sets at or beyond the period counts modulo the
+    period (positions 12 and 2 of a ring of 5 are the same rows); the update
+    brings it back into [0, period)."""
+    say("positioned: caller position beyond the period")
+    n = 1024
+    ring = Ring(rn, [n] * 3, period=5)
+    g = rn.SequenceGraph(ring.table, ring.widths, wl.EPS, rn.F32, position=ring.position(n))
+    assert g.status == rn.RMSN_OK
+    ring.d_pos.fill_(12)
+    g.launch()
+    sync()
+    assert int(ring.d_pos.item()) == 3
+    _check_ring(ring, {2})
+    ring.d_pos.fill_((1 << 62) + 4)          # (2^62 + 4) mod 5 = 3
+    rn.rmsnorm_sequence_eager(ring.table, ring.widths, wl.EPS, rn.F32, position=ring.position(n))
+    sync()
+    assert int(ring.d_pos.item()) == 4
+    _check_ring(ring, {2, 3})
+    g.destroy()
+
+
+def test_update_recaptures_only_when_the_plan_moves(rn, step):
+    """Widths are a capture key only through the launch plan: widths inside
+    the same register buckets keep the graph; widths that move a node to
+    another kernel instance re-capture it; every replay stays exact."""
+    say("plan-keyed re-capture")
+    step.point_at(0)
+    g = rn.SequenceGraph(step.table, step.widths, wl.EPS, rn.F32)
+    assert g.status == rn.RMSN_OK
+    same = [n - 3 if n > 7000 else n for n in step.widths]          # 7165: still 28 chunks
+    st, rec = g.update(same)
+    assert st == rn.RMSN_OK and not rec
+    step.point_at(1, widths=same)
+    step.clear_outputs()
+    g.launch()
+    sync()
+    compare(step.outputs(), step.expected(1, widths=same), "same-plan widths")
+    moved = [4000 if n == 7168 else n for n in step.widths]          # 28 -> 16 chunks
+    st, rec = g.update(moved)
+    assert st == rn.RMSN_OK and rec
+    assert not g.is_fallback() and g.node_count() == len(step.widths)
+    for rep, s in enumerate([2, 0, 1]):
+        step.point_at(s, widths=moved)
+        step.clear_outputs()
+        g.launch()
+        sync()
+        compare(step.outputs(), step.expected(s, widths=moved), f"re-captured replay {rep}")
+    # back to the original plans: re-captured again
+    st, rec = g.update(step.widths)
+    assert st == rn.RMSN_OK and rec
+    step.point_at(0)
+    step.clear_outputs()
+    g.launch()
+    sync()
+    compare(step.outputs(), step.expected(0), "original plans again")
+    g.destroy()
