@@ -53,6 +53,11 @@ def _load():
     lib.rmsn_ref_bf16_to_f32.restype = c_f
     lib.rmsn_ref_f32_to_bf16.argtypes = [c_f]
     lib.rmsn_ref_f32_to_bf16.restype = ctypes.c_uint16
+    lib.rmsn_ref_sumsq_lanes.argtypes = [c_int, c_vp, c_i64, c_int]
+    lib.rmsn_ref_sumsq_lanes.restype = c_f
+    lib.rmsn_ref_rows_lanes.argtypes = [c_int, c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_i64, c_f,
+                                        c_int, c_int]
+    lib.rmsn_ref_rows_lanes.restype = c_int
     lib.rmsn_ref_f32_to_bf16_range.argtypes = [ctypes.c_uint32, c_i64, c_vp]
     lib.rmsn_ref_f32_to_bf16_range.restype = None
     _lib = lib
@@ -112,9 +117,10 @@ def row_bf16(x_bits, w_bits, eps):
     return y
 
 
-def rows(x, w, eps, nthreads=1, out=None):
+def rows(x, w, eps, nthreads=1, out=None, lanes=256):
     """Every row of a 2-D array (float32, or uint16 bf16 bit patterns) against
-    one weight row. Returns (y, threads_used)."""
+    one weight row. Returns (y, threads_used). lanes: 256 (R256) or 128 (the
+    same definition with 128 lane chains in four 32-lane groups)."""
     if x.dtype == np.float32:
         dt, x, w = F32, _f32(x), _f32(w)
     elif x.dtype == np.uint16:
@@ -122,10 +128,32 @@ def rows(x, w, eps, nthreads=1, out=None):
     else:
         raise TypeError("rows: float32 or uint16 (bf16 bits) expected")
     assert x.ndim == 2 and w.shape == (x.shape[1],)
+    assert lanes in (128, 256)
     y = np.empty_like(x) if out is None else out
-    used = _load().rmsn_ref_rows(dt, _ptr(x), x.shape[1], _ptr(w), _ptr(y), y.shape[1],
-                                 x.shape[0], x.shape[1], float(np.float32(eps)), int(nthreads))
+    if lanes == 256:
+        used = _load().rmsn_ref_rows(dt, _ptr(x), x.shape[1], _ptr(w), _ptr(y), y.shape[1],
+                                     x.shape[0], x.shape[1], float(np.float32(eps)), int(nthreads))
+    else:
+        used = _load().rmsn_ref_rows_lanes(dt, _ptr(x), x.shape[1], _ptr(w), _ptr(y), y.shape[1],
+                                           x.shape[0], x.shape[1], float(np.float32(eps)),
+                                           int(lanes), int(nthreads))
     return y, used
+
+
+def sumsq_lanes(x, lanes):
+    """Steps 1-3 with `lanes` lane chains (128 or 256) on a float32 row or a
+    uint16 bf16 row."""
+    if x.dtype == np.uint16:
+        x = _u16(x)
+        return np.float32(_load().rmsn_ref_sumsq_lanes(BF16, _ptr(x), x.size, int(lanes)))
+    x = _f32(x)
+    return np.float32(_load().rmsn_ref_sumsq_lanes(F32, _ptr(x), x.size, int(lanes)))
+
+
+def row_lanes(x, w, eps, lanes):
+    """One row (float32 or uint16 bf16 bits) under the `lanes`-lane definition."""
+    y, _ = rows(np.asarray(x)[None, :], np.asarray(w), eps, lanes=lanes)
+    return y[0]
 
 
 def bf16_to_f32(bits):

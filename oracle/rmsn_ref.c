@@ -23,6 +23,7 @@
 #define LANES 256      /* R256 step 1: number of lane chains          */
 #define WAVE 64        /* R256 step 2: width of each halving tree     */
 #define WAVES (LANES / WAVE)
+#define MAX_LANES 256  /* the lane counts defined here: 256 and 128   */
 
 float rmsn_ref_bf16_to_f32(uint16_t b)
 {
@@ -64,12 +65,13 @@ static float get_bf16(const void* row, int64_t d)
     return rmsn_ref_bf16_to_f32(((const uint16_t*)row)[d]);
 }
 
-static void lane_chains(const void* row, int64_t n, getter get, float p[LANES])
+static void lane_chains(const void* row, int64_t n, getter get, int lanes, float p[MAX_LANES])
 {
-    /* Step 1: lane l accumulates x[l], x[l+256], ... in ascending order. */
-    for (int l = 0; l < LANES; ++l) {
+    /* Step 1: lane l accumulates x[l], x[l+L], x[l+2L], ... in ascending
+     * order (L = lanes: 256 for R256). */
+    for (int l = 0; l < lanes; ++l) {
         float acc = 0.0f;
-        for (int64_t d = l; d < n; d += LANES) {
+        for (int64_t d = l; d < n; d += lanes) {
             float xd = get(row, d);
             acc = fmaf(xd, xd, acc);
         }
@@ -77,13 +79,15 @@ static void lane_chains(const void* row, int64_t n, getter get, float p[LANES])
     }
 }
 
-static void wave_trees(const float p[LANES], float W[WAVES])
+static void wave_trees(const float p[MAX_LANES], int lanes, float W[WAVES])
 {
-    /* Step 2: each 64-lane group is reduced by descending halving. */
+    /* Step 2: each of the four groups of L/4 lanes (64 for R256) is reduced
+     * by descending halving. */
+    const int group = lanes / WAVES;
     for (int w = 0; w < WAVES; ++w) {
-        float q[WAVE];
-        for (int j = 0; j < WAVE; ++j) q[j] = p[WAVE * w + j];
-        for (int s = WAVE / 2; s >= 1; s /= 2)
+        float q[MAX_LANES / WAVES];
+        for (int j = 0; j < group; ++j) q[j] = p[group * w + j];
+        for (int s = group / 2; s >= 1; s /= 2)
             for (int j = 0; j < s; ++j) q[j] = q[j] + q[j + s];
         W[w] = q[0];
     }
@@ -97,22 +101,30 @@ static float block_tree(const float W[WAVES])
     return a + b;
 }
 
-static float sumsq(const void* row, int64_t n, getter get)
+static float sumsq(const void* row, int64_t n, getter get, int lanes)
 {
-    float p[LANES], W[WAVES];
-    lane_chains(row, n, get, p);
-    wave_trees(p, W);
+    float p[MAX_LANES], W[WAVES];
+    lane_chains(row, n, get, lanes, p);
+    wave_trees(p, lanes, W);
     return block_tree(W);
 }
 
-float rmsn_ref_sumsq_f32(const float* x, int64_t n) { return sumsq(x, n, get_f32); }
-float rmsn_ref_sumsq_bf16(const uint16_t* x, int64_t n) { return sumsq(x, n, get_bf16); }
+float rmsn_ref_sumsq_f32(const float* x, int64_t n) { return sumsq(x, n, get_f32, LANES); }
+float rmsn_ref_sumsq_bf16(const uint16_t* x, int64_t n) { return sumsq(x, n, get_bf16, LANES); }
 
 void rmsn_ref_wave_totals_f32(const float* x, int64_t n, float out_w[4])
 {
-    float p[LANES];
-    lane_chains(x, n, get_f32, p);
-    wave_trees(p, out_w);
+    float p[MAX_LANES];
+    lane_chains(x, n, get_f32, LANES, p);
+    wave_trees(p, LANES, out_w);
+}
+
+static int valid_lanes(int lanes) { return lanes == 128 || lanes == 256; }
+
+float rmsn_ref_sumsq_lanes(int dtype, const void* x, int64_t n, int lanes)
+{
+    if (!valid_lanes(lanes)) return NAN;
+    return sumsq(x, n, dtype == RMSN_REF_F32 ? get_f32 : get_bf16, lanes);
 }
 
 float rmsn_ref_inv(float ss, int64_t n, float eps)
@@ -124,23 +136,34 @@ float rmsn_ref_inv(float ss, int64_t n, float eps)
     return inv;
 }
 
-void rmsn_ref_row_f32(const float* x, const float* w, float* y, int64_t n, float eps)
+static void row_f32(const float* x, const float* w, float* y, int64_t n, float eps, int lanes)
 {
-    float inv = rmsn_ref_inv(rmsn_ref_sumsq_f32(x, n), n, eps);
+    float inv = rmsn_ref_inv(sumsq(x, n, get_f32, lanes), n, eps);
     for (int64_t d = 0; d < n; ++d) {
         float a = x[d] * inv;  /* step 8, left to right */
         y[d] = a * w[d];
     }
 }
 
-void rmsn_ref_row_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, float eps)
+static void row_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, float eps,
+                     int lanes)
 {
-    float inv = rmsn_ref_inv(rmsn_ref_sumsq_bf16(x, n), n, eps);
+    float inv = rmsn_ref_inv(sumsq(x, n, get_bf16, lanes), n, eps);
     for (int64_t d = 0; d < n; ++d) {
         float a = rmsn_ref_bf16_to_f32(x[d]) * inv;
         float b = a * rmsn_ref_bf16_to_f32(w[d]);
         y[d] = rmsn_ref_f32_to_bf16(b);
     }
+}
+
+void rmsn_ref_row_f32(const float* x, const float* w, float* y, int64_t n, float eps)
+{
+    row_f32(x, w, y, n, eps, LANES);
+}
+
+void rmsn_ref_row_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, float eps)
+{
+    row_bf16(x, w, y, n, eps, LANES);
 }
 
 /* ---- many rows, optionally on several threads ---------------------------- */
@@ -152,17 +175,18 @@ typedef struct {
     void* y; int64_t ys;
     int64_t r0, r1, n;
     float eps;
+    int lanes;
 } rows_job;
 
 static void run_rows(const rows_job* j)
 {
     for (int64_t r = j->r0; r < j->r1; ++r) {
         if (j->dtype == RMSN_REF_F32)
-            rmsn_ref_row_f32((const float*)j->x + r * j->xs, (const float*)j->w,
-                             (float*)j->y + r * j->ys, j->n, j->eps);
+            row_f32((const float*)j->x + r * j->xs, (const float*)j->w,
+                    (float*)j->y + r * j->ys, j->n, j->eps, j->lanes);
         else
-            rmsn_ref_row_bf16((const uint16_t*)j->x + r * j->xs, (const uint16_t*)j->w,
-                              (uint16_t*)j->y + r * j->ys, j->n, j->eps);
+            row_bf16((const uint16_t*)j->x + r * j->xs, (const uint16_t*)j->w,
+                     (uint16_t*)j->y + r * j->ys, j->n, j->eps, j->lanes);
     }
 }
 
@@ -172,13 +196,14 @@ static void* rows_thread(void* arg)
     return NULL;
 }
 
-int rmsn_ref_rows(int dtype, const void* x, int64_t x_stride, const void* w,
-                  void* y, int64_t y_stride, int64_t rows, int64_t n, float eps,
-                  int nthreads)
+int rmsn_ref_rows_lanes(int dtype, const void* x, int64_t x_stride, const void* w,
+                        void* y, int64_t y_stride, int64_t rows, int64_t n, float eps,
+                        int lanes, int nthreads)
 {
+    if (!valid_lanes(lanes)) return 0;
     if (nthreads < 1) nthreads = 1;
     if ((int64_t)nthreads > rows) nthreads = (int)(rows > 0 ? rows : 1);
-    rows_job base = {dtype, x, x_stride, w, y, y_stride, 0, rows, n, eps};
+    rows_job base = {dtype, x, x_stride, w, y, y_stride, 0, rows, n, eps, lanes};
     if (nthreads == 1) {
         run_rows(&base);
         return 1;
@@ -202,4 +227,12 @@ int rmsn_ref_rows(int dtype, const void* x, int64_t x_stride, const void* w,
     free(jobs);
     free(tid);
     return started > 0 ? started : 1;
+}
+
+int rmsn_ref_rows(int dtype, const void* x, int64_t x_stride, const void* w,
+                  void* y, int64_t y_stride, int64_t rows, int64_t n, float eps,
+                  int nthreads)
+{
+    return rmsn_ref_rows_lanes(dtype, x, x_stride, w, y, y_stride, rows, n, eps, LANES,
+                               nthreads);
 }

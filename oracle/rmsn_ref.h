@@ -61,6 +61,19 @@ int rmsn_ref_rows(int dtype, const void* x, int64_t x_stride, const void* w,
                   void* y, int64_t y_stride, int64_t rows, int64_t n, float eps,
                   int nthreads);
 
+/* The same definition with another lane count L (Lecture 04 section 2.1:
+ * the reduction's thread count decides the bits; the lecture's kernel sums
+ * on 128 threads). R_L: L lane chains as in step 1 with stride L; four
+ * groups of L/4 lanes, each reduced by descending halving L/8, ..., 2, 1;
+ * ss = (W[0] + W[2]) + (W[1] + W[3]); steps 4-8 unchanged. L = 256 is R256;
+ * L = 128 is the four 32-lane groups of the lecture's 128-thread sum.
+ * Other L: the sum returns NaN and the rows call returns 0 having done
+ * nothing. */
+float rmsn_ref_sumsq_lanes(int dtype, const void* x, int64_t n, int lanes);
+int rmsn_ref_rows_lanes(int dtype, const void* x, int64_t x_stride, const void* w,
+                        void* y, int64_t y_stride, int64_t rows, int64_t n, float eps,
+                        int lanes, int nthreads);
+
 /* Exact bf16 widening and the round-to-nearest-even narrowing of step 8. */
 float rmsn_ref_bf16_to_f32(uint16_t b);
 uint16_t rmsn_ref_f32_to_bf16(float v);

@@ -10,7 +10,9 @@ a few tens of thousands of elements.
 Definition followed: Lecture 04 "Launch Geometry: Grids, Occupancy, and 327
 Norms per Token", section 2.1 (narrow sum of squares; block sum; inverse of
 sqrt(ss/(float)n + eps); wide apply), with the lane count, tree order and the
-correctly rounded sqrt-then-divide that this library fixes.
+correctly rounded sqrt-then-divide that this library fixes. `lanes=128` gives
+the same definition with the lecture's 128 summing threads: 128 lane lists
+and four groups of 32.
 """
 import numpy as np
 
@@ -20,10 +22,10 @@ LANES = 256
 GROUP = 64
 
 
-def lane_lists(n):
-    lists = [[] for _ in range(LANES)]
+def lane_lists(n, lanes=LANES):
+    lists = [[] for _ in range(lanes)]
     for d in range(n):
-        lists[d % LANES].append(d)
+        lists[d % lanes].append(d)
     return lists
 
 
@@ -35,15 +37,16 @@ def halve(vals):
     return halve([ex.add(vals[j], vals[j + s]) for j in range(s)])
 
 
-def sumsq(x):
+def sumsq(x, lanes=LANES):
     x = np.asarray(x, dtype=np.float32)
+    group = lanes // 4
     partial = []
-    for idx in lane_lists(len(x)):
+    for idx in lane_lists(len(x), lanes):
         acc = np.float32(0.0)
         for d in idx:
             acc = ex.fma(x[d], x[d], acc)
         partial.append(acc)
-    groups = [halve(partial[GROUP * g: GROUP * (g + 1)]) for g in range(LANES // GROUP)]
+    groups = [halve(partial[group * g: group * (g + 1)]) for g in range(4)]
     return halve(groups)
 
 
@@ -54,8 +57,8 @@ def inv_rms(ss, n, eps):
     return ex.div(np.float32(1.0), r)
 
 
-def row(x, w, eps):
+def row(x, w, eps, lanes=LANES):
     x = np.asarray(x, dtype=np.float32)
     w = np.asarray(w, dtype=np.float32)
-    inv = inv_rms(sumsq(x), len(x), eps)
+    inv = inv_rms(sumsq(x, lanes), len(x), eps)
     return np.array([ex.mul(ex.mul(x[d], inv), w[d]) for d in range(len(x))], dtype=np.float32)

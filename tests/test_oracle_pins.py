@@ -222,6 +222,60 @@ def test_association_probes_discriminate(oracle_mod):
     assert all(told_apart.values()), told_apart
 
 
+# ---- the 128-lane definition (the lecture's thread count) ---------------------
+
+@pytest.mark.parametrize("n", [1, 7, 31, 32, 33, 127, 128, 129, 700, 1536, 7168, 9001])
+def test_l128_second_transcription(oracle_mod, n):
+    """The oracle's 128-lane sum and rows equal the independent transcription
+    (lane lists of stride 128, four 32-lane groups, exact-rational rounding)."""
+    x, w = wl.misc_f32(3000 + n, n, sigma=float(10.0 ** ((n % 5) - 2)))
+    ss = oracle_mod.sumsq_lanes(x, 128)
+    assert bits32(ss) == bits32(r256_second.sumsq(x, lanes=128)), n
+    assert bits32(ss) == bits32(_alt_sumsq(x, lanes=128, group=32)), n
+    if n <= 1536:
+        assert same_bits(oracle_mod.row_lanes(x, w, wl.EPS, 128),
+                         r256_second.row(x, w, wl.EPS, lanes=128))
+    # lanes=256 through the same entry equals the R256 functions
+    assert bits32(oracle_mod.sumsq_lanes(x, 256)) == bits32(oracle_mod.sumsq_f32(x))
+
+
+def test_l128_probes_and_closed_forms(oracle_mod):
+    """The probes tell the two definitions apart (R128 agrees with its own
+    transcription on each); widths up to 8 have the same closed form under
+    both (only the first group's lanes 0..7 hold values); zero padding is
+    inert under R128 too; a bf16 row is its binary32 row rounded once."""
+    differs = False
+    for x in _probe_rows():
+        s128 = oracle_mod.sumsq_lanes(x, 128)
+        assert bits32(s128) == bits32(r256_second.sumsq(x, lanes=128))
+        differs = differs or bits32(s128) != bits32(oracle_mod.sumsq_f32(x))
+    assert differs
+    for x, w, eps in _tiny_rows():
+        assert same_bits(oracle_mod.row_lanes(x, w, eps, 128), closed_form_small(x, w, eps))
+    x, _ = wl.misc_f32(11, 3000)
+    base = oracle_mod.sumsq_lanes(x, 128)
+    for m in (1, 127, 128, 7168):
+        assert bits32(oracle_mod.sumsq_lanes(np.concatenate([x, np.zeros(m, np.float32)]), 128)) == bits32(base)
+    xb, wb = wl.batch64()
+    yb, _ = oracle_mod.rows(xb[:4], wb, wl.EPS, lanes=128)
+    yf, _ = oracle_mod.rows(oracle_mod.bf16_to_f32(xb[:4]), oracle_mod.bf16_to_f32(wb), wl.EPS,
+                            lanes=128)
+    assert np.array_equal(yb, wl.to_bf16_bits(yf))
+    assert bits32(oracle_mod.sumsq_lanes(xb[0], 128)) == bits32(
+        oracle_mod.sumsq_lanes(oracle_mod.bf16_to_f32(xb[0]), 128))
+
+
+def test_l128_float64_error(oracle_mod):
+    """The 128-lane definition is as accurate as R256 on the decode widths:
+    max relative error against the float64 formula below 1e-6."""
+    for i, n in enumerate((7168, 1536, 512)):
+        x, w = wl.misc_f32(4000 + i, n)
+        y = oracle_mod.row_lanes(x, w, wl.EPS, 128)
+        Y = oracle_mod.float64_reference(x, w, wl.EPS)
+        nz = Y != 0
+        assert np.max(np.abs(y[nz] - Y[nz]) / np.abs(Y[nz])) < 1e-6
+
+
 def test_wave_totals_match_second_transcription(oracle_mod):
     x, _ = wl.misc_f32(7, 5000)
     W = oracle_mod.wave_totals_f32(x)
