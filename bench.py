@@ -38,7 +38,9 @@ METRIC = ("RMSNorm achieved HBM GB/s (% of peak) + µs per 327-norm decode step 
           "(graph vs eager)")
 ROTATE = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_8192x7168_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "row_wise_rmsnorm_amd", "csrc", "rmsn_kernels.hip")
+# the sources the prefill kernel is compiled from (its traffic record is tied to them)
+KERNEL_SRCS = [os.path.join(ROOT, "row_wise_rmsnorm_amd", "csrc", f)
+               for f in ("rmsn_kernels.hip", "rmsn_common.h", "rmsn_launch.h")]
 
 
 def log(msg):
@@ -70,8 +72,11 @@ def elapsed_ms(fn, count):
 
 
 def source_digest():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():

@@ -264,17 +264,38 @@ int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_
  *   RMSN_OPT_SPLIT_LOADS:     0 automatic, else 1, 2, 4 or 8 slices per
  *                            wavefront (SPLIT path; a value that would need
  *                            more than 16 wavefronts falls back to automatic)
+ *   RMSN_OPT_APPLY_THREADS:   128-lane build only (RMSN_EINVAL in the default
+ *                            build): threads per row for the elementwise
+ *                            apply, 0 (= 1024), 128, 256, 512 or 1024; the sum
+ *                            always runs on the first 128
  * Returns RMSN_EINVAL for an unknown key or value. Not synchronised with
  * launches on other threads. Environment: RMSN_PATH, RMSN_ROWS_PER_BLOCK,
- * RMSN_STREAMING, RMSN_SPLIT_LOADS. */
+ * RMSN_STREAMING, RMSN_SPLIT_LOADS, RMSN_APPLY_THREADS. */
 enum {
     RMSN_OPT_PATH = 1,
     RMSN_OPT_ROWS_PER_BLOCK = 2,
     RMSN_OPT_STREAMING = 3,
-    RMSN_OPT_SPLIT_LOADS = 4
+    RMSN_OPT_SPLIT_LOADS = 4,
+    RMSN_OPT_APPLY_THREADS = 5
 };
 int rmsnorm_set_option(int key, int value);
 int rmsnorm_get_option(int key, int* value);
+
+/* ---- the association a build computes ---------------------------------------- */
+
+/* Lane chains of the association this library computes: 256 (R256, every
+ * statement above) for the default build librmsnorm_amd.so; 128 for the
+ * reference-compatibility build librmsnorm_amd_l128.so, which sums the row on
+ * 128 threads as Lecture 04 section 2.1's kernel does -- 128 lane chains
+ * (stride 128), four 32-lane groups each reduced by descending halving
+ * 16..1, combine (G0 + G2) + (G1 + G3), steps 4-8 unchanged -- and applies it
+ * on the whole block (RMSN_OPT_APPLY_THREADS). That build has the same entry
+ * points; every launch runs one workgroup per row (plan path RMSN_PATH_BLOCK,
+ * chunks 0, block = the apply width) and RMSN_OPT_PATH, RMSN_OPT_ROWS_PER_BLOCK,
+ * RMSN_OPT_STREAMING and RMSN_OPT_SPLIT_LOADS do not change its launches. The
+ * two builds give different bits (the lane count is part of the numerics);
+ * the apply width of the 128-lane build does not. */
+int rmsnorm_association_lanes(void);
 
 /* ---- diagnostics ----------------------------------------------------------- */
 

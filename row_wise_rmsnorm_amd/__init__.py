@@ -17,11 +17,13 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librmsnorm_amd.so")
+# the 128-lane build (same C ABI; rmsnorm_association_lanes() == 128)
+LIB128_PATH = os.path.join(_HERE, "librmsnorm_amd_l128.so")
 
 RMSN_OK, RMSN_EINVAL, RMSN_EHIP, RMSN_ECAPTURE, RMSN_ENOMEM = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM, PATH_SPLIT, PATH_GROUP = -1, 0, 1, 2, 3, 4
-OPT_PATH, OPT_ROWS_PER_BLOCK, OPT_STREAMING, OPT_SPLIT_LOADS = 1, 2, 3, 4
+OPT_PATH, OPT_ROWS_PER_BLOCK, OPT_STREAMING, OPT_SPLIT_LOADS, OPT_APPLY_THREADS = 1, 2, 3, 4, 5
 MAX_N = 1 << 24
 DESC_BYTES = 32
 
@@ -50,11 +52,13 @@ def _position(position):
     return _Position(ctypes.c_void_p(d_pos.data_ptr()), int(x_pitch), int(y_pitch), int(period))
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"row_wise_rmsnorm_amd: {LIB_PATH} is not built "
+def bind(path):
+    """Load one build of the library (LIB_PATH or LIB128_PATH) and declare the
+    C signatures; returns the ctypes handle."""
+    if not os.path.exists(path):
+        raise ImportError(f"row_wise_rmsnorm_amd: {path} is not built "
                           "(run __graft_entry__.build() or row_wise_rmsnorm_amd/build.py)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i64, i32, f, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_uint32
     c_int = ctypes.c_int
     sig = {
@@ -83,10 +87,12 @@ def _load():
         fn.restype = c_int
     lib.rmsnorm_last_error.argtypes = []
     lib.rmsnorm_last_error.restype = ctypes.c_char_p
+    lib.rmsnorm_association_lanes.argtypes = []
+    lib.rmsnorm_association_lanes.restype = c_int
     return lib
 
 
-_lib = _load()
+_lib = bind(LIB_PATH)
 
 EXPORTED = ("rmsnorm_f32", "rmsnorm_bf16", "rmsnorm_batched_rows", "rmsnorm_sequence_eager",
             "rmsnorm_sequence_graph_create", "rmsnorm_sequence_graph_launch",
@@ -94,7 +100,8 @@ EXPORTED = ("rmsnorm_f32", "rmsnorm_bf16", "rmsnorm_batched_rows", "rmsnorm_sequ
             "rmsnorm_graph_is_fallback", "rmsnorm_last_error", "rmsnorm_plan_query",
             "rmsnorm_set_option", "rmsnorm_get_option", "rmsnorm_diag_inverse",
             "rmsnorm_diag_bf16", "rmsnorm_sequence_eager_positioned",
-            "rmsnorm_sequence_graph_create_positioned", "rmsnorm_sequence_graph_update")
+            "rmsnorm_sequence_graph_create_positioned", "rmsnorm_sequence_graph_update",
+            "rmsnorm_association_lanes")
 
 
 def lib():
@@ -104,6 +111,11 @@ def lib():
 
 def last_error():
     return (_lib.rmsnorm_last_error() or b"").decode()
+
+
+def association_lanes():
+    """Lane chains of the association the loaded library computes (256)."""
+    return _lib.rmsnorm_association_lanes()
 
 
 def _check(status):

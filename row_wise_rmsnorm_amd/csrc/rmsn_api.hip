@@ -454,6 +454,8 @@ int rmsnorm_graph_is_fallback(const rmsn_graph* g, int* out) {
 
 const char* rmsnorm_last_error(void) { return last_error(); }
 
+int rmsnorm_association_lanes(void) { return kAssocLanes; }
+
 int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_info* out) {
     clear_error();
     if (!out) {

@@ -1,0 +1,269 @@
+// rmsn_common.h -- device code shared by every row kernel of the library:
+// global-memory pointer types and scalar bases, element and quad access,
+// the bf16 narrowing, cross-lane moves, steps 4-7 of the association, and
+// the prologue of the descriptor kernels. Layout-specific code (which lane
+// holds which chain) lives with each layout's kernels.
+//
+// Floating point: contraction is off for every file that includes this one;
+// '/' and sqrtf are the correctly rounded sequences HIP generates by default
+// for binary32; f32 denormals are preserved.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rmsn_launch.h"
+
+#pragma clang fp contract(off)
+
+namespace rmsn {
+namespace {
+
+// Global-memory (address space 1) byte pointers. A wave-uniform one held in
+// scalar registers becomes the scalar base of a load's address.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) char* gptr_c;
+typedef __attribute__((address_space(1))) char* gptr;
+
+__device__ __forceinline__ gptr_c scalar_gptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (gptr_c)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ gptr scalar_gptr(void* p) {
+    return (gptr)scalar_gptr(static_cast<const void*>(p));
+}
+__device__ __forceinline__ gptr_c scalar_gptr(gptr_c p) {
+    return scalar_gptr(reinterpret_cast<const void*>(reinterpret_cast<uint64_t>(p)));
+}
+__device__ __forceinline__ gptr scalar_gptr(gptr p) {
+    return (gptr)scalar_gptr(reinterpret_cast<const void*>(reinterpret_cast<uint64_t>(p)));
+}
+
+// ---------------------------------------------------------------------------
+// Element access. bf16 values are their 16-bit patterns; widening is exact.
+
+__device__ __forceinline__ float widen(float v) { return v; }
+__device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// binary32 -> bf16, round to nearest, ties to even (the MODE register's
+// default rounding), denormals kept, NaN -> a quiet NaN: one
+// v_cvt_pk_bf16_f32 per pair of values. Checked against the CPU narrowing for
+// every binary32 bit pattern through rmsnorm_diag_bf16.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ void put(float* p, float v) { *p = v; }
+__device__ __forceinline__ void put(uint16_t* p, float v) { *p = (uint16_t)bf16_bits(v); }
+
+// Four consecutive elements ("a quad") as they sit in registers: binary32
+// quads are 16 bytes, bf16 quads stay packed in 8 bytes and are widened on use.
+template <typename T> struct Quad;
+
+template <> struct Quad<float> {
+    using raw = float4;
+    template <bool NT>
+    static __device__ __forceinline__ raw gload(gptr_c p) {
+        auto* a = reinterpret_cast<const __attribute__((address_space(1))) f32x4*>(p);
+        const f32x4 v = NT ? __builtin_nontemporal_load(a) : *a;
+        return make_float4(v.x, v.y, v.z, v.w);
+    }
+    template <bool NT>
+    static __device__ __forceinline__ void gstore(gptr p, const float v[4]) {
+        f32x4 q;
+        q.x = v[0]; q.y = v[1]; q.z = v[2]; q.w = v[3];
+        auto* a = reinterpret_cast<__attribute__((address_space(1))) f32x4*>(p);
+        if (NT) __builtin_nontemporal_store(q, a);
+        else *a = q;
+    }
+    static __device__ __forceinline__ raw load(const float* p) {
+        return *reinterpret_cast<const float4*>(p);
+    }
+    static __device__ __forceinline__ raw zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    // Elements e..e+3 of a row of width n with e < n < e + 4 possible: the
+    // missing ones read as +0 (addresses are clamped into the row).
+    static __device__ __forceinline__ raw load_tail(const float* p, int e, int n) {
+        raw r;
+        r.x = e + 0 < n ? p[min(e + 0, n - 1)] : 0.f;
+        r.y = e + 1 < n ? p[min(e + 1, n - 1)] : 0.f;
+        r.z = e + 2 < n ? p[min(e + 2, n - 1)] : 0.f;
+        r.w = e + 3 < n ? p[min(e + 3, n - 1)] : 0.f;
+        return r;
+    }
+    static __device__ __forceinline__ void unpack(const raw& r, float v[4]) {
+        v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float v[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+template <> struct Quad<uint16_t> {
+    using raw = uint2;
+    template <bool NT>
+    static __device__ __forceinline__ raw gload(gptr_c p) {
+        auto* a = reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(p);
+        const u32x2 v = NT ? __builtin_nontemporal_load(a) : *a;
+        return make_uint2(v.x, v.y);
+    }
+    template <bool NT>
+    static __device__ __forceinline__ void gstore(gptr p, const float v[4]) {
+        u32x2 q;
+        q.x = bf16_pair(v[0], v[1]);
+        q.y = bf16_pair(v[2], v[3]);
+        auto* a = reinterpret_cast<__attribute__((address_space(1))) u32x2*>(p);
+        if (NT) __builtin_nontemporal_store(q, a);
+        else *a = q;
+    }
+    static __device__ __forceinline__ raw load(const uint16_t* p) {
+        return *reinterpret_cast<const uint2*>(p);
+    }
+    static __device__ __forceinline__ raw zero() { return make_uint2(0u, 0u); }
+    static __device__ __forceinline__ raw load_tail(const uint16_t* p, int e, int n) {
+        const uint32_t b0 = e + 0 < n ? p[min(e + 0, n - 1)] : 0u;
+        const uint32_t b1 = e + 1 < n ? p[min(e + 1, n - 1)] : 0u;
+        const uint32_t b2 = e + 2 < n ? p[min(e + 2, n - 1)] : 0u;
+        const uint32_t b3 = e + 3 < n ? p[min(e + 3, n - 1)] : 0u;
+        return make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
+    static __device__ __forceinline__ void unpack(const raw& r, float v[4]) {
+        v[0] = __uint_as_float(r.x << 16);
+        v[1] = __uint_as_float(r.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(r.y << 16);
+        v[3] = __uint_as_float(r.y & 0xFFFF0000u);
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float v[4]) {
+        uint2 q;
+        q.x = bf16_pair(v[0], v[1]);
+        q.y = bf16_pair(v[2], v[3]);
+        *reinterpret_cast<uint2*>(p) = q;
+    }
+};
+
+// Make the compiler treat a quad's registers as rewritten (the asm is empty):
+// values derived from it before this point (the widened bf16 floats of the
+// reduction) cannot be reused after it, so they need not stay live.
+__device__ __forceinline__ void opaque(float4& r) {
+    asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w));
+}
+__device__ __forceinline__ void opaque(uint2& r) { asm volatile("" : "+v"(r.x), "+v"(r.y)); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane moves.
+
+// Lane i receives lane i+K of its 16-lane DPP row (lanes past the row's end
+// receive 0; the trees never use those lanes' results).
+template <int K>
+__device__ __forceinline__ float row_shl(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + K, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// ---------------------------------------------------------------------------
+// Steps 4-7 of the association: shared by every kernel and the diagnostic.
+
+__device__ __forceinline__ float mean_eps_root(float ss, int n, float eps) {
+    const float m = ss / (float)n;  // n <= 2^24: exact as binary32
+    const float t = m + eps;
+    return sqrtf(t);                // correctly rounded
+}
+__device__ __forceinline__ float reciprocal(float r) { return 1.0f / r; }  // correctly rounded
+__device__ __forceinline__ float inverse_rms(float ss, int n, float eps) {
+    return reciprocal(mean_eps_root(ss, n, eps));
+}
+
+// Element access for the BLOCK layout, where lane l of a wavefront touches
+// element 64g + l of each chunk: consecutive lanes, consecutive elements.
+// Addresses are global (address space 1) byte offsets from the row base.
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    // raw()/value() split a load from its use so that every load of a row can
+    // be issued before any result is consumed.
+    using raw_t = float;
+    static __device__ __forceinline__ raw_t raw(gptr_c row, uint32_t d) {
+        return *reinterpret_cast<const __attribute__((address_space(1))) float*>(row + 4u * d);
+    }
+    static __device__ __forceinline__ float value(raw_t r) { return r; }
+    static __device__ __forceinline__ float load(gptr_c row, uint32_t d) { return raw(row, d); }
+    static __device__ __forceinline__ void store(gptr row, uint32_t d, float v) {
+        *reinterpret_cast<__attribute__((address_space(1))) float*>(row + 4u * d) = v;
+    }
+};
+
+template <> struct Elem<uint16_t> {
+    // 16-bit loads and stores: measured faster here than loading the dword
+    // that holds the element or pairing neighbour lanes into dword stores.
+    using raw_t = uint32_t;
+    static __device__ __forceinline__ raw_t raw(gptr_c row, uint32_t d) {
+        return *reinterpret_cast<const __attribute__((address_space(1))) uint16_t*>(row + 2u * d);
+    }
+    static __device__ __forceinline__ float value(raw_t b) { return __uint_as_float(b << 16); }
+    static __device__ __forceinline__ float load(gptr_c row, uint32_t d) { return value(raw(row, d)); }
+    static __device__ __forceinline__ void store(gptr row, uint32_t d, float v) {
+        *reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(row + 2u * d) =
+            (uint16_t)bf16_bits(v);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Descriptor rows.
+
+// A descriptor row's x and y at the sequence's device-resident position when
+// POS (Lecture 08 "Graph-resident decode", section 2: the varying value lives
+// in device memory and the address is computed on the device): row pointers
+// move by p * pitch bytes, p = position mod period; w does not move.
+// The descriptor (one 32-byte load) and, when POS, the position are read
+// together at kernel start: both are needed before any row address exists,
+// so neither load may wait behind the other or behind the width check.
+template <bool POS>
+__device__ __forceinline__ rmsn_desc desc_load(const rmsn_desc* d, const PosArgs& pa,
+                                               uint64_t* pos) {
+    const rmsn_desc v = *d;
+    uint64_t x = reinterpret_cast<uint64_t>(v.x), w = reinterpret_cast<uint64_t>(v.w);
+    uint64_t y = reinterpret_cast<uint64_t>(v.y), n = (uint64_t)v.n;
+    uint64_t p = POS ? (uint64_t)*pa.d_pos : 0u;
+    // An empty asm that takes every loaded value: the compiler cannot sink
+    // either load below the width check, so both are in flight at once.
+    asm volatile("" : "+s"(x), "+s"(w), "+s"(y), "+s"(n), "+s"(p));
+    *pos = p;
+    rmsn_desc r;
+    r.x = reinterpret_cast<const void*>(x);
+    r.w = reinterpret_cast<const void*>(w);
+    r.y = reinterpret_cast<void*>(y);
+    r.n = (int64_t)n;
+    return r;
+}
+
+template <typename T, bool POS>
+__device__ __forceinline__ void desc_row(const rmsn_desc& d, uint64_t pos, const PosArgs& pa,
+                                         const T*& x, T*& y) {
+    const char* xb = static_cast<const char*>(d.x);
+    char* yb = static_cast<char*>(d.y);
+    if (POS) {
+        // the update keeps the position in [0, period); a caller-set larger
+        // one is reduced here (a 64-bit division, off the common path)
+        const uint64_t period = (uint64_t)pa.period;
+        const int64_t p = (int64_t)(pos < period ? pos : pos % period);
+        xb += p * pa.x_pitch;
+        yb += p * pa.y_pitch;
+    }
+    x = reinterpret_cast<const T*>(xb);
+    y = reinterpret_cast<T*>(yb);
+}
+
+}  // namespace
+}  // namespace rmsn

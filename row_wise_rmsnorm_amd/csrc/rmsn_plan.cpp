@@ -20,6 +20,7 @@ std::atomic<int> g_path{-2};   // -2 = not yet read from the environment
 std::atomic<int> g_rpb{-2};
 std::atomic<int> g_stream{-2};
 std::atomic<int> g_split{-2};
+std::atomic<int> g_apply{-2};
 
 int env_int(const char* name, int dflt) {
     const char* s = std::getenv(name);
@@ -35,6 +36,7 @@ bool valid_path(int v) {
            v == RMSN_PATH_SPLIT || v == RMSN_PATH_GROUP;
 }
 bool valid_split_loads(int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8; }
+bool valid_apply_threads(int v) { return v == 0 || v == 128 || v == 256 || v == 512 || v == 1024; }
 bool valid_rpb(int v) { return v == 0 || v == 4 || v == 8; }
 bool valid_streaming(int v) { return v == -1 || v == 0 || v == 1; }
 
@@ -95,6 +97,16 @@ int option_split_loads() {
     return v;
 }
 
+int option_apply_threads() {
+    int v = g_apply.load(std::memory_order_relaxed);
+    if (v == -2) {
+        v = env_int("RMSN_APPLY_THREADS", 0);
+        if (!valid_apply_threads(v)) v = 0;
+        g_apply.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 int set_option(int key, int value) {
     if (key == RMSN_OPT_PATH) {
         if (!valid_path(value)) {
@@ -128,6 +140,20 @@ int set_option(int key, int value) {
         g_split.store(value, std::memory_order_relaxed);
         return RMSN_OK;
     }
+    if (key == RMSN_OPT_APPLY_THREADS) {
+        if (kAssocLanes != 128) {
+            set_error("rmsnorm_set_option: the apply width is an option of the 128-lane build "
+                      "only (this build computes %d lanes)", kAssocLanes);
+            return RMSN_EINVAL;
+        }
+        if (!valid_apply_threads(value)) {
+            set_error("rmsnorm_set_option: apply threads must be 0, 128, 256, 512 or 1024, got %d",
+                      value);
+            return RMSN_EINVAL;
+        }
+        g_apply.store(value, std::memory_order_relaxed);
+        return RMSN_OK;
+    }
     set_error("rmsnorm_set_option: unknown key %d", key);
     return RMSN_EINVAL;
 }
@@ -141,6 +167,10 @@ int get_option(int key, int* value) {
     if (key == RMSN_OPT_ROWS_PER_BLOCK) { *value = option_rows_per_block(); return RMSN_OK; }
     if (key == RMSN_OPT_STREAMING) { *value = option_streaming(); return RMSN_OK; }
     if (key == RMSN_OPT_SPLIT_LOADS) { *value = option_split_loads(); return RMSN_OK; }
+    if (key == RMSN_OPT_APPLY_THREADS) {
+        *value = kAssocLanes == 128 ? option_apply_threads() : 0;
+        return RMSN_OK;
+    }
     set_error("rmsnorm_get_option: unknown key %d", key);
     return RMSN_EINVAL;
 }
@@ -185,6 +215,22 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
     if (n < 1 || n > RMSN_MAX_N) {
         set_error("n must be in [1, %d], got %lld", RMSN_MAX_N, (long long)n);
         return RMSN_EINVAL;
+    }
+    if (kAssocLanes == 128) {
+        // The 128-lane build: one workgroup per row, 128 threads sum and the
+        // whole block (the apply width) applies; any n, any alignment.
+        const int b = option_apply_threads();
+        Plan p{};
+        p.dtype = dtype;
+        p.path = RMSN_PATH_BLOCK;
+        p.chunks = 0;
+        p.rows_per_block = 1;
+        p.streaming = 0;
+        p.block = b == 0 ? 1024 : b;
+        p.grid = rows;
+        p.loads = 0;
+        *out = p;
+        return RMSN_OK;
     }
     // the power of two (at most 16) that `align` guarantees
     const bool run_time = align == kAlignAtRunTime;

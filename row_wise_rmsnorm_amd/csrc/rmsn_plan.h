@@ -8,9 +8,20 @@
 
 #include "rmsnorm.h"
 
+// Lane chains of the association this build computes: 256 (R256), or 128 for
+// the build that reproduces the 128-thread sum of Lecture 04 section 2.1
+// (compiled with -DRMSN_LANES=128; its only layout is one workgroup per row
+// whose first 128 threads sum and whose every thread applies).
+#ifndef RMSN_LANES
+#define RMSN_LANES 256
+#endif
+
 namespace rmsn {
 
-constexpr int kLanes = 256;      // lane chains of the fixed association
+constexpr int kAssocLanes = RMSN_LANES;
+static_assert(kAssocLanes == 256 || kAssocLanes == 128, "RMSN_LANES must be 256 or 128");
+
+constexpr int kLanes = 256;      // lane chains of R256 (chunk width of its layouts)
 constexpr int kWave = 64;        // CDNA wavefront width
 constexpr int kBlockThreads = 256;
 constexpr int kMaxChunks = 32;   // largest row held in registers: 32 * 256 = 8192
@@ -82,6 +93,7 @@ int option_path();            // -1 automatic, else an RMSN_PATH_* value
 int option_rows_per_block();  // 0 automatic, else 4 or 8
 int option_streaming();       // -1 automatic, 0 off, 1 on
 int option_split_loads();     // 0 automatic, else 1, 2, 4 or 8
+int option_apply_threads();   // 128-lane build: 0 (= 1024) or 128, 256, 512, 1024
 int set_option(int key, int value);
 int get_option(int key, int* value);
 

@@ -43,6 +43,49 @@ def test_library_exports_every_declared_symbol(rn):
     assert set(declared_functions()) == set(rn.EXPORTED)
 
 
+def test_l128_build_exports_the_same_abi(rn):
+    lib = rn.bind(rn.LIB128_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.rmsnorm_association_lanes() == 128
+    assert rn.association_lanes() == 256
+
+
+def test_l128_build_plans_and_options(rn):
+    """The 128-lane build: one workgroup per row whatever the shape or the
+    path option, block = the apply width (default 1024); the apply-width
+    option exists only there."""
+    import ctypes
+    lib = rn.bind(rn.LIB128_PATH)
+    info = rn._PlanInfo()
+
+    def plan(dtype, rows, n, align=16):
+        assert lib.rmsnorm_plan_query(dtype, rows, n, align, ctypes.byref(info)) == rn.RMSN_OK
+        return (info.path, info.chunks, info.block, info.grid, info.loads)
+
+    assert plan(rn.BF16, 8192, 7168) == (rn.PATH_BLOCK, 0, 1024, 8192, 0)
+    assert plan(rn.F32, 1, 1 << 24, 0) == (rn.PATH_BLOCK, 0, 1024, 1, 0)
+    v = ctypes.c_int()
+    try:
+        assert lib.rmsnorm_set_option(rn.OPT_PATH, rn.PATH_SPLIT) == rn.RMSN_OK
+        assert plan(rn.BF16, 8192, 7168)[0] == rn.PATH_BLOCK
+        for b in (128, 256, 512, 1024):
+            assert lib.rmsnorm_set_option(rn.OPT_APPLY_THREADS, b) == rn.RMSN_OK
+            assert lib.rmsnorm_get_option(rn.OPT_APPLY_THREADS, ctypes.byref(v)) == rn.RMSN_OK
+            assert v.value == b and plan(rn.F32, 3, 7168)[2] == b
+        for bad in (64, 100, 2048, -1):
+            assert lib.rmsnorm_set_option(rn.OPT_APPLY_THREADS, bad) == rn.RMSN_EINVAL
+    finally:
+        lib.rmsnorm_set_option(rn.OPT_APPLY_THREADS, 0)
+        lib.rmsnorm_set_option(rn.OPT_PATH, rn.PATH_AUTO)
+    # the default build has no apply-width option
+    with pytest.raises(rn.RmsnormError):
+        rn.set_option(rn.OPT_APPLY_THREADS, 256)
+    assert rn.get_option(rn.OPT_APPLY_THREADS) == 0
+    # argument validation is the same code in both builds
+    assert lib.rmsnorm_batched_rows(0, 0, 64, B16, C16, 64, 2, 64, 1e-6, None) == rn.RMSN_EINVAL
+
+
 def test_desc_layout_is_32_bytes():
     text = open(HEADER).read()
     assert re.search(r"const void\* x;\s*const void\* w;\s*void\* y;\s*int64_t n;", text)
