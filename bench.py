@@ -9,8 +9,9 @@ cache defeated by rotating over 4 buffer sets (940 MB). Also reported:
 * single_norm: latency of one binary32 1 x 7168 norm (Lecture 04 section 2);
 * batch64: the bf16 64 x 7168 batch;
 * decode_step: the 327-norm decode step, eager launches vs one captured
-  graph replay (Lecture 08 section 1), A/A then ABBA x 3 with per-rep
-  numbers and standard errors (Lecture 04 section 6.1);
+  graph replay (Lecture 08 section 1) vs one persistent launch walking the
+  table, A/A controls then ABCCBA x 2 with per-rep numbers and standard
+  errors (Lecture 04 section 6.1);
 * decode_step_positioned: the same step walking a ring of rows through a
   device-resident position that the step itself advances (Lecture 08
   section 2), eager vs graph;
@@ -261,9 +262,11 @@ def bench_decode(rn, torch, np, wl, decode_steps):
         raise RuntimeError(f"graph capture failed: {g.capture_error}")
     eager = lambda i: rn.rmsnorm_sequence_eager(table, widths, eps, rn.F32)
     graph = lambda i: g.launch()
+    persistent = lambda i: rn.rmsnorm_sequence_persistent(table, len(widths), eps, rn.F32)
     for i in range(20):
         eager(i)
         graph(i)
+        persistent(i)
     torch.cuda.synchronize()
     # correctness of the timed arms: graph output == eager output == oracle
     import oracle
@@ -277,27 +280,37 @@ def bench_decode(rn, torch, np, wl, decode_steps):
     ok = all(np.array_equal(a, t.cpu().numpy().view(np.uint32)) for a, t in zip(gbits, ys))
     ok = ok and all(np.array_equal(a, oracle.row_f32(x, w, wl.EPS).view(np.uint32))
                     for a, (x, w) in zip(gbits, rows))
+    for t in ys:
+        t.fill_(float("nan"))
+    persistent(0)
+    torch.cuda.synchronize()
+    ok_p = all(np.array_equal(a, t.cpu().numpy().view(np.uint32)) for a, t in zip(gbits, ys))
 
     def rep(fn):
         return 1000.0 * elapsed_ms(fn, decode_steps) / decode_steps   # us per step
 
-    order = ["A", "A", "B", "B"] + ["A", "B", "B", "A"] * 3     # A/A, B/B, then ABBA x 3
-    arms = {"A": eager, "B": graph}
-    res = {"A": [], "B": [], "sequence": []}
+    # A/A, B/B and C/C controls, then ABCCBA x 2 (each arm 4 reps)
+    order = ["A", "A", "B", "B", "C", "C"] + ["A", "B", "C", "C", "B", "A"] * 2
+    arms = {"A": eager, "B": graph, "C": persistent}
+    res = {"A": [], "B": [], "C": [], "sequence": []}
     for k, a in enumerate(order):
         v = rep(arms[a])
         res["sequence"].append((a, round(v, 2)))
-        if k >= 4:
+        if k >= 6:
             res[a].append(v)
     aa = {"eager_pair_us": [round(v, 2) for a, v in res["sequence"][:2]],
-          "graph_pair_us": [round(v, 2) for a, v in res["sequence"][2:4]]}
-    e, gr = stats(res["A"]), stats(res["B"])
+          "graph_pair_us": [round(v, 2) for a, v in res["sequence"][2:4]],
+          "persistent_pair_us": [round(v, 2) for a, v in res["sequence"][4:6]]}
+    e, gr, pe = stats(res["A"]), stats(res["B"]), stats(res["C"])
     algo = sum(n * 12 for n in widths)
     nodes = g.node_count()
     g.destroy()
     return {
         "eager_us_per_step": e, "graph_us_per_step": gr,
         "speedup_graph_over_eager": e["mean"] / gr["mean"],
+        "persistent_us_per_step": pe,
+        "speedup_persistent_over_graph": gr["mean"] / pe["mean"],
+        "bit_exact_persistent_eq_graph": bool(ok_p),
         "graph_us_per_norm": gr["mean"] / len(widths),
         "eager_us_per_norm": e["mean"] / len(widths),
         "norms_per_s_graph": len(widths) / (gr["mean"] * 1e-6),
@@ -510,7 +523,8 @@ def main():
     log(f"batch64 {b64['us_device']['mean']:.2f} us (graph-captured)")
     dec = bench_decode(rn, torch, np, wl, args.decode_steps)
     log(f"decode eager {dec['eager_us_per_step']['mean']:.1f} us  "
-        f"graph {dec['graph_us_per_step']['mean']:.1f} us")
+        f"graph {dec['graph_us_per_step']['mean']:.1f} us  "
+        f"persistent {dec['persistent_us_per_step']['mean']:.1f} us")
     decp = bench_decode_positioned(rn, torch, np, wl, args.decode_steps)
     log(f"decode positioned eager {decp['eager_us_per_step']['mean']:.1f} us  "
         f"graph {decp['graph_us_per_step']['mean']:.1f} us")

@@ -181,6 +181,25 @@ int rmsnorm_sequence_graph_create_positioned(int dtype, const rmsn_desc* d_table
 int rmsnorm_sequence_graph_update(rmsn_graph* g, const int64_t* h_widths, int32_t count,
                                   int* recaptured);
 
+/* ---- the whole step in one launch ------------------------------------------- */
+
+/* The sequence's count norms, in table order, in ONE kernel launch of one
+ * workgroup that walks the descriptor table (Lecture 08 "Graph-resident
+ * decode", further reading: a persistent kernel as the endpoint of capturing
+ * many). Each row is finished -- its stores ordered before the next row's
+ * loads by a workgroup barrier -- before the next row starts, so a table in
+ * which a later x is an earlier y (y_i == x_j, i < j) computes exactly what
+ * the launch sequence computes; the bits equal rmsnorm_sequence_eager's.
+ * Widths come from the table (any n in [1, 2^24], any element alignment); no
+ * host widths are needed. pos: NULL, or the rows are taken at the position
+ * as in rmsnorm_sequence_eager_positioned and the position is advanced after
+ * the last row. Nothing is allocated or synchronised, so the call may itself
+ * be captured into a caller's graph. RMSN_EINVAL: bad dtype, d_table null or
+ * not 8-byte aligned, count outside [1, RMSN_MAX_SEQUENCE], bad eps or
+ * position. */
+int rmsnorm_sequence_persistent(int dtype, const rmsn_desc* d_table, int32_t count, float eps,
+                                const rmsn_position* pos, void* stream);
+
 /* Number of nodes in the captured graph (0 in eager-fallback mode). */
 int rmsnorm_graph_node_count(const rmsn_graph* g, int64_t* out);
 

@@ -80,6 +80,7 @@ def bind(path):
         "rmsnorm_sequence_graph_create_positioned": [c_int, vp, vp, i32, f,
                                                      ctypes.POINTER(_Position), ctypes.POINTER(vp)],
         "rmsnorm_sequence_graph_update": [vp, vp, i32, ctypes.POINTER(c_int)],
+        "rmsnorm_sequence_persistent": [c_int, vp, i32, f, ctypes.POINTER(_Position), vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -101,7 +102,7 @@ EXPORTED = ("rmsnorm_f32", "rmsnorm_bf16", "rmsnorm_batched_rows", "rmsnorm_sequ
             "rmsnorm_set_option", "rmsnorm_get_option", "rmsnorm_diag_inverse",
             "rmsnorm_diag_bf16", "rmsnorm_sequence_eager_positioned",
             "rmsnorm_sequence_graph_create_positioned", "rmsnorm_sequence_graph_update",
-            "rmsnorm_association_lanes")
+            "rmsnorm_association_lanes", "rmsnorm_sequence_persistent")
 
 
 def lib():
@@ -227,6 +228,13 @@ def rmsnorm_sequence_eager(table, widths, eps, dtype, stream=None, position=None
         _check(_lib.rmsnorm_sequence_eager_positioned(
             int(dtype), ctypes.c_void_p(table.data_ptr()), arr, len(widths), float(eps),
             ctypes.byref(pos), _stream_ptr(stream)))
+
+
+def rmsnorm_sequence_persistent(table, count, eps, dtype, stream=None, position=None):
+    """All `count` norms of the table, in order, in one kernel launch."""
+    pos = ctypes.byref(_position(position)) if position is not None else None
+    _check(_lib.rmsnorm_sequence_persistent(int(dtype), ctypes.c_void_p(table.data_ptr()),
+                                            int(count), float(eps), pos, _stream_ptr(stream)))
 
 
 class SequenceGraph:

@@ -352,6 +352,32 @@ int rmsnorm_sequence_eager_positioned(int dtype, const rmsn_desc* d_table,
     return enqueue_sequence(plans, d_table, eps, &pos, static_cast<hipStream_t>(stream));
 }
 
+int rmsnorm_sequence_persistent(int dtype, const rmsn_desc* d_table, int32_t count, float eps,
+                                const rmsn_position* position, void* stream) {
+    clear_error();
+    if (dtype != RMSN_F32 && dtype != RMSN_BF16) {
+        set_error("unknown dtype %d", dtype);
+        return RMSN_EINVAL;
+    }
+    if (!d_table || (uintptr_t)d_table % alignof(rmsn_desc)) {
+        set_error("d_table must be a non-null, %d-byte aligned device pointer",
+                  (int)alignof(rmsn_desc));
+        return RMSN_EINVAL;
+    }
+    if (count < 1 || count > RMSN_MAX_SEQUENCE) {
+        set_error("count must be in [1, %d], got %d", RMSN_MAX_SEQUENCE, (int)count);
+        return RMSN_EINVAL;
+    }
+    int st = check_eps(eps);
+    if (st != RMSN_OK) return st;
+    PosArgs pos;
+    if (position && (st = check_position(dtype, position, &pos)) != RMSN_OK) return st;
+    const hipError_t e = launch_sequence_persistent(dtype, d_table, count, eps,
+                                                    position ? &pos : nullptr,
+                                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? RMSN_OK : hip_fail("persistent sequence launch", e);
+}
+
 int rmsnorm_sequence_graph_create(int dtype, const rmsn_desc* d_table, const int64_t* h_widths,
                                   int32_t count, float eps, rmsn_graph** out) {
     return create_graph(dtype, d_table, h_widths, count, eps, nullptr, out);

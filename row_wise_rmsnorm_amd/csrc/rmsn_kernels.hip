@@ -382,6 +382,9 @@ struct SplitPart {
 
 // ---------------------------------------------------------------------------
 // GROUP layout: 256 threads per row; wavefront g owns association group g.
+// Instances: Q = 1..8 blocks of 1024 elements (rows up to 8192).
+#define RMSN_FOR_GROUP_BLOCKS(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
+
 // One load per lane covers the group's 64 elements in four consecutive
 // 256-element chunks: lane 16q + t reads elements 256(4m+q) + 64g + 4t + {0..3}
 // of block m (1024 elements). A 4x4 transpose between the lane's 16-lane row
@@ -684,6 +687,71 @@ __global__ __launch_bounds__(256) void k_desc_group(const rmsn_desc* __restrict_
 }
 
 
+// The whole decode step in one launch (Lecture 08 "Graph-resident decode",
+// further reading: a persistent kernel instead of many captured ones). One
+// workgroup walks the descriptor table in order. Each row takes the GROUP
+// path when its width and pointers allow it (quad-aligned, a multiple of 4,
+// at most 8192), else BLOCK's streaming loop; the workgroup barrier that ends
+// each row orders its stores before the next row's loads, so a table whose
+// later x is an earlier y computes exactly what the launch sequence does.
+// Descriptors are read one row ahead (they do not depend on row data); the
+// rows themselves are not prefetched. With POS the rows are taken at the
+// device-resident position, read once, and the last thread stores the next
+// position after the last row (the same update as the sequence's last node).
+template <typename T>
+__device__ __forceinline__ void persistent_row(const rmsn_desc& dd, uint64_t pos, bool posd,
+                                               const PosArgs& pa, float eps, float* lds4) {
+    const int64_t n = dd.n;
+    if (n < 1 || n > RMSN_MAX_N) return;
+    const char* xb = static_cast<const char*>(dd.x);
+    char* yb = static_cast<char*>(dd.y);
+    if (posd) {
+        const uint64_t period = (uint64_t)pa.period;
+        const int64_t p = (int64_t)(pos < period ? pos : pos % period);
+        xb += p * pa.x_pitch;
+        yb += p * pa.y_pitch;
+    }
+    const T* x = reinterpret_cast<const T*>(xb);
+    const T* w = static_cast<const T*>(dd.w);
+    T* y = reinterpret_cast<T*>(yb);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) |
+                        reinterpret_cast<uintptr_t>(y);
+    if ((n & 3) == 0 && n <= 8192 && a % (4 * sizeof(T)) == 0) {
+        switch ((int)((n + 1023) >> 10)) {
+#define RMSN_CASE(Q) \
+    case Q: row_group<T, Q>(x, w, y, (int)n, eps, lds4); break;
+            RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)
+#undef RMSN_CASE
+            default: break;
+        }
+    } else {
+        row_block<T, 0>(x, w, y, (int)n, eps, lds4);
+    }
+}
+
+template <typename T, bool POS>
+__global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __restrict__ d,
+                                                             int32_t count, float eps,
+                                                             PosArgs pa) {
+    __shared__ float lds4[4];
+    uint64_t pos;
+    rmsn_desc next = desc_load<POS>(d, pa, &pos);
+    for (int32_t i = 0; i < count; ++i) {
+        const rmsn_desc cur = next;
+        if (i + 1 < count) {
+            uint64_t unused;
+            next = desc_load<false>(d + i + 1, pa, &unused);
+        }
+        persistent_row<T>(cur, pos, POS, pa, eps, lds4);
+        __syncthreads();  // this row's stores before the next row's loads; lds4 reused
+    }
+    if (POS && threadIdx.x == 0) {
+        const uint64_t per = (uint64_t)pa.period;
+        const uint64_t p = pos < per ? pos : pos % per;
+        const_cast<int64_t*>(pa.d_pos)[0] = (int64_t)(p + 1 == per ? 0 : p + 1);
+    }
+}
+
 template <typename T, int NCH>
 __global__ __launch_bounds__(256) void k_rows_block(const T* x, int64_t xs,
                                                     const T* __restrict__ w, T* y, int64_t ys,
@@ -783,8 +851,6 @@ hipError_t launch_split_t(const Plan& p, const void* x, int64_t xs, const void* 
 #undef RMSN_LAUNCH
     return hipGetLastError();
 }
-
-#define RMSN_FOR_GROUP_BLOCKS(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
 
 template <typename T>
 hipError_t launch_group_t(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
@@ -888,6 +954,28 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
     }
     return p.dtype == RMSN_F32 ? launch_block_t<float>(p, x, xs, w, y, ys, n, eps, stream)
                                : launch_block_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
+}
+
+hipError_t launch_sequence_persistent(int dtype, const rmsn_desc* d, int32_t count, float eps,
+                                     const PosArgs* pos, hipStream_t stream) {
+    const PosArgs none{nullptr, 0, 0, 1};
+    const dim3 grid(1), block(kBlockThreads);
+    if (dtype == RMSN_F32) {
+        if (pos)
+            hipLaunchKernelGGL((k_sequence_persistent<float, true>), grid, block, 0, stream, d,
+                               count, eps, *pos);
+        else
+            hipLaunchKernelGGL((k_sequence_persistent<float, false>), grid, block, 0, stream, d,
+                               count, eps, none);
+    } else {
+        if (pos)
+            hipLaunchKernelGGL((k_sequence_persistent<uint16_t, true>), grid, block, 0, stream, d,
+                               count, eps, *pos);
+        else
+            hipLaunchKernelGGL((k_sequence_persistent<uint16_t, false>), grid, block, 0, stream,
+                               d, count, eps, none);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,

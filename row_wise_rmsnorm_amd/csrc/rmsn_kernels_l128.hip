@@ -93,6 +93,36 @@ __global__ __launch_bounds__(1024) void k_desc_narrow(const rmsn_desc* __restric
     row_narrow<T>(x, static_cast<const T*>(dd.w), y, (int)n, eps, lds4);
 }
 
+// The whole sequence in one launch of one workgroup, rows in table order
+// (the same contract as the default build's persistent kernel).
+template <typename T, bool POS>
+__global__ __launch_bounds__(1024) void k_sequence_narrow(const rmsn_desc* __restrict__ d,
+                                                         int32_t count, float eps, PosArgs pa) {
+    __shared__ float lds4[4];
+    uint64_t pos;
+    rmsn_desc next = desc_load<POS>(d, pa, &pos);
+    for (int32_t i = 0; i < count; ++i) {
+        const rmsn_desc cur = next;
+        if (i + 1 < count) {
+            uint64_t unused;
+            next = desc_load<false>(d + i + 1, pa, &unused);
+        }
+        const int64_t n = cur.n;
+        if (n >= 1 && n <= RMSN_MAX_N) {
+            const T* x;
+            T* y;
+            desc_row<T, POS>(cur, pos, pa, x, y);
+            row_narrow<T>(x, static_cast<const T*>(cur.w), y, (int)n, eps, lds4);
+        }
+        __syncthreads();
+    }
+    if (POS && threadIdx.x == 0) {
+        const uint64_t per = (uint64_t)pa.period;
+        const uint64_t p = pos < per ? pos : pos % per;
+        const_cast<int64_t*>(pa.d_pos)[0] = (int64_t)(p + 1 == per ? 0 : p + 1);
+    }
+}
+
 bool narrow_block(const Plan& p) {
     return p.path == RMSN_PATH_BLOCK &&
            (p.block == 128 || p.block == 256 || p.block == 512 || p.block == 1024);
@@ -127,6 +157,21 @@ hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosAr
     } else {
         if (pos) hipLaunchKernelGGL((k_desc_narrow<uint16_t, true>), dim3(1), block, 0, stream, d, eps, *pos);
         else hipLaunchKernelGGL((k_desc_narrow<uint16_t, false>), dim3(1), block, 0, stream, d, eps, none);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_sequence_persistent(int dtype, const rmsn_desc* d, int32_t count, float eps,
+                                     const PosArgs* pos, hipStream_t stream) {
+    const int b = option_apply_threads();
+    const dim3 grid(1), block((unsigned)(b == 0 ? 1024 : b));
+    const PosArgs none{nullptr, 0, 0, 1};
+    if (dtype == RMSN_F32) {
+        if (pos) hipLaunchKernelGGL((k_sequence_narrow<float, true>), grid, block, 0, stream, d, count, eps, *pos);
+        else hipLaunchKernelGGL((k_sequence_narrow<float, false>), grid, block, 0, stream, d, count, eps, none);
+    } else {
+        if (pos) hipLaunchKernelGGL((k_sequence_narrow<uint16_t, true>), grid, block, 0, stream, d, count, eps, *pos);
+        else hipLaunchKernelGGL((k_sequence_narrow<uint16_t, false>), grid, block, 0, stream, d, count, eps, none);
     }
     return hipGetLastError();
 }

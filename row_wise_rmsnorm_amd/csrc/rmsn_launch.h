@@ -30,6 +30,12 @@ struct PosArgs {
 hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
                        hipStream_t stream);
 
+// All `count` rows of a descriptor table, in order, in one launch of one
+// workgroup; pos: NULL, or the rows are taken at the device-resident position
+// and the position is advanced after the last row.
+hipError_t launch_sequence_persistent(int dtype, const rmsn_desc* d, int32_t count, float eps,
+                                     const PosArgs* pos, hipStream_t stream);
+
 // *d_pos = (*d_pos mod period + 1) mod period on the device (the state
 // update of a positioned sequence).
 hipError_t launch_advance(int64_t* d_pos, int64_t period, hipStream_t stream);

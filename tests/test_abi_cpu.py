@@ -188,6 +188,22 @@ def test_positioned_sequence_validation(rn):
     assert rec.value == 0
 
 
+def test_persistent_sequence_validation(rn):
+    import ctypes
+    L = rn.lib()
+    P = rn._Position
+    f = L.rmsnorm_sequence_persistent
+    assert f(2, A16, 3, 1e-6, None, None) == rn.RMSN_EINVAL
+    assert f(0, 0, 3, 1e-6, None, None) == rn.RMSN_EINVAL
+    assert f(0, A16 + 4, 3, 1e-6, None, None) == rn.RMSN_EINVAL
+    assert f(0, A16, 0, 1e-6, None, None) == rn.RMSN_EINVAL
+    assert f(0, A16, 70000, 1e-6, None, None) == rn.RMSN_EINVAL
+    assert f(0, A16, 3, float("nan"), None, None) == rn.RMSN_EINVAL
+    bad = P(ctypes.c_void_p(C16), 4096, 4096, 0)
+    assert f(0, A16, 3, 1e-6, ctypes.byref(bad), None) == rn.RMSN_EINVAL
+    assert rn.last_error() != ""
+
+
 def test_diag_validation(rn):
     L = rn.lib()
     assert L.rmsnorm_diag_bf16(0xFFFFFFFF, 2, A16, None) == rn.RMSN_EINVAL

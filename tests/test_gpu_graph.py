@@ -525,3 +525,99 @@ def test_update_recaptures_only_when_the_plan_moves(rn, step):
     sync()
     compare(step.outputs(), step.expected(0), "original plans again")
     g.destroy()
+
+
+# ---- the whole step in one launch -------------------------------------------------
+
+def test_persistent_step_matches_oracle_and_eager(rn, step):
+    """One launch walks the 327 descriptors in order: the bits of the eager
+    sequence and of the oracle, on two tables."""
+    say("persistent decode step")
+    for s in (0, 2):
+        step.point_at(s)
+        step.clear_outputs()
+        rn.rmsnorm_sequence_persistent(step.table, len(step.widths), wl.EPS, rn.F32)
+        sync()
+        got = step.outputs()
+        compare(got, step.expected(s), f"persistent set {s}")
+        step.clear_outputs()
+        rn.rmsnorm_sequence_eager(step.table, step.widths, wl.EPS, rn.F32)
+        sync()
+        compare(got, step.outputs(), f"persistent vs eager set {s}")
+    step.point_at(0)
+
+
+@pytest.mark.parametrize("kind,n,offset", [("f32", 7168, 0), ("f32", 1000, 1), ("bf16", 1536, 0),
+                                           ("bf16", 9000, 3), ("f32", 8193, 0)])
+def test_persistent_dependent_chain(rn, kind, n, offset):
+    """Rows that depend on earlier outputs: norm i reads buffer i and writes
+    buffer i+1 (and the last norm works in place), so each row must see the
+    previous row's stores -- the order the launch sequence gives."""
+    import torch
+    from gpu_util import assert_bits_bf16, bf16_host, to_dev_bf16
+    say(f"persistent dependent chain {kind} n={n} offset {offset}")
+    k = 6
+    x0, _ = wl.misc_f32(500 + n, n, sigma=3.0)
+    ws = [wl.misc_f32(600 + n + i, n)[1] for i in range(k)]
+    if kind == "bf16":
+        x0 = wl.to_bf16_bits(x0)
+        ws = [wl.to_bf16_bits(w) for w in ws]
+        tdt, todev, host, check = torch.bfloat16, to_dev_bf16, bf16_host, assert_bits_bf16
+        row = oracle.row_bf16
+    else:
+        tdt, todev, host, check = torch.float32, to_dev_f32, f32_host, assert_bits_f32
+        row = oracle.row_f32
+    bufs = [torch.zeros(n + 4, dtype=tdt, device=dev()) for _ in range(k + 1)]
+    bufs[0][offset:offset + n].copy_(todev(x0))
+    wd = [todev(w) for w in ws]
+    rows = [(bufs[i][offset:offset + n], wd[i], bufs[i + 1][offset:offset + n]) for i in range(k - 1)]
+    rows.append((bufs[k - 1][offset:offset + n], wd[k - 1], bufs[k - 1][offset:offset + n]))
+    table, widths = rn.make_table(rows)
+    dtype = rn.F32 if kind == "f32" else rn.BF16
+    want = []
+    cur = x0
+    for i in range(k):
+        cur = row(cur, ws[i], wl.EPS)
+        want.append(cur)
+    rn.rmsnorm_sequence_persistent(table, k, wl.EPS, dtype)
+    sync()
+    for i in range(k - 2):     # bufs[k - 1] holds step k - 2 only until the in-place step
+        check(host(bufs[i + 1][offset:offset + n]), want[i], f"chain step {i}")
+    check(host(bufs[k - 1][offset:offset + n]), want[k - 1], "in place last step")
+
+
+def test_persistent_positioned_ring(rn):
+    say("persistent positioned ring")
+    n = 7168
+    ring = Ring(rn, [n] * 9, period=4)
+    ring.d_pos.fill_(3)
+    for rep in range(5):
+        rn.rmsnorm_sequence_persistent(ring.table, 9, wl.EPS, rn.F32, position=ring.position(n))
+        sync()
+        assert int(ring.d_pos.item()) == (4 + rep) % 4
+    _check_ring(ring, {0, 1, 2, 3})
+
+
+def test_persistent_call_captured_in_a_graph(rn, step):
+    """The single launch captured by the caller: replays follow table
+    rewrites (three replays, the oracle each time)."""
+    import torch
+    say("persistent call captured")
+    step.point_at(0)
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s_cap):
+        rn.rmsnorm_sequence_persistent(step.table, len(step.widths), wl.EPS, rn.F32)
+        torch.cuda.current_stream().synchronize()
+        with torch.cuda.graph(graph, stream=s_cap):
+            rn.rmsnorm_sequence_persistent(step.table, len(step.widths), wl.EPS, rn.F32)
+    torch.cuda.current_stream().wait_stream(s_cap)
+    sync()
+    for rep, s in enumerate([1, 2, 0]):
+        step.point_at(s)
+        step.clear_outputs()
+        graph.replay()
+        sync()
+        compare(step.outputs(), step.expected(s), f"captured persistent replay {rep}")
+    step.point_at(0)

@@ -163,6 +163,13 @@ def test_l128_sequence_eager_and_graph(rn, l128):
         torch.cuda.synchronize()
         check(f"graph replay {rep}")
     assert l128.rmsnorm_sequence_graph_destroy(h) == rn.RMSN_OK
+    for y in ys:
+        y.fill_(float("nan"))
+    assert l128.rmsnorm_sequence_persistent(rn.F32, ctypes.c_void_p(table.data_ptr()),
+                                            len(widths), float(wl.EPS), None,
+                                            stream()) == rn.RMSN_OK
+    torch.cuda.synchronize()
+    check("persistent")
 
 
 def _dump(path, arrays):
