@@ -92,10 +92,15 @@ int rmsnorm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, f
 
 /* `rows` rows of width n sharing one weight row. Row r of x starts at
  * x + r * x_row_stride elements, row r of y at y + r * y_row_stride.
- * dtype is an rmsn_dtype. Many 16-byte aligned rows run one row per
- * workgroup of several wavefronts with 16-byte loads (RMSN_PATH_SPLIT); few
- * rows run one row per 256-thread workgroup (Lecture 04 section 1: match the
- * grid to the compute units; see rmsnorm_plan_query). */
+ * dtype is an rmsn_dtype. The layout is chosen per launch from measurements
+ * on MI355X (Lecture 04 section 1: match the grid to the machine; see
+ * rmsnorm_plan_query and the RMSN_PATH_* list): fewer than 1024 rows run one
+ * 256-thread workgroup per row (GROUP); many rows of at least 4 KB whose x + y
+ * stay under 64 MiB too, and a workgroup of several wavefronts per row with
+ * 16-byte loads (SPLIT) from 64 MiB; rows under 1 KB run one wavefront per
+ * row (WAVE); rows of 1-4 KB run WAVE under 32 MiB and SPLIT from there.
+ * Rows that are not vector-aligned run BLOCK / STREAM. All give the same
+ * bits. */
 int rmsnorm_batched_rows(int dtype, const void* x, int64_t x_row_stride, const void* w, void* y,
                          int64_t y_row_stride, int64_t rows, int64_t n, float eps, void* stream);
 

@@ -189,18 +189,24 @@ int auto_rows_per_block(int64_t rows) {
     return rows >= 8 * 256 ? 8 : 4;
 }
 
+// x + y bytes of a launch reach `bytes` (no overflow for any valid rows, n).
+static bool footprint_at_least(int dtype, int64_t rows, int64_t n, int64_t bytes) {
+    const int64_t per_row = n * 2 * elem_bytes(dtype);  // n <= 2^24: no overflow
+    return rows >= (bytes + per_row - 1) / per_row;
+}
+
 bool auto_streaming(int dtype, int64_t rows, int64_t n) {
-    return rows * n * 2 * elem_bytes(dtype) >= kStreamBytes;
+    return footprint_at_least(dtype, rows, n, kStreamBytes);
 }
 
 int auto_split_loads(int64_t slices) {
-    // fewest slices per wavefront that keep the row within kSplitTargetWaves
-    // wavefronts (fewer chain hand-offs), else within kMaxSplitWaves
-    for (int i = 0; i < kNumSplitLoads; ++i)
-        if ((slices + kSplitLoads[i] - 1) / kSplitLoads[i] <= kSplitTargetWaves) return kSplitLoads[i];
-    for (int i = 0; i < kNumSplitLoads; ++i)
-        if ((slices + kSplitLoads[i] - 1) / kSplitLoads[i] <= kMaxSplitWaves) return kSplitLoads[i];
-    return 0;
+    // Measured on MI355X (rows of 256..8192 elements, 240 MB launches): one
+    // slice per wavefront for a one-slice row, two for rows of 2..15 slices,
+    // four from 16 slices on (fewer chain hand-offs once a row would need
+    // more than 8 wavefronts); eight only where four would exceed 16.
+    int u = slices <= 1 ? 1 : slices < 16 ? 2 : 4;
+    while ((slices + u - 1) / u > kMaxSplitWaves && u < 8) u *= 2;
+    return (slices + u - 1) / u <= kMaxSplitWaves ? u : 0;
 }
 
 int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
@@ -254,11 +260,25 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
         default: path = -1; break;
     }
     if (path < 0) {
-        // Descriptor rows keep BLOCK: the GROUP descriptor kernel, which also
-        // carries the streaming fallback, measured slower in the decode step.
-        if (can_split && rows >= kWaveMinRows) path = RMSN_PATH_SPLIT;
-        else if (can_wave && rows >= kWaveMinRows) path = RMSN_PATH_WAVE;
-        else if (can_group && !run_time) path = RMSN_PATH_GROUP;
+        // Measured on MI355X (graph-captured launches, widths 256..8192, 16 to
+        // 252 MB, 64 to 245,760 rows): few rows are latency-bound and take
+        // GROUP; many rows of at least 4 KB take GROUP while x + y stay under
+        // 64 MiB and SPLIT beyond; rows under 1 KB take WAVE; rows of 1-4 KB
+        // take WAVE under 32 MiB and SPLIT from there. Descriptor rows keep
+        // BLOCK: the GROUP descriptor kernel, which also carries the
+        // streaming fallback, measured slower in the decode step.
+        const bool many = rows >= kWaveMinRows;
+        const bool big = footprint_at_least(dtype, rows, n, kStreamBytes);
+        const bool mid = footprint_at_least(dtype, rows, n, kStreamBytes / 2);
+        const int64_t row_bytes = n * es;
+        if (run_time) path = can_block ? RMSN_PATH_BLOCK : RMSN_PATH_STREAM;
+        else if (!many && can_group) path = RMSN_PATH_GROUP;
+        else if (many && !big && row_bytes >= 4096 && can_group) path = RMSN_PATH_GROUP;
+        else if (many && row_bytes < 1024 && can_wave) path = RMSN_PATH_WAVE;
+        else if (many && row_bytes < 4096 && !mid && can_wave) path = RMSN_PATH_WAVE;
+        else if (many && can_split) path = RMSN_PATH_SPLIT;
+        else if (many && can_wave) path = RMSN_PATH_WAVE;
+        else if (can_group) path = RMSN_PATH_GROUP;
         else if (can_block) path = RMSN_PATH_BLOCK;
         else if (can_split) path = RMSN_PATH_SPLIT;
         else path = RMSN_PATH_STREAM;

@@ -43,9 +43,6 @@ constexpr int kSliceBytes = 1024;
 constexpr int kMaxSplitWaves = 16;
 constexpr int kSplitLoads[] = {1, 2, 4, 8};
 constexpr int kNumSplitLoads = sizeof(kSplitLoads) / sizeof(kSplitLoads[0]);
-// The automatic choice keeps a row to at most this many wavefronts: each one
-// more is one more hand-off of the lane chains through LDS.
-constexpr int kSplitTargetWaves = 8;
 
 struct Plan {
     int dtype;           // RMSN_F32 / RMSN_BF16
@@ -75,7 +72,8 @@ int chunk_bucket(int64_t n);
 int auto_rows_per_block(int64_t rows);
 bool auto_streaming(int dtype, int64_t rows, int64_t n);
 // Slices per wavefront on the SPLIT path for a row of `slices` slices (0 if
-// the row is too long for kMaxSplitWaves wavefronts).
+// the row is too long for kMaxSplitWaves wavefronts): 1, 2 or 4 by row
+// length, as measured; 8 only where 4 would need more than 16 wavefronts.
 int auto_split_loads(int64_t slices);
 
 // Plan a launch of `rows` rows of width n. `align`: a byte alignment shared by

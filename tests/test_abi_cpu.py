@@ -227,15 +227,27 @@ def test_plan_paths_and_buckets(rn):
     # binary32: 28 slices, four per wavefront
     p = rn.plan_query(rn.F32, 8192, 7168)
     assert (p["path"], p["loads"], p["block"], p["chunks"]) == (rn.PATH_SPLIT, 4, 448, 4)
-    # a 29 MB launch keeps the default cache policy
-    assert rn.plan_query(rn.BF16, 1024, 7168)["streaming"] == 0
+    # many wide rows in a launch under 64 MiB (29 MB here): GROUP, default caching
+    p = rn.plan_query(rn.BF16, 1024, 7168)
+    assert p["path"] == rn.PATH_GROUP and p["streaming"] == 0
+    assert rn.plan_query(rn.BF16, 2048, 7168)["path"] == rn.PATH_GROUP      # 58.7 MB
+    assert rn.plan_query(rn.BF16, 3072, 7168)["path"] == rn.PATH_SPLIT      # 88 MB
+    # rows under 1 KB at any size, and rows of 1-4 KB under 32 MiB: WAVE
+    assert rn.plan_query(rn.BF16, 245760, 256)["path"] == rn.PATH_WAVE      # 252 MB, 512 B rows
+    assert rn.plan_query(rn.BF16, 2730, 1536)["path"] == rn.PATH_WAVE       # 16.8 MB, 3 KB rows
+    assert rn.plan_query(rn.BF16, 8533, 1536)["path"] == rn.PATH_SPLIT      # 52 MB
+    assert rn.plan_query(rn.F32, 25600, 256)["path"] == rn.PATH_SPLIT       # 52 MB, 1 KB rows
+    p = rn.plan_query(rn.BF16, 122880, 512)                                 # 252 MB, 1 KB rows
+    assert (p["path"], p["loads"], p["block"]) == (rn.PATH_SPLIT, 1, 64)
+    p = rn.plan_query(rn.BF16, 40960, 1536)                                 # 3 slices: two per wavefront
+    assert (p["path"], p["loads"], p["block"]) == (rn.PATH_SPLIT, 2, 128)
     # rows aligned to 8 bytes only: one wavefront per row, eight rows per
     # workgroup sharing one LDS copy of w
     p = rn.plan_query(rn.BF16, 8192, 7168, align=8)
     assert p == {"path": rn.PATH_WAVE, "chunks": 28, "rows_per_block": 8, "streaming": 1,
                  "block": 512, "grid": 1024, "loads": 0}
     # fewer than 2048 rows: 4 per workgroup
-    p = rn.plan_query(rn.BF16, 1024, 7168, align=8)
+    p = rn.plan_query(rn.BF16, 1024, 1536, align=8)   # 3 KB rows, 6 MB
     assert p["path"] == rn.PATH_WAVE and p["rows_per_block"] == 4 and p["grid"] == 256
     # a width that is not a whole number of 16-byte vectors: WAVE
     assert rn.plan_query(rn.BF16, 4096, 7164)["path"] == rn.PATH_WAVE
@@ -268,8 +280,8 @@ def test_plan_paths_and_buckets(rn):
     # beyond 8192 elements: SPLIT up to 128 KB rows of whole vectors, else streamed
     p = rn.plan_query(rn.F32, 3, 8193)
     assert p["path"] == rn.PATH_STREAM and p["chunks"] == 0 and p["grid"] == 3
-    p = rn.plan_query(rn.F32, 3, 8196)
-    assert p["path"] == rn.PATH_SPLIT and p["loads"] == 8 and p["block"] == 320
+    p = rn.plan_query(rn.F32, 3, 8196)                                      # 33 slices
+    assert p["path"] == rn.PATH_SPLIT and p["loads"] == 4 and p["block"] == 576
     p = rn.plan_query(rn.BF16, 2, 65536)
     assert p["path"] == rn.PATH_SPLIT and p["loads"] == 8 and p["block"] == 1024
     assert rn.plan_query(rn.BF16, 2, 65544)["path"] == rn.PATH_STREAM
@@ -281,17 +293,19 @@ def test_plan_paths_and_buckets(rn):
                                   (7168, 4), (8196, 4), (12000, 4), (20000, 2), (32768, 4),
                                   (65536, 2)])
 def test_split_geometry(rn, n, es):
-    """Every SPLIT plan: the fewest slices per wavefront keeping a row within 8
-    wavefronts (else 16), and a forced slice count honoured when it fits."""
+    """Every SPLIT plan: one slice per wavefront for a one-slice row, two below
+    16 slices, four from 16 (eight where four would need more than 16
+    wavefronts), and a forced slice count honoured when it fits."""
     dtype = rn.F32 if es == 4 else rn.BF16
     slices = -(-n * es // 1024)
     try:
         rn.set_option(rn.OPT_PATH, rn.PATH_SPLIT)
         p = rn.plan_query(dtype, 5, n)
         assert p["path"] == rn.PATH_SPLIT
-        fits8 = [u for u in (1, 2, 4, 8) if -(-slices // u) <= 8]
-        fits16 = [u for u in (1, 2, 4, 8) if -(-slices // u) <= 16]
-        assert p["loads"] == (fits8[0] if fits8 else fits16[0])
+        u = 1 if slices <= 1 else 2 if slices < 16 else 4
+        while -(-slices // u) > 16:
+            u *= 2
+        assert p["loads"] == u
         assert p["block"] == 64 * -(-slices // p["loads"])
         assert p["chunks"] == p["loads"] * 1024 // (256 * es)
         for u in (1, 2, 4, 8):
