@@ -17,16 +17,19 @@
  *   8. y = (x * inv) * w, left to right; bf16 outputs are rounded once to
  *      nearest even from the binary32 value.
  * Every entry point and every internal code path (register-resident rows,
- * streaming rows, any rows-per-workgroup, eager or graph replay, any pointer
- * alignment) gives the same bits. Denormals are preserved, NaN/Inf propagate
- * per IEEE (bf16 NaN outputs are quiet NaNs; payloads are not specified).
+ * streaming rows, any rows-per-workgroup, eager, graph or persistent replay,
+ * any pointer alignment) gives the same bits. Denormals are preserved, NaN/Inf
+ * propagate per IEEE (bf16 NaN outputs are quiet NaNs; payloads are not
+ * specified). A second build of this same ABI computes the lecture's own
+ * 128-thread sum instead of R256 (see rmsnorm_association_lanes).
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers owned by the caller. The library
  *    never allocates, frees or synchronises inside rmsnorm_f32, rmsnorm_bf16,
- *    rmsnorm_batched_rows, rmsnorm_sequence_eager or
- *    rmsnorm_sequence_graph_launch, so each of them may itself be captured
- *    into a caller's HIP graph.
+ *    rmsnorm_batched_rows, rmsnorm_sequence_eager(_positioned),
+ *    rmsnorm_sequence_persistent or rmsnorm_sequence_graph_launch, so each of
+ *    them may itself be captured into a caller's HIP graph. Only the graph
+ *    creation and update calls create HIP objects.
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *    asynchronously; the return value reports argument and launch errors
  *    only. A fault inside a kernel surfaces at the caller's next

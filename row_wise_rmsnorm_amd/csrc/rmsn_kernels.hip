@@ -10,7 +10,9 @@
 //   group trees  four 64-lane groups, descending halving 32,16,8,4,2,1
 //   combine      ss = (G0 + G2) + (G1 + G3)
 // Every kernel below evaluates exactly these operations in this order; the
-// three row layouts only decide which hardware lane holds which chain.
+// row layouts only decide which hardware lane holds which chain. Steps 4-7,
+// element and quad access and the bf16 narrowing are shared with the other
+// builds (rmsn_common.h).
 //
 // Layouts (all rows are independent; one row never spans workgroups):
 //   WAVE   one wavefront per row. Lane t holds elements 256k + 4t + {0..3}
@@ -39,6 +41,9 @@
 //          left them (1 KB of LDS, one barrier per hand-off), and the last
 //          wavefront runs the group trees. Every wavefront issues all of its
 //          loads at once, so the whole row is in flight from the start.
+// Descriptor kernels run one row read from a device table (BLOCK or GROUP
+// layout, optionally at a device-resident position); the persistent kernel
+// walks a whole table in one workgroup, row after row.
 //
 // Floating point: contraction is off for this file; the one fused operation
 // of the association is written as fmaf. '/' and sqrtf are the correctly
