@@ -29,7 +29,9 @@
  *    rmsnorm_batched_rows, rmsnorm_sequence_eager(_positioned),
  *    rmsnorm_sequence_persistent or rmsnorm_sequence_graph_launch, so each of
  *    them may itself be captured into a caller's HIP graph. Only the graph
- *    creation and update calls create HIP objects.
+ *    creation and update calls create HIP objects; they also allocate a
+ *    256-byte device row for the pre-warm launches and synchronise their own
+ *    private stream, and free the row before they return.
  *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
  *    asynchronously; the return value reports argument and launch errors
  *    only. A fault inside a kernel surfaces at the caller's next
