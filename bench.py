@@ -441,7 +441,8 @@ def cpu_baseline(np, wl, host):
 
 
 def profile_kernels(rn, torch, np, wl):
-    """Short run for counter collection: 5 prefill launches and 5 copies of
+    """Short run for counter collection: 5 prefill launches, 5 launches each
+    of the 64-row bf16 batch and of the single binary32 row, and 5 copies of
     a 1 GiB buffer (a plain copy of known size to scale the counters)."""
     rows, n = wl.PREFILL_SHAPE
     dev = torch.device("cuda", 0)
@@ -452,12 +453,20 @@ def profile_kernels(rn, torch, np, wl):
     y = torch.empty_like(x)
     for _ in range(5):
         rn.rmsnorm_batched_rows(x, w, float(wl.EPS), out=y)
+    xb, yb = x[:64].contiguous(), torch.empty(64, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(5):
+        rn.rmsnorm_batched_rows(xb, w, float(wl.EPS), out=yb)
+    x1 = torch.randn(n, device=dev, generator=g)
+    w1 = 1.0 + 0.1 * torch.randn(n, device=dev, generator=g)
+    y1 = torch.empty_like(x1)
+    for _ in range(5):
+        rn.rmsnorm_f32(x1, w1, float(wl.EPS), out=y1)
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_kernels": "done", "rmsnorm_launches": 5,
+    print(json.dumps({"profile_kernels": "done", "rmsnorm_launches": 15,
                       "copy_bytes_each": src.numel() * 4, "copies": 5}), flush=True)
 
 
