@@ -694,34 +694,42 @@ __global__ __launch_bounds__(256) void k_desc_group(const rmsn_desc* __restrict_
 
 // The whole decode step in one launch (Lecture 08 "Graph-resident decode",
 // further reading: a persistent kernel instead of many captured ones). One
-// workgroup walks the descriptor table in order. Each row takes the GROUP
-// path when its width and pointers allow it (quad-aligned, a multiple of 4,
-// at most 8192), else BLOCK's streaming loop; the workgroup barrier that ends
-// each row orders its stores before the next row's loads, so a table whose
-// later x is an earlier y computes exactly what the launch sequence does.
-// Descriptors are read one row ahead (they do not depend on row data); the
-// rows themselves are not prefetched. With POS the rows are taken at the
-// device-resident position, read once, and the last thread stores the next
-// position after the last row (the same update as the sequence's last node).
+// workgroup walks the descriptor table in order, in one of two ways chosen
+// when the launch starts:
+//  - pipelined, when every row can take the GROUP mapping (width a multiple of
+//    4 and at most 8192, pointers quad-aligned) and no row reads memory that
+//    one of the three rows before it writes, nor writes memory the row just
+//    before it writes: the next row's loads are issued before the current row
+//    is reduced, so one row's memory round trip overlaps the previous row's
+//    work;
+//  - otherwise row after row, with a workgroup barrier after each row that
+//    orders its stores before the next row's loads, so a table whose later x
+//    is an earlier y computes exactly what the launch sequence does.
+// With POS the rows are taken at the device-resident position, read once,
+// and the last thread stores the next position after the last row (the same
+// update as the sequence's last node).
+
+// Row pointers of descriptor `dd` at position `pos`.
+template <typename T, bool POS>
+__device__ __forceinline__ void persistent_ptrs(const rmsn_desc& dd, uint64_t pos,
+                                                const PosArgs& pa, const T*& x, const T*& w,
+                                                T*& y) {
+    desc_row<T, POS>(dd, pos, pa, x, y);
+    w = static_cast<const T*>(dd.w);
+}
+
 template <typename T>
-__device__ __forceinline__ void persistent_row(const rmsn_desc& dd, uint64_t pos, bool posd,
-                                               const PosArgs& pa, float eps, float* lds4) {
-    const int64_t n = dd.n;
-    if (n < 1 || n > RMSN_MAX_N) return;
-    const char* xb = static_cast<const char*>(dd.x);
-    char* yb = static_cast<char*>(dd.y);
-    if (posd) {
-        const uint64_t period = (uint64_t)pa.period;
-        const int64_t p = (int64_t)(pos < period ? pos : pos % period);
-        xb += p * pa.x_pitch;
-        yb += p * pa.y_pitch;
-    }
-    const T* x = reinterpret_cast<const T*>(xb);
-    const T* w = static_cast<const T*>(dd.w);
-    T* y = reinterpret_cast<T*>(yb);
+__device__ __forceinline__ bool group_fits(const T* x, const T* w, const T* y, int64_t n) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) |
                         reinterpret_cast<uintptr_t>(y);
-    if ((n & 3) == 0 && n <= 8192 && a % (4 * sizeof(T)) == 0) {
+    return n >= 1 && n <= 8192 && (n & 3) == 0 && a % (4 * sizeof(T)) == 0;
+}
+
+template <typename T>
+__device__ __forceinline__ void persistent_row(const T* x, const T* w, T* y, int64_t n, float eps,
+                                               float* lds4) {
+    if (n < 1 || n > RMSN_MAX_N) return;
+    if (group_fits<T>(x, w, y, n)) {
         switch ((int)((n + 1023) >> 10)) {
 #define RMSN_CASE(Q) \
     case Q: row_group<T, Q>(x, w, y, (int)n, eps, lds4); break;
@@ -734,26 +742,262 @@ __device__ __forceinline__ void persistent_row(const rmsn_desc& dd, uint64_t pos
     }
 }
 
+// --- Pipelined walk. Every row takes the GROUP mapping at a fixed eight
+// blocks of 1024 elements through buffer loads and stores whose range is the
+// row's byte length: lanes past the row load +0 (fmaf(0, 0, p) == p) and their
+// stores are dropped by the hardware's range check, so every row issues the
+// same instructions whatever its width and the compiler can wait for exactly
+// the row it needs while the next one is in flight.
+
+typedef __amdgpu_buffer_rsrc_t brsrc;
+
+// A buffer resource for `bytes` bytes at p (raw, stride 0; the third word is
+// the gfx9-family untyped format). Offsets at or past `bytes` are out of range.
+__device__ __forceinline__ brsrc row_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+template <typename T> struct PipeQuad;
+template <> struct PipeQuad<float> {
+    typedef u32x4 raw;
+    static __device__ __forceinline__ raw load(brsrc r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    }
+    static __device__ __forceinline__ void store(raw v, brsrc r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+    }
+    static __device__ __forceinline__ void unpack(raw q, float v[4]) {
+        v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+        v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+    }
+    static __device__ __forceinline__ raw apply(raw x, raw w, float inv) {
+        return slice_apply(x, w, inv, 0.0f);
+    }
+};
+template <> struct PipeQuad<uint16_t> {
+    typedef u32x2 raw;
+    static __device__ __forceinline__ raw load(brsrc r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    }
+    static __device__ __forceinline__ void store(raw v, brsrc r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+    }
+    static __device__ __forceinline__ void unpack(raw q, float v[4]) {
+        v[0] = lo_bf16(q.x); v[1] = hi_bf16(q.x); v[2] = lo_bf16(q.y); v[3] = hi_bf16(q.y);
+    }
+    static __device__ __forceinline__ raw apply(raw x, raw w, float inv) {
+        raw o;
+        o.x = apply_pair(x.x, w.x, inv);
+        o.y = apply_pair(x.y, w.y, inv);
+        return o;
+    }
+};
+
+struct PipeRow {
+    brsrc x, w, y;
+    int n;
+};
+
+template <typename T, int QM>
+struct PipeBuf {
+    typename PipeQuad<T>::raw x[QM], w[QM];
+};
+
+// Descriptor i of the table, or the last one past its end (only its base
+// pointers are used then, with an empty range).
+__device__ __forceinline__ rmsn_desc pipe_desc(const rmsn_desc* d, int32_t i, int32_t count) {
+    return d[i < count ? i : count - 1];
+}
+
+// Buffer resources of a row; `real` false gives an empty range (every access
+// out of range, no memory touched) on valid bases.
+template <typename T, bool POS>
+__device__ __forceinline__ PipeRow pipe_row_of(const rmsn_desc& dd, bool real, uint64_t pos,
+                                               const PosArgs& pa) {
+    const T* x;
+    const T* w;
+    T* y;
+    persistent_ptrs<T, POS>(dd, pos, pa, x, w, y);
+    const uint32_t bytes = real ? (uint32_t)dd.n * (uint32_t)sizeof(T) : 0u;
+    return PipeRow{row_rsrc(x, bytes), row_rsrc(w, bytes), row_rsrc(y, bytes), (int)dd.n};
+}
+
+// This lane's byte offset in block m: GROUP's element 1024 m + 256 q + 64 g + 4 t.
+template <typename T>
+__device__ __forceinline__ uint32_t pipe_off(uint32_t lane_off, int m) {
+    return lane_off + (uint32_t)m * 1024u * (uint32_t)sizeof(T);
+}
+
+template <typename T, int QM>
+__device__ __forceinline__ void pipe_issue(PipeBuf<T, QM>& b, const PipeRow& r,
+                                           uint32_t lane_off) {
+#pragma unroll
+    for (int m = 0; m < QM; ++m) b.x[m] = PipeQuad<T>::load(r.x, pipe_off<T>(lane_off, m));
+#pragma unroll
+    for (int m = 0; m < QM; ++m) b.w[m] = PipeQuad<T>::load(r.w, pipe_off<T>(lane_off, m));
+}
+
+// Workgroup barrier for LDS only: it does not wait for this wavefront's
+// global loads and stores (a full barrier would wait for the next row's
+// loads, in flight by design).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <typename T, int QM>
+__device__ __forceinline__ void pipe_compute(const PipeBuf<T, QM>& b, const PipeRow& r,
+                                             uint32_t lane_off, float eps, float* lds4, int g,
+                                             int lane) {
+    float p = 0.0f;
+#pragma unroll
+    for (int m = 0; m < QM; ++m) {
+        float v[4];
+        PipeQuad<T>::unpack(b.x[m], v);
+        transpose4(v);
+        p = fmaf(v[0], v[0], p);  // chunks 4m .. 4m+3 of chain 64g + 4t + q
+        p = fmaf(v[1], v[1], p);
+        p = fmaf(v[2], v[2], p);
+        p = fmaf(v[3], v[3], p);
+    }
+    const float gt = group_sumsq(p);
+    if (lane == 0) lds4[g] = gt;
+    lds_barrier();
+    const float inv = inverse_rms((lds4[0] + lds4[2]) + (lds4[1] + lds4[3]), r.n, eps);
+#pragma unroll
+    for (int m = 0; m < QM; ++m)
+        PipeQuad<T>::store(PipeQuad<T>::apply(b.x[m], b.w[m], inv), r.y,
+                           pipe_off<T>(lane_off, m));
+}
+
+// Whether the table can be walked pipelined (see above), and at how many
+// blocks of 1024 elements: the widest row's, so narrower tables issue fewer
+// loads per row. Every thread checks rows threadIdx.x, threadIdx.x +
+// blockDim.x, ...; the answer (0: not pipelined) is the workgroup's.
+template <typename T, bool POS>
+__device__ __forceinline__ int pipeline_blocks(const rmsn_desc* d, int32_t count, uint64_t pos,
+                                               const PosArgs& pa, int* lds_blocks) {
+    bool bad = false;
+    int blocks = 1;
+    for (int32_t j = threadIdx.x; j < count && !bad; j += blockDim.x) {
+        const rmsn_desc dj = d[j];
+        const T* x;
+        const T* w;
+        T* y;
+        persistent_ptrs<T, POS>(dj, pos, pa, x, w, y);
+        if (!group_fits<T>(x, w, y, dj.n)) {
+            bad = true;
+            break;
+        }
+        blocks = max(blocks, (int)((dj.n + 1023) >> 10));
+        const uintptr_t bx = reinterpret_cast<uintptr_t>(x), bw = reinterpret_cast<uintptr_t>(w);
+        const uintptr_t by = reinterpret_cast<uintptr_t>(y);
+        const uintptr_t len = (uintptr_t)dj.n * sizeof(T);
+        for (int k = 1; k <= 3 && k <= j; ++k) {
+            const rmsn_desc dk = d[j - k];
+            const T* xk;
+            const T* wk;
+            T* yk;
+            persistent_ptrs<T, POS>(dk, pos, pa, xk, wk, yk);
+            const uintptr_t b = reinterpret_cast<uintptr_t>(yk);
+            const uintptr_t lk = (uintptr_t)(dk.n < 0 ? 0 : dk.n) * sizeof(T);
+            const bool reads = (bx < b + lk && b < bx + len) || (bw < b + lk && b < bw + len);
+            const bool writes = k == 1 && by < b + lk && b < by + len;
+            if (reads || writes) bad = true;
+        }
+    }
+    if (threadIdx.x == 0) *lds_blocks = 1;
+    __syncthreads();
+    atomicMax(lds_blocks, blocks);
+    if (__syncthreads_or(bad)) return 0;
+    return *lds_blocks;
+}
+
+template <typename T, bool POS, int QM>
+__device__ __forceinline__ void pipelined_walk(const rmsn_desc* d, int32_t count, float eps,
+                                               uint64_t pos, const PosArgs& pa,
+                                               float (*lds8)[4]) {
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const uint32_t lane_off =
+        (uint32_t)((lane >> 4) * 256 + g * 64 + (lane & 15) * 4) * (uint32_t)sizeof(T);
+    PipeBuf<T, QM> a, b;
+    PipeRow cur = pipe_row_of<T, POS>(pipe_desc(d, 0, count), true, pos, pa);
+    pipe_issue<T, QM>(a, cur, lane_off);
+    // Eight stores to an empty range (dropped by the range check): every row's
+    // loads are then followed by the same eight stores, at the loop's entry as
+    // on its back edge, so the compiler's wait for a row never covers the
+    // previous row's stores.
+    const brsrc none = row_rsrc(pipe_desc(d, 0, count).y, 0u);
+#pragma unroll
+    for (int m = 0; m < QM; ++m)
+        PipeQuad<T>::store(typename PipeQuad<T>::raw{}, none, pipe_off<T>(lane_off, m));
+    rmsn_desc ahead = pipe_desc(d, 1, count);  // descriptors are read one row ahead
+    // Scheduling barriers keep each row's reduction below the next row's load
+    // issue: the reduction waits for its own loads only.
+    for (int32_t i = 0;;) {
+        // row i is in a; row i + 1's loads go into b before row i is reduced
+        PipeRow nxt = pipe_row_of<T, POS>(ahead, i + 1 < count, pos, pa);
+        pipe_issue<T, QM>(b, nxt, lane_off);
+        ahead = pipe_desc(d, i + 2, count);
+        __builtin_amdgcn_sched_barrier(0);
+        pipe_compute<T, QM>(a, cur, lane_off, eps, lds8[0], g, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        if (++i >= count) break;
+        cur = nxt;
+        nxt = pipe_row_of<T, POS>(ahead, i + 1 < count, pos, pa);
+        pipe_issue<T, QM>(a, nxt, lane_off);
+        ahead = pipe_desc(d, i + 2, count);
+        __builtin_amdgcn_sched_barrier(0);
+        pipe_compute<T, QM>(b, cur, lane_off, eps, lds8[1], g, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        if (++i >= count) break;
+        cur = nxt;
+    }
+}
+
+template <typename T, bool POS>
+__device__ __forceinline__ void serial_walk(const rmsn_desc* d, int32_t count, float eps,
+                                            uint64_t pos, const PosArgs& pa, float* lds4) {
+    uint64_t unused;
+    rmsn_desc next = desc_load<false>(d, pa, &unused);
+    for (int32_t i = 0; i < count; ++i) {
+        const rmsn_desc cur = next;
+        if (i + 1 < count) next = desc_load<false>(d + i + 1, pa, &unused);
+        const T* x;
+        const T* w;
+        T* y;
+        persistent_ptrs<T, POS>(cur, pos, pa, x, w, y);
+        persistent_row<T>(x, w, y, cur.n, eps, lds4);
+        __syncthreads();  // this row's stores before the next row's loads; lds4 reused
+    }
+}
+
 template <typename T, bool POS>
 __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __restrict__ d,
                                                              int32_t count, float eps,
                                                              PosArgs pa) {
     __shared__ float lds4[4];
-    uint64_t pos;
-    rmsn_desc next = desc_load<POS>(d, pa, &pos);
-    for (int32_t i = 0; i < count; ++i) {
-        const rmsn_desc cur = next;
-        if (i + 1 < count) {
-            uint64_t unused;
-            next = desc_load<false>(d + i + 1, pa, &unused);
-        }
-        persistent_row<T>(cur, pos, POS, pa, eps, lds4);
-        __syncthreads();  // this row's stores before the next row's loads; lds4 reused
+    __shared__ float lds8[2][4];
+    __shared__ int lds_blocks;
+    uint64_t pos = 0;
+    if (POS) {
+        const uint64_t per = (uint64_t)pa.period;
+        const uint64_t raw = (uint64_t)*pa.d_pos;
+        pos = raw < per ? raw : raw % per;
+    }
+    switch (pipeline_blocks<T, POS>(d, count, pos, pa, &lds_blocks)) {
+#define RMSN_CASE(Q) \
+    case Q: pipelined_walk<T, POS, Q>(d, count, eps, pos, pa, lds8); break;
+        RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)
+#undef RMSN_CASE
+        default: serial_walk<T, POS>(d, count, eps, pos, pa, lds4); break;
     }
     if (POS && threadIdx.x == 0) {
         const uint64_t per = (uint64_t)pa.period;
-        const uint64_t p = pos < per ? pos : pos % per;
-        const_cast<int64_t*>(pa.d_pos)[0] = (int64_t)(p + 1 == per ? 0 : p + 1);
+        const_cast<int64_t*>(pa.d_pos)[0] = (int64_t)(pos + 1 == per ? 0 : pos + 1);
     }
 }
 

@@ -621,3 +621,139 @@ def test_persistent_call_captured_in_a_graph(rn, step):
         sync()
         compare(step.outputs(), step.expected(s), f"captured persistent replay {rep}")
     step.point_at(0)
+
+
+# ---- the persistent launch's two walks ------------------------------------------
+# A table whose rows all fit the GROUP mapping (width a multiple of 4, at most
+# 8192, quad-aligned pointers) and never read what one of the three rows before
+# writes (nor write what the row before writes) is walked with the next row's
+# loads in flight; any other table row after row. Both must give the launch
+# sequence's bits.
+
+def _rows_of(kind, widths, seed):
+    """Seeded host rows (x, w) of the given widths, float32 or bf16 bits."""
+    out = []
+    for i, n in enumerate(widths):
+        x, w = wl.misc_f32(seed + i, n, sigma=2.0)
+        if kind == "bf16":
+            x, w = wl.to_bf16_bits(x), wl.to_bf16_bits(w)
+        out.append((x, w))
+    return out
+
+
+def _dev_kind(kind):
+    import torch
+    from gpu_util import assert_bits_bf16, bf16_host, to_dev_bf16
+    if kind == "bf16":
+        return torch.bfloat16, to_dev_bf16, bf16_host, assert_bits_bf16, oracle.row_bf16, rn_dtype("bf16")
+    return torch.float32, to_dev_f32, f32_host, assert_bits_f32, oracle.row_f32, rn_dtype("f32")
+
+
+def rn_dtype(kind):
+    import row_wise_rmsnorm_amd as m
+    return m.BF16 if kind == "bf16" else m.F32
+
+
+PIPE_WIDTHS = [4, 8, 12, 100, 1000, 1020, 1024, 1028, 3000, 5000, 8188, 8192, 512, 1536, 7168, 4]
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_persistent_pipelined_widths(rn, kind):
+    """Independent rows of every kind of width the pipelined walk takes: a
+    multiple of 4 from 4 to 8192, partial and exact 1024-element blocks."""
+    import torch
+    say(f"persistent pipelined widths {kind}")
+    tdt, todev, host, check, row, dtype = _dev_kind(kind)
+    rows = _rows_of(kind, PIPE_WIDTHS, 7000)
+    xs = [todev(x) for x, _ in rows]
+    ws = [todev(w) for _, w in rows]
+    ys = [torch.full((len(x),), float("nan"), dtype=tdt, device=dev()) for x, _ in rows]
+    table, widths = rn.make_table(list(zip(xs, ws, ys)))
+    for rep in range(2):
+        rn.rmsnorm_sequence_persistent(table, len(widths), wl.EPS, dtype)
+        sync()
+        for i, (x, w) in enumerate(rows):
+            check(host(ys[i]), row(x, w, wl.EPS), f"rep {rep} row {i} n={len(x)}")
+
+
+@pytest.mark.parametrize("kind,odd", [("f32", "width 4097"), ("f32", "width 9000"),
+                                      ("f32", "misaligned"), ("bf16", "width 1001"),
+                                      ("bf16", "misaligned")])
+def test_persistent_table_with_a_row_the_pipeline_cannot_take(rn, kind, odd):
+    """One row the GROUP mapping cannot take sends the whole table down the
+    row-after-row walk; every row still matches the oracle."""
+    import torch
+    say(f"persistent serial fallback {kind} {odd}")
+    tdt, todev, host, check, row, dtype = _dev_kind(kind)
+    widths = [7168, 1536, 512, 7168, 1536]
+    special = 2
+    if odd.startswith("width"):
+        widths[special] = int(odd.split()[1])
+    rows = _rows_of(kind, widths, 7100)
+    xs, ws, ys, views = [], [], [], []
+    for i, (x, w) in enumerate(rows):
+        off = 1 if (odd == "misaligned" and i == special) else 0
+        n = len(x)
+        xb = torch.zeros(n + 8, dtype=tdt, device=dev())
+        xb[off:off + n].copy_(todev(x))
+        yb = torch.full((n + 8,), float("nan"), dtype=tdt, device=dev())
+        xs.append(xb[off:off + n]); ws.append(todev(w)); ys.append(yb[off:off + n])
+    table, widths = rn.make_table(list(zip(xs, ws, ys)))
+    rn.rmsnorm_sequence_persistent(table, len(widths), wl.EPS, dtype)
+    sync()
+    for i, (x, w) in enumerate(rows):
+        check(host(ys[i]), row(x, w, wl.EPS), f"row {i} n={len(x)}")
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("dist", [1, 2, 3, 4, 5])
+def test_persistent_dependency_at_distance(rn, kind, dist):
+    """Row j reads the output of row j - dist (rows 0 .. dist-1 read fresh
+    inputs). Distances 1 to 3 must take the row-after-row walk, larger ones
+    may be pipelined: both give the sequence's bits."""
+    import torch
+    say(f"persistent dependency at distance {dist} {kind}")
+    tdt, todev, host, check, row, dtype = _dev_kind(kind)
+    k, n = 12, 2048
+    rows = _rows_of(kind, [n] * k, 7200 + 10 * dist)
+    xs = [todev(x) for x, _ in rows[:dist]]
+    ws = [todev(w) for _, w in rows]
+    ys = [torch.full((n,), float("nan"), dtype=tdt, device=dev()) for _ in range(k)]
+    for j in range(dist, k):
+        xs.append(ys[j - dist])
+    table, widths = rn.make_table(list(zip(xs, ws, ys)))
+    want = []
+    for j in range(k):
+        x = rows[j][0] if j < dist else want[j - dist]
+        want.append(row(x, rows[j][1], wl.EPS))
+    rn.rmsnorm_sequence_persistent(table, k, wl.EPS, dtype)
+    sync()
+    for j in range(k):
+        check(host(ys[j]), want[j], f"row {j}")
+
+
+@pytest.mark.parametrize("shift", [0, 4, 1000])
+def test_persistent_adjacent_rows_writing_the_same_memory(rn, shift):
+    """Row j writes memory row j - 1 also writes (the same buffer, or shifted
+    by `shift` elements): the later row's values must win, as in the sequence."""
+    import torch
+    say(f"persistent overlapping outputs shift {shift}")
+    n = 2048
+    rows = _rows_of("f32", [n] * 6, 7300 + shift)
+    xs = [to_dev_f32(x) for x, _ in rows]
+    ws = [to_dev_f32(w) for _, w in rows]
+    buf = torch.full((n + shift + 8,), float("nan"), dtype=torch.float32, device=dev())
+    others = [torch.full((n,), float("nan"), dtype=torch.float32, device=dev()) for _ in range(6)]
+    ys = list(others)
+    ys[2] = buf[:n]                    # rows 2 and 3 write overlapping memory
+    ys[3] = buf[shift:shift + n]
+    table, widths = rn.make_table(list(zip(xs, ws, ys)))
+    rn.rmsnorm_sequence_persistent(table, 6, wl.EPS, rn.F32)
+    sync()
+    outs = [oracle.row_f32(x, w, wl.EPS) for x, w in rows]
+    want = np.full(n + shift + 8, np.nan, dtype=np.float32)
+    want[:n] = outs[2]
+    want[shift:shift + n] = outs[3]
+    assert_bits_f32(f32_host(buf)[:n + shift], want[:n + shift], "overlapping outputs")
+    for j in (0, 1, 4, 5):
+        assert_bits_f32(f32_host(ys[j]), outs[j], f"row {j}")
