@@ -872,47 +872,122 @@ __device__ __forceinline__ void pipe_compute(const PipeBuf<T, QM>& b, const Pipe
                            pipe_off<T>(lane_off, m));
 }
 
-// Whether the table can be walked pipelined (see above), and at how many
-// blocks of 1024 elements: the widest row's, so narrower tables issue fewer
-// loads per row. Every thread checks rows threadIdx.x, threadIdx.x +
-// blockDim.x, ...; the answer (0: not pipelined) is the workgroup's.
+// --- Round walk: one wavefront per row, the four wavefronts on four
+// consecutive rows at a time (a round), a workgroup barrier between rounds.
+// A row is the SPLIT layout with a single wavefront: U 1 KB slices, one
+// 16-byte load per lane each, so the wavefront holds the whole row and needs
+// neither LDS nor a hand-off. Every row issues its own number of loads, and
+// the four rows of a round are in flight together.
+
+template <typename T, int U, bool EXACT>
+__device__ __forceinline__ void wave_row_slices(const T* x, const T* w, T* y, int n, float eps,
+                                                int lane) {
+    const uint32_t nvec = (uint32_t)n * (uint32_t)sizeof(T) / 16u;
+    SplitPart<T, U, EXACT, false> part;
+    part.load(scalar_gptr(reinterpret_cast<const char*>(x)),
+              scalar_gptr(reinterpret_cast<const char*>(w)), 0, lane, nvec);
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    part.chains(p, nvec);
+    const float inv = inverse_rms(split_sumsq(p, lane, T()), n, eps);
+    part.apply(inv, scalar_gptr(reinterpret_cast<char*>(y)), 0, lane, nvec);
+}
+
+// Slice buckets of the one-wavefront rows (rows of at most 8192 elements:
+// 32 slices of binary32, 16 of bf16).
+#define RMSN_FOR_ROUND_SLICES(X) X(1) X(2) X(3) X(4) X(6) X(8) X(12) X(16) X(20) X(24) X(28) X(32)
+
+// One row of a round: 1 <= n <= 8192, n * sizeof(T) a multiple of 16, x, w, y
+// 16-byte aligned (checked before the round walk is chosen).
+template <typename T>
+__device__ __forceinline__ void round_row(const T* x, const T* w, T* y, int n, float eps,
+                                          int lane) {
+    const int bytes = n * (int)sizeof(T);
+    const int slices = (bytes + 1023) >> 10;
+#define RMSN_CASE(U)                                                                   \
+    if constexpr (U * 1024 <= 8192 * (int)sizeof(T)) {                                 \
+        if (slices <= U) {                                                             \
+            if (bytes == U * 1024) wave_row_slices<T, U, true>(x, w, y, n, eps, lane);  \
+            else wave_row_slices<T, U, false>(x, w, y, n, eps, lane);                  \
+            return;                                                                    \
+        }                                                                              \
+    }
+    RMSN_FOR_ROUND_SLICES(RMSN_CASE)
+#undef RMSN_CASE
+}
+
 template <typename T, bool POS>
-__device__ __forceinline__ int pipeline_blocks(const rmsn_desc* d, int32_t count, uint64_t pos,
-                                               const PosArgs& pa, int* lds_blocks) {
-    bool bad = false;
+__device__ __forceinline__ void round_walk(const rmsn_desc* d, int32_t count, float eps,
+                                           uint64_t pos, const PosArgs& pa) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    for (int32_t r = 0; r < count; r += 4) {
+        const int32_t j = r + wave;
+        if (j < count) {
+            const rmsn_desc dd = d[j];
+            const T* x;
+            const T* w;
+            T* y;
+            persistent_ptrs<T, POS>(dd, pos, pa, x, w, y);
+            round_row<T>(x, w, y, (int)dd.n, eps, lane);
+        }
+        __syncthreads();  // the round's stores before the next round's loads
+    }
+}
+
+// How the table is walked (see above): kRoundWalk, a block count 1..8 for the
+// pipelined walk (the widest row's), or 0 for row after row. Every thread
+// checks rows threadIdx.x, threadIdx.x + blockDim.x, ...; the answer is the
+// workgroup's.
+constexpr int kRoundWalk = 100;
+
+__device__ __forceinline__ bool ranges_meet(uintptr_t a, uintptr_t la, uintptr_t b, uintptr_t lb) {
+    return a < b + lb && b < a + la;
+}
+
+template <typename T, bool POS>
+__device__ __forceinline__ int walk_mode(const rmsn_desc* d, int32_t count, uint64_t pos,
+                                         const PosArgs& pa, int* lds_blocks) {
+    bool no_pipe = false, no_round = false;
     int blocks = 1;
-    for (int32_t j = threadIdx.x; j < count && !bad; j += blockDim.x) {
+    for (int32_t j = threadIdx.x; j < count; j += blockDim.x) {
         const rmsn_desc dj = d[j];
         const T* x;
         const T* w;
         T* y;
         persistent_ptrs<T, POS>(dj, pos, pa, x, w, y);
-        if (!group_fits<T>(x, w, y, dj.n)) {
-            bad = true;
-            break;
-        }
-        blocks = max(blocks, (int)((dj.n + 1023) >> 10));
         const uintptr_t bx = reinterpret_cast<uintptr_t>(x), bw = reinterpret_cast<uintptr_t>(w);
         const uintptr_t by = reinterpret_cast<uintptr_t>(y);
+        if (!group_fits<T>(x, w, y, dj.n)) {
+            no_pipe = no_round = true;
+            break;
+        }
         const uintptr_t len = (uintptr_t)dj.n * sizeof(T);
-        for (int k = 1; k <= 3 && k <= j; ++k) {
-            const rmsn_desc dk = d[j - k];
+        if (len % 16 || (bx | bw | by) % 16) no_round = true;
+        blocks = max(blocks, (int)((dj.n + 1023) >> 10));
+        // the three rows before (pipelined walk) and the other rows of the
+        // round (round walk)
+        const int32_t r0 = j & ~3;
+        for (int32_t k = max(0, min(j - 3, r0)); k < min(count, r0 + 4); ++k) {
+            if (k == j) continue;
+            const rmsn_desc dk = d[k];
             const T* xk;
             const T* wk;
             T* yk;
             persistent_ptrs<T, POS>(dk, pos, pa, xk, wk, yk);
             const uintptr_t b = reinterpret_cast<uintptr_t>(yk);
             const uintptr_t lk = (uintptr_t)(dk.n < 0 ? 0 : dk.n) * sizeof(T);
-            const bool reads = (bx < b + lk && b < bx + len) || (bw < b + lk && b < bw + len);
-            const bool writes = k == 1 && by < b + lk && b < by + len;
-            if (reads || writes) bad = true;
+            const bool reads = ranges_meet(bx, len, b, lk) || ranges_meet(bw, len, b, lk);
+            const bool writes = ranges_meet(by, len, b, lk);
+            if (k < j && j - k <= 3 && (reads || (writes && k == j - 1))) no_pipe = true;
+            if (k >= r0 && (reads || (writes && k < j))) no_round = true;
         }
     }
     if (threadIdx.x == 0) *lds_blocks = 1;
     __syncthreads();
     atomicMax(lds_blocks, blocks);
-    if (__syncthreads_or(bad)) return 0;
-    return *lds_blocks;
+    const bool round_ok = !__syncthreads_or(no_round);
+    const bool pipe_ok = !__syncthreads_or(no_pipe);
+    return round_ok ? kRoundWalk : pipe_ok ? *lds_blocks : 0;
 }
 
 template <typename T, bool POS, int QM>
@@ -988,7 +1063,8 @@ __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __
         const uint64_t raw = (uint64_t)*pa.d_pos;
         pos = raw < per ? raw : raw % per;
     }
-    switch (pipeline_blocks<T, POS>(d, count, pos, pa, &lds_blocks)) {
+    switch (walk_mode<T, POS>(d, count, pos, pa, &lds_blocks)) {
+        case kRoundWalk: round_walk<T, POS>(d, count, eps, pos, pa); break;
 #define RMSN_CASE(Q) \
     case Q: pipelined_walk<T, POS, Q>(d, count, eps, pos, pa, lds8); break;
         RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)

@@ -623,12 +623,17 @@ def test_persistent_call_captured_in_a_graph(rn, step):
     step.point_at(0)
 
 
-# ---- the persistent launch's two walks ------------------------------------------
-# A table whose rows all fit the GROUP mapping (width a multiple of 4, at most
-# 8192, quad-aligned pointers) and never read what one of the three rows before
-# writes (nor write what the row before writes) is walked with the next row's
-# loads in flight; any other table row after row. Both must give the launch
-# sequence's bits.
+# ---- the persistent launch's three walks -----------------------------------------
+# Round walk: every row a whole number of 16-byte vectors (at most 8192
+# elements, 16-byte aligned) and no row of a round of four consecutive rows
+# reading or writing what another row of the round writes: one wavefront per
+# row, four rows at a time. Pipelined walk: rows fit the GROUP mapping (width a
+# multiple of 4, quad-aligned) and never read what one of the three rows
+# before writes (nor write what the row before writes). Anything else: row
+# after row. All three must give the launch sequence's bits. binary32 rows
+# that fit GROUP are whole vectors, so binary32 tables without in-round
+# dependencies take the round walk; bf16 rows of width 4 mod 8 take the
+# pipelined walk.
 
 def _rows_of(kind, widths, seed):
     """Seeded host rows (x, w) of the given widths, float32 or bf16 bits."""
@@ -655,16 +660,21 @@ def rn_dtype(kind):
 
 
 PIPE_WIDTHS = [4, 8, 12, 100, 1000, 1020, 1024, 1028, 3000, 5000, 8188, 8192, 512, 1536, 7168, 4]
+ROUND_WIDTHS = [8, 16, 64, 256, 264, 512, 1000, 1024, 1032, 3000, 4104, 8184, 8192, 7168, 1536,
+                8, 24]
 
 
-@pytest.mark.parametrize("kind", ["f32", "bf16"])
-def test_persistent_pipelined_widths(rn, kind):
-    """Independent rows of every kind of width the pipelined walk takes: a
-    multiple of 4 from 4 to 8192, partial and exact 1024-element blocks."""
+@pytest.mark.parametrize("kind,widths", [("f32", PIPE_WIDTHS), ("bf16", PIPE_WIDTHS),
+                                         ("f32", ROUND_WIDTHS), ("bf16", ROUND_WIDTHS)],
+                         ids=["f32-mult4", "bf16-mult4", "f32-mult8", "bf16-mult8"])
+def test_persistent_walk_widths(rn, kind, widths):
+    """Independent rows of every kind of width the fast walks take: multiples
+    of 4 (bf16: the pipelined walk; binary32: the round walk) and of 8 (the
+    round walk), from 4 to 8192, partial and exact slices and blocks."""
     import torch
-    say(f"persistent pipelined widths {kind}")
+    say(f"persistent walk widths {kind} {len(widths)} rows")
     tdt, todev, host, check, row, dtype = _dev_kind(kind)
-    rows = _rows_of(kind, PIPE_WIDTHS, 7000)
+    rows = _rows_of(kind, widths, 7000)
     xs = [todev(x) for x, _ in rows]
     ws = [todev(w) for _, w in rows]
     ys = [torch.full((len(x),), float("nan"), dtype=tdt, device=dev()) for x, _ in rows]
@@ -705,16 +715,17 @@ def test_persistent_table_with_a_row_the_pipeline_cannot_take(rn, kind, odd):
         check(host(ys[i]), row(x, w, wl.EPS), f"row {i} n={len(x)}")
 
 
-@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("kind,n", [("f32", 2048), ("bf16", 2048), ("bf16", 2044)])
 @pytest.mark.parametrize("dist", [1, 2, 3, 4, 5])
-def test_persistent_dependency_at_distance(rn, kind, dist):
+def test_persistent_dependency_at_distance(rn, kind, n, dist):
     """Row j reads the output of row j - dist (rows 0 .. dist-1 read fresh
-    inputs). Distances 1 to 3 must take the row-after-row walk, larger ones
-    may be pipelined: both give the sequence's bits."""
+    inputs). Distances 1 to 3 must take the row-after-row walk; 4 and more the
+    round walk (width 2048) or the pipelined walk (bf16 width 2044): all give
+    the sequence's bits."""
     import torch
-    say(f"persistent dependency at distance {dist} {kind}")
+    say(f"persistent dependency at distance {dist} {kind} n={n}")
     tdt, todev, host, check, row, dtype = _dev_kind(kind)
-    k, n = 12, 2048
+    k = 12
     rows = _rows_of(kind, [n] * k, 7200 + 10 * dist)
     xs = [todev(x) for x, _ in rows[:dist]]
     ws = [todev(w) for _, w in rows]
@@ -757,3 +768,29 @@ def test_persistent_adjacent_rows_writing_the_same_memory(rn, shift):
     assert_bits_f32(f32_host(buf)[:n + shift], want[:n + shift], "overlapping outputs")
     for j in (0, 1, 4, 5):
         assert_bits_f32(f32_host(ys[j]), outs[j], f"row {j}")
+
+
+@pytest.mark.parametrize("kind,n", [("f32", 2048), ("bf16", 2044)])
+def test_persistent_row_reads_what_a_later_row_overwrites(rn, kind, n):
+    """Row j reads buffer B that row j + 1 then overwrites: row j must see B's
+    old contents, as in the sequence (no round walk for such a round; the
+    pipelined walk, where it applies, issues row j's loads before row j + 1's
+    stores)."""
+    import torch
+    say(f"persistent write-after-read {kind} n={n}")
+    tdt, todev, host, check, row, dtype = _dev_kind(kind)
+    k = 8
+    rows = _rows_of(kind, [n] * (k + 1), 7400)
+    shared = todev(rows[k][0])           # B: old contents = an extra input row
+    xs = [todev(x) for x, _ in rows[:k]]
+    ws = [todev(w) for _, w in rows[:k]]
+    ys = [torch.full((n,), float("nan"), dtype=tdt, device=dev()) for _ in range(k)]
+    xs[2] = shared                       # row 2 reads B ...
+    ys[3] = shared                       # ... which row 3 overwrites
+    table, widths = rn.make_table(list(zip(xs, ws, ys)))
+    want = [row(x, w, wl.EPS) for x, w in rows[:k]]
+    want[2] = row(rows[k][0], rows[2][1], wl.EPS)
+    rn.rmsnorm_sequence_persistent(table, k, wl.EPS, dtype)
+    sync()
+    for j in range(k):
+        check(host(ys[j]), want[j], f"row {j}")
