@@ -694,20 +694,26 @@ __global__ __launch_bounds__(256) void k_desc_group(const rmsn_desc* __restrict_
 
 // The whole decode step in one launch (Lecture 08 "Graph-resident decode",
 // further reading: a persistent kernel instead of many captured ones). One
-// workgroup walks the descriptor table in order, in one of two ways chosen
-// when the launch starts:
-//  - pipelined, when every row can take the GROUP mapping (width a multiple of
+// workgroup of four wavefronts walks the descriptor table, in one of three
+// ways chosen when the launch starts (every thread checks some rows, then one
+// barrier):
+//  - round walk, when every row is a whole number of 16-byte vectors (at most
+//    8192 elements, 16-byte aligned) and no row of an aligned group of 16 (or
+//    at least of 4) consecutive rows reads or writes memory that another row
+//    of the group writes: each wavefront takes a row of its own and holds it
+//    whole, four rows at a time, and a workgroup barrier after each group
+//    orders the group's stores before the next group's loads;
+//  - pipelined, when every row fits the GROUP mapping (width a multiple of
 //    4 and at most 8192, pointers quad-aligned) and no row reads memory that
 //    one of the three rows before it writes, nor writes memory the row just
-//    before it writes: the next row's loads are issued before the current row
-//    is reduced, so one row's memory round trip overlaps the previous row's
-//    work;
+//    before it writes: the four wavefronts share each row, and the next row's
+//    loads are issued before the current row is reduced;
 //  - otherwise row after row, with a workgroup barrier after each row that
-//    orders its stores before the next row's loads, so a table whose later x
-//    is an earlier y computes exactly what the launch sequence does.
-// With POS the rows are taken at the device-resident position, read once,
-// and the last thread stores the next position after the last row (the same
-// update as the sequence's last node).
+//    orders its stores before the next row's loads.
+// All three compute what the launch sequence computes. With POS the rows are
+// taken at the device-resident position, read once, and the last thread
+// stores the next position after the last row (the same update as the
+// sequence's last node).
 
 // Row pointers of descriptor `dd` at position `pos`.
 template <typename T, bool POS>
@@ -742,12 +748,13 @@ __device__ __forceinline__ void persistent_row(const T* x, const T* w, T* y, int
     }
 }
 
-// --- Pipelined walk. Every row takes the GROUP mapping at a fixed eight
-// blocks of 1024 elements through buffer loads and stores whose range is the
-// row's byte length: lanes past the row load +0 (fmaf(0, 0, p) == p) and their
-// stores are dropped by the hardware's range check, so every row issues the
-// same instructions whatever its width and the compiler can wait for exactly
-// the row it needs while the next one is in flight.
+// --- Pipelined walk. Every row takes the GROUP mapping at the table's widest
+// block count (1024-element blocks) through buffer loads and stores whose
+// range is the row's byte length: lanes past the row load +0
+// (fmaf(0, 0, p) == p) and their stores are dropped by the hardware's range
+// check, so every row issues the same instructions whatever its width and the
+// compiler can wait for exactly the row it needs while the next one is in
+// flight.
 
 typedef __amdgpu_buffer_rsrc_t brsrc;
 
@@ -873,11 +880,11 @@ __device__ __forceinline__ void pipe_compute(const PipeBuf<T, QM>& b, const Pipe
 }
 
 // --- Round walk: one wavefront per row, the four wavefronts on four
-// consecutive rows at a time (a round), a workgroup barrier between rounds.
-// A row is the SPLIT layout with a single wavefront: U 1 KB slices, one
-// 16-byte load per lane each, so the wavefront holds the whole row and needs
-// neither LDS nor a hand-off. Every row issues its own number of loads, and
-// the four rows of a round are in flight together.
+// consecutive rows at a time (a round). A row is the SPLIT layout with a
+// single wavefront: U 1 KB slices, one 16-byte load per lane each, so the
+// wavefront holds the whole row and needs neither LDS nor a hand-off. Every
+// row issues its own number of loads, and the four rows of a round are in
+// flight together.
 
 template <typename T, int U, bool EXACT>
 __device__ __forceinline__ void wave_row_slices(const T* x, const T* w, T* y, int n, float eps,
@@ -915,30 +922,37 @@ __device__ __forceinline__ void round_row(const T* x, const T* w, T* y, int n, f
 #undef RMSN_CASE
 }
 
-template <typename T, bool POS>
+// Rounds of four rows, a workgroup barrier after every K rounds: wavefront w
+// takes rows 4q + w of each group of 4K rows, and the barrier orders the
+// group's stores before the next group's loads.
+template <typename T, bool POS, int K>
 __device__ __forceinline__ void round_walk(const rmsn_desc* d, int32_t count, float eps,
                                            uint64_t pos, const PosArgs& pa) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    for (int32_t r = 0; r < count; r += 4) {
-        const int32_t j = r + wave;
-        if (j < count) {
-            const rmsn_desc dd = d[j];
-            const T* x;
-            const T* w;
-            T* y;
-            persistent_ptrs<T, POS>(dd, pos, pa, x, w, y);
-            round_row<T>(x, w, y, (int)dd.n, eps, lane);
+    for (int32_t r = 0; r < count; r += 4 * K) {
+        for (int q = 0; q < K; ++q) {
+            const int32_t j = r + 4 * q + wave;
+            if (j < count) {
+                const rmsn_desc dd = d[j];
+                const T* x;
+                const T* w;
+                T* y;
+                persistent_ptrs<T, POS>(dd, pos, pa, x, w, y);
+                round_row<T>(x, w, y, (int)dd.n, eps, lane);
+            }
         }
-        __syncthreads();  // the round's stores before the next round's loads
+        __syncthreads();  // the group's stores before the next group's loads
     }
 }
 
-// How the table is walked (see above): kRoundWalk, a block count 1..8 for the
-// pipelined walk (the widest row's), or 0 for row after row. Every thread
-// checks rows threadIdx.x, threadIdx.x + blockDim.x, ...; the answer is the
-// workgroup's.
-constexpr int kRoundWalk = 100;
+// How the table is walked (see above): kRoundWalk16 or kRoundWalk4 (no row of
+// an aligned group of 16 / 4 rows reads or writes what another row of the
+// group writes), a block count 1..8 for the pipelined walk (the widest
+// row's), or 0 for row after row. Every thread checks rows threadIdx.x,
+// threadIdx.x + blockDim.x, ...; the answer is the workgroup's.
+constexpr int kRoundWalk4 = 100;
+constexpr int kRoundWalk16 = 101;
 
 __device__ __forceinline__ bool ranges_meet(uintptr_t a, uintptr_t la, uintptr_t b, uintptr_t lb) {
     return a < b + lb && b < a + la;
@@ -947,7 +961,7 @@ __device__ __forceinline__ bool ranges_meet(uintptr_t a, uintptr_t la, uintptr_t
 template <typename T, bool POS>
 __device__ __forceinline__ int walk_mode(const rmsn_desc* d, int32_t count, uint64_t pos,
                                          const PosArgs& pa, int* lds_blocks) {
-    bool no_pipe = false, no_round = false;
+    bool no_pipe = false, no_round = false, no_round16 = false;
     int blocks = 1;
     for (int32_t j = threadIdx.x; j < count; j += blockDim.x) {
         const rmsn_desc dj = d[j];
@@ -958,16 +972,16 @@ __device__ __forceinline__ int walk_mode(const rmsn_desc* d, int32_t count, uint
         const uintptr_t bx = reinterpret_cast<uintptr_t>(x), bw = reinterpret_cast<uintptr_t>(w);
         const uintptr_t by = reinterpret_cast<uintptr_t>(y);
         if (!group_fits<T>(x, w, y, dj.n)) {
-            no_pipe = no_round = true;
+            no_pipe = no_round = no_round16 = true;
             break;
         }
         const uintptr_t len = (uintptr_t)dj.n * sizeof(T);
-        if (len % 16 || (bx | bw | by) % 16) no_round = true;
+        if (len % 16 || (bx | bw | by) % 16) no_round = no_round16 = true;
         blocks = max(blocks, (int)((dj.n + 1023) >> 10));
         // the three rows before (pipelined walk) and the other rows of the
-        // round (round walk)
-        const int32_t r0 = j & ~3;
-        for (int32_t k = max(0, min(j - 3, r0)); k < min(count, r0 + 4); ++k) {
+        // group of 4 and of 16 (round walks)
+        const int32_t r0 = j & ~3, g0 = j & ~15;
+        for (int32_t k = max(0, min(j - 3, g0)); k < min(count, g0 + 16); ++k) {
             if (k == j) continue;
             const rmsn_desc dk = d[k];
             const T* xk;
@@ -979,15 +993,18 @@ __device__ __forceinline__ int walk_mode(const rmsn_desc* d, int32_t count, uint
             const bool reads = ranges_meet(bx, len, b, lk) || ranges_meet(bw, len, b, lk);
             const bool writes = ranges_meet(by, len, b, lk);
             if (k < j && j - k <= 3 && (reads || (writes && k == j - 1))) no_pipe = true;
-            if (k >= r0 && (reads || (writes && k < j))) no_round = true;
+            const bool meet = reads || (writes && k < j);
+            if (k >= r0 && k < r0 + 4 && meet) no_round = true;
+            if (k >= g0 && meet) no_round16 = true;
         }
     }
     if (threadIdx.x == 0) *lds_blocks = 1;
     __syncthreads();
     atomicMax(lds_blocks, blocks);
+    const bool round16_ok = !__syncthreads_or(no_round16);
     const bool round_ok = !__syncthreads_or(no_round);
     const bool pipe_ok = !__syncthreads_or(no_pipe);
-    return round_ok ? kRoundWalk : pipe_ok ? *lds_blocks : 0;
+    return round16_ok ? kRoundWalk16 : round_ok ? kRoundWalk4 : pipe_ok ? *lds_blocks : 0;
 }
 
 template <typename T, bool POS, int QM>
@@ -1001,9 +1018,9 @@ __device__ __forceinline__ void pipelined_walk(const rmsn_desc* d, int32_t count
     PipeBuf<T, QM> a, b;
     PipeRow cur = pipe_row_of<T, POS>(pipe_desc(d, 0, count), true, pos, pa);
     pipe_issue<T, QM>(a, cur, lane_off);
-    // Eight stores to an empty range (dropped by the range check): every row's
-    // loads are then followed by the same eight stores, at the loop's entry as
-    // on its back edge, so the compiler's wait for a row never covers the
+    // QM stores to an empty range (dropped by the range check): every row's
+    // loads are then followed by the same QM stores, at the loop's entry as on
+    // its back edge, so the compiler's wait for a row never covers the
     // previous row's stores.
     const brsrc none = row_rsrc(pipe_desc(d, 0, count).y, 0u);
 #pragma unroll
@@ -1064,7 +1081,8 @@ __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __
         pos = raw < per ? raw : raw % per;
     }
     switch (walk_mode<T, POS>(d, count, pos, pa, &lds_blocks)) {
-        case kRoundWalk: round_walk<T, POS>(d, count, eps, pos, pa); break;
+        case kRoundWalk16: round_walk<T, POS, 4>(d, count, eps, pos, pa); break;
+        case kRoundWalk4: round_walk<T, POS, 1>(d, count, eps, pos, pa); break;
 #define RMSN_CASE(Q) \
     case Q: pipelined_walk<T, POS, Q>(d, count, eps, pos, pa, lds8); break;
         RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)

@@ -716,16 +716,17 @@ def test_persistent_table_with_a_row_the_pipeline_cannot_take(rn, kind, odd):
 
 
 @pytest.mark.parametrize("kind,n", [("f32", 2048), ("bf16", 2048), ("bf16", 2044)])
-@pytest.mark.parametrize("dist", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("dist", [1, 2, 3, 4, 5, 8, 16, 17])
 def test_persistent_dependency_at_distance(rn, kind, n, dist):
     """Row j reads the output of row j - dist (rows 0 .. dist-1 read fresh
-    inputs). Distances 1 to 3 must take the row-after-row walk; 4 and more the
-    round walk (width 2048) or the pipelined walk (bf16 width 2044): all give
-    the sequence's bits."""
+    inputs). Distances 1 to 3 must take the row-after-row walk; 4 to 15 the
+    round walk with a barrier every 4 rows (width 2048) or the pipelined walk
+    (bf16 width 2044); 16 and more the round walk with a barrier every 16
+    rows: all give the sequence's bits."""
     import torch
     say(f"persistent dependency at distance {dist} {kind} n={n}")
     tdt, todev, host, check, row, dtype = _dev_kind(kind)
-    k = 12
+    k = max(12, dist + 8)
     rows = _rows_of(kind, [n] * k, 7200 + 10 * dist)
     xs = [todev(x) for x, _ in rows[:dist]]
     ws = [todev(w) for _, w in rows]
