@@ -586,13 +586,18 @@ def test_persistent_dependent_chain(rn, kind, n, offset):
     check(host(bufs[k - 1][offset:offset + n]), want[k - 1], "in place last step")
 
 
-def test_persistent_positioned_ring(rn):
-    say("persistent positioned ring")
-    n = 7168
-    ring = Ring(rn, [n] * 9, period=4)
+@pytest.mark.parametrize("kind,n,norms", [("f32", 7168, 9), ("bf16", 1536, 40), ("bf16", 1532, 9),
+                                           ("f32", 1000, 37)])
+def test_persistent_positioned_ring(rn, kind, n, norms):
+    """The persistent launch on a positioned table, every walk it can take
+    (binary32 and bf16 1536: the round walk, over several groups of 16 rows
+    for 40 and 37 norms; bf16 1532: the pipelined walk)."""
+    say(f"persistent positioned ring {kind} n={n} norms={norms}")
+    ring = Ring(rn, [n] * norms, period=4, kind=kind)
+    dt = rn.F32 if kind == "f32" else rn.BF16
     ring.d_pos.fill_(3)
     for rep in range(5):
-        rn.rmsnorm_sequence_persistent(ring.table, 9, wl.EPS, rn.F32, position=ring.position(n))
+        rn.rmsnorm_sequence_persistent(ring.table, norms, wl.EPS, dt, position=ring.position(n))
         sync()
         assert int(ring.d_pos.item()) == (4 + rep) % 4
     _check_ring(ring, {0, 1, 2, 3})
