@@ -953,58 +953,134 @@ __device__ __forceinline__ void round_walk(const rmsn_desc* d, int32_t count, fl
 // threadIdx.x + blockDim.x, ...; the answer is the workgroup's.
 constexpr int kRoundWalk4 = 100;
 constexpr int kRoundWalk16 = 101;
+constexpr int kSpanRows = 1024;  // output ranges published in LDS (16 KB)
 
 __device__ __forceinline__ bool ranges_meet(uintptr_t a, uintptr_t la, uintptr_t b, uintptr_t lb) {
     return a < b + lb && b < a + la;
 }
 
+// Row j's pointers as integers, its byte length, and what the walks need of it.
+template <typename T, bool POS>
+__device__ __forceinline__ void walk_row_facts(const rmsn_desc& dj, uint64_t pos,
+                                               const PosArgs& pa, uintptr_t& bx, uintptr_t& bw,
+                                               uintptr_t& by, uintptr_t& len, bool& fits,
+                                               bool& vec) {
+    const T* x;
+    const T* w;
+    T* y;
+    persistent_ptrs<T, POS>(dj, pos, pa, x, w, y);
+    bx = reinterpret_cast<uintptr_t>(x);
+    bw = reinterpret_cast<uintptr_t>(w);
+    by = reinterpret_cast<uintptr_t>(y);
+    fits = group_fits<T>(x, w, y, dj.n);
+    len = (uintptr_t)(dj.n < 0 ? 0 : dj.n) * sizeof(T);
+    vec = fits && len % 16 == 0 && (bx | bw | by) % 16 == 0;
+}
+
+// What row j finds against row k (k != j): rules of the walks above.
+__device__ __forceinline__ void walk_pair(int32_t j, int32_t k, uintptr_t bx, uintptr_t bw,
+                                          uintptr_t by, uintptr_t len, uintptr_t ky,
+                                          uintptr_t klen, bool& no_pipe, bool& no_round,
+                                          bool& no_round16) {
+    const bool reads = ranges_meet(bx, len, ky, klen) || ranges_meet(bw, len, ky, klen);
+    const bool writes = ranges_meet(by, len, ky, klen);
+    const int32_t r0 = j & ~3, g0 = j & ~15;
+    if (k < j && j - k <= 3 && (reads || (writes && k == j - 1))) no_pipe = true;
+    const bool meet = reads || (writes && k < j);
+    if (k >= r0 && k < r0 + 4 && meet) no_round = true;
+    if (k >= g0 && meet) no_round16 = true;
+}
+
+// How the table is walked (see above): kRoundWalk16 or kRoundWalk4, a block
+// count 1..8 for the pipelined walk (the widest row's), or 0 for row after
+// row. Every thread checks rows threadIdx.x, threadIdx.x + blockDim.x, ...
+// against the rows of their windows (the three rows before, the other rows
+// of their groups of 4 and 16); the answer is the workgroup's. Tables of up to
+// kSpanRows rows first publish every row's output range in LDS, so a check
+// reads 16 bytes of LDS instead of a descriptor from memory.
 template <typename T, bool POS>
 __device__ __forceinline__ int walk_mode(const rmsn_desc* d, int32_t count, uint64_t pos,
-                                         const PosArgs& pa, int* lds_blocks) {
+                                         const PosArgs& pa, int* lds_fold) {
+    __shared__ uintptr_t yspan[kSpanRows][2];  // output start, byte length
     bool no_pipe = false, no_round = false, no_round16 = false;
     int blocks = 1;
-    for (int32_t j = threadIdx.x; j < count; j += blockDim.x) {
-        const rmsn_desc dj = d[j];
-        const T* x;
-        const T* w;
-        T* y;
-        persistent_ptrs<T, POS>(dj, pos, pa, x, w, y);
-        const uintptr_t bx = reinterpret_cast<uintptr_t>(x), bw = reinterpret_cast<uintptr_t>(w);
-        const uintptr_t by = reinterpret_cast<uintptr_t>(y);
-        if (!group_fits<T>(x, w, y, dj.n)) {
-            no_pipe = no_round = no_round16 = true;
-            break;
+    if (count <= kSpanRows) {
+        // at most kSpanRows / 256 rows per thread: their facts stay in registers
+        constexpr int R = kSpanRows / 256;
+        uintptr_t bx[R], bw[R], by[R], len[R];
+        bool live[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int32_t j = threadIdx.x + 256 * r;
+            live[r] = j < count;
+            bool fits = true, vec = true;
+            if (live[r]) {
+                const rmsn_desc dj = d[j];
+                walk_row_facts<T, POS>(dj, pos, pa, bx[r], bw[r], by[r], len[r], fits, vec);
+                yspan[j][0] = by[r];
+                yspan[j][1] = len[r];
+                blocks = max(blocks, (int)((dj.n + 1023) >> 10));
+            }
+            if (!fits) no_pipe = no_round = no_round16 = true;
+            if (!vec) no_round = no_round16 = true;
         }
-        const uintptr_t len = (uintptr_t)dj.n * sizeof(T);
-        if (len % 16 || (bx | bw | by) % 16) no_round = no_round16 = true;
-        blocks = max(blocks, (int)((dj.n + 1023) >> 10));
-        // the three rows before (pipelined walk) and the other rows of the
-        // group of 4 and of 16 (round walks)
-        const int32_t r0 = j & ~3, g0 = j & ~15;
-        for (int32_t k = max(0, min(j - 3, g0)); k < min(count, g0 + 16); ++k) {
-            if (k == j) continue;
-            const rmsn_desc dk = d[k];
-            const T* xk;
-            const T* wk;
-            T* yk;
-            persistent_ptrs<T, POS>(dk, pos, pa, xk, wk, yk);
-            const uintptr_t b = reinterpret_cast<uintptr_t>(yk);
-            const uintptr_t lk = (uintptr_t)(dk.n < 0 ? 0 : dk.n) * sizeof(T);
-            const bool reads = ranges_meet(bx, len, b, lk) || ranges_meet(bw, len, b, lk);
-            const bool writes = ranges_meet(by, len, b, lk);
-            if (k < j && j - k <= 3 && (reads || (writes && k == j - 1))) no_pipe = true;
-            const bool meet = reads || (writes && k < j);
-            if (k >= r0 && k < r0 + 4 && meet) no_round = true;
-            if (k >= g0 && meet) no_round16 = true;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (!live[r]) continue;
+            const int32_t j = threadIdx.x + 256 * r;
+            const int32_t g0 = j & ~15;
+            const int32_t k_end = min(count, g0 + 16);
+#pragma unroll 4
+            for (int32_t k = max(0, min(j - 3, g0)); k < k_end; ++k) {
+                if (k == j) continue;
+                walk_pair(j, k, bx[r], bw[r], by[r], len[r], yspan[k][0], yspan[k][1], no_pipe,
+                          no_round, no_round16);
+            }
+        }
+    } else {
+        for (int32_t j = threadIdx.x; j < count; j += blockDim.x) {
+            const rmsn_desc dj = d[j];
+            uintptr_t bx, bw, by, len;
+            bool fits, vec;
+            walk_row_facts<T, POS>(dj, pos, pa, bx, bw, by, len, fits, vec);
+            if (!fits) {
+                no_pipe = no_round = no_round16 = true;
+                break;
+            }
+            if (!vec) no_round = no_round16 = true;
+            blocks = max(blocks, (int)((dj.n + 1023) >> 10));
+            const int32_t g0 = j & ~15;
+            const int32_t k_end = min(count, g0 + 16);
+            for (int32_t k = max(0, min(j - 3, g0)); k < k_end; ++k) {
+                if (k == j) continue;
+                uintptr_t kx, kw, ky, klen;
+                bool kf, kv;
+                walk_row_facts<T, POS>(d[k], pos, pa, kx, kw, ky, klen, kf, kv);
+                walk_pair(j, k, bx, bw, by, len, ky, klen, no_pipe, no_round, no_round16);
+            }
         }
     }
-    if (threadIdx.x == 0) *lds_blocks = 1;
+    // One exchange for the workgroup: each wavefront folds its lanes (ballots
+    // and a maximum), lane 0 publishes the result, one barrier, every thread
+    // folds the four.
+    const uint32_t flags = (__ballot(no_pipe) ? 1u : 0u) | (__ballot(no_round) ? 2u : 0u) |
+                           (__ballot(no_round16) ? 4u : 0u);
+    int wmax = blocks;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) wmax = max(wmax, __shfl_xor(wmax, o, 64));
+    if ((threadIdx.x & 63) == 0) lds_fold[threadIdx.x >> 6] = (int)(flags << 8) | wmax;
     __syncthreads();
-    atomicMax(lds_blocks, blocks);
-    const bool round16_ok = !__syncthreads_or(no_round16);
-    const bool round_ok = !__syncthreads_or(no_round);
-    const bool pipe_ok = !__syncthreads_or(no_pipe);
-    return round16_ok ? kRoundWalk16 : round_ok ? kRoundWalk4 : pipe_ok ? *lds_blocks : 0;
+    uint32_t all_flags = 0;
+    int all_blocks = 1;
+    for (int wv = 0; wv < (int)(blockDim.x >> 6); ++wv) {
+        all_flags |= (uint32_t)lds_fold[wv] >> 8;
+        all_blocks = max(all_blocks, lds_fold[wv] & 0xFF);
+    }
+    if (!(all_flags & 4u)) return kRoundWalk16;
+    if (!(all_flags & 2u)) return kRoundWalk4;
+    if (!(all_flags & 1u)) return all_blocks;
+    return 0;
 }
 
 template <typename T, bool POS, int QM>
@@ -1073,14 +1149,14 @@ __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __
                                                              PosArgs pa) {
     __shared__ float lds4[4];
     __shared__ float lds8[2][4];
-    __shared__ int lds_blocks;
+    __shared__ int lds_fold[4];
     uint64_t pos = 0;
     if (POS) {
         const uint64_t per = (uint64_t)pa.period;
         const uint64_t raw = (uint64_t)*pa.d_pos;
         pos = raw < per ? raw : raw % per;
     }
-    switch (walk_mode<T, POS>(d, count, pos, pa, &lds_blocks)) {
+    switch (walk_mode<T, POS>(d, count, pos, pa, lds_fold)) {
         case kRoundWalk16: round_walk<T, POS, 4>(d, count, eps, pos, pa); break;
         case kRoundWalk4: round_walk<T, POS, 1>(d, count, eps, pos, pa); break;
 #define RMSN_CASE(Q) \
