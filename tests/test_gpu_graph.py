@@ -721,7 +721,7 @@ def test_persistent_table_with_a_row_the_pipeline_cannot_take(rn, kind, odd):
 
 
 @pytest.mark.parametrize("kind,n", [("f32", 2048), ("bf16", 2048), ("bf16", 2044)])
-@pytest.mark.parametrize("dist", [1, 2, 3, 4, 5, 8, 16, 17])
+@pytest.mark.parametrize("dist", [1, 2, 3, 4, 5, 8, 16, 17, 64, 65])
 def test_persistent_dependency_at_distance(rn, kind, n, dist):
     """Row j reads the output of row j - dist (rows 0 .. dist-1 read fresh
     inputs). Distances 1 to 3 must take the row-after-row walk; 4 to 15 the
