@@ -800,3 +800,30 @@ def test_persistent_row_reads_what_a_later_row_overwrites(rn, kind, n):
     sync()
     for j in range(k):
         check(host(ys[j]), want[j], f"row {j}")
+
+
+@pytest.mark.parametrize("dist", [0, 2, 5])
+def test_persistent_table_beyond_the_lds_check(rn, dist):
+    """More than 1024 rows: the launch-time check reads the descriptors from
+    memory instead of LDS. 1100 independent rows (dist 0: the round walk) or
+    with row j reading row j - dist's output (2: row after row; 5: the round
+    walk with a barrier every 4 rows)."""
+    import torch
+    say(f"persistent 1100-row table, dependency distance {dist}")
+    k, n = 1100, 64
+    rows = _rows_of("f32", [n] * k, 7600 + dist)
+    xs = [to_dev_f32(x) for x, _ in rows]
+    ws = [to_dev_f32(w) for _, w in rows]
+    ys = [torch.full((n,), float("nan"), dtype=torch.float32, device=dev()) for _ in range(k)]
+    want = []
+    for j in range(k):
+        if dist and j >= dist:
+            xs[j] = ys[j - dist]
+            want.append(oracle.row_f32(want[j - dist], rows[j][1], wl.EPS))
+        else:
+            want.append(oracle.row_f32(rows[j][0], rows[j][1], wl.EPS))
+    table, widths = rn.make_table(list(zip(xs, ws, ys)))
+    rn.rmsnorm_sequence_persistent(table, k, wl.EPS, rn.F32)
+    sync()
+    for j in range(k):
+        assert_bits_f32(f32_host(ys[j]), want[j], f"row {j}")
