@@ -4,7 +4,7 @@ sequence, bit for bit against the rows applied in order on the CPU.
 Each table draws a dtype, a row count, a width class (multiples of 8, 4 mod
 8, arbitrary with a few beyond 8192) and per row a width of that class,
 element offsets, and where its x, w and y live: fresh buffers, or x reading
-what an earlier row wrote (at distances of 4 or more, or of 1 or more), x
+what an earlier row wrote (at distances of 4-20, 16-40, or 1 and more), x
 reading a buffer a later row overwrites, y rewriting the row before's
 output. The CPU model keeps every buffer's contents and applies the
 oracle row by row in table order -- the semantics of the launch sequence --
@@ -22,7 +22,7 @@ from gpu_util import dev, say
 
 pytestmark = pytest.mark.gpu
 
-TABLES = 40
+TABLES = 48
 
 
 @pytest.fixture(scope="module")
@@ -49,10 +49,10 @@ def _width(g, cls):
 def _table(g):
     """A list of rows (x, w, y), each a (buffer, offset, n) slice, and the
     buffer sizes. The table's kind decides its dependencies: none, only at
-    distances of 4 rows or more, or anywhere (distances from 1)."""
+    distances of 4 to 20 rows, of 16 to 40 rows, or anywhere (from 1)."""
     count = int(g.choice([1, 2, 3, 5, 9, 16, 17, 33, 64]))
     aligned = g.random() < 0.7
-    deps = str(g.choice(["none", "none", "far", "far", "any"]))
+    deps = str(g.choice(["none", "none", "far", "far", "farther", "any"]))
     cls = str(g.choice(["vec", "vec", "quad", "any"]))
     rate = float(g.choice([0.05, 0.15, 0.3]))
     sizes, rows = [], []
@@ -63,11 +63,11 @@ def _table(g):
         return (len(sizes) - 1, off, n)
 
     shared_n = _width(g, cls) if g.random() < 0.5 else None
-    lo = 4 if deps == "far" else 1
+    lo, hi = {"far": (4, 20), "farther": (16, 40)}.get(deps, (1, 20))
     for j in range(count):
         r = g.random()
         if deps != "none" and j >= lo and r < rate:
-            d = int(g.integers(lo, min(j, 20) + 1))        # read an earlier row's output
+            d = int(g.integers(lo, min(j, hi) + 1))        # read an earlier row's output
             x = rows[j - d][2]
             n = x[2]
         elif deps == "any" and j > 0 and r < rate + 0.05:
