@@ -118,9 +118,9 @@ def bench_prefill(rn, torch, np, wl, steps, warmup):
     # the timed region: `steps` launches, rotating buffer sets
     t_ms = elapsed_ms(step, steps)
     us = 1000.0 * t_ms / steps
-    # per-rep spread over 5 further bursts
+    # per-rep spread over 30 further bursts of `steps` launches
     reps = []
-    for _ in range(5):
+    for _ in range(30):
         reps.append(1000.0 * elapsed_ms(step, steps) / steps)
     # warm arms: one buffer set, so the last-level cache may hold part of it;
     # with the automatic (streaming) plan and with default caching forced
@@ -186,7 +186,7 @@ def bench_prefill_only(rn, torch, np, wl, steps, warmup):
             "plan": rn.plan_query(rn.BF16, rows, n)}
 
 
-def graph_us_per_launch(torch, fn, per_graph=100, replays=20, reps=5):
+def graph_us_per_launch(torch, fn, per_graph=100, replays=20, reps=30):
     """Per-launch device time of `fn` (one launch on the given stream) with no
     host in the loop: `per_graph` launches captured in one graph, replayed
     `replays` times, HIP events around the replays; `reps` repetitions. Each
