@@ -46,6 +46,10 @@
  *  - In-place (y == x) is allowed: each row is read completely before any of
  *    its outputs is written.
  *  - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *  - Threads: every entry point may be called from several host threads at
+ *    once; the error message is per thread and the options are process-wide.
+ *    One graph handle must not be updated, launched or destroyed by two
+ *    threads at the same time (the handle is not locked).
  */
 #ifndef RMSNORM_H
 #define RMSNORM_H
