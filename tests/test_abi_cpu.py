@@ -396,3 +396,33 @@ def test_options_roundtrip_and_force_paths(rn):
         rn.set_option(rn.OPT_ROWS_PER_BLOCK, 0)
         rn.set_option(rn.OPT_STREAMING, -1)
         rn.set_option(rn.OPT_SPLIT_LOADS, 0)
+
+
+def test_error_messages_are_per_thread(rn):
+    """Several host threads rejecting different arguments at once: each reads
+    back its own reason (the message is kept per thread)."""
+    import threading
+    lib = rn.lib()
+    errors = {}
+    barrier = threading.Barrier(4)
+
+    def worker(k):
+        barrier.wait()
+        for _ in range(200):
+            if k % 2 == 0:   # width 0
+                st = lib.rmsnorm_batched_rows(0, 16, 0, 16, 16, 0, 1, 0, ctypes.c_float(1e-6), None)
+                want = "n must be"
+            else:            # negative eps
+                st = lib.rmsnorm_batched_rows(0, 16, 8, 16, 64, 8, 1, 8, ctypes.c_float(-1.0), None)
+                want = "eps must be"
+            msg = lib.rmsnorm_last_error().decode()
+            if st != 1 or want not in msg:
+                errors[k] = (st, msg)
+                return
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
