@@ -426,3 +426,14 @@ def test_error_messages_are_per_thread(rn):
     for t in threads:
         t.join()
     assert not errors, errors
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU only; asking for more exits with status 2 and
+    says so, before touching a GPU."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
