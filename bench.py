@@ -485,7 +485,7 @@ def main():
                          "profiling runs; the default runs them all)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+        print(f"bench.py: this benchmark runs on one GPU only; --gpus {args.gpus} is not "
               "supported (rows shard across GPUs with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)

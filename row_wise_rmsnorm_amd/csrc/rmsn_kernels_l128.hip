@@ -3,7 +3,7 @@
 // Lecture 04 "Launch Geometry: Grids, Occupancy, and 327 Norms per Token",
 // section 2.1: the kernel's sum of squares runs on exactly 128 threads, the
 // elementwise apply on the whole (wider) block, and only the first of the two
-// decides the bits. This build computes that association ("R128"):
+// decides the bits. This library variant computes that association ("R128"):
 //   lane chains  p[l] = fmaf(x[d], x[d], p[l]), d = l, l+128, ... (l < 128)
 //   group trees  four 32-lane groups (the lecture's four warps), descending
 //                halving 16, 8, 4, 2, 1

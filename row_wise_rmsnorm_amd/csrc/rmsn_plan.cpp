@@ -143,7 +143,7 @@ int set_option(int key, int value) {
     if (key == RMSN_OPT_APPLY_THREADS) {
         if (kAssocLanes != 128) {
             set_error("rmsnorm_set_option: the apply width is an option of the 128-lane build "
-                      "only (this build computes %d lanes)", kAssocLanes);
+                      "only (this library computes %d lanes)", kAssocLanes);
             return RMSN_EINVAL;
         }
         if (!valid_apply_threads(value)) {

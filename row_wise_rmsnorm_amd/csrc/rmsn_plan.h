@@ -8,7 +8,7 @@
 
 #include "rmsnorm.h"
 
-// Lane chains of the association this build computes: 256 (R256), or 128 for
+// Lane chains of the association this library variant computes: 256 (R256), or 128 for
 // the build that reproduces the 128-thread sum of Lecture 04 section 2.1
 // (compiled with -DRMSN_LANES=128; its only layout is one workgroup per row
 // whose first 128 threads sum and whose every thread applies).
