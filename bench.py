@@ -21,6 +21,7 @@ cache defeated by rotating over 4 buffer sets (940 MB). Also reported:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D]
        python bench.py --profile-kernels     (short run for rocprofv3 counters)
+       python bench.py --profile-decode      (the same, decode step: eager + persistent)
 """
 import argparse
 import hashlib
@@ -470,6 +471,23 @@ def profile_kernels(rn, torch, np, wl):
                       "copy_bytes_each": src.numel() * 4, "copies": 5}), flush=True)
 
 
+def profile_decode(rn, torch, np, wl):
+    """Short run for counter collection on the decode step: one eager step
+    (327 launches) and three persistent launches of the same table."""
+    rows = wl.decode()
+    dev = torch.device("cuda", 0)
+    xs = [torch.from_numpy(x).to(dev) for x, _ in rows]
+    ws = [torch.from_numpy(w).to(dev) for _, w in rows]
+    ys = [torch.empty_like(t) for t in xs]
+    table, widths = rn.make_table(list(zip(xs, ws, ys)))
+    rn.rmsnorm_sequence_eager(table, widths, float(wl.EPS), rn.F32)
+    for _ in range(3):
+        rn.rmsnorm_sequence_persistent(table, len(widths), float(wl.EPS), rn.F32)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_decode": "done", "eager_launches": len(widths),
+                      "persistent_launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,6 +498,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="short decode-step run for counter collection")
     ap.add_argument("--sections", default="prefill,single,batch64,decode",
                     help="comma list of prefill,single,batch64,decode,positioned (for "
                          "profiling runs; the default runs them all)")
@@ -499,6 +519,9 @@ def main():
     torch.cuda.set_device(0)
     if args.profile_kernels:
         profile_kernels(rn, torch, np, wl)
+        return
+    if args.profile_decode:
+        profile_decode(rn, torch, np, wl)
         return
 
     sections = set(args.sections.split(","))
