@@ -109,7 +109,9 @@ int rmsnorm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, f
  * 16-byte loads (SPLIT) from 64 MiB; rows under 1 KB run one wavefront per
  * row (WAVE); rows of 1-4 KB run WAVE under 32 MiB and SPLIT from there.
  * Rows that are not vector-aligned run BLOCK / STREAM. All give the same
- * bits. */
+ * bits. A dispatch counts its grid in work-items as a 32-bit number, so a
+ * batch needing more than 2^32 - 1 threads (from about 4 million rows) is
+ * issued as consecutive launches of the same layout on `stream`. */
 int rmsnorm_batched_rows(int dtype, const void* x, int64_t x_row_stride, const void* w, void* y,
                          int64_t y_row_stride, int64_t rows, int64_t n, float eps, void* stream);
 
@@ -265,7 +267,8 @@ typedef struct rmsn_plan_info {
                                 streaming); SPLIT: chunks one wavefront holds     */
     int32_t rows_per_block;  /* rows (wavefronts) per workgroup on WAVE, else 1   */
     int32_t block;           /* threads per workgroup                             */
-    int64_t grid;            /* workgroups                                        */
+    int64_t grid;            /* workgroups of the whole batch (beyond 2^32 - 1
+                                threads it goes as several launches)              */
     int32_t streaming;       /* WAVE / SPLIT: 1 = non-temporal loads of x and
                                 stores of y                                       */
     int32_t loads;           /* SPLIT: 16-byte loads per lane (1 KB slices per

@@ -65,9 +65,23 @@ int run_rows(int dtype, const void* x, int64_t xs, const void* w, void* y, int64
     Plan p;
     st = make_plan(dtype, rows, n, rows_alignment(dtype, x, xs, w, y, ys), &p);
     if (st != RMSN_OK) return st;
-    const hipError_t e =
-        launch_rows(p, x, xs, w, y, ys, rows, (int)n, eps, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? RMSN_OK : hip_fail("kernel launch", e);
+    // A batch of more rows than one launch can hold goes as consecutive
+    // launches of the plan's layout (a row's bits do not depend on the launch
+    // it is in). Each piece starts a whole number of rows further on, which
+    // keeps the alignment the plan assumed.
+    const int64_t es = elem_bytes(dtype);
+    const int64_t most = rows_per_launch(p);
+    for (int64_t r0 = 0; r0 < rows; r0 += most) {
+        const int64_t piece = rows - r0 < most ? rows - r0 : most;
+        Plan q = p;
+        q.grid = (piece + p.rows_per_block - 1) / p.rows_per_block;
+        const hipError_t e = launch_rows(
+            q, static_cast<const char*>(x) + r0 * xs * es, xs, w,
+            static_cast<char*>(y) + r0 * ys * es, ys, piece, (int)n, eps,
+            static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail("kernel launch", e);
+    }
+    return RMSN_OK;
 }
 
 int plan_sequence(int dtype, const int64_t* widths, int32_t count, std::vector<Plan>* plans) {

@@ -54,7 +54,8 @@ hipError_t launch_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out,
                             hipStream_t stream) {
     if (count <= 0) return hipSuccess;
     const int64_t blocks = (count + 511) / 512;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    // a dispatch counts its grid in work-items as a 32-bit number
+    if (blocks * 256 > 0xFFFFFFFFll) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k_diag_bf16, dim3((unsigned)blocks), dim3(256), 0, stream, first_bits, count,
                        out);
     return hipGetLastError();
@@ -64,7 +65,7 @@ hipError_t launch_diag_inverse(uint32_t first_bits, int64_t count, int n, float 
                                float* inv_out, hipStream_t stream) {
     if (count <= 0) return hipSuccess;
     const int64_t blocks = (count + 255) / 256;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (blocks * 256 > 0xFFFFFFFFll) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k_diag_inverse, dim3((unsigned)blocks), dim3(256), 0, stream, first_bits,
                        count, n, eps, r_out, inv_out);
     return hipGetLastError();

@@ -58,6 +58,14 @@ struct Plan {
 };
 
 inline int elem_bytes(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
+// Rows one launch of plan p can hold. A dispatch counts its grid in
+// work-items as a 32-bit number, so workgroups * block stays below 2^32 (and
+// workgroups below 2^31); a batch beyond this goes as consecutive launches.
+inline int64_t rows_per_launch(const Plan& p) {
+    int64_t groups = 0xFFFFFFFFll / (p.block > 0 ? p.block : 1);
+    if (groups > 0x7FFFFFFFll) groups = 0x7FFFFFFFll;
+    return groups * (p.rows_per_block > 0 ? p.rows_per_block : 1);
+}
 // Bytes one lane loads per 256-element chunk on the WAVE path: four elements.
 inline int vec_bytes(int dtype) { return 4 * elem_bytes(dtype); }
 // 1 KB slices of a row of width n (the last one may be partial).
