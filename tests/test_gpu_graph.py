@@ -827,3 +827,44 @@ def test_persistent_table_beyond_the_lds_check(rn, dist):
     sync()
     for j in range(k):
         assert_bits_f32(f32_host(ys[j]), want[j], f"row {j}")
+
+
+@pytest.mark.parametrize("arm", ["graph", "eager", "persistent"])
+def test_rows_with_out_of_range_widths_write_nothing(rn, desc_path, arm):
+    """A descriptor whose width, rewritten in the device table, is outside
+    [1, 2^24] (0, negative, 2^24 + 1) makes its row write nothing; the rows
+    around it are still exact. The host widths stay the valid capture-time
+    ones, as a caller's would."""
+    import struct
+    import torch
+    say(f"out-of-range widths ({arm}, {desc_path})")
+    widths = [512, 1536, 7168, 512, 64, 7168, 1024]
+    bad = {1: 0, 3: -3, 4: (1 << 24) + 1}
+    rows = _rows_of("f32", widths, 8100)
+    xs = [to_dev_f32(x) for x, _ in rows]
+    ws = [to_dev_f32(w) for _, w in rows]
+    ys = [torch.full((n,), float("nan"), dtype=torch.float32, device=dev()) for n in widths]
+    table, host_widths = rn.make_table(list(zip(xs, ws, ys)))
+    g = rn.SequenceGraph(table, host_widths, wl.EPS, rn.F32) if arm == "graph" else None
+    for i, n in bad.items():        # the n field of record i: bytes 24..31
+        table[32 * i + 24:32 * i + 32].copy_(torch.frombuffer(bytearray(struct.pack("<q", n)),
+                                                                dtype=torch.uint8))
+    sync()
+    for rep in range(2):
+        for y in ys:
+            y.fill_(float("nan"))
+        if arm == "graph":
+            g.launch()
+        elif arm == "eager":
+            rn.rmsnorm_sequence_eager(table, host_widths, wl.EPS, rn.F32)
+        else:
+            rn.rmsnorm_sequence_persistent(table, len(widths), wl.EPS, rn.F32)
+        sync()
+        for i, (x, w) in enumerate(rows):
+            got = f32_host(ys[i])
+            if i in bad:
+                assert np.isnan(got).all(), f"rep {rep}: row {i} (n={bad[i]}) wrote"
+            else:
+                assert_bits_f32(got, oracle.row_f32(x, w, wl.EPS), f"rep {rep} row {i}")
+    if g is not None:
+        g.destroy()
