@@ -48,7 +48,11 @@ class _Position(ctypes.Structure):
 
 def _position(position):
     """(d_pos int64 device tensor, x_pitch bytes, y_pitch bytes, period) -> struct."""
+    import torch
     d_pos, x_pitch, y_pitch, period = position
+    _device_tensor(d_pos, "d_pos")
+    if d_pos.dtype != torch.int64 or d_pos.numel() < 1:
+        raise ValueError("d_pos must be an int64 device tensor of at least one element")
     return _Position(ctypes.c_void_p(d_pos.data_ptr()), int(x_pitch), int(y_pitch), int(period))
 
 
@@ -125,10 +129,18 @@ def _check(status):
     return status
 
 
-def _stream_ptr(stream):
+def _stream_ptr(stream, device=None):
+    """The HIP stream handle: `stream`, else the current stream of `device`
+    (of the current device when None)."""
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
+    s = torch.cuda.current_stream(device) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on(device):
+    """Context that makes `device` current, so the library launches there."""
+    import torch
+    return torch.cuda.device(device)
 
 
 def _dtype_code(t):
@@ -141,7 +153,8 @@ def _dtype_code(t):
 
 
 def _device_tensor(t, name):
-    if not t.is_cuda:
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     return t
 
@@ -150,63 +163,119 @@ def _out_like(x, out):
     import torch
     if out is None:
         return torch.empty_like(x)
+    _device_tensor(out, "out")
     if out.shape != x.shape or out.dtype != x.dtype or out.device != x.device:
         raise ValueError("out must match x in shape, dtype and device")
     return out
 
 
-def rmsnorm_f32(x, w, eps, out=None, stream=None):
-    """One binary32 row (1-D contiguous tensors)."""
-    _device_tensor(x, "x"), _device_tensor(w, "w")
-    if x.dim() != 1 or not x.is_contiguous() or not w.is_contiguous():
-        raise ValueError("1-D contiguous tensors expected")
+def _weight(x, w, n):
+    """w must be one contiguous row of n elements of x's dtype on x's device:
+    the kernels read n elements of that type from it."""
+    _device_tensor(w, "w")
+    if w.dtype != x.dtype or w.device != x.device:
+        raise ValueError(f"w must have x's dtype and device (x: {x.dtype} on {x.device}, "
+                         f"w: {w.dtype} on {w.device})")
+    if w.dim() != 1 or w.numel() != n or not w.is_contiguous():
+        raise ValueError(f"w must be a contiguous 1-D tensor of {n} elements, got shape "
+                         f"{tuple(w.shape)}")
+    return w
+
+
+def _single_row(x, w, out, dtype):
+    import torch
+    _device_tensor(x, "x")
+    if x.dtype != dtype:
+        raise TypeError(f"{dtype} tensor expected, got {x.dtype}")
+    if x.dim() != 1 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 1-D tensor")
+    _weight(x, w, x.numel())
     y = _out_like(x, out)
-    _check(_lib.rmsnorm_f32(x.data_ptr(), w.data_ptr(), y.data_ptr(), x.numel(),
-                            float(eps), _stream_ptr(stream)))
+    if not y.is_contiguous():
+        raise ValueError("out must be contiguous")
+    return y
+
+
+def rmsnorm_f32(x, w, eps, out=None, stream=None):
+    """One binary32 row (1-D contiguous float32 tensors of one width)."""
+    import torch
+    y = _single_row(x, w, out, torch.float32)
+    with _on(x.device):
+        _check(_lib.rmsnorm_f32(x.data_ptr(), w.data_ptr(), y.data_ptr(), x.numel(),
+                                float(eps), _stream_ptr(stream, x.device)))
     return y
 
 
 def rmsnorm_bf16(x, w, eps, out=None, stream=None):
-    """One bf16 row (1-D contiguous tensors)."""
-    _device_tensor(x, "x"), _device_tensor(w, "w")
-    if x.dim() != 1 or not x.is_contiguous() or not w.is_contiguous():
-        raise ValueError("1-D contiguous tensors expected")
-    y = _out_like(x, out)
-    _check(_lib.rmsnorm_bf16(x.data_ptr(), w.data_ptr(), y.data_ptr(), x.numel(),
-                             float(eps), _stream_ptr(stream)))
+    """One bf16 row (1-D contiguous bfloat16 tensors of one width)."""
+    import torch
+    y = _single_row(x, w, out, torch.bfloat16)
+    with _on(x.device):
+        _check(_lib.rmsnorm_bf16(x.data_ptr(), w.data_ptr(), y.data_ptr(), x.numel(),
+                                 float(eps), _stream_ptr(stream, x.device)))
     return y
 
 
 def rmsnorm_batched_rows(x, w, eps, out=None, stream=None):
     """Every row of a 2-D tensor (unit stride along a row) against w."""
-    _device_tensor(x, "x"), _device_tensor(w, "w")
-    if x.dim() != 2 or x.stride(1) != 1 or not w.is_contiguous():
+    _device_tensor(x, "x")
+    code = _dtype_code(x)
+    if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("2-D tensor with unit stride along rows expected")
+    rows, n = x.shape
+    _weight(x, w, n)
     y = _out_like(x, out)
     if y.stride(1) != 1:
         raise ValueError("out must have unit stride along rows")
-    rows, n = x.shape
     # a single row's stride is never used; torch may report 0 for a size-1 axis
     xs = x.stride(0) if rows > 1 else n
     ys = y.stride(0) if rows > 1 else n
-    _check(_lib.rmsnorm_batched_rows(_dtype_code(x), x.data_ptr(), xs, w.data_ptr(),
-                                     y.data_ptr(), ys, rows, n, float(eps), _stream_ptr(stream)))
+    with _on(x.device):
+        _check(_lib.rmsnorm_batched_rows(code, x.data_ptr(), xs, w.data_ptr(), y.data_ptr(), ys,
+                                         rows, n, float(eps), _stream_ptr(stream, x.device)))
     return y
 
 
 def make_table(rows, device=None):
-    """Device descriptor table from a list of (x, w, y) GPU tensors (each
-    1-D); returns (table tensor, host widths list)."""
+    """Device descriptor table from a list of (x, w, y) GPU tensors: each
+    1-D and contiguous, one dtype and one device for the whole table, and
+    within a row one width. Returns (table tensor, host widths list). The
+    table holds raw pointers: the tensors must outlive every launch that
+    reads it."""
     import struct
     import torch
+    if len(rows) == 0:
+        raise ValueError("a table needs at least one row")
+    first = rows[0][0]
+    _device_tensor(first, "x")
+    _dtype_code(first)
     buf = bytearray()
     widths = []
-    for x, w, y in rows:
+    for i, (x, w, y) in enumerate(rows):
+        for name, t in (("x", x), ("w", w), ("y", y)):
+            _device_tensor(t, f"row {i} {name}")
+            if t.dtype != first.dtype or t.device != first.device:
+                raise ValueError(f"row {i} {name}: every tensor of a table must be "
+                                 f"{first.dtype} on {first.device}")
+            if t.dim() != 1 or not t.is_contiguous() or t.numel() != x.numel():
+                raise ValueError(f"row {i} {name}: contiguous 1-D tensors of one width "
+                                 "expected")
         buf += struct.pack("<QQQq", x.data_ptr(), w.data_ptr(), y.data_ptr(), x.numel())
         widths.append(int(x.numel()))
     host = torch.frombuffer(buf, dtype=torch.uint8)
-    dev = device if device is not None else rows[0][0].device
+    dev = device if device is not None else first.device
     return host.to(dev), widths
+
+
+def _table(table, count):
+    """A device descriptor table of at least `count` records (see make_table)."""
+    import torch
+    _device_tensor(table, "table")
+    if table.dtype != torch.uint8 or not table.is_contiguous() or \
+            table.numel() < DESC_BYTES * int(count):
+        raise ValueError(f"table must be a contiguous uint8 device tensor of at least "
+                         f"{DESC_BYTES} * {int(count)} bytes")
+    return ctypes.c_void_p(table.data_ptr())
 
 
 def _widths_array(widths):
@@ -220,21 +289,25 @@ def rmsnorm_sequence_eager(table, widths, eps, dtype, stream=None, position=None
     for a positioned sequence (rows taken at the device-resident position,
     which the sequence then advances by one)."""
     arr = _widths_array(widths)
-    if position is None:
-        _check(_lib.rmsnorm_sequence_eager(int(dtype), ctypes.c_void_p(table.data_ptr()), arr,
-                                           len(widths), float(eps), _stream_ptr(stream)))
-    else:
-        pos = _position(position)
-        _check(_lib.rmsnorm_sequence_eager_positioned(
-            int(dtype), ctypes.c_void_p(table.data_ptr()), arr, len(widths), float(eps),
-            ctypes.byref(pos), _stream_ptr(stream)))
+    tp = _table(table, len(widths))
+    with _on(table.device):
+        if position is None:
+            _check(_lib.rmsnorm_sequence_eager(int(dtype), tp, arr, len(widths), float(eps),
+                                               _stream_ptr(stream, table.device)))
+        else:
+            pos = _position(position)
+            _check(_lib.rmsnorm_sequence_eager_positioned(
+                int(dtype), tp, arr, len(widths), float(eps), ctypes.byref(pos),
+                _stream_ptr(stream, table.device)))
 
 
 def rmsnorm_sequence_persistent(table, count, eps, dtype, stream=None, position=None):
     """All `count` norms of the table, in order, in one kernel launch."""
+    tp = _table(table, count)
     pos = ctypes.byref(_position(position)) if position is not None else None
-    _check(_lib.rmsnorm_sequence_persistent(int(dtype), ctypes.c_void_p(table.data_ptr()),
-                                            int(count), float(eps), pos, _stream_ptr(stream)))
+    with _on(table.device):
+        _check(_lib.rmsnorm_sequence_persistent(int(dtype), tp, int(count), float(eps), pos,
+                                                _stream_ptr(stream, table.device)))
 
 
 class SequenceGraph:
@@ -243,18 +316,22 @@ class SequenceGraph:
     RMSN_ECAPTURE."""
 
     def __init__(self, table, widths, eps, dtype, position=None):
+        self._h = ctypes.c_void_p()
+        tp = _table(table, len(widths))
         self._table = table  # keep the descriptor table alive with the graph
         self._position = position
+        self._device = table.device
         arr = _widths_array(widths)
         h = ctypes.c_void_p()
-        if position is None:
-            st = _lib.rmsnorm_sequence_graph_create(int(dtype), ctypes.c_void_p(table.data_ptr()),
-                                                    arr, len(widths), float(eps), ctypes.byref(h))
-        else:
-            pos = _position(position)
-            st = _lib.rmsnorm_sequence_graph_create_positioned(
-                int(dtype), ctypes.c_void_p(table.data_ptr()), arr, len(widths), float(eps),
-                ctypes.byref(pos), ctypes.byref(h))
+        with _on(table.device):
+            if position is None:
+                st = _lib.rmsnorm_sequence_graph_create(int(dtype), tp, arr, len(widths),
+                                                        float(eps), ctypes.byref(h))
+            else:
+                pos = _position(position)
+                st = _lib.rmsnorm_sequence_graph_create_positioned(
+                    int(dtype), tp, arr, len(widths), float(eps), ctypes.byref(pos),
+                    ctypes.byref(h))
         if st not in (RMSN_OK, RMSN_ECAPTURE):
             raise RmsnormError(st, last_error())
         self.status = st
@@ -262,13 +339,15 @@ class SequenceGraph:
         self._h = h
 
     def launch(self, stream=None):
-        _check(_lib.rmsnorm_sequence_graph_launch(self._h, _stream_ptr(stream)))
+        with _on(self._device):
+            _check(_lib.rmsnorm_sequence_graph_launch(self._h, _stream_ptr(stream, self._device)))
 
     def update(self, widths):
         """New capture-time widths; returns (status, recaptured)."""
         arr = _widths_array(widths)
         rec = ctypes.c_int()
-        st = _lib.rmsnorm_sequence_graph_update(self._h, arr, len(widths), ctypes.byref(rec))
+        with _on(self._device):
+            st = _lib.rmsnorm_sequence_graph_update(self._h, arr, len(widths), ctypes.byref(rec))
         if st not in (RMSN_OK, RMSN_ECAPTURE):
             raise RmsnormError(st, last_error())
         return st, bool(rec.value)
@@ -320,13 +399,30 @@ def get_option(key):
 
 def diag_bf16(first_bits, count, out, stream=None):
     """Step 8's bf16 narrowing of the kernels over consecutive bit patterns
-    (diagnostic); `out`: a device tensor of at least `count` 2-byte elements."""
-    _check(_lib.rmsnorm_diag_bf16(int(first_bits), int(count), ctypes.c_void_p(out.data_ptr()),
-                                  _stream_ptr(stream)))
+    (diagnostic); `out`: a contiguous device tensor of 2-byte elements, at
+    least `count` of them."""
+    _device_tensor(out, "out")
+    if out.element_size() != 2 or not out.is_contiguous() or out.numel() < int(count):
+        raise ValueError(f"out must be a contiguous device tensor of at least {int(count)} "
+                         "2-byte elements")
+    with _on(out.device):
+        _check(_lib.rmsnorm_diag_bf16(int(first_bits), int(count),
+                                      ctypes.c_void_p(out.data_ptr()),
+                                      _stream_ptr(stream, out.device)))
 
 
 def diag_inverse(first_bits, count, n, eps, r_out, inv_out, stream=None):
-    """Steps 4-7 of the kernels over consecutive bit patterns (diagnostic)."""
-    _check(_lib.rmsnorm_diag_inverse(int(first_bits), int(count), int(n), float(eps),
-                                     ctypes.c_void_p(r_out.data_ptr()),
-                                     ctypes.c_void_p(inv_out.data_ptr()), _stream_ptr(stream)))
+    """Steps 4-7 of the kernels over consecutive bit patterns (diagnostic);
+    r_out, inv_out: contiguous float32 device tensors of at least `count`
+    elements."""
+    import torch
+    for name, t in (("r_out", r_out), ("inv_out", inv_out)):
+        _device_tensor(t, name)
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < int(count):
+            raise ValueError(f"{name} must be a contiguous float32 device tensor of at least "
+                             f"{int(count)} elements")
+    with _on(r_out.device):
+        _check(_lib.rmsnorm_diag_inverse(int(first_bits), int(count), int(n), float(eps),
+                                         ctypes.c_void_p(r_out.data_ptr()),
+                                         ctypes.c_void_p(inv_out.data_ptr()),
+                                         _stream_ptr(stream, r_out.device)))

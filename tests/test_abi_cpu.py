@@ -437,3 +437,16 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_binding_refuses_host_tensors(rn):
+    """The binding takes device tensors only; a host tensor is refused before
+    the library is called (there is no CPU path)."""
+    import torch
+    x = torch.ones(8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rn.rmsnorm_f32(x, x, 1e-6)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rn.rmsnorm_batched_rows(x.view(2, 4), x[:4], 1e-6)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rn.make_table([(x, x, x)])
