@@ -115,6 +115,22 @@ int rmsnorm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, f
 int rmsnorm_batched_rows(int dtype, const void* x, int64_t x_row_stride, const void* w, void* y,
                          int64_t y_row_stride, int64_t rows, int64_t n, float eps, void* stream);
 
+/* rmsnorm_batched_rows with a caller-provided device workspace, which lets
+ * few wide rows (at most 64 rows of at least 64 KB) spread over many CUs:
+ * RMSN_PATH_WIDE, two launches on
+ * `stream`, the group totals of the association passing through the
+ * workspace (Lecture 04 section 1: match the grid to the machine; section
+ * 2.1: the association, and so the bits, stay those of every other path). Any other batch runs exactly as rmsnorm_batched_rows and leaves the
+ * workspace untouched. workspace: DEVICE memory of at least the bytes
+ * rmsnorm_workspace_query reports, 4-byte aligned, overlapping none of x, w,
+ * y; its contents on entry do not matter and on return are unspecified. Calls
+ * that may overlap in time need distinct workspaces. Errors as
+ * rmsnorm_batched_rows, plus RMSN_EINVAL for a workspace the launch needs
+ * that is NULL, too small, misaligned or overlapping the rows. */
+int rmsnorm_batched_rows_ws(int dtype, const void* x, int64_t x_row_stride, const void* w,
+                            void* y, int64_t y_row_stride, int64_t rows, int64_t n, float eps,
+                            void* workspace, int64_t workspace_bytes, void* stream);
+
 /* The norms of a decode step, in order, issued as `count` dependent launches
  * on `stream` (the eager arm). d_table: DEVICE array of count descriptors.
  * h_widths: HOST array of count widths that size each launch (the same plan
@@ -236,8 +252,13 @@ const char* rmsnorm_last_error(void);
  *   RMSN_PATH_BLOCK:  one 256-thread workgroup per row, wavefront g holding
  *                     the 64 lane chains of group g in registers; any element
  *                     alignment, n <= 8192.
- *   RMSN_PATH_STREAM: as BLOCK but streaming the row twice (sum, then apply)
- *                     instead of holding it; any n up to 2^24.
+ *   RMSN_PATH_STREAM: one 256-thread workgroup per row that streams it twice:
+ *                     wavefront g runs the 64 chains of group g with one
+ *                     16-byte (binary32) / 8-byte (bf16) load per lane and
+ *                     1024 elements when x is quad-aligned (element loads
+ *                     otherwise), 16 such loads in flight behind the ones
+ *                     being summed; then the whole workgroup applies the row.
+ *                     Any alignment, any n up to 2^24.
  *   RMSN_PATH_SPLIT:  one workgroup of up to 16 wavefronts per row (Lecture 04
  *                     section 1.1: widen the block until the row's width is
  *                     the parallelism). The row is cut into 1 KB slices, one
@@ -252,13 +273,22 @@ const char* rmsnorm_last_error(void);
  *                     chunks with one 16-byte (binary32) / 8-byte (bf16) load
  *                     per lane and transposes them in registers: a quarter of
  *                     BLOCK's load instructions. Needs quad-aligned pointers
- *                     (16 B / 8 B), n a multiple of 4 and n <= 8192. */
+ *                     (16 B / 8 B), n a multiple of 4 and n <= 8192.
+ *   RMSN_PATH_WIDE:   rmsnorm_batched_rows_ws only: the sum of each row split
+ *                     over four one-wavefront workgroups, one per association
+ *                     group (so four CUs per row; the association allows no
+ *                     more lanes), writing the group totals to the caller's
+ *                     workspace; then a second launch of ceil(n / 4096)
+ *                     workgroups per row combines the totals in the
+ *                     association's order and applies 4096 elements each.
+ *                     Chosen for at most 64 rows of at least 64 KB. */
 enum {
     RMSN_PATH_WAVE = 0,
     RMSN_PATH_BLOCK = 1,
     RMSN_PATH_STREAM = 2,
     RMSN_PATH_SPLIT = 3,
-    RMSN_PATH_GROUP = 4
+    RMSN_PATH_GROUP = 4,
+    RMSN_PATH_WIDE = 5
 };
 
 typedef struct rmsn_plan_info {
@@ -273,7 +303,7 @@ typedef struct rmsn_plan_info {
                                 stores of y                                       */
     int32_t loads;           /* SPLIT: 16-byte loads per lane (1 KB slices per
                                 wavefront); GROUP: loads per lane (1024-element
-                                blocks); else 0                                   */
+                                blocks); WIDE: apply workgroups per row; else 0   */
 } rmsn_plan_info;
 
 /* The launch the library would use for `rows` rows of width n whose row starts
@@ -283,6 +313,12 @@ typedef struct rmsn_plan_info {
  * whose pointers the kernel checks when it runs). Same function the launches
  * use. Returns RMSN_EINVAL for an invalid dtype, rows or n. */
 int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_info* out);
+
+/* The plan rmsnorm_batched_rows_ws would use for `rows` rows of width n at
+ * alignment `align` (as rmsnorm_plan_query), and in *bytes the workspace it
+ * needs (16 bytes per row on RMSN_PATH_WIDE, else 0). plan may be NULL. */
+int rmsnorm_workspace_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_info* plan,
+                            int64_t* bytes);
 
 /* Process-wide overrides, for proving that code paths give identical bits
  * (Lecture 04 section 6: one binary, switchable arms). Defaults come from the

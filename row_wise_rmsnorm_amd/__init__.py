@@ -9,6 +9,9 @@ Function names follow the C entry points:
     rmsnorm_f32(x, w, eps, out=None)           one binary32 row
     rmsnorm_bf16(x, w, eps, out=None)          one bf16 row
     rmsnorm_batched_rows(x, w, eps, out=None)  2-D, rows share w
+    rmsnorm_batched_rows_ws(x, w, eps, out=None, workspace=None)
+                                               the same with a device workspace
+                                               (few very wide rows over many CUs)
     rmsnorm_sequence_eager(table, widths, eps, dtype)
     SequenceGraph(table, widths, eps, dtype)   captured sequence (.launch())
 """
@@ -22,7 +25,8 @@ LIB128_PATH = os.path.join(_HERE, "librmsnorm_amd_l128.so")
 
 RMSN_OK, RMSN_EINVAL, RMSN_EHIP, RMSN_ECAPTURE, RMSN_ENOMEM = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
-PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM, PATH_SPLIT, PATH_GROUP = -1, 0, 1, 2, 3, 4
+PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM, PATH_SPLIT, PATH_GROUP, PATH_WIDE = \
+    -1, 0, 1, 2, 3, 4, 5
 OPT_PATH, OPT_ROWS_PER_BLOCK, OPT_STREAMING, OPT_SPLIT_LOADS, OPT_APPLY_THREADS = 1, 2, 3, 4, 5
 MAX_N = 1 << 24
 DESC_BYTES = 32
@@ -69,6 +73,9 @@ def bind(path):
         "rmsnorm_f32": [vp, vp, vp, i64, f, vp],
         "rmsnorm_bf16": [vp, vp, vp, i64, f, vp],
         "rmsnorm_batched_rows": [c_int, vp, i64, vp, vp, i64, i64, i64, f, vp],
+        "rmsnorm_batched_rows_ws": [c_int, vp, i64, vp, vp, i64, i64, i64, f, vp, i64, vp],
+        "rmsnorm_workspace_query": [c_int, i64, i64, c_int, ctypes.POINTER(_PlanInfo),
+                                    ctypes.POINTER(i64)],
         "rmsnorm_sequence_eager": [c_int, vp, vp, i32, f, vp],
         "rmsnorm_sequence_graph_create": [c_int, vp, vp, i32, f, ctypes.POINTER(vp)],
         "rmsnorm_sequence_graph_launch": [vp, vp],
@@ -106,7 +113,8 @@ EXPORTED = ("rmsnorm_f32", "rmsnorm_bf16", "rmsnorm_batched_rows", "rmsnorm_sequ
             "rmsnorm_set_option", "rmsnorm_get_option", "rmsnorm_diag_inverse",
             "rmsnorm_diag_bf16", "rmsnorm_sequence_eager_positioned",
             "rmsnorm_sequence_graph_create_positioned", "rmsnorm_sequence_graph_update",
-            "rmsnorm_association_lanes", "rmsnorm_sequence_persistent")
+            "rmsnorm_association_lanes", "rmsnorm_sequence_persistent",
+            "rmsnorm_batched_rows_ws", "rmsnorm_workspace_query")
 
 
 def lib():
@@ -233,6 +241,54 @@ def rmsnorm_batched_rows(x, w, eps, out=None, stream=None):
     with _on(x.device):
         _check(_lib.rmsnorm_batched_rows(code, x.data_ptr(), xs, w.data_ptr(), y.data_ptr(), ys,
                                          rows, n, float(eps), _stream_ptr(stream, x.device)))
+    return y
+
+
+def _rows_alignment(x, w, y, xs, ys):
+    """The byte alignment (power of two, at most 16) shared by every row start
+    and w, as the library computes it for a launch."""
+    es = x.element_size()
+    bits = x.data_ptr() | w.data_ptr() | y.data_ptr() | (xs * es) | (ys * es) | 16
+    return bits & -bits
+
+
+def workspace_query(dtype, rows, n, align=16):
+    """(plan dict, workspace bytes) that rmsnorm_batched_rows_ws would use."""
+    info = _PlanInfo()
+    b = ctypes.c_int64()
+    _check(_lib.rmsnorm_workspace_query(int(dtype), int(rows), int(n), int(align),
+                                        ctypes.byref(info), ctypes.byref(b)))
+    return _plan_dict(info), b.value
+
+
+def rmsnorm_batched_rows_ws(x, w, eps, out=None, workspace=None, stream=None):
+    """rmsnorm_batched_rows with a device workspace, so that few very wide
+    rows spread over many CUs (RMSN_PATH_WIDE); same bits. `workspace`: a
+    contiguous uint8 device tensor of at least the queried bytes, or None to
+    take one from torch's allocator when the launch needs it."""
+    import torch
+    _device_tensor(x, "x")
+    code = _dtype_code(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("2-D tensor with unit stride along rows expected")
+    rows, n = x.shape
+    _weight(x, w, n)
+    y = _out_like(x, out)
+    if y.stride(1) != 1:
+        raise ValueError("out must have unit stride along rows")
+    xs = x.stride(0) if rows > 1 else n
+    ys = y.stride(0) if rows > 1 else n
+    _, need = workspace_query(code, rows, n, _rows_alignment(x, w, y, xs, ys))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _device_tensor(workspace, "workspace")
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or \
+            workspace.device != x.device:
+        raise ValueError("workspace must be a contiguous uint8 tensor on x's device")
+    with _on(x.device):
+        _check(_lib.rmsnorm_batched_rows_ws(code, x.data_ptr(), xs, w.data_ptr(), y.data_ptr(),
+                                            ys, rows, n, float(eps), workspace.data_ptr(),
+                                            workspace.numel(), _stream_ptr(stream, x.device)))
     return y
 
 
@@ -382,6 +438,10 @@ def plan_query(dtype, rows, n, aligned=True, align=None):
         align = 16 if aligned else 0
     info = _PlanInfo()
     _check(_lib.rmsnorm_plan_query(int(dtype), int(rows), int(n), int(align), ctypes.byref(info)))
+    return _plan_dict(info)
+
+
+def _plan_dict(info):
     return {"path": info.path, "chunks": info.chunks, "rows_per_block": info.rows_per_block,
             "streaming": info.streaming, "block": info.block, "grid": info.grid,
             "loads": info.loads}

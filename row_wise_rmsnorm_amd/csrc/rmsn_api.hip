@@ -56,15 +56,21 @@ int rows_alignment(int dtype, const void* x, int64_t xs, const void* w, const vo
     return (int)(bits & (~bits + 1));  // lowest set bit
 }
 
+// use_ws: the caller passed a workspace (rmsnorm_batched_rows_ws), so the
+// plan may take the WIDE path, which needs one.
 int run_rows(int dtype, const void* x, int64_t xs, const void* w, void* y, int64_t ys,
-             int64_t rows, int64_t n, float eps, void* stream) {
+             int64_t rows, int64_t n, float eps, bool use_ws, void* ws, int64_t ws_bytes,
+             void* stream) {
     clear_error();
     int st = check_row_args(dtype, x, xs, w, y, ys, rows, n);
     if (st != RMSN_OK) return st;
     if ((st = check_eps(eps)) != RMSN_OK) return st;
     Plan p;
-    st = make_plan(dtype, rows, n, rows_alignment(dtype, x, xs, w, y, ys), &p);
+    st = make_plan(dtype, rows, n, rows_alignment(dtype, x, xs, w, y, ys), &p, use_ws);
     if (st != RMSN_OK) return st;
+    const bool wide = p.path == RMSN_PATH_WIDE;
+    if (wide && (st = check_workspace(dtype, x, xs, w, y, ys, rows, n, ws, ws_bytes)) != RMSN_OK)
+        return st;
     // A batch of more rows than one launch can hold goes as consecutive
     // launches of the plan's layout (a row's bits do not depend on the launch
     // it is in). Each piece starts a whole number of rows further on, which
@@ -74,11 +80,19 @@ int run_rows(int dtype, const void* x, int64_t xs, const void* w, void* y, int64
     for (int64_t r0 = 0; r0 < rows; r0 += most) {
         const int64_t piece = rows - r0 < most ? rows - r0 : most;
         Plan q = p;
-        q.grid = (piece + p.rows_per_block - 1) / p.rows_per_block;
-        const hipError_t e = launch_rows(
-            q, static_cast<const char*>(x) + r0 * xs * es, xs, w,
-            static_cast<char*>(y) + r0 * ys * es, ys, piece, (int)n, eps,
-            static_cast<hipStream_t>(stream));
+        const void* xq = static_cast<const char*>(x) + r0 * xs * es;
+        void* yq = static_cast<char*>(y) + r0 * ys * es;
+        hipError_t e;
+        if (wide) {
+            q.grid = 4 * piece;
+            e = launch_wide_rows(q, xq, xs, w, yq, ys, piece, (int)n, eps,
+                                 static_cast<float*>(ws) + 4 * r0,
+                                 static_cast<hipStream_t>(stream));
+        } else {
+            q.grid = (piece + p.rows_per_block - 1) / p.rows_per_block;
+            e = launch_rows(q, xq, xs, w, yq, ys, piece, (int)n, eps,
+                            static_cast<hipStream_t>(stream));
+        }
         if (e != hipSuccess) return hip_fail("kernel launch", e);
     }
     return RMSN_OK;
@@ -330,17 +344,25 @@ int create_graph(int dtype, const rmsn_desc* d_table, const int64_t* h_widths, i
 extern "C" {
 
 int rmsnorm_f32(const float* x, const float* w, float* y, int64_t n, float eps, void* stream) {
-    return run_rows(RMSN_F32, x, n, w, y, n, 1, n, eps, stream);
+    return run_rows(RMSN_F32, x, n, w, y, n, 1, n, eps, false, nullptr, 0, stream);
 }
 
 int rmsnorm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, float eps,
                  void* stream) {
-    return run_rows(RMSN_BF16, x, n, w, y, n, 1, n, eps, stream);
+    return run_rows(RMSN_BF16, x, n, w, y, n, 1, n, eps, false, nullptr, 0, stream);
 }
 
 int rmsnorm_batched_rows(int dtype, const void* x, int64_t x_row_stride, const void* w, void* y,
                          int64_t y_row_stride, int64_t rows, int64_t n, float eps, void* stream) {
-    return run_rows(dtype, x, x_row_stride, w, y, y_row_stride, rows, n, eps, stream);
+    return run_rows(dtype, x, x_row_stride, w, y, y_row_stride, rows, n, eps, false, nullptr, 0,
+                    stream);
+}
+
+int rmsnorm_batched_rows_ws(int dtype, const void* x, int64_t x_row_stride, const void* w,
+                            void* y, int64_t y_row_stride, int64_t rows, int64_t n, float eps,
+                            void* workspace, int64_t workspace_bytes, void* stream) {
+    return run_rows(dtype, x, x_row_stride, w, y, y_row_stride, rows, n, eps, true, workspace,
+                    workspace_bytes, stream);
 }
 
 int rmsnorm_sequence_eager(int dtype, const rmsn_desc* d_table, const int64_t* h_widths,
@@ -496,6 +518,16 @@ const char* rmsnorm_last_error(void) { return last_error(); }
 
 int rmsnorm_association_lanes(void) { return kAssocLanes; }
 
+static void plan_info(const Plan& p, rmsn_plan_info* out) {
+    out->path = p.path;
+    out->chunks = p.chunks;
+    out->rows_per_block = p.rows_per_block;
+    out->block = p.block;
+    out->grid = p.grid;
+    out->streaming = p.streaming;
+    out->loads = p.loads;
+}
+
 int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_info* out) {
     clear_error();
     if (!out) {
@@ -505,13 +537,22 @@ int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_
     Plan p;
     const int st = make_plan(dtype, rows, n, align, &p);
     if (st != RMSN_OK) return st;
-    out->path = p.path;
-    out->chunks = p.chunks;
-    out->rows_per_block = p.rows_per_block;
-    out->block = p.block;
-    out->grid = p.grid;
-    out->streaming = p.streaming;
-    out->loads = p.loads;
+    plan_info(p, out);
+    return RMSN_OK;
+}
+
+int rmsnorm_workspace_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_info* plan,
+                            int64_t* bytes) {
+    clear_error();
+    if (!bytes) {
+        set_error("null output pointer");
+        return RMSN_EINVAL;
+    }
+    Plan p;
+    const int st = make_plan(dtype, rows, n, align, &p, true);
+    if (st != RMSN_OK) return st;
+    if (plan) plan_info(p, plan);
+    *bytes = workspace_bytes(p, rows);
     return RMSN_OK;
 }
 

@@ -23,6 +23,7 @@ namespace {
 // scalar registers becomes the scalar base of a load's address.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(1))) char* gptr_c;
 typedef __attribute__((address_space(1))) char* gptr;
 
@@ -47,6 +48,9 @@ __device__ __forceinline__ gptr scalar_gptr(gptr p) {
 
 __device__ __forceinline__ float widen(float v) { return v; }
 __device__ __forceinline__ float widen(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// the bf16 elements in the low / high half of a dword
+__device__ __forceinline__ float lo_bf16(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
 // binary32 -> bf16, round to nearest, ties to even (the MODE register's
 // default rounding), denormals kept, NaN -> a quiet NaN: one

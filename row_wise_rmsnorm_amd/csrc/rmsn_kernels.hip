@@ -28,8 +28,9 @@
 //          row shifts; the four group totals meet in 16 bytes of LDS across
 //          one barrier. Element loads are 4/2 bytes, so any element-aligned
 //          pointer works; the row stays in VGPRs (n <= 256 * chunks).
-//   STREAM BLOCK's mapping, but the row is streamed twice (once for the sum,
-//          once for the apply) instead of being held: any n up to 2^24.
+//   (STREAM and WIDE, for rows too wide to hold in registers, are in
+//   rmsn_wide.hip; the descriptor kernels and the persistent walk stream a row
+//   that leaves their register bucket with BLOCK's mapping, row_block<T, 0>.)
 //   GROUP  BLOCK's mapping of chains to threads, but wavefront g reads its
 //          group's 64 elements of four chunks with one 16-byte (binary32) /
 //          8-byte (bf16) load per lane and a 4x4 register transpose (32- and
@@ -53,6 +54,7 @@
 #include <stdint.h>
 
 #include "rmsn_common.h"
+#include "rmsn_group.h"
 #include "rmsn_launch.h"
 
 #pragma clang fp contract(off)
@@ -218,8 +220,6 @@ struct WaveRow {
 // chains of both chunks: lane t < 32 chains 8t..8t+3, lane t + 32 chains
 // 8t+4..8t+7.
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 template <bool NT>
 __device__ __forceinline__ u32x4 gload16(gptr_c p) {
     auto* a = reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(p);
@@ -232,18 +232,6 @@ __device__ __forceinline__ void gstore16(gptr p, u32x4 v) {
     else *a = v;
 }
 
-__device__ __forceinline__ float lo_bf16(uint32_t d) { return __uint_as_float(d << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
-
-// Lanes 0..31 keep their own a and receive b's upper half; lanes 32..63 keep
-// their own b and receive a's lower half -- as (r.first, r.second):
-//   lane i < 32:  first = a[i],      second = a[i + 32]
-//   lane i >= 32: first = b[i - 32], second = b[i]
-struct SwapPair { uint32_t first, second; };
-__device__ __forceinline__ SwapPair swap32(uint32_t a, uint32_t b) {
-    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-    return {r[0], r[1]};
-}
 
 __device__ __forceinline__ void chain4(float p[4], float v0, float v1, float v2, float v3) {
     p[0] = fmaf(v0, v0, p[0]);
@@ -389,46 +377,6 @@ struct SplitPart {
 // GROUP layout: 256 threads per row; wavefront g owns association group g.
 // Instances: Q = 1..8 blocks of 1024 elements (rows up to 8192).
 #define RMSN_FOR_GROUP_BLOCKS(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
-
-// One load per lane covers the group's 64 elements in four consecutive
-// 256-element chunks: lane 16q + t reads elements 256(4m+q) + 64g + 4t + {0..3}
-// of block m (1024 elements). A 4x4 transpose between the lane's 16-lane row
-// q and its register index then leaves lane 16q + t holding chain
-// 64g + 4t + q for chunks 4m .. 4m+3, in order.
-
-// Lanes 0..15 / 32..47 keep their own a and receive b's rows 0 / 2; lanes
-// 16..31 / 48..63 keep their own b and receive a's rows 1 / 3:
-//   first  = a with its odd 16-lane rows replaced by b's even rows
-//   second = b with its even 16-lane rows replaced by a's odd rows
-__device__ __forceinline__ SwapPair swap16(uint32_t a, uint32_t b) {
-    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-    return {r[0], r[1]};
-}
-
-// v[e] of lane 16q + t is X[q][e] (row q, register e); afterwards v[k] of that
-// lane is X[k][q].
-__device__ __forceinline__ void transpose4(float v[4]) {
-    const SwapPair a = swap32(__float_as_uint(v[0]), __float_as_uint(v[2]));
-    const SwapPair b = swap32(__float_as_uint(v[1]), __float_as_uint(v[3]));
-    // rows 0,1 of registers 2,3 moved to rows 2,3 of registers 0,1 and back
-    const SwapPair c = swap16(a.first, b.first);
-    const SwapPair d = swap16(a.second, b.second);
-    v[0] = __uint_as_float(c.first);
-    v[1] = __uint_as_float(c.second);
-    v[2] = __uint_as_float(d.first);
-    v[3] = __uint_as_float(d.second);
-}
-
-// Group tree of the GROUP layout: association lane 64g + 4t + q sits in lane
-// 16q + t. Halving 32/16/8/4 moves t by 8/4/2/1 (DPP row shifts); halving 2
-// and 1 move q by 2 and 1, i.e. lanes 0/32 and 16/48.
-__device__ __forceinline__ float group_sumsq(float p) {
-    p += row_shl<8>(p);
-    p += row_shl<4>(p);
-    p += row_shl<2>(p);
-    p += row_shl<1>(p);
-    return (lane_value(p, 0) + lane_value(p, 32)) + (lane_value(p, 16) + lane_value(p, 48));
-}
 
 // One row on the GROUP layout, Q blocks of 1024 elements: requires
 // 1024 (Q-1) < n <= 1024 Q, n a multiple of 4 and x, w, y aligned to a quad
@@ -1304,7 +1252,6 @@ hipError_t launch_block_t(const Plan& p, const void* x, int64_t xs, const void* 
                            eps);                                                              \
         break;
     switch (p.chunks) {
-        RMSN_CASE(0)
         RMSN_FOR_BUCKETS(RMSN_CASE)
         default: return hipErrorInvalidValue;
     }
@@ -1371,6 +1318,8 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
         return p.dtype == RMSN_F32 ? launch_group_t<float>(p, x, xs, w, y, ys, n, eps, stream)
                                    : launch_group_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
     }
+    if (p.path == RMSN_PATH_STREAM)
+        return launch_stream_rows(p, x, xs, w, y, ys, rows, n, eps, stream);
     return p.dtype == RMSN_F32 ? launch_block_t<float>(p, x, xs, w, y, ys, n, eps, stream)
                                : launch_block_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
 }

@@ -161,6 +161,13 @@ hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosAr
     return hipGetLastError();
 }
 
+// The WIDE path splits R256's four groups over workgroups; this build's plan
+// never takes it.
+hipError_t launch_wide_rows(const Plan&, const void*, int64_t, const void*, void*, int64_t,
+                            int64_t, int, float, float*, hipStream_t) {
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_sequence_persistent(int dtype, const rmsn_desc* d, int32_t count, float eps,
                                      const PosArgs* pos, hipStream_t stream) {
     const int b = option_apply_threads();

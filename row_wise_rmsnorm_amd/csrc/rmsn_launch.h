@@ -1,4 +1,5 @@
-// rmsn_launch.h -- host-side launchers of the gfx950 kernels (rmsn_kernels.hip).
+// rmsn_launch.h -- host-side launchers of the gfx950 kernels (rmsn_kernels.hip,
+// rmsn_wide.hip, rmsn_aux.hip).
 // Each enqueues on `stream` and returns the launch's hipError_t; none
 // allocates or synchronises.
 #pragma once
@@ -14,6 +15,17 @@ namespace rmsn {
 // `rows` rows, one per wavefront, with the geometry of plan `p`.
 hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
                        int64_t ys, int64_t rows, int n, float eps, hipStream_t stream);
+
+// STREAM path (rmsn_wide.hip): one 256-thread workgroup per row, the row
+// streamed twice.
+hipError_t launch_stream_rows(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
+                              int64_t ys, int64_t rows, int n, float eps, hipStream_t stream);
+
+// WIDE path (rmsn_wide.hip): two launches, the group totals of `rows` rows
+// through ws (4 floats per row, device memory).
+hipError_t launch_wide_rows(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
+                            int64_t ys, int64_t rows, int n, float eps, float* ws,
+                            hipStream_t stream);
 
 // The position of a positioned sequence, passed by value to its kernels: the
 // position itself is device memory, read when the kernels run.

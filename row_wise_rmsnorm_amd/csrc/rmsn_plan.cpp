@@ -33,7 +33,7 @@ int env_int(const char* name, int dflt) {
 
 bool valid_path(int v) {
     return v == -1 || v == RMSN_PATH_WAVE || v == RMSN_PATH_BLOCK || v == RMSN_PATH_STREAM ||
-           v == RMSN_PATH_SPLIT || v == RMSN_PATH_GROUP;
+           v == RMSN_PATH_SPLIT || v == RMSN_PATH_GROUP || v == RMSN_PATH_WIDE;
 }
 bool valid_split_loads(int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8; }
 bool valid_apply_threads(int v) { return v == 0 || v == 128 || v == 256 || v == 512 || v == 1024; }
@@ -110,7 +110,7 @@ int option_apply_threads() {
 int set_option(int key, int value) {
     if (key == RMSN_OPT_PATH) {
         if (!valid_path(value)) {
-            set_error("rmsnorm_set_option: path must be -1 (automatic) or 0..4, got %d", value);
+            set_error("rmsnorm_set_option: path must be -1 (automatic) or 0..5, got %d", value);
             return RMSN_EINVAL;
         }
         g_path.store(value, std::memory_order_relaxed);
@@ -209,7 +209,7 @@ int auto_split_loads(int64_t slices) {
     return (slices + u - 1) / u <= kMaxSplitWaves ? u : 0;
 }
 
-int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
+int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out, bool workspace) {
     if (dtype != RMSN_F32 && dtype != RMSN_BF16) {
         set_error("unknown dtype %d", dtype);
         return RMSN_EINVAL;
@@ -250,6 +250,7 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
     const bool can_wave = bucket != 0 && a >= vec_bytes(dtype);
     const bool can_block = bucket != 0;
     const bool can_group = bucket != 0 && n % 4 == 0 && (run_time || a >= vec_bytes(dtype));
+    const bool can_wide = workspace && !run_time;
     int path;
     switch (option_path()) {
         case RMSN_PATH_WAVE: path = can_wave ? RMSN_PATH_WAVE : -1; break;
@@ -257,6 +258,7 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
         case RMSN_PATH_STREAM: path = RMSN_PATH_STREAM; break;
         case RMSN_PATH_SPLIT: path = can_split ? RMSN_PATH_SPLIT : -1; break;
         case RMSN_PATH_GROUP: path = can_group ? RMSN_PATH_GROUP : -1; break;
+        case RMSN_PATH_WIDE: path = can_wide ? RMSN_PATH_WIDE : -1; break;
         default: path = -1; break;
     }
     if (path < 0) {
@@ -272,6 +274,8 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
         const bool mid = footprint_at_least(dtype, rows, n, kStreamBytes / 2);
         const int64_t row_bytes = n * es;
         if (run_time) path = can_block ? RMSN_PATH_BLOCK : RMSN_PATH_STREAM;
+        else if (can_wide && n * es >= kWideMinBytes && rows <= kWideMaxRows)
+            path = RMSN_PATH_WIDE;
         else if (!many && can_group) path = RMSN_PATH_GROUP;
         else if (many && !big && row_bytes >= 4096 && can_group) path = RMSN_PATH_GROUP;
         else if (many && row_bytes < 1024 && can_wave) path = RMSN_PATH_WAVE;
@@ -304,6 +308,15 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out) {
         p.streaming = st < 0 ? (auto_streaming(dtype, rows, n) ? 1 : 0) : st;
         p.block = kWave * (int)((slices + u - 1) / u);
         p.grid = rows;
+    } else if (path == RMSN_PATH_WIDE) {
+        // four one-wavefront workgroups per row (one per group), then
+        // ceil(n / kWideSpan) workgroups of 256 per row for the apply
+        p.loads = (int)((n + kWideSpan - 1) / kWideSpan);
+        p.chunks = 0;
+        p.rows_per_block = 1;
+        p.streaming = 0;
+        p.block = kWave;
+        p.grid = 4 * rows;
     } else if (path == RMSN_PATH_GROUP) {
         p.loads = (int)((n + 1023) / 1024);
         p.chunks = 4 * p.loads;
@@ -411,6 +424,29 @@ int check_sequence_args(int dtype, const rmsn_desc* d_table, const int64_t* h_wi
         }
     }
     return check_eps(eps);
+}
+
+int check_workspace(int dtype, const void* x, int64_t xs, const void* w, const void* y,
+                    int64_t ys, int64_t rows, int64_t n, const void* ws, int64_t ws_bytes) {
+    const int64_t need = rows * 4 * (int64_t)sizeof(float);
+    if (!ws || (uintptr_t)ws % 4) {
+        set_error("the launch needs a non-null, 4-byte aligned workspace (ws=%p)", ws);
+        return RMSN_EINVAL;
+    }
+    if (ws_bytes < need) {
+        set_error("workspace of %lld bytes, the launch needs %lld", (long long)ws_bytes,
+                  (long long)need);
+        return RMSN_EINVAL;
+    }
+    const int64_t es = elem_bytes(dtype);
+    const uintptr_t pw = (uintptr_t)ws;
+    if (overlaps(pw, (uint64_t)need, (uintptr_t)x, (uint64_t)(((rows - 1) * xs + n) * es)) ||
+        overlaps(pw, (uint64_t)need, (uintptr_t)w, (uint64_t)(n * es)) ||
+        overlaps(pw, (uint64_t)need, (uintptr_t)y, (uint64_t)(((rows - 1) * ys + n) * es))) {
+        set_error("the workspace overlaps x, w or y");
+        return RMSN_EINVAL;
+    }
+    return RMSN_OK;
 }
 
 }  // namespace rmsn

@@ -54,7 +54,8 @@ struct Plan {
     int block;           // threads per workgroup
     int64_t grid;        // workgroups
     int loads;           // SPLIT: 16-byte loads per lane (slices per wavefront);
-                         // GROUP: loads per lane (1024-element blocks); else 0
+                         // GROUP: loads per lane (1024-element blocks);
+                         // WIDE: apply workgroups per row; else 0
 };
 
 inline int elem_bytes(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
@@ -62,6 +63,8 @@ inline int elem_bytes(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
 // work-items as a 32-bit number, so workgroups * block stays below 2^32 (and
 // workgroups below 2^31); a batch beyond this goes as consecutive launches.
 inline int64_t rows_per_launch(const Plan& p) {
+    if (p.path == RMSN_PATH_WIDE)  // per row: 4 x 64 threads, then `loads` x 256
+        return 0xFFFFFFFFll / (256ll * (p.loads > 1 ? p.loads : 1));
     int64_t groups = 0xFFFFFFFFll / (p.block > 0 ? p.block : 1);
     if (groups > 0x7FFFFFFFll) groups = 0x7FFFFFFFll;
     return groups * (p.rows_per_block > 0 ? p.rows_per_block : 1);
@@ -91,8 +94,18 @@ int auto_split_loads(int64_t slices);
 // read (only the GROUP path does, falling back to streaming when they do not
 // fit). Returns RMSN_OK or RMSN_EINVAL (bad dtype, rows < 1, n outside
 // [1, 2^24]).
+// workspace: the launch may use one (rmsnorm_batched_rows_ws), which makes
+// the WIDE path available.
 constexpr int kAlignAtRunTime = -1;
-int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out);
+int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out, bool workspace = false);
+// Elements one workgroup of the WIDE path's second launch applies.
+constexpr int64_t kWideSpan = 4096;
+// Rows of at least kWideMinBytes in batches of at most kWideMaxRows rows take
+// the WIDE path when a workspace is available (measured on MI355X: below
+// 64 KB a row is faster on SPLIT's one workgroup, whose loads are all in
+// flight at once, than on two launches).
+constexpr int64_t kWideMinBytes = 64 * 1024;
+constexpr int64_t kWideMaxRows = 64;
 
 // Process-wide options (rmsnorm_set_option); read lazily from the environment.
 int option_path();            // -1 automatic, else an RMSN_PATH_* value
@@ -110,6 +123,16 @@ int check_row_args(int dtype, const void* x, int64_t xs, const void* w, const vo
                    int64_t rows, int64_t n);
 int check_sequence_args(int dtype, const rmsn_desc* d_table, const int64_t* h_widths,
                         int32_t count, float eps);
+// Bytes of workspace plan p needs for `rows` rows (the four group totals of
+// each row on the WIDE path, else none).
+inline int64_t workspace_bytes(const Plan& p, int64_t rows) {
+    return p.path == RMSN_PATH_WIDE ? rows * 4 * (int64_t)sizeof(float) : 0;
+}
+// A WIDE launch's workspace: non-null, 4-byte aligned, at least
+// workspace_bytes, and overlapping none of x, w, y (arguments as
+// check_row_args, which must have passed).
+int check_workspace(int dtype, const void* x, int64_t xs, const void* w, const void* y,
+                    int64_t ys, int64_t rows, int64_t n, const void* ws, int64_t ws_bytes);
 
 void set_error(const char* fmt, ...);
 void clear_error();

@@ -388,7 +388,14 @@ def test_options_roundtrip_and_force_paths(rn):
         with pytest.raises(rn.RmsnormError):
             rn.set_option(rn.OPT_PATH, 7)
         with pytest.raises(rn.RmsnormError):
-            rn.set_option(rn.OPT_PATH, 5)
+            rn.set_option(rn.OPT_PATH, 6)
+        # WIDE needs a workspace: forced, the plain plan falls back to the
+        # automatic choice and the workspace plan takes it for any shape
+        rn.set_option(rn.OPT_PATH, rn.PATH_WIDE)
+        assert rn.plan_query(rn.BF16, 3, 7168)["path"] == rn.PATH_GROUP
+        assert rn.workspace_query(rn.BF16, 3, 100)[0]["path"] == rn.PATH_WIDE
+        assert rn.workspace_query(rn.BF16, 5000, 7168)[1] == 16 * 5000
+        rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
         with pytest.raises(rn.RmsnormError):
             rn.set_option(99, 0)
     finally:
@@ -450,3 +457,52 @@ def test_binding_refuses_host_tensors(rn):
         rn.rmsnorm_batched_rows(x.view(2, 4), x[:4], 1e-6)
     with pytest.raises(ValueError, match="GPU tensor"):
         rn.make_table([(x, x, x)])
+
+
+def test_workspace_query(rn):
+    """WIDE (and a workspace of 16 bytes per row) for at most 64 rows of at
+    least 64 KB; everything else needs none and plans as rmsnorm_plan_query."""
+    for dt in (rn.F32, rn.BF16):
+        es = 4 if dt == rn.F32 else 2
+        for rows, n, wide in ((1, 65536 // es, True), (1, 65536 // es - 1, False),
+                              (1, 1 << 24, True), (64, 65536, True), (65, 65536, False),
+                              (1, 8192, False), (1, 9000, False), (8192, 7168, False),
+                              (3, 100, False)):
+            plan, need = rn.workspace_query(dt, rows, n)
+            assert (plan["path"] == rn.PATH_WIDE) == wide, (dt, rows, n, plan)
+            if wide:
+                assert need == 16 * rows
+                assert plan["grid"] == 4 * rows and plan["block"] == 64
+                assert plan["loads"] == -(-n // 4096)
+            else:
+                assert need == 0 and plan == rn.plan_query(dt, rows, n)
+    # descriptor-row alignment never takes WIDE; bad arguments are refused
+    assert rn.workspace_query(rn.F32, 1, 1 << 20, align=-1)[0]["path"] != rn.PATH_WIDE
+    with pytest.raises(rn.RmsnormError):
+        rn.workspace_query(rn.F32, 0, 100)
+    L = rn.lib()
+    assert L.rmsnorm_workspace_query(0, 1, 100, 16, None, None) == rn.RMSN_EINVAL
+
+
+def test_workspace_rejects(rn):
+    """A WIDE launch refuses a missing, small, misaligned or overlapping
+    workspace before anything is launched (fake, never dereferenced
+    addresses); the plain checks apply first."""
+    L = rn.lib()
+    n = 1 << 16                                   # 256 KB rows: WIDE for a few rows
+    X, W, Y, WS = 0x1000000, 0x2000000, 0x3000000, 0x4000000
+
+    def call(ws, nbytes, rows=2, x=X, y=Y, xs=n, ys=n):
+        return L.rmsnorm_batched_rows_ws(0, x, xs, W, y, ys, rows, n, 1e-6, ws, nbytes, None)
+
+    assert call(0, 64) == rn.RMSN_EINVAL and "workspace" in rn.last_error()
+    assert call(WS + 2, 64) == rn.RMSN_EINVAL and "workspace" in rn.last_error()
+    assert call(WS, 31) == rn.RMSN_EINVAL and "needs 32" in rn.last_error()
+    assert call(X + 4 * n, 64) == rn.RMSN_EINVAL and "overlaps" in rn.last_error()   # in x's row 1
+    assert call(W + 8, 64) == rn.RMSN_EINVAL and "overlaps" in rn.last_error()
+    assert call(Y, 64) == rn.RMSN_EINVAL and "overlaps" in rn.last_error()
+    assert call(WS, 64, xs=n - 1) == rn.RMSN_EINVAL and "stride" in rn.last_error()
+    # a launch that needs no workspace ignores it: validation passes, and
+    # without a GPU the launch then fails with a HIP error, never EINVAL
+    assert L.rmsnorm_batched_rows_ws(0, X, 64, W, Y, 64, 2, 64, 1e-6, 0, 0, None) \
+        != rn.RMSN_EINVAL
