@@ -42,7 +42,7 @@ ROTATE = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_8192x7168_traffic.json")
 # the sources the prefill kernel is compiled from (its traffic record is tied to them)
 KERNEL_SRCS = [os.path.join(ROOT, "row_wise_rmsnorm_amd", "csrc", f)
-               for f in ("rmsn_kernels.hip", "rmsn_common.h", "rmsn_launch.h")]
+               for f in ("rmsn_kernels.hip", "rmsn_common.h", "rmsn_group.h", "rmsn_launch.h")]
 
 
 def log(msg):
@@ -248,6 +248,71 @@ def bench_batch64(rn, torch, np, wl):
     return {"us_device": dev_us, "gbs_device": algo / (dev_us["mean"] * 1e-6) / 1e9,
             "us_back_to_back_host_calls": stats(host), "plan": plan,
             "workgroups_per_cu": plan["grid"] / 256.0}
+
+
+WIDE_SHAPES = [("f32", 1, 1 << 14), ("f32", 1, 1 << 16), ("f32", 1, 1 << 20), ("f32", 1, 1 << 24),
+               ("bf16", 1, 1 << 24), ("bf16", 16, 1 << 18), ("bf16", 64, 1 << 16)]
+
+
+def bench_wide(rn, torch, np, wl):
+    """Few very wide rows (beyond the pages' widths): the plain entry point
+    (STREAM or SPLIT) against the workspace entry point (WIDE), graph-timed,
+    outputs compared bit for bit. Not part of the default run."""
+    dev = torch.device("cuda", 0)
+    eps = float(wl.EPS)
+    out = []
+    for kind, rows, n in WIDE_SHAPES:
+        x = np.stack([wl.misc_f32(4_000_000 + r, n)[0] for r in range(rows)])
+        w = wl.misc_f32(4_000_000, n)[1]
+        if kind == "bf16":
+            code, iv = rn.BF16, torch.int16
+            xd = torch.from_numpy(wl.to_bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
+            wd = torch.from_numpy(wl.to_bf16_bits(w).view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            code, iv = rn.F32, torch.int32
+            xd, wd = torch.from_numpy(x).to(dev), torch.from_numpy(w).to(dev)
+        y1, y2 = torch.empty_like(xd), torch.empty_like(xd)
+        plan, need = rn.workspace_query(code, rows, n)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        big = rows * n >= (1 << 22)
+        kw = dict(per_graph=10, replays=5, reps=5) if big else {}
+        plain = graph_us_per_launch(
+            torch, lambda s: rn.rmsnorm_batched_rows(xd, wd, eps, out=y1, stream=s), **kw)
+        wide = graph_us_per_launch(
+            torch, lambda s: rn.rmsnorm_batched_rows_ws(xd, wd, eps, out=y2, workspace=ws,
+                                                        stream=s), **kw)
+        torch.cuda.synchronize()
+        out.append({"dtype": kind, "rows": rows, "n": n,
+                    "plain_path": rn.plan_query(code, rows, n)["path"], "plain_us": plain["mean"],
+                    "ws_path": plan["path"], "ws_us": wide["mean"],
+                    "bit_exact_ws_eq_plain": bool(torch.equal(y1.view(iv), y2.view(iv)))})
+        log(f"wide {kind} {rows} x {n}: plain {plain['mean']:.1f} us, with workspace "
+            f"{wide['mean']:.1f} us")
+        del xd, wd, y1, y2, ws
+    return out
+
+
+def profile_wide(rn, torch, np, wl):
+    """A short run for a kernel trace of the wide-row paths: every shape of
+    bench_wide, 3 + 20 launches through each entry point (no graph), so the
+    trace can be grouped by shape (grid size)."""
+    dev = torch.device("cuda", 0)
+    eps = float(wl.EPS)
+    for kind, rows, n in WIDE_SHAPES:
+        dt = torch.bfloat16 if kind == "bf16" else torch.float32
+        g = torch.Generator(device=dev)
+        g.manual_seed(rows * 131 + n)
+        x = torch.randn(rows, n, device=dev, generator=g).to(dt)
+        w = (1 + 0.1 * torch.randn(n, device=dev, generator=g)).to(dt)
+        y = torch.empty_like(x)
+        _, need = rn.workspace_query(rn.BF16 if kind == "bf16" else rn.F32, rows, n)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        for _ in range(23):
+            rn.rmsnorm_batched_rows(x, w, eps, out=y)
+        for _ in range(23):
+            rn.rmsnorm_batched_rows_ws(x, w, eps, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"profile wide {kind} {rows} x {n}")
 
 
 def bench_decode(rn, torch, np, wl, decode_steps):
@@ -500,9 +565,12 @@ def main():
     ap.add_argument("--profile-kernels", action="store_true")
     ap.add_argument("--profile-decode", action="store_true",
                     help="short decode-step run for counter collection")
+    ap.add_argument("--profile-wide", action="store_true",
+                    help="a short run of the wide-row shapes for a kernel trace")
     ap.add_argument("--sections", default="prefill,single,batch64,decode",
-                    help="comma list of prefill,single,batch64,decode,positioned (for "
-                         "profiling runs; the default runs them all)")
+                    help="comma list of prefill,single,batch64,decode,positioned,wide (for "
+                         "profiling runs; the default runs the first four; wide: few very "
+                         "wide rows, plain against workspace entry point)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this benchmark runs on one GPU only; --gpus {args.gpus} is not "
@@ -523,6 +591,9 @@ def main():
     if args.profile_decode:
         profile_decode(rn, torch, np, wl)
         return
+    if args.profile_wide:
+        profile_wide(rn, torch, np, wl)
+        return
 
     sections = set(args.sections.split(","))
     full = {"prefill", "single", "batch64", "decode"}
@@ -542,6 +613,8 @@ def main():
         if "positioned" in sections:
             out["decode_step_positioned"] = bench_decode_positioned(rn, torch, np, wl,
                                                                     args.decode_steps)
+        if "wide" in sections:
+            out["wide_rows"] = bench_wide(rn, torch, np, wl)
         print(json.dumps(out), flush=True)
         return
     torch.cuda.synchronize()

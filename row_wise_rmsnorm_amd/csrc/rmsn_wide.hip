@@ -18,8 +18,8 @@
 //                buffer resource ranged to the row (or to its complete blocks):
 //                past it they return +0, which leaves a chain unchanged
 //                (fmaf(0, 0, p) == p for p >= +0), so every batch issues the
-//                same loads and one batch is in flight while the previous one
-//                is consumed.
+//                same loads, and one batch is in flight while the previous
+//                one is summed.
 //   STREAM       one workgroup of four wavefronts per row: the four group
 //                chains, the combine through LDS, then the apply streamed by
 //                the whole workgroup, kSpan elements at a time.
@@ -47,8 +47,13 @@ namespace {
 
 typedef __amdgpu_buffer_rsrc_t brsrc;
 
-constexpr int kBatch = 16;          // 1024-element blocks per batch (quad loads)
-constexpr int kEBatch = 24;         // 256-element chunks per batch (element loads)
+// Loads in flight while a wavefront sums: one batch is summed while the next
+// is loaded -- 1024-element blocks with quad loads, 256-element chunks with
+// element loads. (Measured on MI355X: keeping 16 to 48 blocks in flight,
+// refilled one block or eight at a time, changes nothing; the sum is bound by
+// the chain of dependent multiply-adds, not by memory.)
+constexpr int kBatch = 16;
+constexpr int kEBatch = 24;
 
 // A buffer resource for `bytes` bytes at p (raw, stride 0; the third word is
 // the gfx9-family untyped format). Offsets at or past `bytes` read +0 and
@@ -220,46 +225,88 @@ __device__ __forceinline__ float group_total(const T* x, uint32_t n, uint32_t g)
 }
 
 // ---------------------------------------------------------------------------
-// The apply: y[d] = (x[d] * inv) * w[d] for d in [e0, e0 + kSpan) of a row.
-// 256 threads. With x, w, y quad-aligned and n a multiple of 4, thread i
+// The apply: y[d] = (x[d] * inv) * w[d] for d in [e0, e0 + kSpan) of a row, by
+// 256 threads. QUADS (x, w, y quad-aligned and n a multiple of 4): thread i
 // takes the quads at e0 + 1024j + 4i; otherwise the elements e0 + 256j + i.
-// Accesses past the row read +0 and drop their stores (ranged resources).
+// Accesses past the row read +0 and drop their stores (ranged resources), so
+// a span may run past the row's end.
 
 constexpr uint32_t kSpan = 4096;
 
+struct RowRsrc {
+    brsrc x, w, y;
+};
+
 template <typename T>
-__device__ __forceinline__ void apply_span(const T* x, const T* w, T* y, uint32_t n, float inv,
-                                           uint32_t e0, bool quads) {
-    constexpr uint32_t es = sizeof(T);
-    const uint32_t i = threadIdx.x;
-    const brsrc rx = wide_rsrc(x, n * es), rw = wide_rsrc(w, n * es), ry = wide_rsrc(y, n * es);
-    if (quads) {
-        constexpr int J = kSpan / 1024;
-        typename BQuad<T>::raw xv[J], wv[J];
+__device__ __forceinline__ RowRsrc row_rsrcs(const T* x, const T* w, T* y, uint32_t n) {
+    const uint32_t bytes = n * (uint32_t)sizeof(T);
+    return RowRsrc{wide_rsrc(x, bytes), wide_rsrc(w, bytes), wide_rsrc(y, bytes)};
+}
+
+template <typename T, bool QUADS> struct Span;
+
+template <typename T> struct Span<T, true> {
+    static constexpr int J = kSpan / 1024;
+    typename BQuad<T>::raw x[J], w[J];
+    __device__ __forceinline__ static uint32_t off(uint32_t e0, int j) {
+        return (e0 + 1024u * j + 4u * threadIdx.x) * (uint32_t)sizeof(T);
+    }
+    __device__ __forceinline__ void load(const RowRsrc& r, uint32_t e0) {
 #pragma unroll
-        for (int j = 0; j < J; ++j) xv[j] = BQuad<T>::load(rx, (e0 + 1024u * j + 4u * i) * es);
+        for (int j = 0; j < J; ++j) x[j] = BQuad<T>::load(r.x, off(e0, j));
 #pragma unroll
-        for (int j = 0; j < J; ++j) wv[j] = BQuad<T>::load(rw, (e0 + 1024u * j + 4u * i) * es);
+        for (int j = 0; j < J; ++j) w[j] = BQuad<T>::load(r.w, off(e0, j));
+    }
+    __device__ __forceinline__ void store(const RowRsrc& r, uint32_t e0, float inv) const {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             float a[4], b[4], o[4];
-            BQuad<T>::unpack(xv[j], a);
-            BQuad<T>::unpack(wv[j], b);
+            BQuad<T>::unpack(x[j], a);
+            BQuad<T>::unpack(w[j], b);
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = (a[k] * inv) * b[k];
-            BQuad<T>::store(ry, (e0 + 1024u * j + 4u * i) * es, o);
+            BQuad<T>::store(r.y, off(e0, j), o);
         }
-    } else {
-        constexpr int J = kSpan / 256;
-        typename BElem<T>::raw xv[J], wv[J];
+    }
+};
+
+template <typename T> struct Span<T, false> {
+    static constexpr int J = kSpan / 256;
+    typename BElem<T>::raw x[J], w[J];
+    __device__ __forceinline__ static uint32_t off(uint32_t e0, int j) {
+        return (e0 + 256u * j + threadIdx.x) * (uint32_t)sizeof(T);
+    }
+    __device__ __forceinline__ void load(const RowRsrc& r, uint32_t e0) {
 #pragma unroll
-        for (int j = 0; j < J; ++j) xv[j] = BElem<T>::load(rx, (e0 + 256u * j + i) * es);
+        for (int j = 0; j < J; ++j) x[j] = BElem<T>::load(r.x, off(e0, j));
 #pragma unroll
-        for (int j = 0; j < J; ++j) wv[j] = BElem<T>::load(rw, (e0 + 256u * j + i) * es);
+        for (int j = 0; j < J; ++j) w[j] = BElem<T>::load(r.w, off(e0, j));
+    }
+    __device__ __forceinline__ void store(const RowRsrc& r, uint32_t e0, float inv) const {
 #pragma unroll
         for (int j = 0; j < J; ++j)
-            BElem<T>::store(ry, (e0 + 256u * j + i) * es,
-                            (BElem<T>::value(xv[j]) * inv) * BElem<T>::value(wv[j]));
+            BElem<T>::store(r.y, off(e0, j), (BElem<T>::value(x[j]) * inv) * BElem<T>::value(w[j]));
+    }
+};
+
+// The whole row, two spans in flight: span s + 1 is loaded before span s is
+// applied and stored (its elements are other elements, so an in-place row is
+// safe), and a span's loads are issued before the stores of the span before
+// it, so waiting for them never waits for those stores.
+template <typename T, bool QUADS>
+__device__ __forceinline__ void apply_row(const RowRsrc& r, uint32_t n, float inv) {
+    Span<T, QUADS> a, b;
+    a.load(r, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    for (uint32_t e0 = 0; e0 < n; e0 += 2 * kSpan) {
+        b.load(r, e0 + kSpan);
+        __builtin_amdgcn_sched_barrier(0);
+        a.store(r, e0, inv);
+        __builtin_amdgcn_sched_barrier(0);
+        a.load(r, e0 + 2 * kSpan);
+        __builtin_amdgcn_sched_barrier(0);
+        b.store(r, e0 + kSpan, inv);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -286,9 +333,11 @@ __global__ __launch_bounds__(256) void k_rows_stream(const T* x, int64_t xs, con
     if ((threadIdx.x & 63) == 0) lds4[g] = gt;
     __syncthreads();
     const float inv = inverse_rms((lds4[0] + lds4[2]) + (lds4[1] + lds4[3]), n, eps);
-    const bool quads = quad_rows(xr, w, yr, (uint32_t)n, sizeof(T));
-    for (uint32_t e0 = 0; e0 < (uint32_t)n; e0 += kSpan)
-        apply_span<T>(xr, w, yr, (uint32_t)n, inv, e0, quads);
+    const RowRsrc rr = row_rsrcs<T>(xr, w, yr, (uint32_t)n);
+    if (quad_rows(xr, w, yr, (uint32_t)n, sizeof(T)))
+        apply_row<T, true>(rr, (uint32_t)n, inv);
+    else
+        apply_row<T, false>(rr, (uint32_t)n, inv);
 }
 
 // WIDE, first launch: group blockIdx % 4 of row blockIdx / 4; lane 0 writes
@@ -313,8 +362,16 @@ __global__ __launch_bounds__(256) void k_wide_apply(const T* x, int64_t xs, cons
     const float inv = inverse_rms((gt[0] + gt[2]) + (gt[1] + gt[3]), n, eps);
     const T* xr = x + r * xs;
     T* yr = y + r * ys;
-    apply_span<T>(xr, w, yr, (uint32_t)n, inv, s * kSpan,
-                  quad_rows(xr, w, yr, (uint32_t)n, sizeof(T)));
+    const RowRsrc rr = row_rsrcs<T>(xr, w, yr, (uint32_t)n);
+    if (quad_rows(xr, w, yr, (uint32_t)n, sizeof(T))) {
+        Span<T, true> sp;
+        sp.load(rr, s * kSpan);
+        sp.store(rr, s * kSpan, inv);
+    } else {
+        Span<T, false> sp;
+        sp.load(rr, s * kSpan);
+        sp.store(rr, s * kSpan, inv);
+    }
 }
 
 template <typename T>
