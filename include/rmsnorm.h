@@ -215,19 +215,25 @@ int rmsnorm_sequence_graph_update(rmsn_graph* g, const int64_t* h_widths, int32_
 
 /* ---- the whole step in one launch ------------------------------------------- */
 
-/* The sequence's count norms, in table order, in ONE kernel launch of one
- * workgroup that walks the descriptor table (Lecture 08 "Graph-resident
- * decode", further reading: a persistent kernel as the endpoint of capturing
- * many). Each row is finished -- its stores ordered before the next row's
- * loads by a workgroup barrier -- before the next row starts, so a table in
- * which a later x is an earlier y (y_i == x_j, i < j) computes exactly what
- * the launch sequence computes; the bits equal rmsnorm_sequence_eager's.
+/* The sequence's count norms in ONE kernel launch that walks the descriptor
+ * table (Lecture 08 "Graph-resident decode", further reading: a persistent
+ * kernel as the endpoint of capturing many); the bits equal
+ * rmsnorm_sequence_eager's. Rows that share no memory with any other row
+ * (their reads and output meet no other row's output, their output no other
+ * row's reads) cannot observe the order and run in parallel over up to 255
+ * more workgroups. The others keep table order in the first workgroup: each
+ * is finished -- its stores ordered before the next row's loads by a
+ * workgroup barrier -- before the next starts, so a table in which a later x
+ * is an earlier y (y_i == x_j, i < j) computes exactly what the launch
+ * sequence computes. Tables with a position or of more than 1024 rows, and
+ * RMSN_OPT_PERSISTENT_WORKGROUPS = 1, keep every row in one workgroup.
  * Widths come from the table (any n in [1, 2^24], any element alignment); no
- * host widths are needed. pos: NULL, or the rows are taken at the position
- * as in rmsnorm_sequence_eager_positioned and the position is advanced after
- * the last row. Nothing is allocated or synchronised, so the call may itself
- * be captured into a caller's graph. RMSN_EINVAL: bad dtype, d_table null or
- * not 8-byte aligned, count outside [1, RMSN_MAX_SEQUENCE], bad eps or
+ * host widths are needed. No row may write into the descriptor table itself.
+ * pos: NULL, or the rows are taken at the position as in
+ * rmsnorm_sequence_eager_positioned and the position is advanced after the
+ * last row. Nothing is allocated or synchronised, so the call may itself be
+ * captured into a caller's graph. RMSN_EINVAL: bad dtype, d_table null or not
+ * 8-byte aligned, count outside [1, RMSN_MAX_SEQUENCE], bad eps or
  * position. */
 int rmsnorm_sequence_persistent(int dtype, const rmsn_desc* d_table, int32_t count, float eps,
                                 const rmsn_position* pos, void* stream);
@@ -340,15 +346,22 @@ int rmsnorm_workspace_query(int dtype, int64_t rows, int64_t n, int align, rmsn_
  *                            build): threads per row for the elementwise
  *                            apply, 0 (= 1024), 128, 256, 512 or 1024; the sum
  *                            always runs on the first 128
+ *   RMSN_OPT_PERSISTENT_WORKGROUPS: rmsnorm_sequence_persistent, 0 automatic
+ *                            (rows that share no memory with any other row
+ *                            spread over many workgroups), 1 one workgroup
+ *                            walking the whole table (the 128-lane build
+ *                            always uses one)
  * Returns RMSN_EINVAL for an unknown key or value. Not synchronised with
  * launches on other threads. Environment: RMSN_PATH, RMSN_ROWS_PER_BLOCK,
- * RMSN_STREAMING, RMSN_SPLIT_LOADS, RMSN_APPLY_THREADS. */
+ * RMSN_STREAMING, RMSN_SPLIT_LOADS, RMSN_APPLY_THREADS,
+ * RMSN_PERSISTENT_WORKGROUPS. */
 enum {
     RMSN_OPT_PATH = 1,
     RMSN_OPT_ROWS_PER_BLOCK = 2,
     RMSN_OPT_STREAMING = 3,
     RMSN_OPT_SPLIT_LOADS = 4,
-    RMSN_OPT_APPLY_THREADS = 5
+    RMSN_OPT_APPLY_THREADS = 5,
+    RMSN_OPT_PERSISTENT_WORKGROUPS = 6
 };
 int rmsnorm_set_option(int key, int value);
 int rmsnorm_get_option(int key, int* value);

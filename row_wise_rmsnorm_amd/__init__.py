@@ -28,6 +28,7 @@ F32, BF16 = 0, 1
 PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM, PATH_SPLIT, PATH_GROUP, PATH_WIDE = \
     -1, 0, 1, 2, 3, 4, 5
 OPT_PATH, OPT_ROWS_PER_BLOCK, OPT_STREAMING, OPT_SPLIT_LOADS, OPT_APPLY_THREADS = 1, 2, 3, 4, 5
+OPT_PERSISTENT_WORKGROUPS = 6
 MAX_N = 1 << 24
 DESC_BYTES = 32
 

@@ -53,6 +53,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "rmsn_common.h"
 #include "rmsn_group.h"
 #include "rmsn_launch.h"
@@ -902,6 +904,9 @@ __device__ __forceinline__ void round_walk(const rmsn_desc* d, int32_t count, fl
 constexpr int kRoundWalk4 = 100;
 constexpr int kRoundWalk16 = 101;
 constexpr int kSpanRows = 1024;  // output ranges published in LDS (16 KB)
+// Worker workgroups for free rows: with workgroup 0, one wave of workgroups on
+// the 256 CUs (the kernel's registers allow one workgroup per CU).
+constexpr int kSpreadWorkers = 255;
 
 __device__ __forceinline__ bool ranges_meet(uintptr_t a, uintptr_t la, uintptr_t b, uintptr_t lb) {
     return a < b + lb && b < a + la;
@@ -1091,6 +1096,261 @@ __device__ __forceinline__ void serial_walk(const rmsn_desc* d, int32_t count, f
     }
 }
 
+// --- Free rows over many workgroups. A row whose reads and output meet no
+// other row's output, and whose output meets no other row's reads, can run at
+// any time, in any workgroup: the order of the table cannot be observed on it.
+// With more than one workgroup launched (tables of at most kSpanRows rows, no
+// position), workgroups 1..G-1 take such "free" rows (row j in workgroup
+// 1 + j mod (G-1)) while workgroup 0 runs the others ("bound" rows) in table
+// order. Both sides decide freeness from the same descriptors by the same
+// rule, so every row is run exactly once; no workgroup waits for another.
+
+struct RowSpan {
+    uintptr_t x, w, y, len;  // addresses and byte length; 0 for a width the kernels skip
+};
+
+template <typename T>
+__device__ __forceinline__ RowSpan row_span(const rmsn_desc& dj) {
+    const bool valid = dj.n >= 1 && dj.n <= RMSN_MAX_N;
+    return RowSpan{reinterpret_cast<uintptr_t>(dj.x), reinterpret_cast<uintptr_t>(dj.w),
+                   reinterpret_cast<uintptr_t>(dj.y),
+                   valid ? (uintptr_t)dj.n * sizeof(T) : (uintptr_t)0};
+}
+
+// Rows a and b (both non-empty) meet: one reads or writes memory the other
+// writes. Branch-free (bitwise operators): a few compares on one LDS load of
+// each row, not a chain of branches each waiting for its own load.
+__device__ __forceinline__ bool rows_meet(const RowSpan& a, const RowSpan& b) {
+    const uintptr_t ae = a.len, be = b.len;
+    const bool xb = (a.x < b.y + be) & (b.y < a.x + ae);   // a reads b's output (x)
+    const bool wb = (a.w < b.y + be) & (b.y < a.w + ae);   // a reads b's output (w)
+    const bool yy = (a.y < b.y + be) & (b.y < a.y + ae);   // outputs overlap
+    const bool xa = (b.x < a.y + ae) & (a.y < b.x + be);   // b reads a's output (x)
+    const bool wa = (b.w < a.y + ae) & (a.y < b.w + be);   // b reads a's output (w)
+    return (ae != 0) & (be != 0) & (xb | wb | yy | xa | wa);
+}
+
+// The same rows as 32-bit offsets from the table's lowest address with their
+// ends, when every row lies within 4 GB of it (as rows from one allocator
+// do): the test is then ten 32-bit compares. A row the kernels skip is all
+// 0xFFFFFFFF, which meets nothing.
+struct RowSpan32 {
+    uint32_t x, xe, w, we, y, ye;
+};
+
+__device__ __forceinline__ RowSpan32 row_span32(const RowSpan& r, uintptr_t base) {
+    if (r.len == 0) return RowSpan32{~0u, ~0u, ~0u, ~0u, ~0u, ~0u};
+    const uint32_t x = (uint32_t)(r.x - base), w = (uint32_t)(r.w - base);
+    const uint32_t y = (uint32_t)(r.y - base), l = (uint32_t)r.len;
+    return RowSpan32{x, x + l, w, w + l, y, y + l};
+}
+
+__device__ __forceinline__ bool rows_meet(const RowSpan32& a, const RowSpan32& b) {
+    return ((a.x < b.ye) & (b.y < a.xe)) | ((a.w < b.ye) & (b.y < a.we)) |
+           ((a.y < b.ye) & (b.y < a.ye)) | ((b.x < a.ye) & (a.y < b.xe)) |
+           ((b.w < a.ye) & (a.y < b.we));
+}
+
+// True in every thread when p holds in any thread of the workgroup (a ballot
+// per wavefront, one LDS word each, one barrier; the answer is read into a
+// scalar register). fold4 is free again when it returns.
+__device__ __forceinline__ bool workgroup_any(bool p, int* fold4) {
+    const int wave_any = __ballot(p) != 0;  // every lane takes part in the ballot
+    if ((threadIdx.x & 63) == 0) fold4[threadIdx.x >> 6] = wave_any;
+    __syncthreads();
+    const int any = fold4[0] | fold4[1] | fold4[2] | fold4[3];
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(any) != 0;
+}
+
+// One row, its pointers taken from the descriptor (a wave-uniform load), not
+// from the LDS copy used for the overlap tests.
+template <typename T>
+__device__ __forceinline__ void spread_row(const rmsn_desc& dj, float eps, float* lds4) {
+    persistent_row<T>(static_cast<const T*>(dj.x), static_cast<const T*>(dj.w),
+                      static_cast<T*>(dj.y), dj.n, eps, lds4);
+}
+
+// Whether any row of the table meets another one (rows_meet), decided in
+// O(count log count) rather than by testing every pair: the outputs are
+// sorted by start address (a bitonic sort in LDS); then no row meets another
+// exactly when each output ends at or before the next one starts and no
+// row's x or w range meets another row's output. Once the outputs are
+// disjoint their ends are sorted as well, so the first output that ends
+// past a read range's start is found by binary search, and the outputs that
+// meet that range follow it; a row's own output (in-place) is skipped, and
+// the one after it is then the next candidate. mine[r] is row
+// threadIdx.x + 256 r. Every thread gets the answer.
+template <int R>
+__device__ __forceinline__ bool any_row_meets(const RowSpan (&mine)[R], int32_t count,
+                                              int* fold4) {
+    __shared__ uint64_t o_start[kSpanRows], o_end[kSpanRows];
+    __shared__ uint16_t o_row[kSpanRows];
+    int32_t m = 2;
+    while (m < count) m <<= 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int32_t j = threadIdx.x + 256 * r;
+        if (j >= m) continue;
+        const bool out = j < count && mine[r].len != 0;  // an empty row writes nothing
+        o_start[j] = out ? (uint64_t)mine[r].y : ~0ull;
+        o_end[j] = out ? (uint64_t)(mine[r].y + mine[r].len) : ~0ull;
+        o_row[j] = (uint16_t)j;
+    }
+    __syncthreads();
+    for (int32_t k = 2; k <= m; k <<= 1) {
+        for (int32_t s = k >> 1; s > 0; s >>= 1) {
+            for (int32_t t = threadIdx.x; t < (m >> 1); t += 256) {
+                const int32_t i = 2 * t - (t & (s - 1)), l = i + s;
+                const uint64_t a = o_start[i], b = o_start[l];
+                if ((i & k) == 0 ? a > b : a < b) {
+                    const uint64_t ea = o_end[i], eb = o_end[l];
+                    const uint16_t ra = o_row[i], rb = o_row[l];
+                    o_start[i] = b;
+                    o_start[l] = a;
+                    o_end[i] = eb;
+                    o_end[l] = ea;
+                    o_row[i] = rb;
+                    o_row[l] = ra;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    bool meet = false;
+    for (int32_t i = threadIdx.x; i + 1 < m; i += 256)
+        meet |= (o_start[i + 1] != ~0ull) & (o_end[i] > o_start[i + 1]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int32_t j = threadIdx.x + 256 * r;
+        if (j >= count || mine[r].len == 0) continue;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint64_t a = q ? (uint64_t)mine[r].w : (uint64_t)mine[r].x;
+            const uint64_t b = a + mine[r].len;
+            int32_t p = 0, left = m;  // first p with o_end[p] > a
+            while (left > 0) {
+                const int32_t h = left >> 1;
+                if (o_end[p + h] <= a) {
+                    p += h + 1;
+                    left -= h + 1;
+                } else {
+                    left = h;
+                }
+            }
+            if (p < m && o_start[p] < b) {
+                if (o_row[p] != j) meet = true;
+                else if (p + 1 < m && o_start[p + 1] < b) meet = true;
+            }
+        }
+    }
+    return workgroup_any(meet, fold4);
+}
+
+// Which rows meet another row, on spans of type S in LDS (RowSpan or
+// RowSpan32). Workers (blockIdx > 0) test their row against every row, 256 at
+// a time, and run it when it meets none. In workgroup 0 wavefront v decides
+// rows v, v + 4, ...: its lanes test the row against 64 rows at a time and a
+// ballot gives the answer, so no lane writes inside the loop; then the marked
+// ("bound") rows run in table order, found 64 at a time by a ballot over the
+// marks. Returns as spread_rows does.
+template <typename T, typename S>
+__device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const rmsn_desc* d,
+                                          int32_t count, float eps, float* lds4, int* fold4) {
+    if (blockIdx.x != 0) {
+        const int32_t workers = (int32_t)gridDim.x - 1;
+        for (int32_t j = (int32_t)blockIdx.x - 1; j < count; j += workers) {
+            const S sj = span[j];
+            bool meet = false;
+            for (int32_t k = threadIdx.x; k < count; k += blockDim.x)
+                meet |= (k != j) & rows_meet(sj, span[k]);
+            if (workgroup_any(meet, fold4)) continue;  // bound: workgroup 0 runs it in order
+            spread_row<T>(d[j], eps, lds4);
+            __syncthreads();  // lds4 is reused by the next row
+        }
+        return true;
+    }
+    const int32_t wave = (int32_t)(threadIdx.x >> 6), lane = (int32_t)(threadIdx.x & 63);
+    for (int32_t j = wave; j < count; j += 4) {
+        const S sj = span[j];
+        bool meet = false;
+#pragma unroll 4
+        for (int32_t k = lane; k < count; k += 64) meet |= (k != j) & rows_meet(sj, span[k]);
+        const bool any = __ballot(meet) != 0;
+        if (lane == 0) bound[j] = any;
+    }
+    __syncthreads();
+    bool some_free = false;
+    for (int32_t j = threadIdx.x; j < count; j += blockDim.x) some_free = some_free || !bound[j];
+    if (!workgroup_any(some_free, fold4)) return false;
+    // the bound rows, row after row, in table order
+    for (int32_t j0 = 0; j0 < count; j0 += 64) {
+        unsigned long long marks = __ballot(j0 + lane < count && bound[j0 + lane] != 0);
+        while (marks) {
+            const int32_t j = j0 + __builtin_ctzll(marks);
+            marks &= marks - 1;
+            spread_row<T>(d[j], eps, lds4);
+            __syncthreads();  // this row's stores before the next bound row's loads
+        }
+    }
+    return true;
+}
+
+// Returns true when this workgroup's part of the table is done, false (in
+// workgroup 0 only) when no row is free, so the ordered walk takes the whole
+// table. (No row writes into the table itself: the walks read descriptors as
+// they go, and this step reads them all first.)
+template <typename T>
+__device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, float eps,
+                                            float* lds4, int* fold4) {
+    __shared__ RowSpan span[kSpanRows];   // 64-bit spans, or RowSpan32 in the same bytes
+    __shared__ uint8_t bound[kSpanRows];
+    __shared__ unsigned long long lo_hi[2];
+    if (threadIdx.x == 0) {
+        lo_hi[0] = ~0ull;
+        lo_hi[1] = 0ull;
+    }
+    __syncthreads();
+    constexpr int R = kSpanRows / 256;     // rows per thread (blockDim.x == 256)
+    RowSpan mine[R];
+    uint64_t lo = ~0ull, hi = 0ull;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int32_t j = threadIdx.x + 256 * r;
+        mine[r] = j < count ? row_span<T>(d[j]) : RowSpan{0, 0, 0, 0};
+        if (mine[r].len != 0) {
+            lo = min(lo, (uint64_t)min(mine[r].x, min(mine[r].w, mine[r].y)));
+            hi = max(hi, (uint64_t)max(mine[r].x, max(mine[r].w, mine[r].y)) + mine[r].len);
+        }
+    }
+    // no row meets another (the usual table): the workers run every row
+    if (blockIdx.x == 0 && !any_row_meets(mine, count, fold4)) return true;
+    // lowest and highest address: within the wavefront, then one LDS atomic each
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        lo = min(lo, (uint64_t)__shfl_xor((unsigned long long)lo, o, 64));
+        hi = max(hi, (uint64_t)__shfl_xor((unsigned long long)hi, o, 64));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        atomicMin(&lo_hi[0], (unsigned long long)lo);
+        atomicMax(&lo_hi[1], (unsigned long long)hi);
+    }
+    __syncthreads();
+    const uintptr_t base = (uintptr_t)lo_hi[0];
+    const bool narrow = lo_hi[1] <= lo_hi[0] || lo_hi[1] - lo_hi[0] < 0xFFFFFFFFull;
+    RowSpan32* span32 = reinterpret_cast<RowSpan32*>(span);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int32_t j = threadIdx.x + 256 * r;
+        if (j >= count) continue;
+        if (narrow) span32[j] = row_span32(mine[r], base);
+        else span[j] = mine[r];
+    }
+    __syncthreads();
+    return narrow ? spread_on<T>(span32, bound, d, count, eps, lds4, fold4)
+                  : spread_on<T>(static_cast<const RowSpan*>(span), bound, d, count, eps, lds4, fold4);
+}
+
 template <typename T, bool POS>
 __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __restrict__ d,
                                                              int32_t count, float eps,
@@ -1104,6 +1364,9 @@ __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __
         const uint64_t raw = (uint64_t)*pa.d_pos;
         pos = raw < per ? raw : raw % per;
     }
+    // the launcher gives more than one workgroup only to position-free tables
+    // of at most kSpanRows rows
+    if (!POS && gridDim.x > 1 && spread_rows<T>(d, count, eps, lds4, lds_fold)) return;
     switch (walk_mode<T, POS>(d, count, pos, pa, lds_fold)) {
         case kRoundWalk16: round_walk<T, POS, 4>(d, count, eps, pos, pa); break;
         case kRoundWalk4: round_walk<T, POS, 1>(d, count, eps, pos, pa); break;
@@ -1327,7 +1590,10 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
 hipError_t launch_sequence_persistent(int dtype, const rmsn_desc* d, int32_t count, float eps,
                                      const PosArgs* pos, hipStream_t stream) {
     const PosArgs none{nullptr, 0, 0, 1};
-    const dim3 grid(1), block(kBlockThreads);
+    // workgroup 0 plus one worker per row (at most kSpreadWorkers) for free rows
+    const bool spread = pos == nullptr && count > 1 && count <= kSpanRows &&
+                        option_persistent_workgroups() == 0;
+    const dim3 grid(spread ? 1u + (unsigned)std::min(count, kSpreadWorkers) : 1u), block(kBlockThreads);
     if (dtype == RMSN_F32) {
         if (pos)
             hipLaunchKernelGGL((k_sequence_persistent<float, true>), grid, block, 0, stream, d,

@@ -21,6 +21,7 @@ std::atomic<int> g_rpb{-2};
 std::atomic<int> g_stream{-2};
 std::atomic<int> g_split{-2};
 std::atomic<int> g_apply{-2};
+std::atomic<int> g_pwg{-2};
 
 int env_int(const char* name, int dflt) {
     const char* s = std::getenv(name);
@@ -39,6 +40,7 @@ bool valid_split_loads(int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v
 bool valid_apply_threads(int v) { return v == 0 || v == 128 || v == 256 || v == 512 || v == 1024; }
 bool valid_rpb(int v) { return v == 0 || v == 4 || v == 8; }
 bool valid_streaming(int v) { return v == -1 || v == 0 || v == 1; }
+bool valid_persistent_wg(int v) { return v == 0 || v == 1; }
 
 // Byte ranges [a, a+la) and [b, b+lb) intersect.
 bool overlaps(uintptr_t a, uint64_t la, uintptr_t b, uint64_t lb) {
@@ -107,6 +109,16 @@ int option_apply_threads() {
     return v;
 }
 
+int option_persistent_workgroups() {
+    int v = g_pwg.load(std::memory_order_relaxed);
+    if (v == -2) {
+        v = env_int("RMSN_PERSISTENT_WORKGROUPS", 0);
+        if (!valid_persistent_wg(v)) v = 0;
+        g_pwg.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 int set_option(int key, int value) {
     if (key == RMSN_OPT_PATH) {
         if (!valid_path(value)) {
@@ -154,6 +166,15 @@ int set_option(int key, int value) {
         g_apply.store(value, std::memory_order_relaxed);
         return RMSN_OK;
     }
+    if (key == RMSN_OPT_PERSISTENT_WORKGROUPS) {
+        if (!valid_persistent_wg(value)) {
+            set_error("rmsnorm_set_option: persistent workgroups must be 0 (automatic) or 1, got %d",
+                      value);
+            return RMSN_EINVAL;
+        }
+        g_pwg.store(value, std::memory_order_relaxed);
+        return RMSN_OK;
+    }
     set_error("rmsnorm_set_option: unknown key %d", key);
     return RMSN_EINVAL;
 }
@@ -171,6 +192,7 @@ int get_option(int key, int* value) {
         *value = kAssocLanes == 128 ? option_apply_threads() : 0;
         return RMSN_OK;
     }
+    if (key == RMSN_OPT_PERSISTENT_WORKGROUPS) { *value = option_persistent_workgroups(); return RMSN_OK; }
     set_error("rmsnorm_get_option: unknown key %d", key);
     return RMSN_EINVAL;
 }

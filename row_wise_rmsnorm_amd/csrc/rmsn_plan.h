@@ -113,6 +113,7 @@ int option_rows_per_block();  // 0 automatic, else 4 or 8
 int option_streaming();       // -1 automatic, 0 off, 1 on
 int option_split_loads();     // 0 automatic, else 1, 2, 4 or 8
 int option_apply_threads();   // 128-lane build: 0 (= 1024) or 128, 256, 512, 1024
+int option_persistent_workgroups();  // 0 automatic, 1 one workgroup
 int set_option(int key, int value);
 int get_option(int key, int* value);
 

@@ -99,6 +99,15 @@ def step(rn):
     return Step(rn, wl.decode())
 
 
+@pytest.fixture(params=[0, 1], ids=["spread", "one-workgroup"])
+def pwg(rn, request):
+    """The persistent launch with free rows spread over many workgroups (the
+    default) or the whole table walked by one workgroup."""
+    rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, request.param)
+    yield request.param
+    rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 0)
+
+
 @pytest.fixture(params=["auto", "block", "group"])
 def desc_path(rn, request):
     """Plan the captured nodes (and the eager arm) with the automatic choice,
@@ -529,7 +538,7 @@ def test_update_recaptures_only_when_the_plan_moves(rn, step):
 
 # ---- the whole step in one launch -------------------------------------------------
 
-def test_persistent_step_matches_oracle_and_eager(rn, step):
+def test_persistent_step_matches_oracle_and_eager(rn, step, pwg):
     """One launch walks the 327 descriptors in order: the bits of the eager
     sequence and of the oracle, on two tables."""
     say("persistent decode step")
@@ -549,7 +558,7 @@ def test_persistent_step_matches_oracle_and_eager(rn, step):
 
 @pytest.mark.parametrize("kind,n,offset", [("f32", 7168, 0), ("f32", 1000, 1), ("bf16", 1536, 0),
                                            ("bf16", 9000, 3), ("f32", 8193, 0)])
-def test_persistent_dependent_chain(rn, kind, n, offset):
+def test_persistent_dependent_chain(rn, kind, n, offset, pwg):
     """Rows that depend on earlier outputs: norm i reads buffer i and writes
     buffer i+1 (and the last norm works in place), so each row must see the
     previous row's stores -- the order the launch sequence gives."""
@@ -603,7 +612,7 @@ def test_persistent_positioned_ring(rn, kind, n, norms):
     _check_ring(ring, {0, 1, 2, 3})
 
 
-def test_persistent_call_captured_in_a_graph(rn, step):
+def test_persistent_call_captured_in_a_graph(rn, step, pwg):
     """The single launch captured by the caller: replays follow table
     rewrites (three replays, the oracle each time)."""
     import torch
@@ -672,7 +681,7 @@ ROUND_WIDTHS = [8, 16, 64, 256, 264, 512, 1000, 1024, 1032, 3000, 4104, 8184, 81
 @pytest.mark.parametrize("kind,widths", [("f32", PIPE_WIDTHS), ("bf16", PIPE_WIDTHS),
                                          ("f32", ROUND_WIDTHS), ("bf16", ROUND_WIDTHS)],
                          ids=["f32-mult4", "bf16-mult4", "f32-mult8", "bf16-mult8"])
-def test_persistent_walk_widths(rn, kind, widths):
+def test_persistent_walk_widths(rn, kind, widths, pwg):
     """Independent rows of every kind of width the fast walks take: multiples
     of 4 (bf16: the pipelined walk; binary32: the round walk) and of 8 (the
     round walk), from 4 to 8192, partial and exact slices and blocks."""
@@ -694,7 +703,7 @@ def test_persistent_walk_widths(rn, kind, widths):
 @pytest.mark.parametrize("kind,odd", [("f32", "width 4097"), ("f32", "width 9000"),
                                       ("f32", "misaligned"), ("bf16", "width 1001"),
                                       ("bf16", "misaligned")])
-def test_persistent_table_with_a_row_the_pipeline_cannot_take(rn, kind, odd):
+def test_persistent_table_with_a_row_the_pipeline_cannot_take(rn, kind, odd, pwg):
     """One row the GROUP mapping cannot take sends the whole table down the
     row-after-row walk; every row still matches the oracle."""
     import torch
@@ -722,7 +731,7 @@ def test_persistent_table_with_a_row_the_pipeline_cannot_take(rn, kind, odd):
 
 @pytest.mark.parametrize("kind,n", [("f32", 2048), ("bf16", 2048), ("bf16", 2044)])
 @pytest.mark.parametrize("dist", [1, 2, 3, 4, 5, 8, 16, 17, 64, 65])
-def test_persistent_dependency_at_distance(rn, kind, n, dist):
+def test_persistent_dependency_at_distance(rn, kind, n, dist, pwg):
     """Row j reads the output of row j - dist (rows 0 .. dist-1 read fresh
     inputs). Distances 1 to 3 must take the row-after-row walk; 4 to 15 the
     round walk with a barrier every 4 rows (width 2048) or the pipelined walk
@@ -750,7 +759,7 @@ def test_persistent_dependency_at_distance(rn, kind, n, dist):
 
 
 @pytest.mark.parametrize("shift", [0, 4, 1000])
-def test_persistent_adjacent_rows_writing_the_same_memory(rn, shift):
+def test_persistent_adjacent_rows_writing_the_same_memory(rn, shift, pwg):
     """Row j writes memory row j - 1 also writes (the same buffer, or shifted
     by `shift` elements): the later row's values must win, as in the sequence."""
     import torch
@@ -777,7 +786,7 @@ def test_persistent_adjacent_rows_writing_the_same_memory(rn, shift):
 
 
 @pytest.mark.parametrize("kind,n", [("f32", 2048), ("bf16", 2044)])
-def test_persistent_row_reads_what_a_later_row_overwrites(rn, kind, n):
+def test_persistent_row_reads_what_a_later_row_overwrites(rn, kind, n, pwg):
     """Row j reads buffer B that row j + 1 then overwrites: row j must see B's
     old contents, as in the sequence (no round walk for such a round; the
     pipelined walk, where it applies, issues row j's loads before row j + 1's
@@ -830,7 +839,7 @@ def test_persistent_table_beyond_the_lds_check(rn, dist):
 
 
 @pytest.mark.parametrize("arm", ["graph", "eager", "persistent"])
-def test_rows_with_out_of_range_widths_write_nothing(rn, desc_path, arm):
+def test_rows_with_out_of_range_widths_write_nothing(rn, desc_path, arm, pwg):
     """A descriptor whose width, rewritten in the device table, is outside
     [1, 2^24] (0, negative, 2^24 + 1) makes its row write nothing; the rows
     around it are still exact. The host widths stay the valid capture-time
@@ -868,3 +877,58 @@ def test_rows_with_out_of_range_widths_write_nothing(rn, desc_path, arm):
                 assert_bits_f32(got, oracle.row_f32(x, w, wl.EPS), f"rep {rep} row {i}")
     if g is not None:
         g.destroy()
+
+
+def _apply_in_order(rows, host, kind):
+    """The launch sequence on the CPU: every row, in table order, on copies of
+    the buffers (rows are ((buffer, offset, n), w, y) slices)."""
+    want = [h.copy() for h in host]
+    row_fn = oracle.row_bf16 if kind == "bf16" else oracle.row_f32
+    for (xb, xo, n), (wb, wo, _), (yb, yo, _) in rows:
+        want[yb][yo:yo + n] = row_fn(want[xb][xo:xo + n].copy(), want[wb][wo:wo + n].copy(), wl.EPS)
+    return want
+
+
+def test_persistent_spread_mixed_table(rn, pwg):
+    """Free rows (their own buffers, an in-place one, several reading one x and
+    one w), a chain of rows each reading the previous one's output, and two
+    rows writing the same output, interleaved in one table: every buffer ends
+    as the rows applied in table order on the CPU leave it."""
+    import torch
+    say(f"persistent mixed table, workgroups option {pwg}")
+    g = np.random.Generator(np.random.PCG64(77))
+    sizes, rows = [], []
+
+    def buf(n):
+        sizes.append(n + 8)
+        return len(sizes) - 1
+
+    shared_x, shared_w = buf(1536), buf(1536)
+    chain = [buf(2048) for _ in range(6)]
+    twice = buf(512)
+    chain_w = buf(2048)
+    plan = []
+    for i in range(40):
+        kind_of = i % 5
+        if kind_of == 0 and i // 5 < 5:                 # chain step i//5: reads chain[k], writes chain[k+1]
+            k = i // 5
+            plan.append(((chain[k], 0, 2048), (chain_w, 0, 2048), (chain[k + 1], 0, 2048)))
+        elif kind_of == 1:                              # free row reading the shared x and w
+            plan.append(((shared_x, 0, 1536), (shared_w, 0, 1536), (buf(1536), 0, 1536)))
+        elif kind_of == 2 and i in (7, 27):             # two rows writing the same output
+            plan.append(((buf(512), 0, 512), (buf(512), 0, 512), (twice, 0, 512)))
+        elif kind_of == 3:                              # free row in place
+            b = buf(7168)
+            plan.append(((b, 4, 7164), (buf(7164), 0, 7164), (b, 4, 7164)))
+        else:                                           # free row on its own buffers
+            n = int(g.choice([64, 512, 1000, 7168, 9000]))
+            plan.append(((buf(n), 0, n), (buf(n), 0, n), (buf(n), 0, n)))
+    host = [wl.misc_f32(88_000 + b, size)[0] for b, size in enumerate(sizes)]
+    want = _apply_in_order(plan, host, "f32")
+    bufs = [to_dev_f32(h) for h in host]
+    table, _ = rn.make_table([(bufs[xb][xo:xo + n], bufs[wb][wo:wo + n], bufs[yb][yo:yo + n])
+                              for (xb, xo, n), (wb, wo, _), (yb, yo, _) in plan])
+    rn.rmsnorm_sequence_persistent(table, len(plan), wl.EPS, rn.F32)
+    sync()
+    for b, t in enumerate(bufs):
+        assert_bits_f32(f32_host(t), want[b], f"buffer {b}")

@@ -4,13 +4,16 @@ sequence, bit for bit against the rows applied in order on the CPU.
 Each table draws a dtype, a row count, a width class (multiples of 8, 4 mod
 8, arbitrary with a few beyond 8192) and per row a width of that class,
 element offsets, and where its x, w and y live: fresh buffers, or x reading
-what an earlier row wrote (at distances of 4-20, 16-40, or 1 and more), x
+what an earlier row wrote (at distances of 4-20, 16-40, 1 and more, or every
+row the one before), x
 reading a buffer a later row overwrites, y rewriting the row before's
 output. The CPU model keeps every buffer's contents and applies the
 oracle row by row in table order -- the semantics of the launch sequence --
 and the whole of every buffer, padding included, must match after the
-persistent launch and after the eager sequence. Which of the persistent
-kernel's walks a table takes depends on what it draws; all must agree.
+persistent launch (free rows spread over workgroups, and the whole table in
+one workgroup) and after the eager sequence. Which of the persistent kernel's
+walks a table takes, and how many of its rows are free, depends on what it
+draws; all must agree.
 """
 import numpy as np
 import pytest
@@ -49,10 +52,11 @@ def _width(g, cls):
 def _table(g):
     """A list of rows (x, w, y), each a (buffer, offset, n) slice, and the
     buffer sizes. The table's kind decides its dependencies: none, only at
-    distances of 4 to 20 rows, of 16 to 40 rows, or anywhere (from 1)."""
+    distances of 4 to 20 rows, of 16 to 40 rows, anywhere (from 1), or a
+    chain (every row reads the output of the row before)."""
     count = int(g.choice([1, 2, 3, 5, 9, 16, 17, 33, 64]))
     aligned = g.random() < 0.7
-    deps = str(g.choice(["none", "none", "far", "far", "farther", "any"]))
+    deps = str(g.choice(["none", "none", "far", "far", "farther", "any", "chain"]))
     cls = str(g.choice(["vec", "vec", "quad", "any"]))
     rate = float(g.choice([0.05, 0.15, 0.3]))
     sizes, rows = [], []
@@ -66,7 +70,10 @@ def _table(g):
     lo, hi = {"far": (4, 20), "farther": (16, 40)}.get(deps, (1, 20))
     for j in range(count):
         r = g.random()
-        if deps != "none" and j >= lo and r < rate:
+        if deps == "chain" and j > 0:                     # every row reads the row before's output
+            x = rows[j - 1][2]
+            n = x[2]
+        elif deps not in ("none", "chain") and j >= lo and r < rate:
             d = int(g.integers(lo, min(j, hi) + 1))        # read an earlier row's output
             x = rows[j - d][2]
             n = x[2]
@@ -139,7 +146,28 @@ def _walk(rows, es):
     return "row-after-row"
 
 
+def _free_kinds(rows, es):
+    """'all free', 'mixed' or 'all bound': rows whose reads and output meet no
+    other row's output and whose output meets no other row's reads are free
+    (the persistent launch spreads them over workgroups)."""
+    base = {}
+    rng = []
+    for x, w, y in rows:
+        rng.append([(base.setdefault(b, len(base) << 32) + o * es, n * es) for b, o, n in (x, w, y)])
+
+    def meet(a, b):
+        return a[1] > 0 and b[1] > 0 and a[0] < b[0] + b[1] and b[0] < a[0] + a[1]
+
+    def meets_output(j, k):
+        return any(meet(rng[j][i], rng[k][2]) for i in range(3))
+
+    free = [not any(k != j and (meets_output(j, k) or meets_output(k, j)) for k in range(len(rows)))
+            for j in range(len(rows))]
+    return "all free" if all(free) else ("all bound" if not any(free) else "mixed")
+
+
 WALKS_SEEN = set()
+SPREAD_SEEN = set()
 
 
 @pytest.mark.parametrize("block", range(4))
@@ -150,6 +178,8 @@ def test_persistent_fuzz(rn, block):
         rows, sizes = _table(g)
         walk = _walk(rows, 2 if kind == "bf16" else 4)
         WALKS_SEEN.add(walk)
+        if len(rows) > 1:
+            SPREAD_SEEN.add(_free_kinds(rows, 2 if kind == "bf16" else 4))
         say(f"persistent fuzz block {block} table {t}: {kind}, {len(rows)} rows, {walk}, "
             f"widths {[r[0][2] for r in rows][:12]}...")
         seed = 3_000_000 + 10_000 * block + 100 * t
@@ -171,13 +201,17 @@ def test_persistent_fuzz(rn, block):
             tdt, dtype = torch.float32, rn.F32
             todev = lambda a: torch.from_numpy(a.copy()).to(dev())
             tohost = lambda t_: t_.cpu().numpy()
-        for arm in ("persistent", "eager"):
+        for arm in ("persistent", "persistent one workgroup", "eager"):
             bufs = [todev(h) for h in host]
             table, widths = rn.make_table([(bufs[xb][xo:xo + n], bufs[wb][wo:wo + n],
                                             bufs[yb][yo:yo + n])
                                            for (xb, xo, n), (wb, wo, _), (yb, yo, _) in rows])
-            if arm == "persistent":
-                rn.rmsnorm_sequence_persistent(table, len(rows), wl.EPS, dtype)
+            if arm.startswith("persistent"):
+                rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 1 if arm.endswith("workgroup") else 0)
+                try:
+                    rn.rmsnorm_sequence_persistent(table, len(rows), wl.EPS, dtype)
+                finally:
+                    rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 0)
             else:
                 rn.rmsnorm_sequence_eager(table, widths, wl.EPS, dtype)
             torch.cuda.synchronize()
@@ -192,7 +226,9 @@ def test_persistent_fuzz(rn, block):
 
 
 def test_persistent_fuzz_reached_every_walk():
-    """The tables above drew conditions for each of the four walks."""
+    """The tables above drew conditions for each of the four walks of one
+    workgroup, and tables whose rows are all free, partly free and all bound."""
     if len(WALKS_SEEN) == 0:
         pytest.skip("the fuzz tables did not run in this session")
     assert WALKS_SEEN == {"round16", "round4", "pipelined", "row-after-row"}, WALKS_SEEN
+    assert SPREAD_SEEN == {"all free", "mixed", "all bound"}, SPREAD_SEEN
