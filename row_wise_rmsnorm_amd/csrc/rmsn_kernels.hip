@@ -1172,51 +1172,67 @@ __device__ __forceinline__ void spread_row(const rmsn_desc& dj, float eps, float
 }
 
 // Whether any row of the table meets another one (rows_meet), decided in
-// O(count log count) rather than by testing every pair: the outputs are
-// sorted by start address (a bitonic sort in LDS); then no row meets another
-// exactly when each output ends at or before the next one starts and no
-// row's x or w range meets another row's output. Once the outputs are
-// disjoint their ends are sorted as well, so the first output that ends
-// past a read range's start is found by binary search, and the outputs that
-// meet that range follow it; a row's own output (in-place) is skipped, and
-// the one after it is then the next candidate. mine[r] is row
-// threadIdx.x + 256 r. Every thread gets the answer.
+// O(count log count) rather than by testing every pair: the outputs are put
+// in order of start address; then no row meets another exactly when each
+// output ends at or before the next one starts and no row's x or w range
+// meets another row's output. Once the outputs are disjoint their ends are
+// in order as well, so the first output that ends past a read range's start
+// is found by binary search, and the outputs that meet that range follow it;
+// a row's own output (in-place) is skipped, and the one after it is then the
+// next candidate. The order is a rank sort: the key start * 2^16 + row is
+// unique, and each lane counts the keys below its own, reading them as LDS
+// broadcasts with no barrier between steps. An output past 2^48 (beyond the
+// key) returns true, leaving the decision to the exact all-pairs test.
+// mine[r] is row threadIdx.x + 256 r. Every thread gets the answer.
+template <int RE, int R>
+__device__ __forceinline__ void key_ranks(const uint64_t* o_key, int32_t count,
+                                          const uint64_t (&key)[R], int32_t (&rank)[R]) {
+#pragma unroll 8
+    for (int32_t k = 0; k < count; ++k) {
+        const uint64_t kk = o_key[k];  // the same word in every lane
+#pragma unroll
+        for (int r = 0; r < RE; ++r) rank[r] += kk < key[r] ? 1 : 0;
+    }
+}
+
 template <int R>
 __device__ __forceinline__ bool any_row_meets(const RowSpan (&mine)[R], int32_t count,
                                               int* fold4) {
-    __shared__ uint64_t o_start[kSpanRows], o_end[kSpanRows];
+    __shared__ uint64_t o_key[kSpanRows], o_start[kSpanRows], o_end[kSpanRows];
     __shared__ uint16_t o_row[kSpanRows];
+    constexpr uint64_t kNoOutput = 0xFFFFFFFFFFFFull;  // the key's start for an empty row
     int32_t m = 2;
     while (m < count) m <<= 1;
+    uint64_t key[R];
+    int32_t rank[R];
+    bool high = false;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int32_t j = threadIdx.x + 256 * r;
+        const bool out = j < count && mine[r].len != 0;  // an empty row writes nothing
+        high |= out && ((uint64_t)(mine[r].y + mine[r].len) >> 48) != 0;
+        key[r] = ((out ? (uint64_t)mine[r].y : kNoOutput) << 16) | (uint64_t)j;
+        rank[r] = 0;
+        if (j < count) o_key[j] = key[r];
+    }
+    if (workgroup_any(high, fold4)) return true;  // its barrier also publishes o_key
+    switch ((count + 255) >> 8) {
+        case 1: key_ranks<1>(o_key, count, key, rank); break;
+        case 2: key_ranks<2>(o_key, count, key, rank); break;
+        case 3: key_ranks<3>(o_key, count, key, rank); break;
+        default: key_ranks<4>(o_key, count, key, rank); break;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int32_t j = threadIdx.x + 256 * r;
         if (j >= m) continue;
-        const bool out = j < count && mine[r].len != 0;  // an empty row writes nothing
-        o_start[j] = out ? (uint64_t)mine[r].y : ~0ull;
-        o_end[j] = out ? (uint64_t)(mine[r].y + mine[r].len) : ~0ull;
-        o_row[j] = (uint16_t)j;
+        const bool out = j < count && mine[r].len != 0;
+        const int32_t p = j < count ? rank[r] : j;  // padding sorts after every row
+        o_start[p] = out ? (uint64_t)mine[r].y : ~0ull;
+        o_end[p] = out ? (uint64_t)(mine[r].y + mine[r].len) : ~0ull;
+        o_row[p] = (uint16_t)j;
     }
     __syncthreads();
-    for (int32_t k = 2; k <= m; k <<= 1) {
-        for (int32_t s = k >> 1; s > 0; s >>= 1) {
-            for (int32_t t = threadIdx.x; t < (m >> 1); t += 256) {
-                const int32_t i = 2 * t - (t & (s - 1)), l = i + s;
-                const uint64_t a = o_start[i], b = o_start[l];
-                if ((i & k) == 0 ? a > b : a < b) {
-                    const uint64_t ea = o_end[i], eb = o_end[l];
-                    const uint16_t ra = o_row[i], rb = o_row[l];
-                    o_start[i] = b;
-                    o_start[l] = a;
-                    o_end[i] = eb;
-                    o_end[l] = ea;
-                    o_row[i] = rb;
-                    o_row[l] = ra;
-                }
-            }
-            __syncthreads();
-        }
-    }
     bool meet = false;
     for (int32_t i = threadIdx.x; i + 1 < m; i += 256)
         meet |= (o_start[i + 1] != ~0ull) & (o_end[i] > o_start[i + 1]);
