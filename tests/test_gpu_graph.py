@@ -932,3 +932,50 @@ def test_persistent_spread_mixed_table(rn, pwg):
     sync()
     for b, t in enumerate(bufs):
         assert_bits_f32(f32_host(t), want[b], f"buffer {b}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("what", ["x", "w", "y", "touch"])
+@pytest.mark.parametrize("writer_first", [True, False], ids=["writer_first", "reader_first"])
+def test_persistent_spread_one_element_overlap(rn, pwg, what, writer_first):
+    """Among 60 free rows, one row's x (or w, or output) shares exactly one
+    element with another row's output: the writer's last element is the
+    other range's first. Those two rows must keep table order. With 'touch'
+    the other x starts just past the writer's output, so nothing is shared
+    and every row is free. Every buffer ends as the rows applied in table
+    order on the CPU leave it."""
+    say(f"persistent one-element overlap {what}, writer first {writer_first}, "
+        f"workgroups option {pwg}")
+    n = 512
+    sizes, plan = [], []
+
+    def buf(m):
+        sizes.append(m)
+        return len(sizes) - 1
+
+    big = buf(2 * n)                       # the writer's output is big[0:n]
+    start = n if what == "touch" else n - 1
+    writer = ((buf(n), 0, n), (buf(n), 0, n), (big, 0, n))
+    if what == "y":
+        other = ((buf(n), 0, n), (buf(n), 0, n), (big, start, n))
+    elif what == "w":
+        other = ((buf(n), 0, n), (big, start, n), (buf(n), 0, n))
+    else:
+        other = ((big, start, n), (buf(n), 0, n), (buf(n), 0, n))
+    first, second = (writer, other) if writer_first else (other, writer)
+    for i in range(62):
+        if i == 20:
+            plan.append(first)
+        elif i == 41:
+            plan.append(second)
+        else:
+            plan.append(((buf(n), 0, n), (buf(n), 0, n), (buf(n), 0, n)))
+    host = [wl.misc_f32(91_000 + b, size)[0] for b, size in enumerate(sizes)]
+    want = _apply_in_order(plan, host, "f32")
+    bufs = [to_dev_f32(h) for h in host]
+    table, _ = rn.make_table([(bufs[xb][xo:xo + m], bufs[wb][wo:wo + m], bufs[yb][yo:yo + m])
+                              for (xb, xo, m), (wb, wo, _), (yb, yo, _) in plan])
+    rn.rmsnorm_sequence_persistent(table, len(plan), wl.EPS, rn.F32)
+    sync()
+    for b, t in enumerate(bufs):
+        assert_bits_f32(f32_host(t), want[b], f"buffer {b}")
