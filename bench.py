@@ -469,6 +469,17 @@ def bench_decode_positioned(rn, torch, np, wl, decode_steps, period=4):
     torch.cuda.synchronize()
     ok = ok and int(d_pos.item()) == 0
     ok = ok and all(np.array_equal(a, y.cpu().numpy().view(np.uint32)) for a, y in zip(want, ys))
+    # the same cycle as one persistent launch per step (its norms share no
+    # memory: spread over workgroups, the position advanced by its own launch)
+    pers = lambda i: rn.rmsnorm_sequence_persistent(table, len(widths), eps, rn.F32, position=pos)
+    for y in ys:
+        y.fill_(float("nan"))
+    torch.cuda.synchronize()
+    for _ in range(period):
+        pers(0)
+    torch.cuda.synchronize()
+    ok_p = int(d_pos.item()) == 0
+    ok_p = ok_p and all(np.array_equal(a, y.cpu().numpy().view(np.uint32)) for a, y in zip(want, ys))
     for i in range(20):
         eager(i)
         graph(i)
@@ -483,21 +494,33 @@ def bench_decode_positioned(rn, torch, np, wl, decode_steps, period=4):
         eager(i)
         graph(i)
         graph1(i)
-    res = {"A": [], "B": [], "C": []}
-    for a in ["A", "B", "C", "C", "B", "A"] * 2:
-        fn = {"A": eager, "B": graph, "C": graph1}[a]
+    for i in range(20):
+        pers(i)
+    res = {"A": [], "B": [], "C": [], "D": []}
+    for a in ["A", "B", "C", "D", "D", "C", "B", "A"] * 2:
+        fn = {"A": eager, "B": graph, "C": graph1, "D": pers}[a]
         res[a].append(1000.0 * elapsed_ms(fn, decode_steps) / decode_steps)
+    rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 1)
+    try:
+        pers(0)
+        one_wg = [1000.0 * elapsed_ms(pers, decode_steps) / decode_steps for _ in range(2)]
+    finally:
+        rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 0)
     nodes = g.node_count()
     g.destroy()
     g1.destroy()
-    e, gr, g1s = stats(res["A"]), stats(res["B"]), stats(res["C"])
+    e, gr, g1s, ps = stats(res["A"]), stats(res["B"]), stats(res["C"]), stats(res["D"])
     return {"eager_us_per_step": e, "graph_us_per_step": gr,
-            "graph_period1_us_per_step": g1s,
+            "graph_period1_us_per_step": g1s, "persistent_us_per_step": ps,
+            "persistent_one_workgroup_us_per_step": stats(one_wg),
+            "bit_exact_one_cycle_persistent_eq_eager": bool(ok_p),
             "speedup_graph_over_eager": e["mean"] / gr["mean"], "graph_nodes": nodes,
             "period": period, "bit_exact_one_cycle_graph_eq_eager": bool(ok),
             "note": ("327 norm nodes + 1 position-update node; each replay normalises the next "
                      "position's rows, no host work between replays; graph_period1: the same "
-                     "graph on a ring of one position (same rows every step); ABCCBA x 2")}
+                     "graph on a ring of one position (same rows every step); persistent: one "
+                     "launch per step spread over workgroups plus the position's update launch; "
+                     "ABCDDCBA x 2")}
 
 
 def cpu_baseline(np, wl, host):
@@ -673,7 +696,9 @@ def main():
         f"{dec['persistent_chained_table_us_per_step']['mean']:.1f})")
     decp = bench_decode_positioned(rn, torch, np, wl, args.decode_steps)
     log(f"decode positioned eager {decp['eager_us_per_step']['mean']:.1f} us  "
-        f"graph {decp['graph_us_per_step']['mean']:.1f} us")
+        f"graph {decp['graph_us_per_step']['mean']:.1f} us  "
+        f"persistent {decp['persistent_us_per_step']['mean']:.1f} us "
+        f"(one workgroup {decp['persistent_one_workgroup_us_per_step']['mean']:.1f})")
     traffic, traffic_rec = measured_traffic()
     gpu_s = time.time() - t_start
     cpu = None

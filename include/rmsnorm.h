@@ -225,13 +225,15 @@ int rmsnorm_sequence_graph_update(rmsn_graph* g, const int64_t* h_widths, int32_
  * is finished -- its stores ordered before the next row's loads by a
  * workgroup barrier -- before the next starts, so a table in which a later x
  * is an earlier y (y_i == x_j, i < j) computes exactly what the launch
- * sequence computes. Tables with a position or of more than 1024 rows, and
+ * sequence computes. Tables of more than 1024 rows, and
  * RMSN_OPT_PERSISTENT_WORKGROUPS = 1, keep every row in one workgroup.
  * Widths come from the table (any n in [1, 2^24], any element alignment); no
  * host widths are needed. No row may write into the descriptor table itself.
  * pos: NULL, or the rows are taken at the position as in
  * rmsnorm_sequence_eager_positioned and the position is advanced after the
- * last row. Nothing is allocated or synchronised, so the call may itself be
+ * last row (when the rows are spread over workgroups, by a second, one-thread
+ * launch on the same stream, so that every workgroup reads the same
+ * position). Nothing is allocated or synchronised, so the call may itself be
  * captured into a caller's graph. RMSN_EINVAL: bad dtype, d_table null or not
  * 8-byte aligned, count outside [1, RMSN_MAX_SEQUENCE], bad eps or
  * position. */

@@ -1099,21 +1099,25 @@ __device__ __forceinline__ void serial_walk(const rmsn_desc* d, int32_t count, f
 // --- Free rows over many workgroups. A row whose reads and output meet no
 // other row's output, and whose output meets no other row's reads, can run at
 // any time, in any workgroup: the order of the table cannot be observed on it.
-// With more than one workgroup launched (tables of at most kSpanRows rows, no
-// position), workgroups 1..G-1 take such "free" rows (row j in workgroup
-// 1 + j mod (G-1)) while workgroup 0 runs the others ("bound" rows) in table
-// order. Both sides decide freeness from the same descriptors by the same
+// With more than one workgroup launched (tables of at most kSpanRows rows; a
+// positioned table's rows taken at its position), workgroups 1..G-1 take such
+// "free" rows (row j in workgroup 1 + j mod (G-1)) while workgroup 0 runs the
+// others ("bound" rows) in table order. Both sides decide freeness from the same descriptors by the same
 // rule, so every row is run exactly once; no workgroup waits for another.
 
 struct RowSpan {
     uintptr_t x, w, y, len;  // addresses and byte length; 0 for a width the kernels skip
 };
 
-template <typename T>
-__device__ __forceinline__ RowSpan row_span(const rmsn_desc& dj) {
+template <typename T, bool POS>
+__device__ __forceinline__ RowSpan row_span(const rmsn_desc& dj, uint64_t pos, const PosArgs& pa) {
+    const T* x;
+    const T* w;
+    T* y;
+    persistent_ptrs<T, POS>(dj, pos, pa, x, w, y);  // the row where it is taken at this position
     const bool valid = dj.n >= 1 && dj.n <= RMSN_MAX_N;
-    return RowSpan{reinterpret_cast<uintptr_t>(dj.x), reinterpret_cast<uintptr_t>(dj.w),
-                   reinterpret_cast<uintptr_t>(dj.y),
+    return RowSpan{reinterpret_cast<uintptr_t>(x), reinterpret_cast<uintptr_t>(w),
+                   reinterpret_cast<uintptr_t>(y),
                    valid ? (uintptr_t)dj.n * sizeof(T) : (uintptr_t)0};
 }
 
@@ -1165,10 +1169,14 @@ __device__ __forceinline__ bool workgroup_any(bool p, int* fold4) {
 
 // One row, its pointers taken from the descriptor (a wave-uniform load), not
 // from the LDS copy used for the overlap tests.
-template <typename T>
-__device__ __forceinline__ void spread_row(const rmsn_desc& dj, float eps, float* lds4) {
-    persistent_row<T>(static_cast<const T*>(dj.x), static_cast<const T*>(dj.w),
-                      static_cast<T*>(dj.y), dj.n, eps, lds4);
+template <typename T, bool POS>
+__device__ __forceinline__ void spread_row(const rmsn_desc& dj, uint64_t pos, const PosArgs& pa,
+                                           float eps, float* lds4) {
+    const T* x;
+    const T* w;
+    T* y;
+    persistent_ptrs<T, POS>(dj, pos, pa, x, w, y);
+    persistent_row<T>(x, w, y, dj.n, eps, lds4);
 }
 
 // Whether any row of the table meets another one (rows_meet), decided in
@@ -1270,9 +1278,10 @@ __device__ __forceinline__ bool any_row_meets(const RowSpan (&mine)[R], int32_t 
 // ballot gives the answer, so no lane writes inside the loop; then the marked
 // ("bound") rows run in table order, found 64 at a time by a ballot over the
 // marks. Returns as spread_rows does.
-template <typename T, typename S>
+template <typename T, bool POS, typename S>
 __device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const rmsn_desc* d,
-                                          int32_t count, float eps, float* lds4, int* fold4) {
+                                          int32_t count, float eps, uint64_t pos,
+                                          const PosArgs& pa, float* lds4, int* fold4) {
     if (blockIdx.x != 0) {
         const int32_t workers = (int32_t)gridDim.x - 1;
         for (int32_t j = (int32_t)blockIdx.x - 1; j < count; j += workers) {
@@ -1281,7 +1290,7 @@ __device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const r
             for (int32_t k = threadIdx.x; k < count; k += blockDim.x)
                 meet |= (k != j) & rows_meet(sj, span[k]);
             if (workgroup_any(meet, fold4)) continue;  // bound: workgroup 0 runs it in order
-            spread_row<T>(d[j], eps, lds4);
+            spread_row<T, POS>(d[j], pos, pa, eps, lds4);
             __syncthreads();  // lds4 is reused by the next row
         }
         return true;
@@ -1305,7 +1314,7 @@ __device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const r
         while (marks) {
             const int32_t j = j0 + __builtin_ctzll(marks);
             marks &= marks - 1;
-            spread_row<T>(d[j], eps, lds4);
+            spread_row<T, POS>(d[j], pos, pa, eps, lds4);
             __syncthreads();  // this row's stores before the next bound row's loads
         }
     }
@@ -1316,9 +1325,10 @@ __device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const r
 // workgroup 0 only) when no row is free, so the ordered walk takes the whole
 // table. (No row writes into the table itself: the walks read descriptors as
 // they go, and this step reads them all first.)
-template <typename T>
+template <typename T, bool POS>
 __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, float eps,
-                                            float* lds4, int* fold4) {
+                                            uint64_t pos, const PosArgs& pa, float* lds4,
+                                            int* fold4) {
     __shared__ RowSpan span[kSpanRows];   // 64-bit spans, or RowSpan32 in the same bytes
     __shared__ uint8_t bound[kSpanRows];
     __shared__ unsigned long long lo_hi[2];
@@ -1333,7 +1343,7 @@ __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, f
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int32_t j = threadIdx.x + 256 * r;
-        mine[r] = j < count ? row_span<T>(d[j]) : RowSpan{0, 0, 0, 0};
+        mine[r] = j < count ? row_span<T, POS>(d[j], pos, pa) : RowSpan{0, 0, 0, 0};
         if (mine[r].len != 0) {
             lo = min(lo, (uint64_t)min(mine[r].x, min(mine[r].w, mine[r].y)));
             hi = max(hi, (uint64_t)max(mine[r].x, max(mine[r].w, mine[r].y)) + mine[r].len);
@@ -1363,8 +1373,9 @@ __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, f
         else span[j] = mine[r];
     }
     __syncthreads();
-    return narrow ? spread_on<T>(span32, bound, d, count, eps, lds4, fold4)
-                  : spread_on<T>(static_cast<const RowSpan*>(span), bound, d, count, eps, lds4, fold4);
+    return narrow ? spread_on<T, POS>(span32, bound, d, count, eps, pos, pa, lds4, fold4)
+                  : spread_on<T, POS>(static_cast<const RowSpan*>(span), bound, d, count, eps, pos,
+                                      pa, lds4, fold4);
 }
 
 template <typename T, bool POS>
@@ -1380,9 +1391,9 @@ __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __
         const uint64_t raw = (uint64_t)*pa.d_pos;
         pos = raw < per ? raw : raw % per;
     }
-    // the launcher gives more than one workgroup only to position-free tables
-    // of at most kSpanRows rows
-    if (!POS && gridDim.x > 1 && spread_rows<T>(d, count, eps, lds4, lds_fold)) return;
+    // the launcher gives more than one workgroup only to tables of at most
+    // kSpanRows rows
+    if (gridDim.x > 1 && spread_rows<T, POS>(d, count, eps, pos, pa, lds4, lds_fold)) return;
     switch (walk_mode<T, POS>(d, count, pos, pa, lds_fold)) {
         case kRoundWalk16: round_walk<T, POS, 4>(d, count, eps, pos, pa); break;
         case kRoundWalk4: round_walk<T, POS, 1>(d, count, eps, pos, pa); break;
@@ -1392,7 +1403,9 @@ __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __
 #undef RMSN_CASE
         default: serial_walk<T, POS>(d, count, eps, pos, pa, lds4); break;
     }
-    if (POS && threadIdx.x == 0) {
+    // with more than one workgroup the launcher advances the position in a
+    // launch of its own, once every workgroup has read it
+    if (POS && gridDim.x == 1 && threadIdx.x == 0) {
         const uint64_t per = (uint64_t)pa.period;
         const_cast<int64_t*>(pa.d_pos)[0] = (int64_t)(pos + 1 == per ? 0 : pos + 1);
     }
@@ -1607,8 +1620,7 @@ hipError_t launch_sequence_persistent(int dtype, const rmsn_desc* d, int32_t cou
                                      const PosArgs* pos, hipStream_t stream) {
     const PosArgs none{nullptr, 0, 0, 1};
     // workgroup 0 plus one worker per row (at most kSpreadWorkers) for free rows
-    const bool spread = pos == nullptr && count > 1 && count <= kSpanRows &&
-                        option_persistent_workgroups() == 0;
+    const bool spread = count > 1 && count <= kSpanRows && option_persistent_workgroups() == 0;
     const dim3 grid(spread ? 1u + (unsigned)std::min(count, kSpreadWorkers) : 1u), block(kBlockThreads);
     if (dtype == RMSN_F32) {
         if (pos)
@@ -1625,7 +1637,11 @@ hipError_t launch_sequence_persistent(int dtype, const rmsn_desc* d, int32_t cou
             hipLaunchKernelGGL((k_sequence_persistent<uint16_t, false>), grid, block, 0, stream,
                                d, count, eps, none);
     }
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    // the rows of every workgroup are taken at the position read when the
+    // kernel starts; it is advanced after all of them, by the next launch
+    if (e != hipSuccess || !spread || pos == nullptr) return e;
+    return launch_advance(const_cast<int64_t*>(pos->d_pos), pos->period, stream);
 }
 
 hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,

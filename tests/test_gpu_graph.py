@@ -597,11 +597,13 @@ def test_persistent_dependent_chain(rn, kind, n, offset, pwg):
 
 @pytest.mark.parametrize("kind,n,norms", [("f32", 7168, 9), ("bf16", 1536, 40), ("bf16", 1532, 9),
                                            ("f32", 1000, 37)])
-def test_persistent_positioned_ring(rn, kind, n, norms):
-    """The persistent launch on a positioned table, every walk it can take
-    (binary32 and bf16 1536: the round walk, over several groups of 16 rows
-    for 40 and 37 norms; bf16 1532: the pipelined walk)."""
-    say(f"persistent positioned ring {kind} n={n} norms={norms}")
+def test_persistent_positioned_ring(rn, kind, n, norms, pwg):
+    """The persistent launch on a positioned table: its rows spread over
+    workgroups (the position then advanced by a launch of its own), or every
+    walk one workgroup can take (binary32 and bf16 1536: the round walk, over
+    several groups of 16 rows for 40 and 37 norms; bf16 1532: the pipelined
+    walk)."""
+    say(f"persistent positioned ring {kind} n={n} norms={norms} workgroups option {pwg}")
     ring = Ring(rn, [n] * norms, period=4, kind=kind)
     dt = rn.F32 if kind == "f32" else rn.BF16
     ring.d_pos.fill_(3)
@@ -636,6 +638,35 @@ def test_persistent_call_captured_in_a_graph(rn, step, pwg):
         compare(step.outputs(), step.expected(s), f"captured persistent replay {rep}")
     step.point_at(0)
 
+
+
+def test_persistent_positioned_call_captured_in_a_graph(rn, pwg):
+    """The positioned persistent call captured by the caller (rows spread over
+    workgroups: the rows' launch and the position's own update launch): each
+    replay takes the rows at the next position and advances it."""
+    import torch
+    n, norms = 1536, 12
+    say(f"persistent positioned call captured, workgroups option {pwg}")
+    ring = Ring(rn, [n] * norms, period=4, kind="f32")
+    ring.d_pos.fill_(1)
+    sync()
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s_cap):
+        rn.rmsnorm_sequence_persistent(ring.table, norms, wl.EPS, rn.F32, position=ring.position(n))
+        torch.cuda.current_stream().synchronize()
+        with torch.cuda.graph(graph, stream=s_cap):
+            rn.rmsnorm_sequence_persistent(ring.table, norms, wl.EPS, rn.F32,
+                                           position=ring.position(n))
+    torch.cuda.current_stream().wait_stream(s_cap)
+    sync()
+    assert int(ring.d_pos.item()) == 2   # the call before the capture ran at position 1
+    for rep in range(5):
+        graph.replay()
+        sync()
+        assert int(ring.d_pos.item()) == (3 + rep) % 4, f"replay {rep}"
+    _check_ring(ring, {0, 1, 2, 3})
 
 # ---- the persistent launch's three walks -----------------------------------------
 # Round walk: every row a whole number of 16-byte vectors (at most 8192
