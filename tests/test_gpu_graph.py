@@ -1010,3 +1010,47 @@ def test_persistent_spread_one_element_overlap(rn, pwg, what, writer_first):
     sync()
     for b, t in enumerate(bufs):
         assert_bits_f32(f32_host(t), want[b], f"buffer {b}")
+
+
+def test_persistent_positioned_mixed_table(rn, pwg):
+    """A positioned table (rings of 4 positions, one pitch) whose rows at
+    every position include a chain (row 1 reads row 0's output, row 10 works
+    in place on row 1's output) among free rows: one launch per position
+    through a whole cycle leaves every buffer as the rows applied in table
+    order, position after position, on the CPU."""
+    import torch
+    say(f"persistent positioned mixed table, workgroups option {pwg}")
+    n, period = 1536, 4
+    sizes, plan = [], []
+
+    def buf(m):
+        sizes.append(m)
+        return len(sizes) - 1
+
+    ring = lambda: buf(period * n)
+    x0, y0, y1 = ring(), ring(), ring()
+    plan.append(((x0, 0, n), (buf(n), 0, n), (y0, 0, n)))        # row 0
+    plan.append(((y0, 0, n), (buf(n), 0, n), (y1, 0, n)))        # row 1 reads row 0's output
+    for _ in range(8):                                           # rows 2..9: free
+        plan.append(((ring(), 0, n), (buf(n), 0, n), (ring(), 0, n)))
+    plan.append(((y1, 0, n), (buf(n), 0, n), (y1, 0, n)))        # row 10: in place on row 1's output
+    for _ in range(5):                                           # rows 11..15: free
+        plan.append(((ring(), 0, n), (buf(n), 0, n), (ring(), 0, n)))
+    rings = {b for (xb, _, _), _, (yb, _, _) in plan for b in (xb, yb)}
+    host = [wl.misc_f32(93_000 + b, size)[0] for b, size in enumerate(sizes)]
+    want = host
+    for p in range(period):
+        want = _apply_in_order([((xb, xo + p * n, m), w, (yb, yo + p * n, m))
+                                for (xb, xo, m), w, (yb, yo, _) in plan], want, "f32")
+    bufs = [to_dev_f32(h) for h in host]
+    assert all(sizes[b] == period * n for b in rings)
+    table, _ = rn.make_table([(bufs[xb][xo:xo + m], bufs[wb][wo:wo + m], bufs[yb][yo:yo + m])
+                              for (xb, xo, m), (wb, wo, _), (yb, yo, _) in plan])
+    d_pos = torch.zeros(1, dtype=torch.int64, device="cuda")
+    for p in range(period):
+        rn.rmsnorm_sequence_persistent(table, len(plan), wl.EPS, rn.F32,
+                                       position=(d_pos, n * 4, n * 4, period))
+        sync()
+        assert int(d_pos.item()) == (p + 1) % period
+    for b, t in enumerate(bufs):
+        assert_bits_f32(f32_host(t), want[b], f"buffer {b}")
