@@ -1179,19 +1179,22 @@ __device__ __forceinline__ void spread_row(const rmsn_desc& dj, uint64_t pos, co
     persistent_row<T>(x, w, y, dj.n, eps, lds4);
 }
 
-// Whether any row of the table meets another one (rows_meet), decided in
-// O(count log count) rather than by testing every pair: the outputs are put
-// in order of start address; then no row meets another exactly when each
-// output ends at or before the next one starts and no row's x or w range
-// meets another row's output. Once the outputs are disjoint their ends are
-// in order as well, so the first output that ends past a read range's start
-// is found by binary search, and the outputs that meet that range follow it;
-// a row's own output (in-place) is skipped, and the one after it is then the
-// next candidate. The order is a rank sort: the key start * 2^16 + row is
-// unique, and each lane counts the keys below its own, reading them as LDS
-// broadcasts with no barrier between steps. An output past 2^48 (beyond the
-// key) returns true, leaving the decision to the exact all-pairs test.
-// mine[r] is row threadIdx.x + 256 r. Every thread gets the answer.
+// Which rows meet another one (rows_meet), found without testing every pair
+// when the outputs are disjoint: the outputs are put in order of start
+// address, and they are disjoint exactly when each one ends at or before the
+// next one starts. Their ends are then in order as well, so for each x or w
+// range the first output ending past its start is found by binary search, and
+// the outputs meeting the range are that one and those after it that start
+// before the range ends; both rows of every such pair (the row's own output,
+// in place, aside) are bound. With disjoint outputs no other pair meets. The
+// order is a rank sort: the key start * 2^16 + row is unique, and each lane
+// counts the keys below its own, reading them as LDS broadcasts with no
+// barrier between steps. Returns kNoneBound, kBoundMarked (bound[j] is 1
+// exactly for the bound rows), or kBoundUnknown when outputs overlap or lie
+// past 2^48 (beyond the key): the all-pairs test then decides.
+// mine[r] is row threadIdx.x + 256 r. Every thread gets the same answer.
+constexpr int kNoneBound = 0, kBoundMarked = 1, kBoundUnknown = 2;
+
 template <int RE, int R>
 __device__ __forceinline__ void key_ranks(const uint64_t* o_key, int32_t count,
                                           const uint64_t (&key)[R], int32_t (&rank)[R]) {
@@ -1204,8 +1207,8 @@ __device__ __forceinline__ void key_ranks(const uint64_t* o_key, int32_t count,
 }
 
 template <int R>
-__device__ __forceinline__ bool any_row_meets(const RowSpan (&mine)[R], int32_t count,
-                                              int* fold4) {
+__device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t count,
+                                               uint8_t* bound, int* fold4) {
     __shared__ uint64_t o_key[kSpanRows], o_start[kSpanRows], o_end[kSpanRows];
     __shared__ uint16_t o_row[kSpanRows];
     constexpr uint64_t kNoOutput = 0xFFFFFFFFFFFFull;  // the key's start for an empty row
@@ -1223,7 +1226,7 @@ __device__ __forceinline__ bool any_row_meets(const RowSpan (&mine)[R], int32_t 
         rank[r] = 0;
         if (j < count) o_key[j] = key[r];
     }
-    if (workgroup_any(high, fold4)) return true;  // its barrier also publishes o_key
+    if (workgroup_any(high, fold4)) return kBoundUnknown;  // its barrier also publishes o_key
     switch ((count + 255) >> 8) {
         case 1: key_ranks<1>(o_key, count, key, rank); break;
         case 2: key_ranks<2>(o_key, count, key, rank); break;
@@ -1241,9 +1244,13 @@ __device__ __forceinline__ bool any_row_meets(const RowSpan (&mine)[R], int32_t 
         o_row[p] = (uint16_t)j;
     }
     __syncthreads();
-    bool meet = false;
+    bool overlap = false;
     for (int32_t i = threadIdx.x; i + 1 < m; i += 256)
-        meet |= (o_start[i + 1] != ~0ull) & (o_end[i] > o_start[i + 1]);
+        overlap |= (o_start[i + 1] != ~0ull) & (o_end[i] > o_start[i + 1]);
+    if (workgroup_any(overlap, fold4)) return kBoundUnknown;
+    for (int32_t j = threadIdx.x; j < count; j += 256) bound[j] = 0;
+    __syncthreads();
+    bool meet = false;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int32_t j = threadIdx.x + 256 * r;
@@ -1262,26 +1269,32 @@ __device__ __forceinline__ bool any_row_meets(const RowSpan (&mine)[R], int32_t 
                     left = h;
                 }
             }
-            if (p < m && o_start[p] < b) {
-                if (o_row[p] != j) meet = true;
-                else if (p + 1 < m && o_start[p + 1] < b) meet = true;
+            for (; p < m && o_start[p] < b; ++p) {
+                const int32_t o = o_row[p];
+                if (o == j) continue;
+                meet = true;
+                bound[j] = 1;  // every writer stores the same value
+                bound[o] = 1;
             }
         }
     }
-    return workgroup_any(meet, fold4);
+    // the barriers inside also publish bound[]
+    return workgroup_any(meet, fold4) ? kBoundMarked : kNoneBound;
 }
 
 // Which rows meet another row, on spans of type S in LDS (RowSpan or
 // RowSpan32). Workers (blockIdx > 0) test their row against every row, 256 at
-// a time, and run it when it meets none. In workgroup 0 wavefront v decides
+// a time, and run it when it meets none. In workgroup 0 (unless the ordered
+// outputs already marked the bound rows: `marked`) wavefront v decides
 // rows v, v + 4, ...: its lanes test the row against 64 rows at a time and a
 // ballot gives the answer, so no lane writes inside the loop; then the marked
 // ("bound") rows run in table order, found 64 at a time by a ballot over the
 // marks. Returns as spread_rows does.
 template <typename T, bool POS, typename S>
-__device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const rmsn_desc* d,
-                                          int32_t count, float eps, uint64_t pos,
-                                          const PosArgs& pa, float* lds4, int* fold4) {
+__device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, bool marked,
+                                          const rmsn_desc* d, int32_t count, float eps,
+                                          uint64_t pos, const PosArgs& pa, float* lds4,
+                                          int* fold4) {
     if (blockIdx.x != 0) {
         const int32_t workers = (int32_t)gridDim.x - 1;
         for (int32_t j = (int32_t)blockIdx.x - 1; j < count; j += workers) {
@@ -1296,7 +1309,7 @@ __device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const r
         return true;
     }
     const int32_t wave = (int32_t)(threadIdx.x >> 6), lane = (int32_t)(threadIdx.x & 63);
-    for (int32_t j = wave; j < count; j += 4) {
+    for (int32_t j = marked ? count : wave; j < count; j += 4) {
         const S sj = span[j];
         bool meet = false;
 #pragma unroll 4
@@ -1350,7 +1363,11 @@ __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, f
         }
     }
     // no row meets another (the usual table): the workers run every row
-    if (blockIdx.x == 0 && !any_row_meets(mine, count, fold4)) return true;
+    int found = kBoundUnknown;
+    if (blockIdx.x == 0) {
+        found = find_bound_rows(mine, count, bound, fold4);
+        if (found == kNoneBound) return true;
+    }
     // lowest and highest address: within the wavefront, then one LDS atomic each
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -1373,9 +1390,10 @@ __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, f
         else span[j] = mine[r];
     }
     __syncthreads();
-    return narrow ? spread_on<T, POS>(span32, bound, d, count, eps, pos, pa, lds4, fold4)
-                  : spread_on<T, POS>(static_cast<const RowSpan*>(span), bound, d, count, eps, pos,
-                                      pa, lds4, fold4);
+    const bool marked = found == kBoundMarked;
+    return narrow ? spread_on<T, POS>(span32, bound, marked, d, count, eps, pos, pa, lds4, fold4)
+                  : spread_on<T, POS>(static_cast<const RowSpan*>(span), bound, marked, d, count,
+                                      eps, pos, pa, lds4, fold4);
 }
 
 template <typename T, bool POS>
