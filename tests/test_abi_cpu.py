@@ -398,11 +398,20 @@ def test_options_roundtrip_and_force_paths(rn):
         rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
         with pytest.raises(rn.RmsnormError):
             rn.set_option(99, 0)
+        # the persistent launch: 0 automatic (free rows spread), 1 one workgroup
+        assert rn.get_option(rn.OPT_PERSISTENT_WORKGROUPS) == 0
+        rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 1)
+        assert rn.get_option(rn.OPT_PERSISTENT_WORKGROUPS) == 1
+        for bad in (2, -1, 256):
+            with pytest.raises(rn.RmsnormError):
+                rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, bad)
+        assert rn.get_option(rn.OPT_PERSISTENT_WORKGROUPS) == 1
     finally:
         rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
         rn.set_option(rn.OPT_ROWS_PER_BLOCK, 0)
         rn.set_option(rn.OPT_STREAMING, -1)
         rn.set_option(rn.OPT_SPLIT_LOADS, 0)
+        rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 0)
 
 
 def test_error_messages_are_per_thread(rn):
