@@ -1250,32 +1250,34 @@ __device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t
     if (workgroup_any(overlap, fold4)) return kBoundUnknown;
     for (int32_t j = threadIdx.x; j < count; j += 256) bound[j] = 0;
     __syncthreads();
+    // every lane's 2R searches side by side: a branch-free lower bound with
+    // the same log2(m) steps for all, so their LDS reads are in flight together
+    constexpr int NQ = 2 * R;
+    uint64_t lo[NQ], hi[NQ];
+    int32_t at[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const RowSpan& rs = mine[i >> 1];
+        lo[i] = (i & 1) ? (uint64_t)rs.w : (uint64_t)rs.x;
+        hi[i] = lo[i] + rs.len;
+        at[i] = 0;  // every output before at[i] ends at or before lo[i]
+    }
+    for (int32_t step = m >> 1; step > 0; step >>= 1) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) at[i] += o_end[at[i] + step - 1] <= lo[i] ? step : 0;
+    }
     bool meet = false;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int32_t j = threadIdx.x + 256 * r;
-        if (j >= count || mine[r].len == 0) continue;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const uint64_t a = q ? (uint64_t)mine[r].w : (uint64_t)mine[r].x;
-            const uint64_t b = a + mine[r].len;
-            int32_t p = 0, left = m;  // first p with o_end[p] > a
-            while (left > 0) {
-                const int32_t h = left >> 1;
-                if (o_end[p + h] <= a) {
-                    p += h + 1;
-                    left -= h + 1;
-                } else {
-                    left = h;
-                }
-            }
-            for (; p < m && o_start[p] < b; ++p) {
-                const int32_t o = o_row[p];
-                if (o == j) continue;
-                meet = true;
-                bound[j] = 1;  // every writer stores the same value
-                bound[o] = 1;
-            }
+    for (int i = 0; i < NQ; ++i) {
+        const int32_t j = threadIdx.x + 256 * (i >> 1);
+        if (j >= count || mine[i >> 1].len == 0) continue;
+        int32_t p = at[i] + (o_end[at[i]] <= lo[i] ? 1 : 0);  // first output ending past lo[i]
+        for (; p < m && o_start[p] < hi[i]; ++p) {
+            const int32_t o = o_row[p];
+            if (o == j) continue;
+            meet = true;
+            bound[j] = 1;  // every writer stores the same value
+            bound[o] = 1;
         }
     }
     // the barriers inside also publish bound[]
