@@ -968,14 +968,16 @@ def test_persistent_spread_mixed_table(rn, pwg):
 @pytest.mark.gpu
 @pytest.mark.parametrize("what", ["x", "w", "y", "touch"])
 @pytest.mark.parametrize("writer_first", [True, False], ids=["writer_first", "reader_first"])
-def test_persistent_spread_one_element_overlap(rn, pwg, what, writer_first):
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_persistent_spread_one_element_overlap(rn, pwg, what, writer_first, kind):
     """Among 60 free rows, one row's x (or w, or output) shares exactly one
     element with another row's output: the writer's last element is the
     other range's first. Those two rows must keep table order. With 'touch'
     the other x starts just past the writer's output, so nothing is shared
     and every row is free. Every buffer ends as the rows applied in table
-    order on the CPU leave it."""
-    say(f"persistent one-element overlap {what}, writer first {writer_first}, "
+    order on the CPU leave it. In bf16 the shared element is 2 bytes."""
+    from gpu_util import assert_bits_bf16, bf16_host, to_dev_bf16
+    say(f"persistent one-element overlap {what} {kind}, writer first {writer_first}, "
         f"workgroups option {pwg}")
     n = 512
     sizes, plan = [], []
@@ -1002,14 +1004,19 @@ def test_persistent_spread_one_element_overlap(rn, pwg, what, writer_first):
         else:
             plan.append(((buf(n), 0, n), (buf(n), 0, n), (buf(n), 0, n)))
     host = [wl.misc_f32(91_000 + b, size)[0] for b, size in enumerate(sizes)]
-    want = _apply_in_order(plan, host, "f32")
-    bufs = [to_dev_f32(h) for h in host]
+    if kind == "bf16":
+        host = [wl.to_bf16_bits(h) for h in host]
+    want = _apply_in_order(plan, host, kind)
+    bufs = [to_dev_bf16(h) if kind == "bf16" else to_dev_f32(h) for h in host]
     table, _ = rn.make_table([(bufs[xb][xo:xo + m], bufs[wb][wo:wo + m], bufs[yb][yo:yo + m])
                               for (xb, xo, m), (wb, wo, _), (yb, yo, _) in plan])
-    rn.rmsnorm_sequence_persistent(table, len(plan), wl.EPS, rn.F32)
+    rn.rmsnorm_sequence_persistent(table, len(plan), wl.EPS, rn.BF16 if kind == "bf16" else rn.F32)
     sync()
     for b, t in enumerate(bufs):
-        assert_bits_f32(f32_host(t), want[b], f"buffer {b}")
+        if kind == "bf16":
+            assert_bits_bf16(bf16_host(t), want[b], f"buffer {b}")
+        else:
+            assert_bits_f32(f32_host(t), want[b], f"buffer {b}")
 
 
 def test_persistent_positioned_mixed_table(rn, pwg):
