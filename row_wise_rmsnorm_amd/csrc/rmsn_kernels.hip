@@ -1167,6 +1167,17 @@ __device__ __forceinline__ bool workgroup_any(bool p, int* fold4) {
     return __builtin_amdgcn_readfirstlane(any) != 0;
 }
 
+// Bit 0: a holds in some thread of the workgroup; bit 1: b does. As
+// workgroup_any, one barrier to publish and one to free fold4.
+__device__ __forceinline__ int workgroup_any2(bool a, bool b, int* fold4) {
+    const int wave_any = (__ballot(a) != 0 ? 1 : 0) | (__ballot(b) != 0 ? 2 : 0);
+    if ((threadIdx.x & 63) == 0) fold4[threadIdx.x >> 6] = wave_any;
+    __syncthreads();
+    const int any = fold4[0] | fold4[1] | fold4[2] | fold4[3];
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(any);
+}
+
 // One row, its pointers taken from the descriptor (a wave-uniform load), not
 // from the LDS copy used for the overlap tests.
 template <typename T, bool POS>
@@ -1226,7 +1237,7 @@ __device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t
         rank[r] = 0;
         if (j < count) o_key[j] = key[r];
     }
-    if (workgroup_any(high, fold4)) return kBoundUnknown;  // its barrier also publishes o_key
+    __syncthreads();  // o_key published
     switch ((count + 255) >> 8) {
         case 1: key_ranks<1>(o_key, count, key, rank); break;
         case 2: key_ranks<2>(o_key, count, key, rank); break;
@@ -1243,13 +1254,14 @@ __device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t
         o_end[p] = out ? (uint64_t)(mine[r].y + mine[r].len) : ~0ull;
         o_row[p] = (uint16_t)j;
     }
-    __syncthreads();
-    bool overlap = false;
-    for (int32_t i = threadIdx.x; i + 1 < m; i += 256)
-        overlap |= (o_start[i + 1] != ~0ull) & (o_end[i] > o_start[i + 1]);
-    if (workgroup_any(overlap, fold4)) return kBoundUnknown;
     for (int32_t j = threadIdx.x; j < count; j += 256) bound[j] = 0;
     __syncthreads();
+    // keys past 2^48 or overlapping outputs leave the answer unknown; the
+    // searches below still stay in bounds (the ranks are a permutation), and
+    // the all-pairs marking then rewrites every mark they made
+    bool unknown = high;
+    for (int32_t i = threadIdx.x; i + 1 < m; i += 256)
+        unknown |= (o_start[i + 1] != ~0ull) & (o_end[i] > o_start[i + 1]);
     // every lane's 2R searches side by side: a branch-free lower bound with
     // the same log2(m) steps for all, so their LDS reads are in flight together
     constexpr int NQ = 2 * R;
@@ -1281,7 +1293,8 @@ __device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t
         }
     }
     // the barriers inside also publish bound[]
-    return workgroup_any(meet, fold4) ? kBoundMarked : kNoneBound;
+    const int any = workgroup_any2(unknown, meet, fold4);
+    return (any & 1) ? kBoundUnknown : (any & 2) ? kBoundMarked : kNoneBound;
 }
 
 // Which rows meet another row, on spans of type S in LDS (RowSpan or
