@@ -515,3 +515,27 @@ def test_workspace_rejects(rn):
     # without a GPU the launch then fails with a HIP error, never EINVAL
     assert L.rmsnorm_batched_rows_ws(0, X, 64, W, Y, 64, 2, 64, 1e-6, 0, 0, None) \
         != rn.RMSN_EINVAL
+
+
+def test_build_scripts_load_without_the_package():
+    # On a fresh checkout the library is not built yet, and the package refuses
+    # to import; the build entry must reach the build scripts without it.
+    import subprocess
+    import sys
+    code = (
+        "import sys\n"
+        "class Block:\n"
+        "    def find_spec(self, name, path=None, target=None):\n"
+        "        if name.split('.')[0] == 'row_wise_rmsnorm_amd':\n"
+        "            raise ImportError('package imported before the build')\n"
+        "        return None\n"
+        "sys.meta_path.insert(0, Block())\n"
+        f"sys.path.insert(0, {ROOT!r})\n"
+        "import __graft_entry__ as g\n"
+        "import os\n"
+        "h = g._load_script(os.path.join('row_wise_rmsnorm_amd', 'build.py'))\n"
+        "o = g._load_script(os.path.join('oracle', 'build.py'))\n"
+        "assert callable(h.build) and callable(o.build)\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
