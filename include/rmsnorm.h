@@ -26,7 +26,7 @@
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers owned by the caller. The library
  *    never allocates, frees or synchronises inside rmsnorm_f32, rmsnorm_bf16,
- *    rmsnorm_batched_rows, rmsnorm_sequence_eager(_positioned),
+ *    rmsnorm_batched_rows(_ws, _noalloc), rmsnorm_sequence_eager(_positioned),
  *    rmsnorm_sequence_persistent or rmsnorm_sequence_graph_launch, so each of
  *    them may itself be captured into a caller's HIP graph. Only the graph
  *    creation and update calls create HIP objects; they also allocate a
@@ -130,6 +130,25 @@ int rmsnorm_batched_rows(int dtype, const void* x, int64_t x_row_stride, const v
 int rmsnorm_batched_rows_ws(int dtype, const void* x, int64_t x_row_stride, const void* w,
                             void* y, int64_t y_row_stride, int64_t rows, int64_t n, float eps,
                             void* workspace, int64_t workspace_bytes, void* stream);
+
+/* rmsnorm_batched_rows_ws for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same plan, kernels and bits, with the WIDE path's group
+ * totals in a workspace the library holds instead of the caller's. That
+ * workspace is a fixed 64 KB device array, one per GPU, kept until the
+ * process ends; it holds the totals of at most 4096 rows, so a launch whose
+ * plan would need more (only possible with RMSN_OPT_PATH forced to
+ * RMSN_PATH_WIDE) is refused with RMSN_EINVAL before anything is enqueued.
+ * Nothing is allocated, freed or synchronised; the first call on a device
+ * looks up that device's copy of the array (hipGetSymbolAddress), so make
+ * one call outside any capture first. Every call on a GPU shares that GPU's
+ * array and leaves its last contents there: calls that may overlap in time
+ * on one GPU (other streams, other host threads) race and must not be
+ * issued. Errors as rmsnorm_batched_rows_ws, without the caller workspace's
+ * checks. */
+int rmsnorm_batched_rows_noalloc(int dtype, const void* x, int64_t x_row_stride, const void* w,
+                                 void* y, int64_t y_row_stride, int64_t rows, int64_t n,
+                                 float eps, void* stream);
 
 /* The norms of a decode step, in order, issued as `count` dependent launches
  * on `stream` (the eager arm). d_table: DEVICE array of count descriptors.

@@ -12,6 +12,9 @@ Function names follow the C entry points:
     rmsnorm_batched_rows_ws(x, w, eps, out=None, workspace=None)
                                                the same with a device workspace
                                                (few very wide rows over many CUs)
+    rmsnorm_batched_rows_noalloc(x, w, eps, out=None)
+                                               the same with the library's own
+                                               workspace (allocates nothing)
     rmsnorm_sequence_eager(table, widths, eps, dtype)
     SequenceGraph(table, widths, eps, dtype)   captured sequence (.launch())
 """
@@ -75,6 +78,7 @@ def bind(path):
         "rmsnorm_bf16": [vp, vp, vp, i64, f, vp],
         "rmsnorm_batched_rows": [c_int, vp, i64, vp, vp, i64, i64, i64, f, vp],
         "rmsnorm_batched_rows_ws": [c_int, vp, i64, vp, vp, i64, i64, i64, f, vp, i64, vp],
+        "rmsnorm_batched_rows_noalloc": [c_int, vp, i64, vp, vp, i64, i64, i64, f, vp],
         "rmsnorm_workspace_query": [c_int, i64, i64, c_int, ctypes.POINTER(_PlanInfo),
                                     ctypes.POINTER(i64)],
         "rmsnorm_sequence_eager": [c_int, vp, vp, i32, f, vp],
@@ -115,7 +119,8 @@ EXPORTED = ("rmsnorm_f32", "rmsnorm_bf16", "rmsnorm_batched_rows", "rmsnorm_sequ
             "rmsnorm_diag_bf16", "rmsnorm_sequence_eager_positioned",
             "rmsnorm_sequence_graph_create_positioned", "rmsnorm_sequence_graph_update",
             "rmsnorm_association_lanes", "rmsnorm_sequence_persistent",
-            "rmsnorm_batched_rows_ws", "rmsnorm_workspace_query")
+            "rmsnorm_batched_rows_ws", "rmsnorm_workspace_query",
+            "rmsnorm_batched_rows_noalloc")
 
 
 def lib():
@@ -290,6 +295,29 @@ def rmsnorm_batched_rows_ws(x, w, eps, out=None, workspace=None, stream=None):
         _check(_lib.rmsnorm_batched_rows_ws(code, x.data_ptr(), xs, w.data_ptr(), y.data_ptr(),
                                             ys, rows, n, float(eps), workspace.data_ptr(),
                                             workspace.numel(), _stream_ptr(stream, x.device)))
+    return y
+
+
+def rmsnorm_batched_rows_noalloc(x, w, eps, out=None, stream=None):
+    """rmsnorm_batched_rows_ws with the library's own per-GPU workspace
+    instead of a caller's: nothing is allocated (pass `out` for that), same
+    bits. Calls that overlap in time on one GPU share that workspace and must
+    not be issued."""
+    _device_tensor(x, "x")
+    code = _dtype_code(x)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("2-D tensor with unit stride along rows expected")
+    rows, n = x.shape
+    _weight(x, w, n)
+    y = _out_like(x, out)
+    if y.stride(1) != 1:
+        raise ValueError("out must have unit stride along rows")
+    xs = x.stride(0) if rows > 1 else n
+    ys = y.stride(0) if rows > 1 else n
+    with _on(x.device):
+        _check(_lib.rmsnorm_batched_rows_noalloc(code, x.data_ptr(), xs, w.data_ptr(),
+                                                 y.data_ptr(), ys, rows, n, float(eps),
+                                                 _stream_ptr(stream, x.device)))
     return y
 
 

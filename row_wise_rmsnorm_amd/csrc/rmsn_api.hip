@@ -14,9 +14,11 @@
 // the same plan function (section 2).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -25,6 +27,11 @@
 #include "rmsnorm.h"
 
 using namespace rmsn;
+
+// The library's own workspace (rmsnorm_batched_rows_noalloc): the group
+// totals of up to 4096 rows on the WIDE path, one copy per GPU.
+constexpr int64_t kScratchBytes = 64 * 1024;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
 
 struct rmsn_graph {
     int dtype = RMSN_F32;
@@ -56,21 +63,75 @@ int rows_alignment(int dtype, const void* x, int64_t xs, const void* w, const vo
     return (int)(bits & (~bits + 1));  // lowest set bit
 }
 
-// use_ws: the caller passed a workspace (rmsnorm_batched_rows_ws), so the
-// plan may take the WIDE path, which needs one.
+// ---------------------------------------------------------------------------
+// The library's own workspace, `scratch` above: every device that loads the
+// library holds its own copy until the process ends. Host code never passes
+// `scratch` itself to a kernel -- on the host that name is a stand-in, not a
+// device address -- but the address hipGetSymbolAddress returns for the
+// current device, looked up once per device on its first call.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (*out), looked up on its first use.
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    if (dev < 0 || dev >= kMaxDevices) {
+        set_error("device %d is beyond the %d devices the library keeps a workspace for", dev,
+                  kMaxDevices);
+        return RMSN_EHIP;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_fail("hipGetSymbolAddress (library workspace)", e);
+            if (!p) {
+                set_error("hipGetSymbolAddress returned a null library workspace");
+                return RMSN_EHIP;
+            }
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return RMSN_OK;
+}
+
+// Where a WIDE launch's group totals go: the caller's workspace
+// (rmsnorm_batched_rows_ws), the library's own (rmsnorm_batched_rows_noalloc),
+// or none (rmsnorm_batched_rows: the plan never takes WIDE).
+enum class Ws { kNone, kCaller, kLibrary };
+
 int run_rows(int dtype, const void* x, int64_t xs, const void* w, void* y, int64_t ys,
-             int64_t rows, int64_t n, float eps, bool use_ws, void* ws, int64_t ws_bytes,
+             int64_t rows, int64_t n, float eps, Ws ws_kind, void* ws, int64_t ws_bytes,
              void* stream) {
     clear_error();
     int st = check_row_args(dtype, x, xs, w, y, ys, rows, n);
     if (st != RMSN_OK) return st;
     if ((st = check_eps(eps)) != RMSN_OK) return st;
     Plan p;
-    st = make_plan(dtype, rows, n, rows_alignment(dtype, x, xs, w, y, ys), &p, use_ws);
+    st = make_plan(dtype, rows, n, rows_alignment(dtype, x, xs, w, y, ys), &p,
+                   ws_kind != Ws::kNone);
     if (st != RMSN_OK) return st;
     const bool wide = p.path == RMSN_PATH_WIDE;
-    if (wide && (st = check_workspace(dtype, x, xs, w, y, ys, rows, n, ws, ws_bytes)) != RMSN_OK)
+    if (wide && ws_kind == Ws::kCaller &&
+        (st = check_workspace(dtype, x, xs, w, y, ys, rows, n, ws, ws_bytes)) != RMSN_OK)
         return st;
+    if (wide && ws_kind == Ws::kLibrary) {
+        const int64_t need = workspace_bytes(p, rows);
+        if (need > kScratchBytes) {
+            set_error("the launch needs %lld bytes of workspace and the library holds %lld "
+                      "(at most %lld rows on the WIDE path); use rmsnorm_batched_rows_ws",
+                      (long long)need, (long long)kScratchBytes,
+                      (long long)(kScratchBytes / 16));
+            return RMSN_EINVAL;
+        }
+        if ((st = scratch_address(&ws)) != RMSN_OK) return st;
+    }
     // A batch of more rows than one launch can hold goes as consecutive
     // launches of the plan's layout (a row's bits do not depend on the launch
     // it is in). Each piece starts a whole number of rows further on, which
@@ -344,25 +405,32 @@ int create_graph(int dtype, const rmsn_desc* d_table, const int64_t* h_widths, i
 extern "C" {
 
 int rmsnorm_f32(const float* x, const float* w, float* y, int64_t n, float eps, void* stream) {
-    return run_rows(RMSN_F32, x, n, w, y, n, 1, n, eps, false, nullptr, 0, stream);
+    return run_rows(RMSN_F32, x, n, w, y, n, 1, n, eps, Ws::kNone, nullptr, 0, stream);
 }
 
 int rmsnorm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, float eps,
                  void* stream) {
-    return run_rows(RMSN_BF16, x, n, w, y, n, 1, n, eps, false, nullptr, 0, stream);
+    return run_rows(RMSN_BF16, x, n, w, y, n, 1, n, eps, Ws::kNone, nullptr, 0, stream);
 }
 
 int rmsnorm_batched_rows(int dtype, const void* x, int64_t x_row_stride, const void* w, void* y,
                          int64_t y_row_stride, int64_t rows, int64_t n, float eps, void* stream) {
-    return run_rows(dtype, x, x_row_stride, w, y, y_row_stride, rows, n, eps, false, nullptr, 0,
-                    stream);
+    return run_rows(dtype, x, x_row_stride, w, y, y_row_stride, rows, n, eps, Ws::kNone, nullptr,
+                    0, stream);
 }
 
 int rmsnorm_batched_rows_ws(int dtype, const void* x, int64_t x_row_stride, const void* w,
                             void* y, int64_t y_row_stride, int64_t rows, int64_t n, float eps,
                             void* workspace, int64_t workspace_bytes, void* stream) {
-    return run_rows(dtype, x, x_row_stride, w, y, y_row_stride, rows, n, eps, true, workspace,
-                    workspace_bytes, stream);
+    return run_rows(dtype, x, x_row_stride, w, y, y_row_stride, rows, n, eps, Ws::kCaller,
+                    workspace, workspace_bytes, stream);
+}
+
+int rmsnorm_batched_rows_noalloc(int dtype, const void* x, int64_t x_row_stride, const void* w,
+                                 void* y, int64_t y_row_stride, int64_t rows, int64_t n,
+                                 float eps, void* stream) {
+    return run_rows(dtype, x, x_row_stride, w, y, y_row_stride, rows, n, eps, Ws::kLibrary,
+                    nullptr, 0, stream);
 }
 
 int rmsnorm_sequence_eager(int dtype, const rmsn_desc* d_table, const int64_t* h_widths,

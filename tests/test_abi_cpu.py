@@ -539,3 +539,31 @@ def test_build_scripts_load_without_the_package():
     )
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_noalloc_rejects(rn):
+    """The allocation-free entry point checks its arguments as the plain one
+    does, and refuses a launch whose group totals would not fit the library's
+    64 KB workspace (only reachable with the WIDE path forced) before any HIP
+    call; a launch that fits gets past validation (without a GPU it then
+    fails with a HIP error, never EINVAL)."""
+    L = rn.lib()
+    n = 1 << 14                                   # 64 KB binary32 rows
+    X, W, Y = 0x10000000, 0x20000000, 0x30000000
+
+    def call(rows, x=X, w=W, y=Y, xs=n, ys=n, eps=1e-6, dtype=0):
+        return L.rmsnorm_batched_rows_noalloc(dtype, x, xs, w, y, ys, rows, n, eps, None)
+
+    assert call(2, x=0) == rn.RMSN_EINVAL and "null" in rn.last_error()
+    assert call(2, xs=n - 1) == rn.RMSN_EINVAL and "stride" in rn.last_error()
+    assert call(2, eps=-1.0) == rn.RMSN_EINVAL and "eps" in rn.last_error()
+    assert call(2, dtype=7) == rn.RMSN_EINVAL
+    rn.set_option(rn.OPT_PATH, rn.PATH_WIDE)
+    try:
+        assert rn.workspace_query(rn.F32, 4097, n)[1] == 16 * 4097
+        assert call(4097) == rn.RMSN_EINVAL
+        assert "65536" in rn.last_error() and "4096 rows" in rn.last_error()
+        assert call(4096) != rn.RMSN_EINVAL
+    finally:
+        rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
+    assert call(2) != rn.RMSN_EINVAL
