@@ -95,7 +95,12 @@ typedef struct rmsn_graph rmsn_graph;
 /* One binary32 row: y[0..n) from x[0..n) and w[0..n). Lecture 04 section 2. */
 int rmsnorm_f32(const float* x, const float* w, float* y, int64_t n, float eps, void* stream);
 
-/* One bf16 row (bit patterns); binary32 arithmetic, one rounding at the store. */
+/* One bf16 row (bit patterns); binary32 arithmetic, one rounding at the store.
+ * The operation is Lecture 04 section 2's; the pages' kernel is binary32 only
+ * (rms_norm_f32), so the bf16 storage format -- exact widening of x and w,
+ * binary32 arithmetic, one round-to-nearest-even narrowing of y -- is taken
+ * from this library's bf16 workloads (the 64 x 7168 and 8192 x 7168 batches),
+ * not from the pages. */
 int rmsnorm_bf16(const uint16_t* x, const uint16_t* w, uint16_t* y, int64_t n, float eps,
                  void* stream);
 
@@ -117,11 +122,11 @@ int rmsnorm_batched_rows(int dtype, const void* x, int64_t x_row_stride, const v
 
 /* rmsnorm_batched_rows with a caller-provided device workspace, which lets
  * few wide rows (at most 64 rows of at least 64 KB) spread over many CUs:
- * RMSN_PATH_WIDE, two launches on
- * `stream`, the group totals of the association passing through the
- * workspace (Lecture 04 section 1: match the grid to the machine; section
- * 2.1: the association, and so the bits, stay those of every other path). Any other batch runs exactly as rmsnorm_batched_rows and leaves the
- * workspace untouched. workspace: DEVICE memory of at least the bytes
+ * RMSN_PATH_WIDE, two launches on `stream`, the group totals of the
+ * association passing through the workspace (Lecture 04 section 1: match the
+ * grid to the machine; section 2.1: the association, and so the bits, stay
+ * those of every other path). Any other batch runs exactly as
+ * rmsnorm_batched_rows and leaves the workspace untouched. workspace: DEVICE memory of at least the bytes
  * rmsnorm_workspace_query reports, 4-byte aligned, overlapping none of x, w,
  * y; its contents on entry do not matter and on return are unspecified. Calls
  * that may overlap in time need distinct workspaces. Errors as
@@ -153,7 +158,11 @@ int rmsnorm_batched_rows_noalloc(int dtype, const void* x, int64_t x_row_stride,
 /* The norms of a decode step, in order, issued as `count` dependent launches
  * on `stream` (the eager arm). d_table: DEVICE array of count descriptors.
  * h_widths: HOST array of count widths that size each launch (the same plan
- * function sizes graph nodes, so both arms launch identical kernels). */
+ * function sizes graph nodes, so both arms launch identical kernels).
+ * Lecture 08 "Graph-resident decode", section 1: the eager decode step pays
+ * one host submission per kernel, the launch bill the graph removes; section
+ * 4: the eager result is what every replay is compared against. Lecture 04
+ * section 6: both arms live in one binary. */
 int rmsnorm_sequence_eager(int dtype, const rmsn_desc* d_table, const int64_t* h_widths,
                            int32_t count, float eps, void* stream);
 
@@ -169,11 +178,18 @@ int rmsnorm_sequence_eager(int dtype, const rmsn_desc* d_table, const int64_t* h
 int rmsnorm_sequence_graph_create(int dtype, const rmsn_desc* d_table, const int64_t* h_widths,
                                   int32_t count, float eps, rmsn_graph** out);
 
-/* Replay the whole sequence with one graph launch on `stream`. */
+/* Replay the whole sequence with one graph launch on `stream` (Lecture 08
+ * "Graph-resident decode", section 1: one submission replays every captured
+ * node). On an eager-fallback handle (RMSN_ECAPTURE at creation) the same
+ * launches are issued one by one instead (section 3: degrade, do not fail).
+ * RMSN_EINVAL for a NULL handle; RMSN_EHIP if the launch fails. */
 int rmsnorm_sequence_graph_launch(rmsn_graph* g, void* stream);
 
 /* Release the graph and the handle. NULL is accepted. Does not synchronise:
- * the caller makes sure no launch of it is still pending. */
+ * the caller makes sure no launch of it is still pending. Lecture 08
+ * "Graph-resident decode", sections 1-2: the executable graph is a per-process
+ * object owned by whoever captured it; the device descriptor table it reads
+ * stays the caller's. */
 int rmsnorm_sequence_graph_destroy(rmsn_graph* g);
 
 /* ---- positioned sequences: the step's state update inside the graph ------ */
@@ -259,13 +275,24 @@ int rmsnorm_sequence_graph_update(rmsn_graph* g, const int64_t* h_widths, int32_
 int rmsnorm_sequence_persistent(int dtype, const rmsn_desc* d_table, int32_t count, float eps,
                                 const rmsn_position* pos, void* stream);
 
-/* Number of nodes in the captured graph (0 in eager-fallback mode). */
+/* Number of nodes in the captured graph (0 in eager-fallback mode): count,
+ * plus one for a positioned sequence's update. Lecture 08 "Graph-resident
+ * decode", section 1 reports its graph by node count (4,257 per rank); this
+ * is the same figure for a captured norm sequence. RMSN_EINVAL for a NULL
+ * handle or output. */
 int rmsnorm_graph_node_count(const rmsn_graph* g, int64_t* out);
 
-/* 1 if the handle replays eagerly because capture failed, else 0. */
+/* 1 if the handle replays eagerly because capture failed, else 0 (Lecture 08
+ * "Graph-resident decode", section 3: a capture that fails falls back to
+ * eager launches, and the fallback must be visible, not silent). */
 int rmsnorm_graph_is_fallback(const rmsn_graph* g, int* out);
 
-/* Human-readable reason for the last failure on this thread ("" if none). */
+/* Human-readable reason for the last failure on this thread ("" if none).
+ * Lecture 08 "Graph-resident decode", section 3: an error raised inside a
+ * capture (or by a kernel) surfaces later and elsewhere, so each failing call
+ * records which call and which HIP error it was, and the status code alone
+ * never has to be decoded. The string is owned by the library and valid until
+ * the thread's next call into it. */
 const char* rmsnorm_last_error(void);
 
 /* ---- launch planning (host only, no HIP call) ---------------------------- */
