@@ -335,14 +335,26 @@ const char* rmsnorm_last_error(void);
  *                     workspace; then a second launch of ceil(n / 4096)
  *                     workgroups per row combines the totals in the
  *                     association's order and applies 4096 elements each.
- *                     Chosen for at most 64 rows of at least 64 KB. */
+ *                     Chosen for at most 64 rows of at least 64 KB.
+ *   RMSN_PATH_REPLICA: one launch of `parts` GROUP workgroups per row (Lecture
+ *                     04 section 1: fill the machine; section 2.1: only the
+ *                     apply may be spread, the sum keeps its association).
+ *                     Each workgroup reads the whole row's x and computes the
+ *                     whole sum -- the same bits in every workgroup, no
+ *                     exchange between them -- and applies and stores only
+ *                     its share of the row's 1024-element blocks, loading w
+ *                     for those blocks only. Same conditions as GROUP; parts
+ *                     from RMSN_OPT_REPLICA_PARTS (at most the row's blocks).
+ *                     In-place launches (y == x) never take it: a workgroup
+ *                     still reading the row would see its siblings' stores. */
 enum {
     RMSN_PATH_WAVE = 0,
     RMSN_PATH_BLOCK = 1,
     RMSN_PATH_STREAM = 2,
     RMSN_PATH_SPLIT = 3,
     RMSN_PATH_GROUP = 4,
-    RMSN_PATH_WIDE = 5
+    RMSN_PATH_WIDE = 5,
+    RMSN_PATH_REPLICA = 6
 };
 
 typedef struct rmsn_plan_info {
@@ -356,8 +368,10 @@ typedef struct rmsn_plan_info {
     int32_t streaming;       /* WAVE / SPLIT: 1 = non-temporal loads of x and
                                 stores of y                                       */
     int32_t loads;           /* SPLIT: 16-byte loads per lane (1 KB slices per
-                                wavefront); GROUP: loads per lane (1024-element
-                                blocks); WIDE: apply workgroups per row; else 0   */
+                                wavefront); GROUP, REPLICA: loads per lane
+                                (1024-element blocks); WIDE: apply workgroups per
+                                row; else 0                                       */
+    int32_t parts;           /* REPLICA: workgroups per row; else 1              */
 } rmsn_plan_info;
 
 /* The launch the library would use for `rows` rows of width n whose row starts
@@ -399,17 +413,21 @@ int rmsnorm_workspace_query(int dtype, int64_t rows, int64_t n, int align, rmsn_
  *                            spread over many workgroups), 1 one workgroup
  *                            walking the whole table (the 128-lane build
  *                            always uses one)
+ *   RMSN_OPT_REPLICA_PARTS:   RMSN_PATH_REPLICA, 0 automatic (4), else 1..8
+ *                            workgroups per row (capped at the row's
+ *                            1024-element blocks)
  * Returns RMSN_EINVAL for an unknown key or value. Not synchronised with
  * launches on other threads. Environment: RMSN_PATH, RMSN_ROWS_PER_BLOCK,
  * RMSN_STREAMING, RMSN_SPLIT_LOADS, RMSN_APPLY_THREADS,
- * RMSN_PERSISTENT_WORKGROUPS. */
+ * RMSN_PERSISTENT_WORKGROUPS, RMSN_REPLICA_PARTS. */
 enum {
     RMSN_OPT_PATH = 1,
     RMSN_OPT_ROWS_PER_BLOCK = 2,
     RMSN_OPT_STREAMING = 3,
     RMSN_OPT_SPLIT_LOADS = 4,
     RMSN_OPT_APPLY_THREADS = 5,
-    RMSN_OPT_PERSISTENT_WORKGROUPS = 6
+    RMSN_OPT_PERSISTENT_WORKGROUPS = 6,
+    RMSN_OPT_REPLICA_PARTS = 7
 };
 int rmsnorm_set_option(int key, int value);
 int rmsnorm_get_option(int key, int* value);

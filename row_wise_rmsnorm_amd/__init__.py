@@ -30,8 +30,10 @@ RMSN_OK, RMSN_EINVAL, RMSN_EHIP, RMSN_ECAPTURE, RMSN_ENOMEM = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 PATH_AUTO, PATH_WAVE, PATH_BLOCK, PATH_STREAM, PATH_SPLIT, PATH_GROUP, PATH_WIDE = \
     -1, 0, 1, 2, 3, 4, 5
+PATH_REPLICA = 6
 OPT_PATH, OPT_ROWS_PER_BLOCK, OPT_STREAMING, OPT_SPLIT_LOADS, OPT_APPLY_THREADS = 1, 2, 3, 4, 5
 OPT_PERSISTENT_WORKGROUPS = 6
+OPT_REPLICA_PARTS = 7
 MAX_N = 1 << 24
 DESC_BYTES = 32
 
@@ -46,7 +48,7 @@ class _PlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("chunks", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("streaming", ctypes.c_int32),
-                ("loads", ctypes.c_int32)]
+                ("loads", ctypes.c_int32), ("parts", ctypes.c_int32)]
 
 
 class _Position(ctypes.Structure):
@@ -473,7 +475,7 @@ def plan_query(dtype, rows, n, aligned=True, align=None):
 def _plan_dict(info):
     return {"path": info.path, "chunks": info.chunks, "rows_per_block": info.rows_per_block,
             "streaming": info.streaming, "block": info.block, "grid": info.grid,
-            "loads": info.loads}
+            "loads": info.loads, "parts": info.parts}
 
 
 def set_option(key, value):

@@ -115,7 +115,7 @@ int run_rows(int dtype, const void* x, int64_t xs, const void* w, void* y, int64
     if ((st = check_eps(eps)) != RMSN_OK) return st;
     Plan p;
     st = make_plan(dtype, rows, n, rows_alignment(dtype, x, xs, w, y, ys), &p,
-                   ws_kind != Ws::kNone);
+                   ws_kind != Ws::kNone, x == y);
     if (st != RMSN_OK) return st;
     const bool wide = p.path == RMSN_PATH_WIDE;
     if (wide && ws_kind == Ws::kCaller &&
@@ -150,7 +150,9 @@ int run_rows(int dtype, const void* x, int64_t xs, const void* w, void* y, int64
                                  static_cast<float*>(ws) + 4 * r0,
                                  static_cast<hipStream_t>(stream));
         } else {
-            q.grid = (piece + p.rows_per_block - 1) / p.rows_per_block;
+            q.grid = p.path == RMSN_PATH_REPLICA
+                         ? piece * p.parts
+                         : (piece + p.rows_per_block - 1) / p.rows_per_block;
             e = launch_rows(q, xq, xs, w, yq, ys, piece, (int)n, eps,
                             static_cast<hipStream_t>(stream));
         }
@@ -359,7 +361,7 @@ bool same_launches(const std::vector<Plan>& a, const std::vector<Plan>& b) {
         const Plan& q = b[i];
         if (p.path != q.path || p.chunks != q.chunks || p.loads != q.loads ||
             p.block != q.block || p.grid != q.grid || p.rows_per_block != q.rows_per_block ||
-            p.streaming != q.streaming)
+            p.streaming != q.streaming || p.parts != q.parts)
             return false;
     }
     return true;
@@ -590,6 +592,7 @@ static void plan_info(const Plan& p, rmsn_plan_info* out) {
     out->path = p.path;
     out->chunks = p.chunks;
     out->rows_per_block = p.rows_per_block;
+    out->parts = p.parts;
     out->block = p.block;
     out->grid = p.grid;
     out->streaming = p.streaming;

@@ -385,9 +385,14 @@ struct SplitPart {
 // (16 B binary32, 8 B bf16). Blocks below Q-1 are complete; in the last one,
 // quads past the row are loaded from the row's last quad (an in-row address)
 // and masked to +0 after every load has been issued.
+//
+// m0, m1: the blocks [m0, m1) this workgroup applies and stores (wave-uniform;
+// the whole row by default). Every call reads the whole of x and computes the
+// whole row's sum, so a row may be applied by several workgroups, each taking
+// a block range (REPLICA), with every workgroup's inv bit-identical.
 template <typename T, int Q>
 __device__ __forceinline__ void row_group(const T* x, const T* __restrict__ w, T* y, int n,
-                                          float eps, float* lds4) {
+                                          float eps, float* lds4, int m0 = 0, int m1 = Q) {
     using QD = Quad<T>;
     constexpr uint32_t es = sizeof(T);
     const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -406,7 +411,8 @@ __device__ __forceinline__ void row_group(const T* x, const T* __restrict__ w, T
 #pragma unroll
     for (int m = 0; m < Q; ++m) {
         const uint32_t e = m + 1 < Q || exact ? 1024u * m + off : min(1024u * m + off, last);
-        wr[m] = QD::template gload<false>(wg + e * es);
+        if (m >= m0 && m < m1) wr[m] = QD::template gload<false>(wg + e * es);
+        else wr[m] = QD::zero();
     }
     __builtin_amdgcn_sched_barrier(0);
     const bool tail_in = exact || 1024u * (Q - 1) + off < (uint32_t)n;
@@ -429,6 +435,7 @@ __device__ __forceinline__ void row_group(const T* x, const T* __restrict__ w, T
     gptr yg = scalar_gptr(reinterpret_cast<char*>(y));
 #pragma unroll
     for (int m = 0; m < Q; ++m) {
+        if (m < m0 || m >= m1) continue;
         if (m + 1 == Q && !tail_in) continue;
         float v[4], wv[4], o[4];
         QD::unpack(xr[m], v);
@@ -616,6 +623,23 @@ __global__ __launch_bounds__(256) void k_rows_group(const T* x, int64_t xs,
     __shared__ float lds4[4];
     const int64_t r = blockIdx.x;
     row_group<T, Q>(x + r * xs, w, y + r * ys, n, eps, lds4);
+}
+
+// REPLICA layout: `parts` workgroups per row (blockIdx = row * parts + part),
+// each the GROUP layout over the whole row's x -- the same sum, so the same
+// inv in every workgroup -- applying and storing only its share of the
+// row's 1024-element blocks. No workgroup reads what another writes; x is
+// read `parts` times (from the caches after the first), w and y once.
+template <typename T, int Q>
+__global__ __launch_bounds__(256) void k_rows_replica(const T* x, int64_t xs,
+                                                      const T* __restrict__ w, T* y, int64_t ys,
+                                                      int n, float eps, uint32_t parts) {
+    __shared__ float lds4[4];
+    const uint32_t b = blockIdx.x;
+    const int64_t r = b / parts;
+    const int part = (int)(b - (uint32_t)r * parts);
+    const int m0 = (part * Q) / (int)parts, m1 = ((part + 1) * Q) / (int)parts;
+    row_group<T, Q>(x + r * xs, w, y + r * ys, n, eps, lds4, m0, m1);
 }
 
 // GROUP-layout descriptor row: the captured instance Q is used when the row
@@ -1565,6 +1589,27 @@ hipError_t launch_group_t(const Plan& p, const void* x, int64_t xs, const void* 
 }
 
 template <typename T>
+hipError_t launch_replica_t(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
+                            int64_t ys, int n, float eps, hipStream_t s) {
+    const T* xp = static_cast<const T*>(x);
+    const T* wp = static_cast<const T*>(w);
+    T* yp = static_cast<T*>(y);
+    const dim3 grid((unsigned)p.grid), block(256);
+    const uint32_t parts = (uint32_t)p.parts;
+#define RMSN_CASE(Q)                                                                          \
+    case Q:                                                                                   \
+        hipLaunchKernelGGL((k_rows_replica<T, Q>), grid, block, 0, s, xp, xs, wp, yp, ys, n, \
+                           eps, parts);                                                       \
+        break;
+    switch (p.loads) {
+        RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)
+        default: return hipErrorInvalidValue;
+    }
+#undef RMSN_CASE
+    return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_block_t(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
                           int64_t ys, int n, float eps, hipStream_t s) {
     const T* xp = static_cast<const T*>(x);
@@ -1642,6 +1687,17 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
             return hipErrorInvalidValue;
         return p.dtype == RMSN_F32 ? launch_group_t<float>(p, x, xs, w, y, ys, n, eps, stream)
                                    : launch_group_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
+    }
+    if (p.path == RMSN_PATH_REPLICA) {
+        // each of the plan's `parts` workgroups per row takes at least one
+        // of the row's blocks
+        const int q = (n + 1023) / 1024;
+        if ((n & 3) != 0 || p.loads != q || p.block != kBlockThreads ||
+            p.parts < 1 || p.parts > q || p.grid != rows * p.parts)
+            return hipErrorInvalidValue;
+        return p.dtype == RMSN_F32
+                   ? launch_replica_t<float>(p, x, xs, w, y, ys, n, eps, stream)
+                   : launch_replica_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
     }
     if (p.path == RMSN_PATH_STREAM)
         return launch_stream_rows(p, x, xs, w, y, ys, rows, n, eps, stream);

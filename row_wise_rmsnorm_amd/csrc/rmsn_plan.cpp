@@ -22,6 +22,7 @@ std::atomic<int> g_stream{-2};
 std::atomic<int> g_split{-2};
 std::atomic<int> g_apply{-2};
 std::atomic<int> g_pwg{-2};
+std::atomic<int> g_parts{-2};
 
 int env_int(const char* name, int dflt) {
     const char* s = std::getenv(name);
@@ -34,13 +35,15 @@ int env_int(const char* name, int dflt) {
 
 bool valid_path(int v) {
     return v == -1 || v == RMSN_PATH_WAVE || v == RMSN_PATH_BLOCK || v == RMSN_PATH_STREAM ||
-           v == RMSN_PATH_SPLIT || v == RMSN_PATH_GROUP || v == RMSN_PATH_WIDE;
+           v == RMSN_PATH_SPLIT || v == RMSN_PATH_GROUP || v == RMSN_PATH_WIDE ||
+           v == RMSN_PATH_REPLICA;
 }
 bool valid_split_loads(int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8; }
 bool valid_apply_threads(int v) { return v == 0 || v == 128 || v == 256 || v == 512 || v == 1024; }
 bool valid_rpb(int v) { return v == 0 || v == 4 || v == 8; }
 bool valid_streaming(int v) { return v == -1 || v == 0 || v == 1; }
 bool valid_persistent_wg(int v) { return v == 0 || v == 1; }
+bool valid_parts(int v) { return v >= 0 && v <= 8; }
 
 // Byte ranges [a, a+la) and [b, b+lb) intersect.
 bool overlaps(uintptr_t a, uint64_t la, uintptr_t b, uint64_t lb) {
@@ -119,10 +122,20 @@ int option_persistent_workgroups() {
     return v;
 }
 
+int option_replica_parts() {
+    int v = g_parts.load(std::memory_order_relaxed);
+    if (v == -2) {
+        v = env_int("RMSN_REPLICA_PARTS", 0);
+        if (!valid_parts(v)) v = 0;
+        g_parts.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 int set_option(int key, int value) {
     if (key == RMSN_OPT_PATH) {
         if (!valid_path(value)) {
-            set_error("rmsnorm_set_option: path must be -1 (automatic) or 0..5, got %d", value);
+            set_error("rmsnorm_set_option: path must be -1 (automatic) or 0..6, got %d", value);
             return RMSN_EINVAL;
         }
         g_path.store(value, std::memory_order_relaxed);
@@ -175,6 +188,15 @@ int set_option(int key, int value) {
         g_pwg.store(value, std::memory_order_relaxed);
         return RMSN_OK;
     }
+    if (key == RMSN_OPT_REPLICA_PARTS) {
+        if (!valid_parts(value)) {
+            set_error("rmsnorm_set_option: replica parts must be 0 (automatic) or 1..8, got %d",
+                      value);
+            return RMSN_EINVAL;
+        }
+        g_parts.store(value, std::memory_order_relaxed);
+        return RMSN_OK;
+    }
     set_error("rmsnorm_set_option: unknown key %d", key);
     return RMSN_EINVAL;
 }
@@ -193,6 +215,7 @@ int get_option(int key, int* value) {
         return RMSN_OK;
     }
     if (key == RMSN_OPT_PERSISTENT_WORKGROUPS) { *value = option_persistent_workgroups(); return RMSN_OK; }
+    if (key == RMSN_OPT_REPLICA_PARTS) { *value = option_replica_parts(); return RMSN_OK; }
     set_error("rmsnorm_get_option: unknown key %d", key);
     return RMSN_EINVAL;
 }
@@ -231,7 +254,8 @@ int auto_split_loads(int64_t slices) {
     return (slices + u - 1) / u <= kMaxSplitWaves ? u : 0;
 }
 
-int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out, bool workspace) {
+int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out, bool workspace,
+              bool in_place) {
     if (dtype != RMSN_F32 && dtype != RMSN_BF16) {
         set_error("unknown dtype %d", dtype);
         return RMSN_EINVAL;
@@ -250,6 +274,7 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out, bool wor
         const int b = option_apply_threads();
         Plan p{};
         p.dtype = dtype;
+        p.parts = 1;
         p.path = RMSN_PATH_BLOCK;
         p.chunks = 0;
         p.rows_per_block = 1;
@@ -281,6 +306,9 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out, bool wor
         case RMSN_PATH_SPLIT: path = can_split ? RMSN_PATH_SPLIT : -1; break;
         case RMSN_PATH_GROUP: path = can_group ? RMSN_PATH_GROUP : -1; break;
         case RMSN_PATH_WIDE: path = can_wide ? RMSN_PATH_WIDE : -1; break;
+        case RMSN_PATH_REPLICA:
+            path = can_group && !run_time && !in_place ? RMSN_PATH_REPLICA : -1;
+            break;
         default: path = -1; break;
     }
     if (path < 0) {
@@ -312,6 +340,7 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out, bool wor
     Plan p{};
     p.dtype = dtype;
     p.path = path;
+    p.parts = 1;
     const int st = option_streaming();
     if (path == RMSN_PATH_WAVE) {
         int rpb = option_rows_per_block();
@@ -346,6 +375,17 @@ int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out, bool wor
         p.streaming = 0;
         p.block = kBlockThreads;
         p.grid = rows;
+    } else if (path == RMSN_PATH_REPLICA) {
+        // GROUP over the whole row in each of `parts` workgroups per row, each
+        // applying a share of the row's blocks
+        p.loads = (int)((n + 1023) / 1024);
+        p.chunks = 4 * p.loads;
+        p.rows_per_block = 1;
+        p.streaming = 0;
+        p.block = kBlockThreads;
+        const int want = option_replica_parts() ? option_replica_parts() : kReplicaParts;
+        p.parts = want < p.loads ? want : p.loads;
+        p.grid = rows * p.parts;
     } else {
         p.chunks = path == RMSN_PATH_BLOCK ? bucket : 0;
         p.rows_per_block = 1;

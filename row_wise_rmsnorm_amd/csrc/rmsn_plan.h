@@ -54,8 +54,10 @@ struct Plan {
     int block;           // threads per workgroup
     int64_t grid;        // workgroups
     int loads;           // SPLIT: 16-byte loads per lane (slices per wavefront);
-                         // GROUP: loads per lane (1024-element blocks);
+                         // GROUP, REPLICA: loads per lane (1024-element blocks);
                          // WIDE: apply workgroups per row; else 0
+    int parts;           // REPLICA: workgroups per row, each applying a share of
+                         // the row's blocks; else 1
 };
 
 inline int elem_bytes(int dtype) { return dtype == RMSN_F32 ? 4 : 2; }
@@ -67,6 +69,7 @@ inline int64_t rows_per_launch(const Plan& p) {
         return 0xFFFFFFFFll / (256ll * (p.loads > 1 ? p.loads : 1));
     int64_t groups = 0xFFFFFFFFll / (p.block > 0 ? p.block : 1);
     if (groups > 0x7FFFFFFFll) groups = 0x7FFFFFFFll;
+    if (p.path == RMSN_PATH_REPLICA) return groups / (p.parts > 0 ? p.parts : 1);
     return groups * (p.rows_per_block > 0 ? p.rows_per_block : 1);
 }
 // Bytes one lane loads per 256-element chunk on the WAVE path: four elements.
@@ -95,9 +98,12 @@ int auto_split_loads(int64_t slices);
 // fit). Returns RMSN_OK or RMSN_EINVAL (bad dtype, rows < 1, n outside
 // [1, 2^24]).
 // workspace: the launch may use one (rmsnorm_batched_rows_ws), which makes
-// the WIDE path available.
+// the WIDE path available. in_place: y == x; such a launch never takes
+// REPLICA, whose workgroups read the whole row while their siblings store
+// their shares of it.
 constexpr int kAlignAtRunTime = -1;
-int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out, bool workspace = false);
+int make_plan(int dtype, int64_t rows, int64_t n, int align, Plan* out, bool workspace = false,
+              bool in_place = false);
 // Elements one workgroup of the WIDE path's second launch applies.
 constexpr int64_t kWideSpan = 4096;
 // Rows of at least kWideMinBytes in batches of at most kWideMaxRows rows take
@@ -106,6 +112,9 @@ constexpr int64_t kWideSpan = 4096;
 // flight at once, than on two launches).
 constexpr int64_t kWideMinBytes = 64 * 1024;
 constexpr int64_t kWideMaxRows = 64;
+// REPLICA path: workgroups per row when not set by option (capped at the
+// row's block count).
+constexpr int kReplicaParts = 4;
 
 // Process-wide options (rmsnorm_set_option); read lazily from the environment.
 int option_path();            // -1 automatic, else an RMSN_PATH_* value
@@ -114,6 +123,7 @@ int option_streaming();       // -1 automatic, 0 off, 1 on
 int option_split_loads();     // 0 automatic, else 1, 2, 4 or 8
 int option_apply_threads();   // 128-lane build: 0 (= 1024) or 128, 256, 512, 1024
 int option_persistent_workgroups();  // 0 automatic, 1 one workgroup
+int option_replica_parts();   // 0 automatic, else 1..8 workgroups per row
 int set_option(int key, int value);
 int get_option(int key, int* value);
 

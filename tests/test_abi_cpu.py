@@ -223,7 +223,7 @@ def test_plan_paths_and_buckets(rn):
     # slices (16-byte loads) per wavefront; a 235 MB launch streams (non-temporal)
     p = rn.plan_query(rn.BF16, 8192, 7168, aligned=True)
     assert p == {"path": rn.PATH_SPLIT, "chunks": 4, "rows_per_block": 1, "streaming": 1,
-                 "block": 448, "grid": 8192, "loads": 2}
+                 "block": 448, "grid": 8192, "loads": 2, "parts": 1}
     # binary32: 28 slices, four per wavefront
     p = rn.plan_query(rn.F32, 8192, 7168)
     assert (p["path"], p["loads"], p["block"], p["chunks"]) == (rn.PATH_SPLIT, 4, 448, 4)
@@ -245,7 +245,7 @@ def test_plan_paths_and_buckets(rn):
     # workgroup sharing one LDS copy of w
     p = rn.plan_query(rn.BF16, 8192, 7168, align=8)
     assert p == {"path": rn.PATH_WAVE, "chunks": 28, "rows_per_block": 8, "streaming": 1,
-                 "block": 512, "grid": 1024, "loads": 0}
+                 "block": 512, "grid": 1024, "loads": 0, "parts": 1}
     # fewer than 2048 rows: 4 per workgroup
     p = rn.plan_query(rn.BF16, 1024, 1536, align=8)   # 3 KB rows, 6 MB
     assert p["path"] == rn.PATH_WAVE and p["rows_per_block"] == 4 and p["grid"] == 256
@@ -256,10 +256,10 @@ def test_plan_paths_and_buckets(rn):
     # quad-aligned or the width is not a whole number of quads
     p = rn.plan_query(rn.BF16, 64, 7168, aligned=True)
     assert p == {"path": rn.PATH_GROUP, "chunks": 28, "rows_per_block": 1, "streaming": 0,
-                 "block": 256, "grid": 64, "loads": 7}
+                 "block": 256, "grid": 64, "loads": 7, "parts": 1}
     p = rn.plan_query(rn.BF16, 64, 7168, aligned=False)
     assert p == {"path": rn.PATH_BLOCK, "chunks": 28, "rows_per_block": 1, "streaming": 0,
-                 "block": 256, "grid": 64, "loads": 0}
+                 "block": 256, "grid": 64, "loads": 0, "parts": 1}
     assert rn.plan_query(rn.BF16, 64, 7166)["path"] == rn.PATH_BLOCK
     # single rows
     assert rn.plan_query(rn.F32, 1, 7168)["path"] == rn.PATH_GROUP
@@ -269,7 +269,7 @@ def test_plan_paths_and_buckets(rn):
     # descriptor rows of the decode step: BLOCK instances by width
     assert rn.plan_query(rn.F32, 1, 7168, align=-1) == {
         "path": rn.PATH_BLOCK, "chunks": 28, "rows_per_block": 1, "streaming": 0,
-        "block": 256, "grid": 1, "loads": 0}
+        "block": 256, "grid": 1, "loads": 0, "parts": 1}
     assert rn.plan_query(rn.F32, 1, 1536, align=-1)["chunks"] == 6
     assert rn.plan_query(rn.F32, 1, 512, align=-1)["chunks"] == 2
     # unaligned rows never take the WAVE, SPLIT or GROUP path
@@ -357,7 +357,7 @@ def test_options_roundtrip_and_force_paths(rn):
         rn.set_option(rn.OPT_PATH, rn.PATH_GROUP)
         p = rn.plan_query(rn.BF16, 64, 7168, align=8)
         assert p == {"path": rn.PATH_GROUP, "chunks": 28, "rows_per_block": 1, "streaming": 0,
-                     "block": 256, "grid": 64, "loads": 7}
+                     "block": 256, "grid": 64, "loads": 7, "parts": 1}
         assert rn.plan_query(rn.F32, 1, 1536)["loads"] == 2
         assert rn.plan_query(rn.F32, 1, 4)["loads"] == 1
         assert rn.plan_query(rn.F32, 1, 1025, align=16)["path"] == rn.PATH_BLOCK   # not whole quads
@@ -388,7 +388,7 @@ def test_options_roundtrip_and_force_paths(rn):
         with pytest.raises(rn.RmsnormError):
             rn.set_option(rn.OPT_PATH, 7)
         with pytest.raises(rn.RmsnormError):
-            rn.set_option(rn.OPT_PATH, 6)
+            rn.set_option(rn.OPT_PATH, -2)
         # WIDE needs a workspace: forced, the plain plan falls back to the
         # automatic choice and the workspace plan takes it for any shape
         rn.set_option(rn.OPT_PATH, rn.PATH_WIDE)
@@ -567,3 +567,32 @@ def test_noalloc_rejects(rn):
     finally:
         rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
     assert call(2) != rn.RMSN_EINVAL
+
+
+def test_replica_plan(rn):
+    """REPLICA (forced only): `parts` GROUP workgroups per row, parts from the
+    option (default 4), capped at the row's 1024-element blocks; the grid is
+    rows x parts; rows GROUP cannot take and descriptor rows fall back to the
+    automatic choice."""
+    try:
+        rn.set_option(rn.OPT_PATH, rn.PATH_REPLICA)
+        p = rn.plan_query(rn.F32, 1, 7168)
+        assert (p["path"], p["parts"], p["grid"], p["loads"], p["block"]) == \
+            (rn.PATH_REPLICA, 4, 4, 7, 256)
+        p = rn.plan_query(rn.BF16, 64, 7168)
+        assert (p["path"], p["parts"], p["grid"]) == (rn.PATH_REPLICA, 4, 256)
+        for parts, want in ((1, 1), (2, 2), (7, 7), (8, 7)):
+            rn.set_option(rn.OPT_REPLICA_PARTS, parts)
+            assert rn.get_option(rn.OPT_REPLICA_PARTS) == parts
+            p = rn.plan_query(rn.BF16, 64, 7168)
+            assert (p["parts"], p["grid"]) == (want, 64 * want), parts
+        assert rn.plan_query(rn.F32, 3, 512)["parts"] == 1        # one block: one part
+        assert rn.plan_query(rn.F32, 3, 8190)["path"] == rn.PATH_BLOCK   # n % 4: BLOCK
+        assert rn.plan_query(rn.F32, 1, 7168, align=-1)["path"] != rn.PATH_REPLICA
+        for bad in (-1, 9):
+            with pytest.raises(rn.RmsnormError):
+                rn.set_option(rn.OPT_REPLICA_PARTS, bad)
+    finally:
+        rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
+        rn.set_option(rn.OPT_REPLICA_PARTS, 0)
+    assert rn.plan_query(rn.F32, 1, 7168)["path"] == rn.PATH_GROUP

@@ -4,8 +4,8 @@ Each case draws a dtype, a row count, a width (biased towards the widths the
 layouts care about: multiples of 4, 8, 256 and 1024, one more or one less,
 and arbitrary values), independent element offsets of x, w and y, row
 strides with padding, sometimes in-place rows, a path setting (automatic, or
-one path forced, with random rows-per-workgroup, streaming and
-slices-per-wavefront options), and whether the launch goes through the
+one path forced, with random rows-per-workgroup, streaming,
+slices-per-wavefront and workgroups-per-row options), and whether the launch goes through the
 workspace entry point (always when WIDE is forced). Every output element is
 compared with the CPU oracle, and the padding around the rows must stay
 untouched.
@@ -35,6 +35,7 @@ def _reset(rn):
     rn.set_option(rn.OPT_ROWS_PER_BLOCK, 0)
     rn.set_option(rn.OPT_STREAMING, -1)
     rn.set_option(rn.OPT_SPLIT_LOADS, 0)
+    rn.set_option(rn.OPT_REPLICA_PARTS, 0)
 
 
 def _width(g):
@@ -66,7 +67,8 @@ def _case(g, i):
     in_place = g.random() < 0.15
     if in_place:
         oy, ys = ox, xs
-    path = int(g.choice([-1, -1, 0, 1, 2, 3, 4, 5]))
+    path = int(g.choice([-1, -1, 0, 1, 2, 3, 4, 5, 6]))
+    parts = int(g.integers(0, 9))
     rpb = int(g.choice([0, 4, 8]))
     streaming = int(g.choice([-1, 0, 1]))
     loads = int(g.choice([0, 1, 2, 4, 8]))
@@ -74,7 +76,7 @@ def _case(g, i):
     ws = path == 5 or g.random() < 0.3
     return dict(i=i, kind=kind, n=n, rows=rows, ox=ox, ow=ow, oy=oy, xs=xs, ys=ys,
                 in_place=in_place, path=path, rpb=rpb, streaming=streaming, loads=loads,
-                sigma=sigma, ws=ws)
+                parts=parts, sigma=sigma, ws=ws)
 
 
 @pytest.mark.parametrize("block", range(6))
@@ -113,6 +115,7 @@ def test_fuzz(rn, block):
             rn.set_option(rn.OPT_ROWS_PER_BLOCK, c["rpb"])
             rn.set_option(rn.OPT_STREAMING, c["streaming"])
             rn.set_option(rn.OPT_SPLIT_LOADS, c["loads"])
+            rn.set_option(rn.OPT_REPLICA_PARTS, c["parts"])
             if c["ws"]:
                 rn.rmsnorm_batched_rows_ws(bx_rows, bw[c["ow"]:c["ow"] + n], wl.EPS, out=by_rows)
             else:
