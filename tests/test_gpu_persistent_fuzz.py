@@ -54,7 +54,7 @@ def _table(g):
     buffer sizes. The table's kind decides its dependencies: none, only at
     distances of 4 to 20 rows, of 16 to 40 rows, anywhere (from 1), or a
     chain (every row reads the output of the row before)."""
-    count = int(g.choice([1, 2, 3, 5, 9, 16, 17, 33, 64]))
+    count = int(g.choice([1, 2, 3, 5, 9, 16, 17, 33, 64, 300, 700, 1024]))
     aligned = g.random() < 0.7
     deps = str(g.choice(["none", "none", "far", "far", "farther", "any", "chain"]))
     cls = str(g.choice(["vec", "vec", "quad", "any"]))
