@@ -15,6 +15,15 @@ cache defeated by rotating over 4 buffer sets (940 MB). Also reported:
 * decode_step_positioned: the same step walking a ring of rows through a
   device-resident position that the step itself advances (Lecture 08
   section 2), eager vs graph;
+* dispatch_floor_us: a graph-captured one-element launch, the floor under the
+  graph-timed figures; the single norm and the batch are also given above it;
+* decode_step_nodes: per-node time of each descriptor kernel of the step;
+* persistent_check: the persistent launch on tiny independent rows (its
+  dispatch plus the first workgroup's overlap check);
+* geometry_audit: every kernel of these workloads with grid, block,
+  workgroups per CU, calls and time per step, its bandwidth floor and
+  measured / floor, ranked by the time per step above the floor (Lecture 04,
+  Lab);
 * roofline: the prefill kernel against the 8 TB/s HBM peak;
 * prefill.wave_path_us: the same launches on the one-wavefront-per-row layout;
 * cpu_baseline: the CPU oracle timed on this host (a reported baseline only).
@@ -22,6 +31,7 @@ cache defeated by rotating over 4 buffer sets (940 MB). Also reported:
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D]
        python bench.py --profile-kernels     (short run for rocprofv3 counters)
        python bench.py --profile-decode      (the same, decode step: eager + persistent)
+       python bench.py --profile-persistent spread|one|chained   (one persistent arm)
 """
 import argparse
 import hashlib
@@ -252,6 +262,140 @@ def bench_batch64(rn, torch, np, wl):
             "workgroups_per_cu": plan["grid"] / 256.0}
 
 
+def bench_dispatch_floor(rn, torch):
+    """What a graph-captured launch costs with (almost) no work: torch's fill
+    of one element, and this library's norm of a one-element row (one
+    256-thread workgroup: one load of x and w, the sum, the inverse, one
+    store). The single norm and the 64-row batch are reported against it."""
+    dev = torch.device("cuda", 0)
+    one = torch.zeros(1, device=dev)
+    x1 = torch.ones(1, device=dev)
+    w1 = torch.ones(1, device=dev)
+    y1 = torch.empty(1, device=dev)
+    fill = graph_us_per_launch(torch, lambda s: one.fill_(1.0), reps=10)
+    norm1 = graph_us_per_launch(
+        torch, lambda s: rn.rmsnorm_f32(x1, w1, 1e-6, out=y1, stream=s), reps=10)
+    return {"torch_fill_1_element_us": fill, "rmsnorm_1_element_us": norm1,
+            "note": ("100 launches captured in one graph, replayed; each launch pays the graph's "
+                     "per-node dispatch: the floor under every graph-timed figure here")}
+
+
+def bench_decode_nodes(rn, torch, np, wl, reps=10, replays=200):
+    """Per-node time of the decode step's descriptor kernels, one instance at a
+    time: the step's rows of one width captured as their own graph (the same
+    kernels, plans and rows as the step), replay time / rows. Each width also
+    on the other descriptor layout (GROUP when the plan takes BLOCK), the two
+    interleaved, outputs compared bit for bit."""
+    rows = wl.decode()
+    dev = torch.device("cuda", 0)
+    eps = float(wl.EPS)
+    out = {}
+    for width in sorted({len(x) for x, _ in rows}, reverse=True):
+        sel = [(x, w) for x, w in rows if len(x) == width]
+        xs = [torch.from_numpy(x).to(dev) for x, _ in sel]
+        ws = [torch.from_numpy(w).to(dev) for _, w in sel]
+        ys = [torch.empty_like(t) for t in xs]
+        table, widths = rn.make_table(list(zip(xs, ws, ys)))
+        plan = rn.plan_query(rn.F32, 1, width, align=-1)
+        other = rn.PATH_GROUP if plan["path"] != rn.PATH_GROUP else rn.PATH_BLOCK
+        graphs = {"plan": rn.SequenceGraph(table, widths, eps, rn.F32)}
+        rn.set_option(rn.OPT_PATH, other)
+        try:
+            graphs["other"] = rn.SequenceGraph(table, widths, eps, rn.F32)
+            other_plan = rn.plan_query(rn.F32, 1, width, align=-1)
+        finally:
+            rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
+        for g in graphs.values():
+            if g.status != rn.RMSN_OK:
+                raise RuntimeError(f"graph capture failed: {g.capture_error}")
+            for _ in range(20):
+                g.launch()
+        bits = {}
+        for k, g in graphs.items():
+            g.launch()
+            torch.cuda.synchronize()
+            bits[k] = [t.cpu().numpy().view(np.uint32).copy() for t in ys]
+        same = all(np.array_equal(a, b) for a, b in zip(bits["plan"], bits["other"]))
+        per = {"plan": [], "other": []}
+        for r in range(reps):
+            for k in (("plan", "other") if r % 2 == 0 else ("other", "plan")):
+                g = graphs[k]
+                per[k].append(1000.0 * elapsed_ms(lambda i: g.launch(), replays)
+                              / (replays * len(sel)))
+        out[str(width)] = {"rows_per_step": len(sel), "us_per_node": stats(per["plan"]),
+                           "plan": plan, "other_layout_us_per_node": stats(per["other"]),
+                           "other_layout_plan": other_plan, "bit_exact_layouts": bool(same)}
+        for g in graphs.values():
+            g.destroy()
+    return out
+
+
+def bench_persistent_check(rn, torch, np, wl, decode_steps):
+    """The persistent launch's own cost: 327 independent rows of 4 elements
+    (their work is negligible, so the launch time is the dispatch plus the
+    first workgroup's check of which rows may overlap), against one such row
+    (no check: one workgroup)."""
+    dev = torch.device("cuda", 0)
+    eps = float(wl.EPS)
+
+    def arm(count):
+        xs = [torch.ones(4, device=dev) for _ in range(count)]
+        ws = [torch.ones(4, device=dev) for _ in range(count)]
+        ys = [torch.empty(4, device=dev) for _ in range(count)]
+        table, _ = rn.make_table(list(zip(xs, ws, ys)))
+        fn = lambda i: rn.rmsnorm_sequence_persistent(table, count, eps, rn.F32)
+        for i in range(20):
+            fn(i)
+        return stats([1000.0 * elapsed_ms(fn, decode_steps) / decode_steps for _ in range(4)])
+
+    return {"check_327_rows_us": arm(327), "one_row_us": arm(1),
+            "note": ("327 independent 4-element rows spread over 256 workgroups: the first "
+                     "workgroup checks every pair of rows (rank sort of the outputs, searches) "
+                     "while the others run the rows; one row: a single workgroup, no check")}
+
+
+def geometry_audit(single, b64, dec, nodes, pre, plan_prefill):
+    """Every kernel of the four timed workloads (Lecture 04, Lab: grid, block,
+    calls, time, the bandwidth floor, measured over floor), ranked by the time
+    per step spent above the floor."""
+    peak = PEAK_HBM_GBS * 1e3          # bytes per microsecond
+    cu = 256
+    rows = []
+
+    def add(workload, kernel, grid, block, calls, mean, sd, nbytes):
+        floor = nbytes / peak
+        rows.append({"workload": workload, "kernel": kernel, "grid": grid, "block": block,
+                     "workgroups_per_cu": round(grid / cu, 4), "calls_per_step": calls,
+                     "us_per_call": round(mean, 3), "sd_us": round(sd, 3),
+                     "us_per_step": round(calls * mean, 3), "bytes_per_call": nbytes,
+                     "floor_us": round(floor, 4), "measured_over_floor": round(mean / floor, 1),
+                     "above_floor_us_per_step": round(calls * (mean - floor), 3)})
+
+    n = 7168
+    add("prefill 8192x7168 bf16", "k_rows_split (SPLIT, 7 wavefronts, 2 slices each)",
+        plan_prefill["grid"], plan_prefill["block"], 1, pre["us_per_launch"],
+        pre["reps_us"]["sd"], 8192 * n * 4 + n * 2)
+    s = single["us_per_norm_device"]
+    add("single norm 1x7168 f32", "k_rows_group (GROUP, Q=7)", single["plan"]["grid"],
+        single["plan"]["block"], 1, s["mean"], s["sd"], n * 12)
+    b = b64["us_device"]
+    add("batch 64x7168 bf16", "k_rows_group (GROUP, Q=7)", b64["plan"]["grid"],
+        b64["plan"]["block"], 1, b["mean"], b["sd"], 64 * n * 4 + n * 2)
+    for width, v in nodes.items():
+        wd = int(width)
+        add("decode step, graph", f"k_desc_block (BLOCK, {v['plan']['chunks']} chunks), width {wd}",
+            1, 256, v["rows_per_step"], v["us_per_node"]["mean"], v["us_per_node"]["sd"], wd * 12)
+    step_bytes = dec["algo_bytes_per_step"]
+    gdev = dec["persistent_graph_captured_us_per_step"]
+    for key, name, grid in (("spread", "spread over workgroups", 256),
+                            ("one_workgroup", "one workgroup", 1),
+                            ("chained_table", "chained table (every row bound)", 256)):
+        add("decode step, persistent (graph-timed)", f"k_sequence_persistent, {name}", grid, 256,
+            1, gdev[key]["mean"], gdev[key]["sd"], step_bytes)
+    rows.sort(key=lambda r: -r["above_floor_us_per_step"])
+    return rows
+
+
 WIDE_SHAPES = [("f32", 1, 1 << 14), ("f32", 1, 1 << 16), ("f32", 1, 1 << 20), ("f32", 1, 1 << 24),
                ("bf16", 1, 1 << 24), ("bf16", 16, 1 << 18), ("bf16", 64, 1 << 16)]
 
@@ -396,6 +540,18 @@ def bench_decode(rn, torch, np, wl, decode_steps):
     torch.cuda.synchronize()
     ok_c = all(np.array_equal(a, t.cpu().numpy().view(np.uint32)) for a, t in zip(want, ys))
     chained_us = stats([rep(chained) for _ in range(4)])
+    # the same three arms captured in a graph (no host in the loop): the
+    # persistent kernel's own time on the device
+    pers_s = lambda tbl: (lambda st: rn.rmsnorm_sequence_persistent(tbl, len(widths), eps, rn.F32,
+                                                                    stream=st))
+    dev_spread = graph_us_per_launch(torch, pers_s(table), per_graph=50, replays=10, reps=10)
+    rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 1)
+    try:
+        dev_one = graph_us_per_launch(torch, pers_s(table), per_graph=10, replays=5, reps=5)
+    finally:
+        rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 0)
+    dev_chained = graph_us_per_launch(torch, pers_s(ctable), per_graph=10, replays=5, reps=5)
+    timeouts = rn.diag_walk_timeouts(reset=True)
     algo = sum(n * 12 for n in widths)
     nodes = g.node_count()
     g.destroy()
@@ -407,11 +563,17 @@ def bench_decode(rn, torch, np, wl, decode_steps):
         "bit_exact_persistent_eq_graph": bool(ok_p),
         "persistent_one_workgroup_us_per_step": one_wg,
         "persistent_chained_table_us_per_step": chained_us,
+        "persistent_graph_captured_us_per_step": {"spread": dev_spread, "one_workgroup": dev_one,
+                                                  "chained_table": dev_chained},
+        "persistent_walk_timeouts": timeouts,
         "bit_exact_chained_persistent_eq_eager": bool(ok_c),
         "persistent_note": ("the step's norms share no memory, so the persistent launch runs them "
                             "on up to 256 workgroups; one_workgroup: the whole table walked by one "
                             "workgroup; chained_table: the same widths with norm j reading the "
-                            "previous same-width norm's output, so every row keeps table order"),
+                            "previous same-width norm's output, so every row keeps table order; "
+                            "the *_us_per_step figures are host calls timed back to back, the "
+                            "graph_captured ones the same launches replayed from a graph "
+                            "(device time, no host in the loop)"),
         "graph_us_per_norm": gr["mean"] / len(widths),
         "eager_us_per_norm": e["mean"] / len(widths),
         "norms_per_s_graph": len(widths) / (gr["mean"] * 1e-6),
@@ -615,6 +777,35 @@ def profile_decode(rn, torch, np, wl):
                       "persistent_launches": 3}), flush=True)
 
 
+def profile_persistent(rn, torch, np, wl, arm, launches=200):
+    """A short run of one persistent arm of the decode step, so a kernel trace
+    has one row per arm: 'spread' (the step's independent rows over up to 256
+    workgroups), 'one' (the whole table in one workgroup), 'chained' (each norm
+    reading the previous same-width norm's output: every row in table order)."""
+    rows = wl.decode()
+    dev = torch.device("cuda", 0)
+    xs = [torch.from_numpy(x).to(dev) for x, _ in rows]
+    ws = [torch.from_numpy(w).to(dev) for _, w in rows]
+    ys = [torch.empty_like(t) for t in xs]
+    widths = [len(x) for x, _ in rows]
+    if arm == "chained":
+        last, cx = {}, []
+        for j, n in enumerate(widths):
+            cx.append(ys[last[n]] if n in last else xs[j])
+            last[n] = j
+        table, _ = rn.make_table(list(zip(cx, ws, ys)))
+    else:
+        table, _ = rn.make_table(list(zip(xs, ws, ys)))
+    rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 1 if arm == "one" else 0)
+    try:
+        for _ in range(launches):
+            rn.rmsnorm_sequence_persistent(table, len(widths), float(wl.EPS), rn.F32)
+        torch.cuda.synchronize()
+    finally:
+        rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 0)
+    print(json.dumps({"profile_persistent": arm, "launches": launches}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -629,6 +820,8 @@ def main():
                     help="short decode-step run for counter collection")
     ap.add_argument("--profile-wide", action="store_true",
                     help="a short run of the wide-row shapes for a kernel trace")
+    ap.add_argument("--profile-persistent", choices=["spread", "one", "chained"],
+                    help="200 launches of one persistent arm of the decode step (kernel trace)")
     ap.add_argument("--sections", default="prefill,single,batch64,decode",
                     help="comma list of prefill,single,batch64,decode,positioned,wide (for "
                          "profiling runs; the default runs the first four; wide: few very "
@@ -655,6 +848,9 @@ def main():
         return
     if args.profile_wide:
         profile_wide(rn, torch, np, wl)
+        return
+    if args.profile_persistent:
+        profile_persistent(rn, torch, np, wl, args.profile_persistent)
         return
 
     sections = set(args.sections.split(","))
@@ -689,11 +885,22 @@ def main():
     b64 = bench_batch64(rn, torch, np, wl)
     log(f"batch64 {b64['us_device']['mean']:.2f} us (graph-captured)")
     dec = bench_decode(rn, torch, np, wl, args.decode_steps)
+    gd = dec["persistent_graph_captured_us_per_step"]
+    log(f"persistent, graph-timed: spread {gd['spread']['mean']:.2f} us, one workgroup "
+        f"{gd['one_workgroup']['mean']:.1f} us, chained {gd['chained_table']['mean']:.1f} us; "
+        f"walk timeouts {dec['persistent_walk_timeouts']}")
     log(f"decode eager {dec['eager_us_per_step']['mean']:.1f} us  "
         f"graph {dec['graph_us_per_step']['mean']:.1f} us  "
         f"persistent {dec['persistent_us_per_step']['mean']:.1f} us (one workgroup "
         f"{dec['persistent_one_workgroup_us_per_step']['mean']:.1f}, chained table "
         f"{dec['persistent_chained_table_us_per_step']['mean']:.1f})")
+    floor = bench_dispatch_floor(rn, torch)
+    log(f"dispatch floor: torch fill {floor['torch_fill_1_element_us']['mean']:.2f} us, "
+        f"1-element norm {floor['rmsnorm_1_element_us']['mean']:.2f} us (graph-captured)")
+    nodes = bench_decode_nodes(rn, torch, np, wl)
+    pcheck = bench_persistent_check(rn, torch, np, wl, args.decode_steps)
+    log(f"persistent check: 327 tiny rows {pcheck['check_327_rows_us']['mean']:.2f} us, "
+        f"one row {pcheck['one_row_us']['mean']:.2f} us")
     decp = bench_decode_positioned(rn, torch, np, wl, args.decode_steps)
     log(f"decode positioned eager {decp['eager_us_per_step']['mean']:.1f} us  "
         f"graph {decp['graph_us_per_step']['mean']:.1f} us  "
@@ -750,7 +957,16 @@ def main():
         },
         "single_norm": single,
         "batch64": b64,
+        "dispatch_floor_us": round(floor["rmsnorm_1_element_us"]["mean"], 3),
+        "dispatch_floor": floor,
+        "single_norm_us_above_floor": round(single["us_per_norm_device"]["mean"]
+                                            - floor["rmsnorm_1_element_us"]["mean"], 3),
+        "batch64_us_above_floor": round(b64["us_device"]["mean"]
+                                        - floor["rmsnorm_1_element_us"]["mean"], 3),
         "decode_step": dec,
+        "decode_step_nodes": nodes,
+        "persistent_check": pcheck,
+        "geometry_audit": geometry_audit(single, b64, dec, nodes, pre, pre["plan"]),
         "decode_step_positioned": decp,
         "traffic_record": traffic_rec,
         "gpu_section_s": round(gpu_s, 1),

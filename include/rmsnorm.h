@@ -256,12 +256,19 @@ int rmsnorm_sequence_graph_update(rmsn_graph* g, const int64_t* h_widths, int32_
  * rmsnorm_sequence_eager's. Rows that share no memory with any other row
  * (their reads and output meet no other row's output, their output no other
  * row's reads) cannot observe the order and run in parallel over up to 255
- * more workgroups. The others keep table order in the first workgroup: each
- * is finished -- its stores ordered before the next row's loads by a
- * workgroup barrier -- before the next starts, so a table in which a later x
- * is an earlier y (y_i == x_j, i < j) computes exactly what the launch
- * sequence computes. Tables of more than 1024 rows, and
- * RMSN_OPT_PERSISTENT_WORKGROUPS = 1, keep every row in one workgroup.
+ * more workgroups. The others ("bound") keep table order in the first
+ * workgroup, so a table in which a later x is an earlier y (y_i == x_j,
+ * i < j) computes exactly what the launch sequence computes. When every bound
+ * row is a whole number of 16-byte vectors, 16-byte aligned and at most 8192
+ * elements, the four wavefronts of that workgroup take one bound row each and
+ * a row starts only once every earlier bound row it shares memory with has
+ * finished (its stores complete), found among the 64 bound rows before it;
+ * independent bound rows overlap. Otherwise each bound row is finished --
+ * its stores ordered before the next row's loads by a workgroup barrier --
+ * before the next starts. The waits are bounded (RMSN_OPT_WALK_SPIN_CAP); a
+ * wait that runs out is counted (rmsnorm_diag_walk_timeouts). Tables of more
+ * than 1024 rows, and RMSN_OPT_PERSISTENT_WORKGROUPS = 1, keep every row in
+ * one workgroup.
  * Widths come from the table (any n in [1, 2^24], any element alignment); no
  * host widths are needed. No row may write into the descriptor table itself.
  * pos: NULL, or the rows are taken at the position as in
@@ -416,10 +423,17 @@ int rmsnorm_workspace_query(int dtype, int64_t rows, int64_t n, int align, rmsn_
  *   RMSN_OPT_REPLICA_PARTS:   RMSN_PATH_REPLICA, 0 automatic (4), else 1..8
  *                            workgroups per row (capped at the row's
  *                            1024-element blocks)
+ *   RMSN_OPT_WALK_SPIN_CAP:   rmsnorm_sequence_persistent, 0 default (2^22),
+ *                            else 1..2^30: polls one wait of the ordered walk
+ *                            may take before it gives up ordering the rest of
+ *                            the launch and counts a timeout (see
+ *                            rmsnorm_diag_walk_timeouts). A wait can always
+ *                            end, so the default is never reached; a cap of
+ *                            1 forces timeouts, for testing that path.
  * Returns RMSN_EINVAL for an unknown key or value. Not synchronised with
  * launches on other threads. Environment: RMSN_PATH, RMSN_ROWS_PER_BLOCK,
  * RMSN_STREAMING, RMSN_SPLIT_LOADS, RMSN_APPLY_THREADS,
- * RMSN_PERSISTENT_WORKGROUPS, RMSN_REPLICA_PARTS. */
+ * RMSN_PERSISTENT_WORKGROUPS, RMSN_REPLICA_PARTS, RMSN_WALK_SPIN_CAP. */
 enum {
     RMSN_OPT_PATH = 1,
     RMSN_OPT_ROWS_PER_BLOCK = 2,
@@ -427,7 +441,8 @@ enum {
     RMSN_OPT_SPLIT_LOADS = 4,
     RMSN_OPT_APPLY_THREADS = 5,
     RMSN_OPT_PERSISTENT_WORKGROUPS = 6,
-    RMSN_OPT_REPLICA_PARTS = 7
+    RMSN_OPT_REPLICA_PARTS = 7,
+    RMSN_OPT_WALK_SPIN_CAP = 8
 };
 int rmsnorm_set_option(int key, int value);
 int rmsnorm_get_option(int key, int* value);
@@ -465,6 +480,17 @@ int rmsnorm_diag_inverse(uint32_t first_bits, int64_t count, int64_t n, float ep
  * binary32 pattern. RMSN_EINVAL if the range leaves 32 bits or out is null or
  * odd. */
 int rmsnorm_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out, void* stream);
+
+/* Waits of rmsnorm_sequence_persistent's ordered walk that ran out of polls
+ * (RMSN_OPT_WALK_SPIN_CAP) on the current device since the last reset: *out
+ * (host). A launch in which a wait timed out stops ordering its rows, so its
+ * outputs are not to be trusted; the count is the device-side error flag of
+ * that walk (Lecture 08 "Graph-resident decode", section 3: an error raised
+ * inside the step surfaces later, so it must be recorded where it happened).
+ * reset != 0 sets the counter to 0 after reading it. Synchronous (device to
+ * host copy): call it between launches, not inside a capture. RMSN_EINVAL for
+ * a null out. */
+int rmsnorm_diag_walk_timeouts(uint32_t* out, int reset);
 
 #ifdef __cplusplus
 }

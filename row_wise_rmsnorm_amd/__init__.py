@@ -34,6 +34,7 @@ PATH_REPLICA = 6
 OPT_PATH, OPT_ROWS_PER_BLOCK, OPT_STREAMING, OPT_SPLIT_LOADS, OPT_APPLY_THREADS = 1, 2, 3, 4, 5
 OPT_PERSISTENT_WORKGROUPS = 6
 OPT_REPLICA_PARTS = 7
+OPT_WALK_SPIN_CAP = 8
 MAX_N = 1 << 24
 DESC_BYTES = 32
 
@@ -81,6 +82,7 @@ def bind(path):
         "rmsnorm_batched_rows": [c_int, vp, i64, vp, vp, i64, i64, i64, f, vp],
         "rmsnorm_batched_rows_ws": [c_int, vp, i64, vp, vp, i64, i64, i64, f, vp, i64, vp],
         "rmsnorm_batched_rows_noalloc": [c_int, vp, i64, vp, vp, i64, i64, i64, f, vp],
+        "rmsnorm_diag_walk_timeouts": [ctypes.POINTER(u32), c_int],
         "rmsnorm_workspace_query": [c_int, i64, i64, c_int, ctypes.POINTER(_PlanInfo),
                                     ctypes.POINTER(i64)],
         "rmsnorm_sequence_eager": [c_int, vp, vp, i32, f, vp],
@@ -122,7 +124,7 @@ EXPORTED = ("rmsnorm_f32", "rmsnorm_bf16", "rmsnorm_batched_rows", "rmsnorm_sequ
             "rmsnorm_sequence_graph_create_positioned", "rmsnorm_sequence_graph_update",
             "rmsnorm_association_lanes", "rmsnorm_sequence_persistent",
             "rmsnorm_batched_rows_ws", "rmsnorm_workspace_query",
-            "rmsnorm_batched_rows_noalloc")
+            "rmsnorm_batched_rows_noalloc", "rmsnorm_diag_walk_timeouts")
 
 
 def lib():
@@ -500,6 +502,16 @@ def diag_bf16(first_bits, count, out, stream=None):
         _check(_lib.rmsnorm_diag_bf16(int(first_bits), int(count),
                                       ctypes.c_void_p(out.data_ptr()),
                                       _stream_ptr(stream, out.device)))
+
+
+def diag_walk_timeouts(reset=False, device=None):
+    """Ordered waits of the persistent launch that ran out of polls on the
+    device since the last reset (synchronous); reset=True clears the count."""
+    import torch
+    v = ctypes.c_uint32()
+    with _on(torch.cuda.current_device() if device is None else device):
+        _check(_lib.rmsnorm_diag_walk_timeouts(ctypes.byref(v), 1 if reset else 0))
+    return v.value
 
 
 def diag_inverse(first_bits, count, n, eps, r_out, inv_out, stream=None):

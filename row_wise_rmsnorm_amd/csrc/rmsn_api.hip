@@ -637,6 +637,16 @@ int rmsnorm_get_option(int key, int* value) {
     return get_option(key, value);
 }
 
+int rmsnorm_diag_walk_timeouts(uint32_t* out, int reset) {
+    clear_error();
+    if (!out) {
+        set_error("null output pointer");
+        return RMSN_EINVAL;
+    }
+    const hipError_t e = walk_timeouts(out, reset != 0);
+    return e == hipSuccess ? RMSN_OK : hip_fail("reading the walk timeout counter", e);
+}
+
 int rmsnorm_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out, void* stream) {
     clear_error();
     if (!out) {

@@ -336,11 +336,26 @@ struct SplitPart {
     }
 
     __device__ __forceinline__ void load(gptr_c x, gptr_c w, int s, int lane, uint32_t nvec) {
+        load_x(x, s, lane, nvec);
+        load_w(w, s, lane, nvec);
+    }
+    // The two halves of load(), for callers that issue w's loads earlier.
+    __device__ __forceinline__ void load_x(gptr_c x, int s, int lane, uint32_t nvec) {
         vi0 = (uint32_t)(s * U) * 64u + (uint32_t)lane;
         if (EXACT) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 xr[u] = gload16<NT>(scalar_gptr(x + base_bytes(s, u)) + lane_bytes(lane, u));
+        } else {
+            const uint32_t last = nvec - 1u;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                xr[u] = gload16<NT>(x + min(vi0 + 64u * (uint32_t)u, last) * 16u);
+        }
+    }
+    __device__ __forceinline__ void load_w(gptr_c w, int s, int lane, uint32_t nvec) {
+        const uint32_t v0 = (uint32_t)(s * U) * 64u + (uint32_t)lane;
+        if (EXACT) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 wr[u] = gload16<false>(scalar_gptr(w + base_bytes(s, u)) + lane_bytes(lane, u));
@@ -348,10 +363,7 @@ struct SplitPart {
             const uint32_t last = nvec - 1u;
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                xr[u] = gload16<NT>(x + min(vi0 + 64u * (uint32_t)u, last) * 16u);
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                wr[u] = gload16<false>(w + min(vi0 + 64u * (uint32_t)u, last) * 16u);
+                wr[u] = gload16<false>(w + min(v0 + 64u * (uint32_t)u, last) * 16u);
         }
     }
 
@@ -1173,6 +1185,14 @@ __device__ __forceinline__ RowSpan32 row_span32(const RowSpan& r, uintptr_t base
     return RowSpan32{x, x + l, w, w + l, y, y + l};
 }
 
+// Row a's w range meets row b's output.
+__device__ __forceinline__ bool w_meets_output(const RowSpan& a, const RowSpan& b) {
+    return (a.len != 0) & (b.len != 0) & (a.w < b.y + b.len) & (b.y < a.w + a.len);
+}
+__device__ __forceinline__ bool w_meets_output(const RowSpan32& a, const RowSpan32& b) {
+    return (a.w < b.ye) & (b.y < a.we);
+}
+
 __device__ __forceinline__ bool rows_meet(const RowSpan32& a, const RowSpan32& b) {
     return ((a.x < b.ye) & (b.y < a.xe)) | ((a.w < b.ye) & (b.y < a.we)) |
            ((a.y < b.ye) & (b.y < a.ye)) | ((b.x < a.ye) & (a.y < b.xe)) |
@@ -1321,6 +1341,137 @@ __device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t
     return (any & 1) ? kBoundUnknown : (any & 2) ? kBoundMarked : kNoneBound;
 }
 
+// --- Dependency walk: the bound rows in table order on four wavefronts,
+// each row waiting only for the rows it depends on. Rows are the walk list
+// lst[0..nb) (table indices). For each, dep is the latest earlier row of the
+// list it meets (rows_meet: either reads what the other writes, or both write
+// the same memory), found among the kDagWindow rows before it; if none of
+// those meets it, every row before the window counts as a dependency. dep_w is
+// the same for the earlier outputs that meet its w alone. Wavefront v takes
+// list entries v, v + 4, ... in order, and next[v] is the entry it is on (past
+// its last one when done): all entries up to d are complete exactly when every
+// other wavefront's next is past d. A row issues its w loads once dep_w is
+// complete, its x loads once dep is complete, then sums, applies and stores,
+// waits for its stores and moves next[v] on. The wavefront holding the lowest
+// pending entry always finds its dependencies complete, so the walk never
+// stalls; every wait is still bounded by `cap` polls, after which the walk
+// stops waiting (abort), counts the timeout in g_walk_timeouts and finishes
+// its rows unordered. Every row is a whole number of 16-byte vectors, at most
+// 8192 elements, 16-byte aligned (the round walk's one-wavefront rows).
+constexpr int kDagWindow = 64;
+constexpr uint32_t kDagSpinCap = 1u << 22;
+
+__device__ unsigned int g_walk_timeouts;
+
+// Wait until every list entry up to dep is complete (see above); false when
+// the wait ran out of polls (the walk then aborts its ordering).
+__device__ __forceinline__ bool dag_wait(const int* next, int* abort, int wave, int dep,
+                                         uint32_t cap) {
+    if (dep < 0) return true;
+    for (uint32_t spin = 0;; ++spin) {
+        const bool ok = __hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+        bool all = true;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            all &= (v == wave) |
+                   (__hip_atomic_load(next + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > dep);
+        if (__builtin_amdgcn_readfirstlane((int)(ok | all))) break;
+        if (spin >= cap) {
+            if ((threadIdx.x & 63) == 0) {
+                __hip_atomic_store(abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(&g_walk_timeouts, 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // the rows' stores before our loads
+    return true;
+}
+
+template <typename T, int U, bool EXACT>
+__device__ __forceinline__ void dag_row_slices(const T* x, const T* w, T* y, int n, float eps,
+                                               int lane, const int* next, int* abort, int wave,
+                                               int dep_w, int dep, uint32_t cap) {
+    const uint32_t nvec = (uint32_t)n * (uint32_t)sizeof(T) / 16u;
+    SplitPart<T, U, EXACT, false> part;
+    dag_wait(next, abort, wave, dep_w, cap);
+    part.load_w(scalar_gptr(reinterpret_cast<const char*>(w)), 0, lane, nvec);
+    dag_wait(next, abort, wave, dep, cap);
+    part.load_x(scalar_gptr(reinterpret_cast<const char*>(x)), 0, lane, nvec);
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    part.chains(p, nvec);
+    const float inv = inverse_rms(split_sumsq(p, lane, T()), n, eps);
+    part.apply(inv, scalar_gptr(reinterpret_cast<char*>(y)), 0, lane, nvec);
+}
+
+// One row of the dependency walk (the round walk's one-wavefront layout).
+template <typename T>
+__device__ __forceinline__ void dag_row(const T* x, const T* w, T* y, int n, float eps, int lane,
+                                        const int* next, int* abort, int wave, int dep_w,
+                                        int dep, uint32_t cap) {
+    const int bytes = n * (int)sizeof(T);
+    const int slices = (bytes + 1023) >> 10;
+#define RMSN_CASE(U)                                                                          \
+    if constexpr (U * 1024 <= 8192 * (int)sizeof(T)) {                                        \
+        if (slices <= U) {                                                                    \
+            if (bytes == U * 1024)                                                            \
+                dag_row_slices<T, U, true>(x, w, y, n, eps, lane, next, abort, wave, dep_w,   \
+                                           dep, cap);                                         \
+            else                                                                              \
+                dag_row_slices<T, U, false>(x, w, y, n, eps, lane, next, abort, wave, dep_w,  \
+                                            dep, cap);                                        \
+            return;                                                                           \
+        }                                                                                     \
+    }
+    RMSN_FOR_ROUND_SLICES(RMSN_CASE)
+#undef RMSN_CASE
+}
+
+template <typename T, bool POS, typename S>
+__device__ __forceinline__ void dag_walk(const S* span, const uint16_t* lst, int32_t nb,
+                                         const rmsn_desc* d, float eps, uint64_t pos,
+                                         const PosArgs& pa, uint32_t cap) {
+    __shared__ int16_t dep[kSpanRows], dep_w[kSpanRows];
+    __shared__ int next[4];
+    __shared__ int abort;
+    for (int32_t i = threadIdx.x; i < nb; i += blockDim.x) {
+        const S a = span[lst[i]];
+        const int32_t lo = max(0, i - kDagWindow);
+        int32_t da = -1, dw = -1;
+        for (int32_t k = i - 1; k >= lo; --k) {
+            const S b = span[lst[k]];
+            if (da < 0 && rows_meet(a, b)) da = k;
+            if (w_meets_output(a, b)) {
+                dw = k;  // meeting w is meeting: da is set too
+                break;
+            }
+        }
+        dep[i] = (int16_t)(da >= 0 ? da : lo - 1);
+        dep_w[i] = (int16_t)(dw >= 0 ? dw : lo - 1);
+    }
+    if (threadIdx.x < 4) next[threadIdx.x] = (int)threadIdx.x;
+    if (threadIdx.x == 0) abort = 0;
+    __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    for (int32_t i = wave; i < nb; i += 4) {
+        const rmsn_desc dd = d[lst[i]];
+        const T* x;
+        const T* w;
+        T* y;
+        persistent_ptrs<T, POS>(dd, pos, pa, x, w, y);
+        dag_row<T>(x, w, y, (int)dd.n, eps, lane, next, &abort, wave, dep_w[i], dep[i], cap);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // our stores before the mark
+        if (lane == 0)
+            __hip_atomic_store(next + wave, (int)(i + 4), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if (lane == 0)
+        __hip_atomic_store(next + wave, 0x7FFFFFFF, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // Which rows meet another row, on spans of type S in LDS (RowSpan or
 // RowSpan32). Workers (blockIdx > 0) test their row against every row, 256 at
 // a time, and run it when it meets none. In workgroup 0 (unless the ordered
@@ -1330,10 +1481,10 @@ __device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t
 // ("bound") rows run in table order, found 64 at a time by a ballot over the
 // marks. Returns as spread_rows does.
 template <typename T, bool POS, typename S>
-__device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, bool marked,
-                                          const rmsn_desc* d, int32_t count, float eps,
-                                          uint64_t pos, const PosArgs& pa, float* lds4,
-                                          int* fold4) {
+__device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const uint8_t* rvec,
+                                          bool marked, const rmsn_desc* d, int32_t count,
+                                          float eps, uint64_t pos, const PosArgs& pa, float* lds4,
+                                          int* fold4, uint32_t cap) {
     if (blockIdx.x != 0) {
         const int32_t workers = (int32_t)gridDim.x - 1;
         for (int32_t j = (int32_t)blockIdx.x - 1; j < count; j += workers) {
@@ -1357,6 +1508,28 @@ __device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, bool ma
         if (lane == 0) bound[j] = any;
     }
     __syncthreads();
+    // every bound row in the one-wavefront layout: the dependency walk
+    bool not_vec = false;
+    for (int32_t j = threadIdx.x; j < count; j += blockDim.x) not_vec |= bound[j] && !rvec[j];
+    if (!workgroup_any(not_vec, fold4)) {
+        __shared__ uint16_t lst[kSpanRows];
+        __shared__ int32_t nb_shared;
+        if (wave == 0) {
+            // the bound rows in table order, 64 at a time by a ballot
+            int32_t nb = 0;
+            for (int32_t j0 = 0; j0 < count; j0 += 64) {
+                const bool b = j0 + lane < count && bound[j0 + lane] != 0;
+                const unsigned long long marks = __ballot(b);
+                if (b) lst[nb + __builtin_popcountll(marks & ((1ull << lane) - 1ull))] =
+                    (uint16_t)(j0 + lane);
+                nb += __builtin_popcountll(marks);
+            }
+            if (lane == 0) nb_shared = nb;
+        }
+        __syncthreads();
+        dag_walk<T, POS, S>(span, lst, nb_shared, d, eps, pos, pa, cap);
+        return true;
+    }
     bool some_free = false;
     for (int32_t j = threadIdx.x; j < count; j += blockDim.x) some_free = some_free || !bound[j];
     if (!workgroup_any(some_free, fold4)) return false;
@@ -1380,9 +1553,10 @@ __device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, bool ma
 template <typename T, bool POS>
 __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, float eps,
                                             uint64_t pos, const PosArgs& pa, float* lds4,
-                                            int* fold4) {
+                                            int* fold4, uint32_t cap) {
     __shared__ RowSpan span[kSpanRows];   // 64-bit spans, or RowSpan32 in the same bytes
     __shared__ uint8_t bound[kSpanRows];
+    __shared__ uint8_t rvec[kSpanRows];   // the row fits the one-wavefront layout
     __shared__ unsigned long long lo_hi[2];
     if (threadIdx.x == 0) {
         lo_hi[0] = ~0ull;
@@ -1425,20 +1599,24 @@ __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, f
     for (int r = 0; r < R; ++r) {
         const int32_t j = threadIdx.x + 256 * r;
         if (j >= count) continue;
-        if (narrow) span32[j] = row_span32(mine[r], base);
-        else span[j] = mine[r];
+        const RowSpan& m = mine[r];
+        rvec[j] = m.len != 0 && m.len % 16 == 0 && m.len <= 8192 * sizeof(T) &&
+                  ((m.x | m.w | m.y) & 15) == 0;
+        if (narrow) span32[j] = row_span32(m, base);
+        else span[j] = m;
     }
     __syncthreads();
     const bool marked = found == kBoundMarked;
-    return narrow ? spread_on<T, POS>(span32, bound, marked, d, count, eps, pos, pa, lds4, fold4)
-                  : spread_on<T, POS>(static_cast<const RowSpan*>(span), bound, marked, d, count,
-                                      eps, pos, pa, lds4, fold4);
+    return narrow ? spread_on<T, POS>(span32, bound, rvec, marked, d, count, eps, pos, pa, lds4,
+                                      fold4, cap)
+                  : spread_on<T, POS>(static_cast<const RowSpan*>(span), bound, rvec, marked, d,
+                                      count, eps, pos, pa, lds4, fold4, cap);
 }
 
 template <typename T, bool POS>
 __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __restrict__ d,
                                                              int32_t count, float eps,
-                                                             PosArgs pa) {
+                                                             PosArgs pa, uint32_t cap) {
     __shared__ float lds4[4];
     __shared__ float lds8[2][4];
     __shared__ int lds_fold[4];
@@ -1450,7 +1628,7 @@ __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __
     }
     // the launcher gives more than one workgroup only to tables of at most
     // kSpanRows rows
-    if (gridDim.x > 1 && spread_rows<T, POS>(d, count, eps, pos, pa, lds4, lds_fold)) return;
+    if (gridDim.x > 1 && spread_rows<T, POS>(d, count, eps, pos, pa, lds4, lds_fold, cap)) return;
     switch (walk_mode<T, POS>(d, count, pos, pa, lds_fold)) {
         case kRoundWalk16: round_walk<T, POS, 4>(d, count, eps, pos, pa); break;
         case kRoundWalk4: round_walk<T, POS, 1>(d, count, eps, pos, pa); break;
@@ -1711,26 +1889,37 @@ hipError_t launch_sequence_persistent(int dtype, const rmsn_desc* d, int32_t cou
     // workgroup 0 plus one worker per row (at most kSpreadWorkers) for free rows
     const bool spread = count > 1 && count <= kSpanRows && option_persistent_workgroups() == 0;
     const dim3 grid(spread ? 1u + (unsigned)std::min(count, kSpreadWorkers) : 1u), block(kBlockThreads);
+    const int opt_cap = option_walk_spin_cap();
+    const uint32_t cap = opt_cap > 0 ? (uint32_t)opt_cap : kDagSpinCap;
     if (dtype == RMSN_F32) {
         if (pos)
             hipLaunchKernelGGL((k_sequence_persistent<float, true>), grid, block, 0, stream, d,
-                               count, eps, *pos);
+                               count, eps, *pos, cap);
         else
             hipLaunchKernelGGL((k_sequence_persistent<float, false>), grid, block, 0, stream, d,
-                               count, eps, none);
+                               count, eps, none, cap);
     } else {
         if (pos)
             hipLaunchKernelGGL((k_sequence_persistent<uint16_t, true>), grid, block, 0, stream, d,
-                               count, eps, *pos);
+                               count, eps, *pos, cap);
         else
             hipLaunchKernelGGL((k_sequence_persistent<uint16_t, false>), grid, block, 0, stream,
-                               d, count, eps, none);
+                               d, count, eps, none, cap);
     }
     const hipError_t e = hipGetLastError();
     // the rows of every workgroup are taken at the position read when the
     // kernel starts; it is advanced after all of them, by the next launch
     if (e != hipSuccess || !spread || pos == nullptr) return e;
     return launch_advance(const_cast<int64_t*>(pos->d_pos), pos->period, stream);
+}
+
+hipError_t walk_timeouts(uint32_t* out, bool reset) {
+    hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_walk_timeouts), sizeof(uint32_t), 0,
+                                       hipMemcpyDeviceToHost);
+    if (e != hipSuccess || !reset) return e;
+    const uint32_t zero = 0;
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_walk_timeouts), &zero, sizeof zero, 0,
+                             hipMemcpyHostToDevice);
 }
 
 hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,

@@ -48,6 +48,10 @@ hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosAr
 hipError_t launch_sequence_persistent(int dtype, const rmsn_desc* d, int32_t count, float eps,
                                      const PosArgs* pos, hipStream_t stream);
 
+// Timeouts of the persistent launch's ordered waits since the last reset
+// (the library's device counter; synchronous copies), and reset it if asked.
+hipError_t walk_timeouts(uint32_t* out, bool reset);
+
 // *d_pos = (*d_pos mod period + 1) mod period on the device (the state
 // update of a positioned sequence).
 hipError_t launch_advance(int64_t* d_pos, int64_t period, hipStream_t stream);

@@ -23,6 +23,7 @@ std::atomic<int> g_split{-2};
 std::atomic<int> g_apply{-2};
 std::atomic<int> g_pwg{-2};
 std::atomic<int> g_parts{-2};
+std::atomic<int> g_spin{-1};
 
 int env_int(const char* name, int dflt) {
     const char* s = std::getenv(name);
@@ -44,6 +45,7 @@ bool valid_rpb(int v) { return v == 0 || v == 4 || v == 8; }
 bool valid_streaming(int v) { return v == -1 || v == 0 || v == 1; }
 bool valid_persistent_wg(int v) { return v == 0 || v == 1; }
 bool valid_parts(int v) { return v >= 0 && v <= 8; }
+bool valid_spin_cap(int v) { return v >= 0 && v <= (1 << 30); }
 
 // Byte ranges [a, a+la) and [b, b+lb) intersect.
 bool overlaps(uintptr_t a, uint64_t la, uintptr_t b, uint64_t lb) {
@@ -132,6 +134,16 @@ int option_replica_parts() {
     return v;
 }
 
+int option_walk_spin_cap() {
+    int v = g_spin.load(std::memory_order_relaxed);
+    if (v == -1) {
+        v = env_int("RMSN_WALK_SPIN_CAP", 0);
+        if (!valid_spin_cap(v)) v = 0;
+        g_spin.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 int set_option(int key, int value) {
     if (key == RMSN_OPT_PATH) {
         if (!valid_path(value)) {
@@ -197,6 +209,15 @@ int set_option(int key, int value) {
         g_parts.store(value, std::memory_order_relaxed);
         return RMSN_OK;
     }
+    if (key == RMSN_OPT_WALK_SPIN_CAP) {
+        if (!valid_spin_cap(value)) {
+            set_error("rmsnorm_set_option: walk spin cap must be 0 (default) or 1..2^30, got %d",
+                      value);
+            return RMSN_EINVAL;
+        }
+        g_spin.store(value, std::memory_order_relaxed);
+        return RMSN_OK;
+    }
     set_error("rmsnorm_set_option: unknown key %d", key);
     return RMSN_EINVAL;
 }
@@ -216,6 +237,7 @@ int get_option(int key, int* value) {
     }
     if (key == RMSN_OPT_PERSISTENT_WORKGROUPS) { *value = option_persistent_workgroups(); return RMSN_OK; }
     if (key == RMSN_OPT_REPLICA_PARTS) { *value = option_replica_parts(); return RMSN_OK; }
+    if (key == RMSN_OPT_WALK_SPIN_CAP) { *value = option_walk_spin_cap(); return RMSN_OK; }
     set_error("rmsnorm_get_option: unknown key %d", key);
     return RMSN_EINVAL;
 }

@@ -124,6 +124,7 @@ int option_split_loads();     // 0 automatic, else 1, 2, 4 or 8
 int option_apply_threads();   // 128-lane build: 0 (= 1024) or 128, 256, 512, 1024
 int option_persistent_workgroups();  // 0 automatic, 1 one workgroup
 int option_replica_parts();   // 0 automatic, else 1..8 workgroups per row
+int option_walk_spin_cap();   // 0 default, else polls per ordered wait (>= 1)
 int set_option(int key, int value);
 int get_option(int key, int* value);
 

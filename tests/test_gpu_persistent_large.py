@@ -15,7 +15,10 @@ both ends of one allocation of more than 4 GB, so the ranges are compared as
 
 Every buffer is compared whole after the persistent launch (free rows spread
 over workgroups, then the whole table in one workgroup) and after the eager
-launch sequence.
+launch sequence. The decode step's widths chained (each norm reading the
+previous same-width norm's output, every row bound) run through the first
+workgroup's dependency walk, replayed three times; forcing its ordered waits
+to time out (a spin cap of one poll) must end the launch and be counted.
 """
 import numpy as np
 import pytest
@@ -272,3 +275,76 @@ def test_rows_more_than_4gb_apart(rn, kind):
                                 f"{int(np.argmin(same))} of {len(same)}")
     del big
     torch.cuda.empty_cache()
+
+
+def _chained_decode(kind):
+    """The decode step's widths, each norm reading the previous norm of its
+    width's output (every row bound to table order): three chains, of 7168,
+    1536 and 512 wide rows, interleaved as in the step."""
+    widths = wl.decode_widths()
+    t = Table()
+    last = {}
+    for n in widths:
+        x = t.rows[last[n]][2] if n in last else t.fresh(n)
+        t.add(x, t.fresh(n), t.fresh(n))
+        last[n] = len(t.rows) - 1
+    return t
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_chained_decode_table(rn, kind):
+    """Every row bound, chains at distances 1 to 8: the first workgroup's
+    dependency walk (all rows whole 16-byte vectors) against the rows applied
+    in order; no ordered wait may time out."""
+    t = _chained_decode(kind)
+    say(f"persistent chained decode table {kind}: {len(t.rows)} rows")
+    host = _host_buffers(t, kind, 6_000_000)
+    want = _in_order(t, host, kind)
+    todev, tohost, bits = _codec(kind)
+    dtype = rn.BF16 if kind == "bf16" else rn.F32
+    rn.diag_walk_timeouts(reset=True)
+    for arm in ARMS[:2]:
+        bufs = [todev(h) for h in host]
+        table, widths = rn.make_table([(bufs[xb][xo:xo + n], bufs[wb][wo:wo + n],
+                                        bufs[yb][yo:yo + n])
+                                       for (xb, xo, n), (wb, wo, _), (yb, yo, _) in t.rows])
+        for rep in range(3):                       # replays on the same buffers: results move on
+            _launch(rn, arm, table, widths, len(t.rows), dtype)
+            exp = want if rep == 0 else _in_order(t, [tohost(b) for b in prev], kind)
+            for b, buf in enumerate(bufs):
+                same = tohost(buf).view(bits) == exp[b].view(bits)
+                assert same.all(), (f"{arm} replay {rep}: chained {kind} buffer {b}: first "
+                                    f"difference at {int(np.argmin(same))} of {len(same)}")
+            prev = [b.clone() for b in bufs]
+    assert rn.diag_walk_timeouts() == 0
+
+
+def test_walk_timeout_is_counted(rn):
+    """A spin cap of one poll makes the ordered waits of a chained table time
+    out: the launch still ends, and the device counter reports it (the rows'
+    outputs are then not ordered and are not checked). With the default cap
+    the same table is exact again and nothing is counted."""
+    t = _chained_decode("f32")
+    host = _host_buffers(t, "f32", 6_100_000)
+    todev, tohost, bits = _codec("f32")
+    bufs = [todev(h) for h in host]
+    table, widths = rn.make_table([(bufs[xb][xo:xo + n], bufs[wb][wo:wo + n], bufs[yb][yo:yo + n])
+                                   for (xb, xo, n), (wb, wo, _), (yb, yo, _) in t.rows])
+    rn.diag_walk_timeouts(reset=True)
+    rn.set_option(rn.OPT_WALK_SPIN_CAP, 1)
+    try:
+        assert rn.get_option(rn.OPT_WALK_SPIN_CAP) == 1
+        for _ in range(3):
+            _launch(rn, "persistent", table, widths, len(t.rows), rn.F32)
+    finally:
+        rn.set_option(rn.OPT_WALK_SPIN_CAP, 0)
+    assert rn.diag_walk_timeouts(reset=True) > 0
+    assert rn.diag_walk_timeouts() == 0
+    bufs = [todev(h) for h in host]
+    table, widths = rn.make_table([(bufs[xb][xo:xo + n], bufs[wb][wo:wo + n], bufs[yb][yo:yo + n])
+                                   for (xb, xo, n), (wb, wo, _), (yb, yo, _) in t.rows])
+    _launch(rn, "persistent", table, widths, len(t.rows), rn.F32)
+    want = _in_order(t, host, "f32")
+    for b, buf in enumerate(bufs):
+        assert (tohost(buf).view(bits) == want[b].view(bits)).all(), b
+    assert rn.diag_walk_timeouts() == 0
