@@ -18,8 +18,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "librmsnorm_amd.so")
 LIB128 = os.path.join(HERE, "librmsnorm_amd_l128.so")
 SOURCES = [os.path.join(HERE, "csrc", f) for f in
-           ("rmsn_kernels.hip", "rmsn_wide.hip", "rmsn_aux.hip", "rmsn_api.hip",
-            "rmsn_plan.cpp")]
+           ("rmsn_kernels.hip", "rmsn_persistent.hip", "rmsn_wide.hip", "rmsn_aux.hip",
+            "rmsn_api.hip", "rmsn_plan.cpp")]
 SOURCES128 = [os.path.join(HERE, "csrc", f) for f in
               ("rmsn_kernels_l128.hip", "rmsn_aux.hip", "rmsn_api.hip", "rmsn_plan.cpp")]
 ARCH = os.environ.get("RMSN_OFFLOAD_ARCH", "gfx950")

@@ -43,8 +43,9 @@
 //          wavefront runs the group trees. Every wavefront issues all of its
 //          loads at once, so the whole row is in flight from the start.
 // Descriptor kernels run one row read from a device table (BLOCK or GROUP
-// layout, optionally at a device-resident position); the persistent kernel
-// walks a whole table in one workgroup, row after row.
+// layout, optionally at a device-resident position). The layouts' device code
+// is in rmsn_rows.h; the persistent launch, which walks a whole table in one
+// kernel, is in rmsn_persistent.hip.
 //
 // Floating point: contraction is off for this file; the one fused operation
 // of the association is written as fmaf. '/' and sqrtf are the correctly
@@ -53,509 +54,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <algorithm>
-
 #include "rmsn_common.h"
 #include "rmsn_group.h"
 #include "rmsn_launch.h"
+#include "rmsn_rows.h"
 
 #pragma clang fp contract(off)
 
 namespace rmsn {
 namespace {
-
-// ---------------------------------------------------------------------------
-// WAVE layout: one wavefront per row, lane t holds chains 4t..4t+3.
-
-// Group trees and combine for the WAVE layout. On entry lane t's p[e] is the
-// finished chain of association lane 4t+e; group g = lanes 16g..16g+15, where
-// association lane 64g+j sits in wavefront lane 16g + j/4, register j%4.
-__device__ __forceinline__ float wave_sumsq(float p0, float p1, float p2, float p3) {
-    // halving s = 32, 16, 8, 4: partner j+s is s/4 wavefront lanes further
-    p0 += row_shl<8>(p0); p1 += row_shl<8>(p1); p2 += row_shl<8>(p2); p3 += row_shl<8>(p3);
-    p0 += row_shl<4>(p0); p1 += row_shl<4>(p1); p2 += row_shl<4>(p2); p3 += row_shl<4>(p3);
-    p0 += row_shl<2>(p0); p1 += row_shl<2>(p1); p2 += row_shl<2>(p2); p3 += row_shl<2>(p3);
-    p0 += row_shl<1>(p0); p1 += row_shl<1>(p1); p2 += row_shl<1>(p2); p3 += row_shl<1>(p3);
-    // halving s = 2 and 1 inside the lane
-    const float g = (p0 + p2) + (p1 + p3);
-    // group totals sit in lanes 0, 16, 32, 48
-    const float g0 = lane_value(g, 0), g1 = lane_value(g, 16);
-    const float g2 = lane_value(g, 32), g3 = lane_value(g, 48);
-    return (g0 + g2) + (g1 + g3);
-}
-
-// Chunks a kernel instance may assume complete: the plan picks the smallest
-// bucket holding the row, so a row using bucket NCH has more than
-// 256 * (previous bucket) elements.
-constexpr int prev_bucket(int nch) {
-    return nch <= 1 ? 0 : nch <= 2 ? 1 : nch <= 4 ? 2 : nch <= 6 ? 4 : nch <= 8 ? 6
-         : nch <= 12 ? 8 : nch <= 16 ? 12 : nch <= 20 ? 16 : nch <= 24 ? 20 : nch <= 28 ? 24 : 28;
-}
-
-// Resident wavefronts per SIMD the WAVE kernels are compiled for: the row's
-// registers (4 values per chunk; bf16 packed two per VGPR), the ragged-tail
-// chunk unless the width is exactly 256 * NCH, and a few for chains,
-// addresses and temporaries, out of 512 VGPRs per SIMD lane.
-template <typename T, int NCH, bool EXACT>
-constexpr int wave_occupancy() {
-    constexpr int q = sizeof(T) == 4 ? 4 : 2;
-    constexpr int regs = NCH * q + (EXACT ? 0 : q) + 16 + (sizeof(T) == 4 ? 8 : 0);
-    constexpr int w = 512 / ((regs + 7) / 8 * 8);
-    return w > 8 ? 8 : (w < 1 ? 1 : w);
-}
-
-// One row held by one wavefront: load() issues every load of the row, finish()
-// reduces, normalises and stores it. NT: non-temporal (streaming) hints on the
-// row's loads and stores, for batches too large for the caches to help.
-// Requires 256 * prev_bucket(NCH) < n <= 256 * NCH, and n == 256 * NCH when
-// EXACT (both guaranteed by the plan).
-template <typename T, int NCH, bool EXACT, bool NT>
-struct WaveRow {
-    using Q = Quad<T>;
-    static constexpr int MINF = EXACT ? NCH : prev_bucket(NCH);
-    // Addresses are a scalar base per 4 KB of the row (the reach of the
-    // instruction's immediate offset) plus an unsigned per-lane byte offset, so
-    // every load and store uses the scalar-base addressing mode instead of a
-    // 64-bit address pair per lane.
-    static constexpr uint32_t chunk_bytes = 256u * sizeof(T);
-    static constexpr int per_base = 4096 / chunk_bytes;
-
-    typename Q::raw xr[NCH];
-    typename Q::raw xt;
-
-    // Chunks [0, full) are complete; chunk `full` is the ragged tail when n is
-    // not a multiple of 256. `full` is wave-uniform, so the tests are scalar
-    // branches; chunks below MINF need none (none at all when EXACT).
-    static __device__ __forceinline__ int full_chunks(int n) { return EXACT ? NCH : (n >> 8); }
-
-    __device__ __forceinline__ void load(const T* x, int n, int lane) {
-        const int full = full_chunks(n);
-        const uint32_t lane_bytes = (uint32_t)lane * (uint32_t)(4 * sizeof(T));
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            if (k < MINF || k < full) {
-                gptr_c base =
-                    scalar_gptr(reinterpret_cast<const char*>(x) + (k / per_base) * 4096);
-                xr[k] = Q::template gload<NT>(base + lane_bytes +
-                                              (uint32_t)(k % per_base) * chunk_bytes);
-            }
-        }
-        xt = Q::zero();
-        if (!EXACT && (n & 255)) xt = Q::load_tail(x, (full << 8) + (lane << 2), n);
-    }
-
-    // wl: the weight row staged in LDS as quads (quad q = elements 4q..4q+3);
-    // w: the same row in global memory, read only for the ragged tail.
-    __device__ __forceinline__ void finish(const T* __restrict__ w,
-                                           const typename Q::raw* wl, T* y, int n, float eps,
-                                           int lane) {
-        const int full = full_chunks(n);
-        const uint32_t lane_bytes = (uint32_t)lane * (uint32_t)(4 * sizeof(T));
-        // Lane chains in ascending chunk order; the tail chunk comes last and
-        // reads +0 past the row (fmaf(0, 0, p) == p for p >= +0). The per-chunk
-        // scheduling barriers keep each chunk's widening next to its four fmas,
-        // so widened copies of later chunks are never live with the packed row.
-        __builtin_amdgcn_sched_barrier(0);
-        float p0 = 0.0f, p1 = 0.0f, p2 = 0.0f, p3 = 0.0f;
-#pragma unroll
-        for (int k = 0; k < NCH; ++k) {
-            if (k < MINF || k < full) {
-                float v[4];
-                Q::unpack(xr[k], v);
-                p0 = fmaf(v[0], v[0], p0);
-                p1 = fmaf(v[1], v[1], p1);
-                p2 = fmaf(v[2], v[2], p2);
-                p3 = fmaf(v[3], v[3], p3);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (!EXACT) {
-            float v[4];
-            Q::unpack(xt, v);
-            p0 = fmaf(v[0], v[0], p0);
-            p1 = fmaf(v[1], v[1], p1);
-            p2 = fmaf(v[2], v[2], p2);
-            p3 = fmaf(v[3], v[3], p3);
-        }
-        const float inv = inverse_rms(wave_sumsq(p0, p1, p2, p3), n, eps);
-#pragma unroll
-        for (int k = 0; k < NCH; ++k)
-            if (k < MINF || k < full) opaque(xr[k]);
-        // Apply two chunks at a time. The scheduling barrier stops the compiler
-        // from hoisting every LDS weight read to the top (LDS cannot alias the
-        // global stores), which would hold the whole weight row in registers.
-#pragma unroll
-        for (int k0 = 0; k0 < NCH; k0 += 2) {
-#pragma unroll
-            for (int k = k0; k < k0 + 2 && k < NCH; ++k) {
-                if (k < MINF || k < full) {
-                    float v[4], wv[4], o[4];
-                    Q::unpack(xr[k], v);
-                    Q::unpack(wl[(k << 6) + lane], wv);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = (v[i] * inv) * wv[i];
-                    gptr base = scalar_gptr(reinterpret_cast<char*>(y) + (k / per_base) * 4096);
-                    Q::template gstore<NT>(base + lane_bytes +
-                                               (uint32_t)(k % per_base) * chunk_bytes, o);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (!EXACT && (n & 255)) {
-            const int et = (full << 8) + (lane << 2);
-            float v[4];
-            Q::unpack(xt, v);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (et + i < n) put(y + et + i, (v[i] * inv) * widen(w[et + i]));
-        }
-    }
-};
-
-// ---------------------------------------------------------------------------
-// SPLIT layout: a row is a sequence of 1 KB slices; lane t of a wavefront
-// loads bytes 16t..16t+15 of a slice. A binary32 slice is one 256-element
-// chunk and lane t's four values are the chains 4t..4t+3, as on the WAVE
-// path. A bf16 slice is two chunks: lane t < 32 loads elements 8t..8t+7 of
-// the first, lane t + 32 the same elements of the second. One 32-lane swap
-// per register pair regroups them so that every lane holds the same four
-// chains of both chunks: lane t < 32 chains 8t..8t+3, lane t + 32 chains
-// 8t+4..8t+7.
-
-template <bool NT>
-__device__ __forceinline__ u32x4 gload16(gptr_c p) {
-    auto* a = reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(p);
-    return NT ? __builtin_nontemporal_load(a) : *a;
-}
-template <bool NT>
-__device__ __forceinline__ void gstore16(gptr p, u32x4 v) {
-    auto* a = reinterpret_cast<__attribute__((address_space(1))) u32x4*>(p);
-    if (NT) __builtin_nontemporal_store(v, a);
-    else *a = v;
-}
-
-
-__device__ __forceinline__ void chain4(float p[4], float v0, float v1, float v2, float v3) {
-    p[0] = fmaf(v0, v0, p[0]);
-    p[1] = fmaf(v1, v1, p[1]);
-    p[2] = fmaf(v2, v2, p[2]);
-    p[3] = fmaf(v3, v3, p[3]);
-}
-
-// One slice into the lane chains, chunks in ascending order.
-__device__ __forceinline__ void slice_chains(float p[4], u32x4 v, float) {
-    chain4(p, __uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-           __uint_as_float(v.w));
-}
-__device__ __forceinline__ void slice_chains(float p[4], u32x4 v, uint16_t) {
-    // first chunk: dwords x, y of the lower half-wave; second chunk: the same
-    // dwords of the upper half-wave (see swap32)
-    const SwapPair a = swap32(v.x, v.z);
-    const SwapPair b = swap32(v.y, v.w);
-    chain4(p, lo_bf16(a.first), hi_bf16(a.first), lo_bf16(b.first), hi_bf16(b.first));
-    chain4(p, lo_bf16(a.second), hi_bf16(a.second), lo_bf16(b.second), hi_bf16(b.second));
-}
-
-// Group trees and combine for the SPLIT layout.
-__device__ __forceinline__ float split_sumsq(const float p[4], int, float) {
-    return wave_sumsq(p[0], p[1], p[2], p[3]);  // binary32: the WAVE layout
-}
-// bf16: group g is lanes 8g..8g+7 and 8g+32..8g+39; association lane 64g+j
-// sits in lane 8g + (j/8) + 32*((j/4)&1), register j%4.
-__device__ __forceinline__ float split_sumsq(const float p[4], int lane, uint16_t) {
-    float q[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        // halving s = 32, 16, 8: partner j+s is s/8 lanes further
-        q[e] = p[e] + row_shl<4>(p[e]);
-        q[e] = q[e] + row_shl<2>(q[e]);
-        q[e] = q[e] + row_shl<1>(q[e]);
-    }
-    // j = e sits in lane 8g, j = 4+e in lane 8g+32. Halving s = 4 pairs the
-    // two: the lower lane adds registers 0 and 2, the upper lane 1 and 3.
-    const SwapPair s01 = swap32(__float_as_uint(q[0]), __float_as_uint(q[1]));
-    const SwapPair s23 = swap32(__float_as_uint(q[2]), __float_as_uint(q[3]));
-    const bool low = lane < 32;
-    const float a0 = low ? q[0] : __uint_as_float(s01.first);   // j = e (e = 0 or 1)
-    const float a4 = low ? __uint_as_float(s01.second) : q[1];  // j = e + 4
-    const float c0 = low ? q[2] : __uint_as_float(s23.first);   // j = e + 2
-    const float c4 = low ? __uint_as_float(s23.second) : q[3];  // j = e + 6
-    // s = 2 in the lane; s = 1 between lane 8g (e = 0) and lane 8g+32 (e = 1)
-    const float t = (a0 + a4) + (c0 + c4);
-    const float g0 = lane_value(t, 0) + lane_value(t, 32);
-    const float g1 = lane_value(t, 8) + lane_value(t, 40);
-    const float g2 = lane_value(t, 16) + lane_value(t, 48);
-    const float g3 = lane_value(t, 24) + lane_value(t, 56);
-    return (g0 + g2) + (g1 + g3);
-}
-
-// y = (x * inv) * w for one slice, packed back into 16 bytes.
-__device__ __forceinline__ u32x4 slice_apply(u32x4 x, u32x4 w, float inv, float) {
-    u32x4 o;
-    o.x = __float_as_uint((__uint_as_float(x.x) * inv) * __uint_as_float(w.x));
-    o.y = __float_as_uint((__uint_as_float(x.y) * inv) * __uint_as_float(w.y));
-    o.z = __float_as_uint((__uint_as_float(x.z) * inv) * __uint_as_float(w.z));
-    o.w = __float_as_uint((__uint_as_float(x.w) * inv) * __uint_as_float(w.w));
-    return o;
-}
-__device__ __forceinline__ uint32_t apply_pair(uint32_t x, uint32_t w, float inv) {
-    const float lo = (lo_bf16(x) * inv) * lo_bf16(w);
-    const float hi = (hi_bf16(x) * inv) * hi_bf16(w);
-    return bf16_pair(lo, hi);
-}
-__device__ __forceinline__ u32x4 slice_apply(u32x4 x, u32x4 w, float inv, uint16_t) {
-    u32x4 o;
-    o.x = apply_pair(x.x, w.x, inv);
-    o.y = apply_pair(x.y, w.y, inv);
-    o.z = apply_pair(x.z, w.z, inv);
-    o.w = apply_pair(x.w, w.w, inv);
-    return o;
-}
-
-// The U slices wavefront s of a row owns: slices s*U .. s*U+U-1. nvec is the
-// row's length in 16-byte vectors (the plan makes n * sizeof(T) a multiple of
-// 16); vector v*64 + lane of the row is this lane's part of slice v. EXACT:
-// every slice of every wavefront is complete (nvec == 64 * U * wavefronts).
-// Otherwise vectors past the row are loaded from the row's last vector (an
-// in-row address, so no load needs a branch), count as +0 in the chains and
-// are not stored.
-template <typename T, int U, bool EXACT, bool NT>
-struct SplitPart {
-    u32x4 xr[U], wr[U];
-    uint32_t vi0;  // this lane's vector index in its first slice
-
-    // A scalar base per 4 slices keeps each load's offset in the immediate field.
-    static __device__ __forceinline__ uint32_t base_bytes(int s, int u) {
-        return (uint32_t)(s * U + (u & ~3)) * 1024u;
-    }
-    static __device__ __forceinline__ uint32_t lane_bytes(int lane, int u) {
-        return (uint32_t)lane * 16u + (uint32_t)(u & 3) * 1024u;
-    }
-    __device__ __forceinline__ bool in_row(int u, uint32_t nvec) const {
-        return EXACT || vi0 + 64u * (uint32_t)u < nvec;
-    }
-
-    __device__ __forceinline__ void load(gptr_c x, gptr_c w, int s, int lane, uint32_t nvec) {
-        load_x(x, s, lane, nvec);
-        load_w(w, s, lane, nvec);
-    }
-    // The two halves of load(), for callers that issue w's loads earlier.
-    __device__ __forceinline__ void load_x(gptr_c x, int s, int lane, uint32_t nvec) {
-        vi0 = (uint32_t)(s * U) * 64u + (uint32_t)lane;
-        if (EXACT) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                xr[u] = gload16<NT>(scalar_gptr(x + base_bytes(s, u)) + lane_bytes(lane, u));
-        } else {
-            const uint32_t last = nvec - 1u;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                xr[u] = gload16<NT>(x + min(vi0 + 64u * (uint32_t)u, last) * 16u);
-        }
-    }
-    __device__ __forceinline__ void load_w(gptr_c w, int s, int lane, uint32_t nvec) {
-        const uint32_t v0 = (uint32_t)(s * U) * 64u + (uint32_t)lane;
-        if (EXACT) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                wr[u] = gload16<false>(scalar_gptr(w + base_bytes(s, u)) + lane_bytes(lane, u));
-        } else {
-            const uint32_t last = nvec - 1u;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                wr[u] = gload16<false>(w + min(v0 + 64u * (uint32_t)u, last) * 16u);
-        }
-    }
-
-    __device__ __forceinline__ void chains(float p[4], uint32_t nvec) const {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const u32x4 v = in_row(u, nvec) ? xr[u] : u32x4{0u, 0u, 0u, 0u};
-            slice_chains(p, v, T());
-        }
-    }
-
-    __device__ __forceinline__ void apply(float inv, gptr y, int s, int lane, uint32_t nvec) const {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const u32x4 o = slice_apply(xr[u], wr[u], inv, T());
-            if (EXACT)
-                gstore16<NT>(scalar_gptr(y + base_bytes(s, u)) + lane_bytes(lane, u), o);
-            else if (in_row(u, nvec))
-                gstore16<NT>(y + (vi0 + 64u * (uint32_t)u) * 16u, o);
-        }
-    }
-};
-
-// ---------------------------------------------------------------------------
-// GROUP layout: 256 threads per row; wavefront g owns association group g.
-// Instances: Q = 1..8 blocks of 1024 elements (rows up to 8192).
-#define RMSN_FOR_GROUP_BLOCKS(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
-
-// One row on the GROUP layout, Q blocks of 1024 elements: requires
-// 1024 (Q-1) < n <= 1024 Q, n a multiple of 4 and x, w, y aligned to a quad
-// (16 B binary32, 8 B bf16). Blocks below Q-1 are complete; in the last one,
-// quads past the row are loaded from the row's last quad (an in-row address)
-// and masked to +0 after every load has been issued.
-//
-// m0, m1: the blocks [m0, m1) this workgroup applies and stores (wave-uniform;
-// the whole row by default). Every call reads the whole of x and computes the
-// whole row's sum, so a row may be applied by several workgroups, each taking
-// a block range (REPLICA), with every workgroup's inv bit-identical.
-template <typename T, int Q>
-__device__ __forceinline__ void row_group(const T* x, const T* __restrict__ w, T* y, int n,
-                                          float eps, float* lds4, int m0 = 0, int m1 = Q) {
-    using QD = Quad<T>;
-    constexpr uint32_t es = sizeof(T);
-    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const uint32_t off = (uint32_t)((lane >> 4) * 256 + g * 64 + (lane & 15) * 4);  // elements
-    const uint32_t last = (uint32_t)n - 4u;
-    const bool exact = n == 1024 * Q;
-    typename QD::raw xr[Q], wr[Q];
-    gptr_c xg = scalar_gptr(reinterpret_cast<const char*>(x));
-    gptr_c wg = scalar_gptr(reinterpret_cast<const char*>(w));
-#pragma unroll
-    for (int m = 0; m < Q; ++m) {
-        const uint32_t e = m + 1 < Q || exact ? 1024u * m + off : min(1024u * m + off, last);
-        xr[m] = QD::template gload<false>(xg + e * es);
-    }
-#pragma unroll
-    for (int m = 0; m < Q; ++m) {
-        const uint32_t e = m + 1 < Q || exact ? 1024u * m + off : min(1024u * m + off, last);
-        if (m >= m0 && m < m1) wr[m] = QD::template gload<false>(wg + e * es);
-        else wr[m] = QD::zero();
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    const bool tail_in = exact || 1024u * (Q - 1) + off < (uint32_t)n;
-    float p = 0.0f;
-#pragma unroll
-    for (int m = 0; m < Q; ++m) {
-        float v[4];
-        QD::unpack(xr[m], v);
-        if (m + 1 == Q && !tail_in) v[0] = v[1] = v[2] = v[3] = 0.0f;
-        transpose4(v);
-        p = fmaf(v[0], v[0], p);  // chunks 4m, 4m+1, 4m+2, 4m+3 of chain 64g + 4t + q
-        p = fmaf(v[1], v[1], p);
-        p = fmaf(v[2], v[2], p);
-        p = fmaf(v[3], v[3], p);
-    }
-    const float gt = group_sumsq(p);
-    if (lane == 0) lds4[g] = gt;
-    __syncthreads();
-    const float inv = inverse_rms((lds4[0] + lds4[2]) + (lds4[1] + lds4[3]), n, eps);
-    gptr yg = scalar_gptr(reinterpret_cast<char*>(y));
-#pragma unroll
-    for (int m = 0; m < Q; ++m) {
-        if (m < m0 || m >= m1) continue;
-        if (m + 1 == Q && !tail_in) continue;
-        float v[4], wv[4], o[4];
-        QD::unpack(xr[m], v);
-        QD::unpack(wr[m], wv);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = (v[i] * inv) * wv[i];
-        QD::template gstore<false>(yg + (1024u * m + off) * es, o);
-    }
-}
-
-
-// ---------------------------------------------------------------------------
-// BLOCK / STREAM layout: 256 threads per row, thread l = chain l, wave g = group g.
-
-// Descending halving over the 64 lanes of this wavefront; the total lands in lane 0.
-__device__ __forceinline__ float group_tree(float v) {
-    v += __shfl_down(v, 32, 64);
-    v += __shfl_down(v, 16, 64);
-    v += row_shl<8>(v);
-    v += row_shl<4>(v);
-    v += row_shl<2>(v);
-    v += row_shl<1>(v);
-    return v;
-}
-
-// Group trees, the combine through LDS, and steps 4-7. Every thread of the
-// block calls this once per row with its finished chain p.
-__device__ __forceinline__ float block_inverse(float p, int n, float eps, float* lds4) {
-    const float g = group_tree(p);
-    if ((threadIdx.x & 63) == 0) lds4[threadIdx.x >> 6] = g;
-    __syncthreads();
-    const float ss = (lds4[0] + lds4[2]) + (lds4[1] + lds4[3]);
-    return inverse_rms(ss, n, eps);
-}
-
-// NCH > 0: rows with 256 * prev_bucket(NCH) < n <= 256 * NCH are held in
-// registers; any other n (possible for descriptor rows rewritten between graph
-// replays) is streamed. NCH == 0: always streamed. x, w, y are global memory.
-template <typename T, int NCH>
-__device__ __forceinline__ void row_block(const T* x, const T* __restrict__ w, T* y, int n,
-                                          float eps, float* lds4) {
-    using E = Elem<T>;
-    constexpr int MINF = prev_bucket(NCH);
-    const uint32_t l = threadIdx.x;  // association lane 0..255
-    const int full = n >> 8;         // complete 256-element chunks (wave-uniform)
-    gptr_c xg = scalar_gptr(x);
-    gptr_c wg = scalar_gptr(w);
-    gptr yg = scalar_gptr(y);
-    float p = 0.0f;
-    if (NCH > 0 && full >= MINF && full + ((n & 255) != 0) <= NCH) {
-        constexpr int R = NCH > 0 ? NCH : 1;
-        // a scalar base per 4 KB of the row keeps every chunk's offset in the
-        // instruction's immediate field
-        constexpr uint32_t per_base = 4096 / (256 * sizeof(T));
-        // Chunks below MINF are complete. The others (the bucket's top chunks:
-        // complete, ragged or past the row) are loaded from a clamped, in-row
-        // index without branches and masked to +0 past the row only after every
-        // load of x and w has been issued (the scheduling barrier keeps the
-        // compiler from waiting for x before issuing w).
-        typename E::raw_t xr[R], wr[R];
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const uint32_t kb = (uint32_t)(k / per_base) * 4096u;
-            const uint32_t d = (uint32_t)(k % per_base) * 256u + l;
-            if (k < MINF)
-                xr[k] = E::raw(scalar_gptr(xg + kb), d);
-            else
-                xr[k] = E::raw(xg, min(((uint32_t)k << 8) + l, (uint32_t)n - 1u));
-        }
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const uint32_t kb = (uint32_t)(k / per_base) * 4096u;
-            const uint32_t d = (uint32_t)(k % per_base) * 256u + l;
-            if (k < MINF)
-                wr[k] = E::raw(scalar_gptr(wg + kb), d);
-            else
-                wr[k] = E::raw(wg, min(((uint32_t)k << 8) + l, (uint32_t)n - 1u));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        float xv[R], wv[R];
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            xv[k] = E::value(xr[k]);
-            wv[k] = E::value(wr[k]);
-            if (k >= MINF && ((uint32_t)k << 8) + l >= (uint32_t)n) xv[k] = 0.0f;
-            p = fmaf(xv[k], xv[k], p);  // +0 past the row: no change
-        }
-        const float inv = block_inverse(p, n, eps, lds4);
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const float v = (xv[k] * inv) * wv[k];
-            if (k < MINF) {
-                const uint32_t kb = (uint32_t)(k / per_base) * 4096u;
-                E::store(scalar_gptr(yg + kb), (uint32_t)(k % per_base) * 256u + l, v);
-            } else if (((uint32_t)k << 8) + l < (uint32_t)n) {
-                E::store(yg, ((uint32_t)k << 8) + l, v);
-            }
-        }
-    } else {
-        for (uint32_t d = l; d < (uint32_t)n; d += 256) {
-            const float v = E::load(xg, d);
-            p = fmaf(v, v, p);
-        }
-        const float inv = block_inverse(p, n, eps, lds4);
-        for (uint32_t d = l; d < (uint32_t)n; d += 256)
-            E::store(yg, d, (E::load(xg, d) * inv) * E::load(wg, d));
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Kernels.
@@ -675,975 +182,6 @@ __global__ __launch_bounds__(256) void k_desc_group(const rmsn_desc* __restrict_
         row_group<T, Q>(x, w, y, (int)n, eps, lds4);
     else
         row_block<T, 0>(x, w, y, (int)n, eps, lds4);
-}
-
-
-// The whole decode step in one launch (Lecture 08 "Graph-resident decode",
-// further reading: a persistent kernel instead of many captured ones). One
-// workgroup of four wavefronts walks the descriptor table, in one of three
-// ways chosen when the launch starts (every thread checks some rows, then one
-// barrier):
-//  - round walk, when every row is a whole number of 16-byte vectors (at most
-//    8192 elements, 16-byte aligned) and no row of an aligned group of 16 (or
-//    at least of 4) consecutive rows reads or writes memory that another row
-//    of the group writes: each wavefront takes a row of its own and holds it
-//    whole, four rows at a time, and a workgroup barrier after each group
-//    orders the group's stores before the next group's loads;
-//  - pipelined, when every row fits the GROUP mapping (width a multiple of
-//    4 and at most 8192, pointers quad-aligned) and no row reads memory that
-//    one of the three rows before it writes, nor writes memory the row just
-//    before it writes: the four wavefronts share each row, and the next row's
-//    loads are issued before the current row is reduced;
-//  - otherwise row after row, with a workgroup barrier after each row that
-//    orders its stores before the next row's loads.
-// All three compute what the launch sequence computes. With POS the rows are
-// taken at the device-resident position, read once, and the last thread
-// stores the next position after the last row (the same update as the
-// sequence's last node).
-
-// Row pointers of descriptor `dd` at position `pos`.
-template <typename T, bool POS>
-__device__ __forceinline__ void persistent_ptrs(const rmsn_desc& dd, uint64_t pos,
-                                                const PosArgs& pa, const T*& x, const T*& w,
-                                                T*& y) {
-    desc_row<T, POS>(dd, pos, pa, x, y);
-    w = static_cast<const T*>(dd.w);
-}
-
-template <typename T>
-__device__ __forceinline__ bool group_fits(const T* x, const T* w, const T* y, int64_t n) {
-    const uintptr_t a = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) |
-                        reinterpret_cast<uintptr_t>(y);
-    return n >= 1 && n <= 8192 && (n & 3) == 0 && a % (4 * sizeof(T)) == 0;
-}
-
-template <typename T>
-__device__ __forceinline__ void persistent_row(const T* x, const T* w, T* y, int64_t n, float eps,
-                                               float* lds4) {
-    if (n < 1 || n > RMSN_MAX_N) return;
-    if (group_fits<T>(x, w, y, n)) {
-        switch ((int)((n + 1023) >> 10)) {
-#define RMSN_CASE(Q) \
-    case Q: row_group<T, Q>(x, w, y, (int)n, eps, lds4); break;
-            RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)
-#undef RMSN_CASE
-            default: break;
-        }
-    } else {
-        row_block<T, 0>(x, w, y, (int)n, eps, lds4);
-    }
-}
-
-// --- Pipelined walk. Every row takes the GROUP mapping at the table's widest
-// block count (1024-element blocks) through buffer loads and stores whose
-// range is the row's byte length: lanes past the row load +0
-// (fmaf(0, 0, p) == p) and their stores are dropped by the hardware's range
-// check, so every row issues the same instructions whatever its width and the
-// compiler can wait for exactly the row it needs while the next one is in
-// flight.
-
-typedef __amdgpu_buffer_rsrc_t brsrc;
-
-// A buffer resource for `bytes` bytes at p (raw, stride 0; the third word is
-// the gfx9-family untyped format). Offsets at or past `bytes` are out of range.
-__device__ __forceinline__ brsrc row_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-template <typename T> struct PipeQuad;
-template <> struct PipeQuad<float> {
-    typedef u32x4 raw;
-    static __device__ __forceinline__ raw load(brsrc r, uint32_t off) {
-        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    }
-    static __device__ __forceinline__ void store(raw v, brsrc r, uint32_t off) {
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
-    }
-    static __device__ __forceinline__ void unpack(raw q, float v[4]) {
-        v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
-        v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
-    }
-    static __device__ __forceinline__ raw apply(raw x, raw w, float inv) {
-        return slice_apply(x, w, inv, 0.0f);
-    }
-};
-template <> struct PipeQuad<uint16_t> {
-    typedef u32x2 raw;
-    static __device__ __forceinline__ raw load(brsrc r, uint32_t off) {
-        return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-    }
-    static __device__ __forceinline__ void store(raw v, brsrc r, uint32_t off) {
-        __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
-    }
-    static __device__ __forceinline__ void unpack(raw q, float v[4]) {
-        v[0] = lo_bf16(q.x); v[1] = hi_bf16(q.x); v[2] = lo_bf16(q.y); v[3] = hi_bf16(q.y);
-    }
-    static __device__ __forceinline__ raw apply(raw x, raw w, float inv) {
-        raw o;
-        o.x = apply_pair(x.x, w.x, inv);
-        o.y = apply_pair(x.y, w.y, inv);
-        return o;
-    }
-};
-
-struct PipeRow {
-    brsrc x, w, y;
-    int n;
-};
-
-template <typename T, int QM>
-struct PipeBuf {
-    typename PipeQuad<T>::raw x[QM], w[QM];
-};
-
-// Descriptor i of the table, or the last one past its end (only its base
-// pointers are used then, with an empty range).
-__device__ __forceinline__ rmsn_desc pipe_desc(const rmsn_desc* d, int32_t i, int32_t count) {
-    return d[i < count ? i : count - 1];
-}
-
-// Buffer resources of a row; `real` false gives an empty range (every access
-// out of range, no memory touched) on valid bases.
-template <typename T, bool POS>
-__device__ __forceinline__ PipeRow pipe_row_of(const rmsn_desc& dd, bool real, uint64_t pos,
-                                               const PosArgs& pa) {
-    const T* x;
-    const T* w;
-    T* y;
-    persistent_ptrs<T, POS>(dd, pos, pa, x, w, y);
-    const uint32_t bytes = real ? (uint32_t)dd.n * (uint32_t)sizeof(T) : 0u;
-    return PipeRow{row_rsrc(x, bytes), row_rsrc(w, bytes), row_rsrc(y, bytes), (int)dd.n};
-}
-
-// This lane's byte offset in block m: GROUP's element 1024 m + 256 q + 64 g + 4 t.
-template <typename T>
-__device__ __forceinline__ uint32_t pipe_off(uint32_t lane_off, int m) {
-    return lane_off + (uint32_t)m * 1024u * (uint32_t)sizeof(T);
-}
-
-template <typename T, int QM>
-__device__ __forceinline__ void pipe_issue(PipeBuf<T, QM>& b, const PipeRow& r,
-                                           uint32_t lane_off) {
-#pragma unroll
-    for (int m = 0; m < QM; ++m) b.x[m] = PipeQuad<T>::load(r.x, pipe_off<T>(lane_off, m));
-#pragma unroll
-    for (int m = 0; m < QM; ++m) b.w[m] = PipeQuad<T>::load(r.w, pipe_off<T>(lane_off, m));
-}
-
-// Workgroup barrier for LDS only: it does not wait for this wavefront's
-// global loads and stores (a full barrier would wait for the next row's
-// loads, in flight by design).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-template <typename T, int QM>
-__device__ __forceinline__ void pipe_compute(const PipeBuf<T, QM>& b, const PipeRow& r,
-                                             uint32_t lane_off, float eps, float* lds4, int g,
-                                             int lane) {
-    float p = 0.0f;
-#pragma unroll
-    for (int m = 0; m < QM; ++m) {
-        float v[4];
-        PipeQuad<T>::unpack(b.x[m], v);
-        transpose4(v);
-        p = fmaf(v[0], v[0], p);  // chunks 4m .. 4m+3 of chain 64g + 4t + q
-        p = fmaf(v[1], v[1], p);
-        p = fmaf(v[2], v[2], p);
-        p = fmaf(v[3], v[3], p);
-    }
-    const float gt = group_sumsq(p);
-    if (lane == 0) lds4[g] = gt;
-    lds_barrier();
-    const float inv = inverse_rms((lds4[0] + lds4[2]) + (lds4[1] + lds4[3]), r.n, eps);
-#pragma unroll
-    for (int m = 0; m < QM; ++m)
-        PipeQuad<T>::store(PipeQuad<T>::apply(b.x[m], b.w[m], inv), r.y,
-                           pipe_off<T>(lane_off, m));
-}
-
-// --- Round walk: one wavefront per row, the four wavefronts on four
-// consecutive rows at a time (a round). A row is the SPLIT layout with a
-// single wavefront: U 1 KB slices, one 16-byte load per lane each, so the
-// wavefront holds the whole row and needs neither LDS nor a hand-off. Every
-// row issues its own number of loads, and the four rows of a round are in
-// flight together.
-
-template <typename T, int U, bool EXACT>
-__device__ __forceinline__ void wave_row_slices(const T* x, const T* w, T* y, int n, float eps,
-                                                int lane) {
-    const uint32_t nvec = (uint32_t)n * (uint32_t)sizeof(T) / 16u;
-    SplitPart<T, U, EXACT, false> part;
-    part.load(scalar_gptr(reinterpret_cast<const char*>(x)),
-              scalar_gptr(reinterpret_cast<const char*>(w)), 0, lane, nvec);
-    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    part.chains(p, nvec);
-    const float inv = inverse_rms(split_sumsq(p, lane, T()), n, eps);
-    part.apply(inv, scalar_gptr(reinterpret_cast<char*>(y)), 0, lane, nvec);
-}
-
-// Slice buckets of the one-wavefront rows (rows of at most 8192 elements:
-// 32 slices of binary32, 16 of bf16).
-#define RMSN_FOR_ROUND_SLICES(X) X(1) X(2) X(3) X(4) X(6) X(8) X(12) X(16) X(20) X(24) X(28) X(32)
-
-// One row of a round: 1 <= n <= 8192, n * sizeof(T) a multiple of 16, x, w, y
-// 16-byte aligned (checked before the round walk is chosen).
-template <typename T>
-__device__ __forceinline__ void round_row(const T* x, const T* w, T* y, int n, float eps,
-                                          int lane) {
-    const int bytes = n * (int)sizeof(T);
-    const int slices = (bytes + 1023) >> 10;
-#define RMSN_CASE(U)                                                                   \
-    if constexpr (U * 1024 <= 8192 * (int)sizeof(T)) {                                 \
-        if (slices <= U) {                                                             \
-            if (bytes == U * 1024) wave_row_slices<T, U, true>(x, w, y, n, eps, lane);  \
-            else wave_row_slices<T, U, false>(x, w, y, n, eps, lane);                  \
-            return;                                                                    \
-        }                                                                              \
-    }
-    RMSN_FOR_ROUND_SLICES(RMSN_CASE)
-#undef RMSN_CASE
-}
-
-// Rounds of four rows, a workgroup barrier after every K rounds: wavefront w
-// takes rows 4q + w of each group of 4K rows, and the barrier orders the
-// group's stores before the next group's loads.
-template <typename T, bool POS, int K>
-__device__ __forceinline__ void round_walk(const rmsn_desc* d, int32_t count, float eps,
-                                           uint64_t pos, const PosArgs& pa) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    for (int32_t r = 0; r < count; r += 4 * K) {
-        for (int q = 0; q < K; ++q) {
-            const int32_t j = r + 4 * q + wave;
-            if (j < count) {
-                const rmsn_desc dd = d[j];
-                const T* x;
-                const T* w;
-                T* y;
-                persistent_ptrs<T, POS>(dd, pos, pa, x, w, y);
-                round_row<T>(x, w, y, (int)dd.n, eps, lane);
-            }
-        }
-        __syncthreads();  // the group's stores before the next group's loads
-    }
-}
-
-// How the table is walked (see above): kRoundWalk16 or kRoundWalk4 (no row of
-// an aligned group of 16 / 4 rows reads or writes what another row of the
-// group writes), a block count 1..8 for the pipelined walk (the widest
-// row's), or 0 for row after row. Every thread checks rows threadIdx.x,
-// threadIdx.x + blockDim.x, ...; the answer is the workgroup's.
-constexpr int kRoundWalk4 = 100;
-constexpr int kRoundWalk16 = 101;
-constexpr int kSpanRows = 1024;  // output ranges published in LDS (16 KB)
-// Worker workgroups for free rows: with workgroup 0, one wave of workgroups on
-// the 256 CUs (the kernel's registers allow one workgroup per CU).
-constexpr int kSpreadWorkers = 255;
-
-__device__ __forceinline__ bool ranges_meet(uintptr_t a, uintptr_t la, uintptr_t b, uintptr_t lb) {
-    return a < b + lb && b < a + la;
-}
-
-// Row j's pointers as integers, its byte length, and what the walks need of it.
-template <typename T, bool POS>
-__device__ __forceinline__ void walk_row_facts(const rmsn_desc& dj, uint64_t pos,
-                                               const PosArgs& pa, uintptr_t& bx, uintptr_t& bw,
-                                               uintptr_t& by, uintptr_t& len, bool& fits,
-                                               bool& vec) {
-    const T* x;
-    const T* w;
-    T* y;
-    persistent_ptrs<T, POS>(dj, pos, pa, x, w, y);
-    bx = reinterpret_cast<uintptr_t>(x);
-    bw = reinterpret_cast<uintptr_t>(w);
-    by = reinterpret_cast<uintptr_t>(y);
-    fits = group_fits<T>(x, w, y, dj.n);
-    len = (uintptr_t)(dj.n < 0 ? 0 : dj.n) * sizeof(T);
-    vec = fits && len % 16 == 0 && (bx | bw | by) % 16 == 0;
-}
-
-// What row j finds against row k (k != j): rules of the walks above.
-__device__ __forceinline__ void walk_pair(int32_t j, int32_t k, uintptr_t bx, uintptr_t bw,
-                                          uintptr_t by, uintptr_t len, uintptr_t ky,
-                                          uintptr_t klen, bool& no_pipe, bool& no_round,
-                                          bool& no_round16) {
-    const bool reads = ranges_meet(bx, len, ky, klen) || ranges_meet(bw, len, ky, klen);
-    const bool writes = ranges_meet(by, len, ky, klen);
-    const int32_t r0 = j & ~3, g0 = j & ~15;
-    if (k < j && j - k <= 3 && (reads || (writes && k == j - 1))) no_pipe = true;
-    const bool meet = reads || (writes && k < j);
-    if (k >= r0 && k < r0 + 4 && meet) no_round = true;
-    if (k >= g0 && meet) no_round16 = true;
-}
-
-// How the table is walked (see above): kRoundWalk16 or kRoundWalk4, a block
-// count 1..8 for the pipelined walk (the widest row's), or 0 for row after
-// row. Every thread checks rows threadIdx.x, threadIdx.x + blockDim.x, ...
-// against the rows of their windows (the three rows before, the other rows
-// of their groups of 4 and 16); the answer is the workgroup's. Tables of up to
-// kSpanRows rows first publish every row's output range in LDS, so a check
-// reads 16 bytes of LDS instead of a descriptor from memory.
-template <typename T, bool POS>
-__device__ __forceinline__ int walk_mode(const rmsn_desc* d, int32_t count, uint64_t pos,
-                                         const PosArgs& pa, int* lds_fold) {
-    __shared__ uintptr_t yspan[kSpanRows][2];  // output start, byte length
-    bool no_pipe = false, no_round = false, no_round16 = false;
-    int blocks = 1;
-    if (count <= kSpanRows) {
-        // at most kSpanRows / 256 rows per thread: their facts stay in registers
-        constexpr int R = kSpanRows / 256;
-        uintptr_t bx[R], bw[R], by[R], len[R];
-        bool live[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int32_t j = threadIdx.x + 256 * r;
-            live[r] = j < count;
-            bool fits = true, vec = true;
-            if (live[r]) {
-                const rmsn_desc dj = d[j];
-                walk_row_facts<T, POS>(dj, pos, pa, bx[r], bw[r], by[r], len[r], fits, vec);
-                yspan[j][0] = by[r];
-                yspan[j][1] = len[r];
-                blocks = max(blocks, (int)((dj.n + 1023) >> 10));
-            }
-            if (!fits) no_pipe = no_round = no_round16 = true;
-            if (!vec) no_round = no_round16 = true;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if (!live[r]) continue;
-            const int32_t j = threadIdx.x + 256 * r;
-            const int32_t g0 = j & ~15;
-            const int32_t k_end = min(count, g0 + 16);
-#pragma unroll 4
-            for (int32_t k = max(0, min(j - 3, g0)); k < k_end; ++k) {
-                if (k == j) continue;
-                walk_pair(j, k, bx[r], bw[r], by[r], len[r], yspan[k][0], yspan[k][1], no_pipe,
-                          no_round, no_round16);
-            }
-        }
-    } else {
-        for (int32_t j = threadIdx.x; j < count; j += blockDim.x) {
-            const rmsn_desc dj = d[j];
-            uintptr_t bx, bw, by, len;
-            bool fits, vec;
-            walk_row_facts<T, POS>(dj, pos, pa, bx, bw, by, len, fits, vec);
-            if (!fits) {
-                no_pipe = no_round = no_round16 = true;
-                break;
-            }
-            if (!vec) no_round = no_round16 = true;
-            blocks = max(blocks, (int)((dj.n + 1023) >> 10));
-            const int32_t g0 = j & ~15;
-            const int32_t k_end = min(count, g0 + 16);
-            for (int32_t k = max(0, min(j - 3, g0)); k < k_end; ++k) {
-                if (k == j) continue;
-                uintptr_t kx, kw, ky, klen;
-                bool kf, kv;
-                walk_row_facts<T, POS>(d[k], pos, pa, kx, kw, ky, klen, kf, kv);
-                walk_pair(j, k, bx, bw, by, len, ky, klen, no_pipe, no_round, no_round16);
-            }
-        }
-    }
-    // One exchange for the workgroup: each wavefront folds its lanes (ballots
-    // and a maximum), lane 0 publishes the result, one barrier, every thread
-    // folds the four.
-    const uint32_t flags = (__ballot(no_pipe) ? 1u : 0u) | (__ballot(no_round) ? 2u : 0u) |
-                           (__ballot(no_round16) ? 4u : 0u);
-    int wmax = blocks;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) wmax = max(wmax, __shfl_xor(wmax, o, 64));
-    if ((threadIdx.x & 63) == 0) lds_fold[threadIdx.x >> 6] = (int)(flags << 8) | wmax;
-    __syncthreads();
-    uint32_t all_flags = 0;
-    int all_blocks = 1;
-    for (int wv = 0; wv < (int)(blockDim.x >> 6); ++wv) {
-        all_flags |= (uint32_t)lds_fold[wv] >> 8;
-        all_blocks = max(all_blocks, lds_fold[wv] & 0xFF);
-    }
-    if (!(all_flags & 4u)) return kRoundWalk16;
-    if (!(all_flags & 2u)) return kRoundWalk4;
-    if (!(all_flags & 1u)) return all_blocks;
-    return 0;
-}
-
-template <typename T, bool POS, int QM>
-__device__ __forceinline__ void pipelined_walk(const rmsn_desc* d, int32_t count, float eps,
-                                               uint64_t pos, const PosArgs& pa,
-                                               float (*lds8)[4]) {
-    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const uint32_t lane_off =
-        (uint32_t)((lane >> 4) * 256 + g * 64 + (lane & 15) * 4) * (uint32_t)sizeof(T);
-    PipeBuf<T, QM> a, b;
-    PipeRow cur = pipe_row_of<T, POS>(pipe_desc(d, 0, count), true, pos, pa);
-    pipe_issue<T, QM>(a, cur, lane_off);
-    // QM stores to an empty range (dropped by the range check): every row's
-    // loads are then followed by the same QM stores, at the loop's entry as on
-    // its back edge, so the compiler's wait for a row never covers the
-    // previous row's stores.
-    const brsrc none = row_rsrc(pipe_desc(d, 0, count).y, 0u);
-#pragma unroll
-    for (int m = 0; m < QM; ++m)
-        PipeQuad<T>::store(typename PipeQuad<T>::raw{}, none, pipe_off<T>(lane_off, m));
-    rmsn_desc ahead = pipe_desc(d, 1, count);  // descriptors are read one row ahead
-    // Scheduling barriers keep each row's reduction below the next row's load
-    // issue: the reduction waits for its own loads only.
-    for (int32_t i = 0;;) {
-        // row i is in a; row i + 1's loads go into b before row i is reduced
-        PipeRow nxt = pipe_row_of<T, POS>(ahead, i + 1 < count, pos, pa);
-        pipe_issue<T, QM>(b, nxt, lane_off);
-        ahead = pipe_desc(d, i + 2, count);
-        __builtin_amdgcn_sched_barrier(0);
-        pipe_compute<T, QM>(a, cur, lane_off, eps, lds8[0], g, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        if (++i >= count) break;
-        cur = nxt;
-        nxt = pipe_row_of<T, POS>(ahead, i + 1 < count, pos, pa);
-        pipe_issue<T, QM>(a, nxt, lane_off);
-        ahead = pipe_desc(d, i + 2, count);
-        __builtin_amdgcn_sched_barrier(0);
-        pipe_compute<T, QM>(b, cur, lane_off, eps, lds8[1], g, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        if (++i >= count) break;
-        cur = nxt;
-    }
-}
-
-template <typename T, bool POS>
-__device__ __forceinline__ void serial_walk(const rmsn_desc* d, int32_t count, float eps,
-                                            uint64_t pos, const PosArgs& pa, float* lds4) {
-    uint64_t unused;
-    rmsn_desc next = desc_load<false>(d, pa, &unused);
-    for (int32_t i = 0; i < count; ++i) {
-        const rmsn_desc cur = next;
-        if (i + 1 < count) next = desc_load<false>(d + i + 1, pa, &unused);
-        const T* x;
-        const T* w;
-        T* y;
-        persistent_ptrs<T, POS>(cur, pos, pa, x, w, y);
-        persistent_row<T>(x, w, y, cur.n, eps, lds4);
-        __syncthreads();  // this row's stores before the next row's loads; lds4 reused
-    }
-}
-
-// --- Free rows over many workgroups. A row whose reads and output meet no
-// other row's output, and whose output meets no other row's reads, can run at
-// any time, in any workgroup: the order of the table cannot be observed on it.
-// With more than one workgroup launched (tables of at most kSpanRows rows; a
-// positioned table's rows taken at its position), workgroups 1..G-1 take such
-// "free" rows (row j in workgroup 1 + j mod (G-1)) while workgroup 0 runs the
-// others ("bound" rows) in table order. Both sides decide freeness from the same descriptors by the same
-// rule, so every row is run exactly once; no workgroup waits for another.
-
-struct RowSpan {
-    uintptr_t x, w, y, len;  // addresses and byte length; 0 for a width the kernels skip
-};
-
-template <typename T, bool POS>
-__device__ __forceinline__ RowSpan row_span(const rmsn_desc& dj, uint64_t pos, const PosArgs& pa) {
-    const T* x;
-    const T* w;
-    T* y;
-    persistent_ptrs<T, POS>(dj, pos, pa, x, w, y);  // the row where it is taken at this position
-    const bool valid = dj.n >= 1 && dj.n <= RMSN_MAX_N;
-    return RowSpan{reinterpret_cast<uintptr_t>(x), reinterpret_cast<uintptr_t>(w),
-                   reinterpret_cast<uintptr_t>(y),
-                   valid ? (uintptr_t)dj.n * sizeof(T) : (uintptr_t)0};
-}
-
-// Rows a and b (both non-empty) meet: one reads or writes memory the other
-// writes. Branch-free (bitwise operators): a few compares on one LDS load of
-// each row, not a chain of branches each waiting for its own load.
-__device__ __forceinline__ bool rows_meet(const RowSpan& a, const RowSpan& b) {
-    const uintptr_t ae = a.len, be = b.len;
-    const bool xb = (a.x < b.y + be) & (b.y < a.x + ae);   // a reads b's output (x)
-    const bool wb = (a.w < b.y + be) & (b.y < a.w + ae);   // a reads b's output (w)
-    const bool yy = (a.y < b.y + be) & (b.y < a.y + ae);   // outputs overlap
-    const bool xa = (b.x < a.y + ae) & (a.y < b.x + be);   // b reads a's output (x)
-    const bool wa = (b.w < a.y + ae) & (a.y < b.w + be);   // b reads a's output (w)
-    return (ae != 0) & (be != 0) & (xb | wb | yy | xa | wa);
-}
-
-// The same rows as 32-bit offsets from the table's lowest address with their
-// ends, when every row lies within 4 GB of it (as rows from one allocator
-// do): the test is then ten 32-bit compares. A row the kernels skip is all
-// 0xFFFFFFFF, which meets nothing.
-struct RowSpan32 {
-    uint32_t x, xe, w, we, y, ye;
-};
-
-__device__ __forceinline__ RowSpan32 row_span32(const RowSpan& r, uintptr_t base) {
-    if (r.len == 0) return RowSpan32{~0u, ~0u, ~0u, ~0u, ~0u, ~0u};
-    const uint32_t x = (uint32_t)(r.x - base), w = (uint32_t)(r.w - base);
-    const uint32_t y = (uint32_t)(r.y - base), l = (uint32_t)r.len;
-    return RowSpan32{x, x + l, w, w + l, y, y + l};
-}
-
-// Row a's w range meets row b's output.
-__device__ __forceinline__ bool w_meets_output(const RowSpan& a, const RowSpan& b) {
-    return (a.len != 0) & (b.len != 0) & (a.w < b.y + b.len) & (b.y < a.w + a.len);
-}
-__device__ __forceinline__ bool w_meets_output(const RowSpan32& a, const RowSpan32& b) {
-    return (a.w < b.ye) & (b.y < a.we);
-}
-
-__device__ __forceinline__ bool rows_meet(const RowSpan32& a, const RowSpan32& b) {
-    return ((a.x < b.ye) & (b.y < a.xe)) | ((a.w < b.ye) & (b.y < a.we)) |
-           ((a.y < b.ye) & (b.y < a.ye)) | ((b.x < a.ye) & (a.y < b.xe)) |
-           ((b.w < a.ye) & (a.y < b.we));
-}
-
-// True in every thread when p holds in any thread of the workgroup (a ballot
-// per wavefront, one LDS word each, one barrier; the answer is read into a
-// scalar register). fold4 is free again when it returns.
-__device__ __forceinline__ bool workgroup_any(bool p, int* fold4) {
-    const int wave_any = __ballot(p) != 0;  // every lane takes part in the ballot
-    if ((threadIdx.x & 63) == 0) fold4[threadIdx.x >> 6] = wave_any;
-    __syncthreads();
-    const int any = fold4[0] | fold4[1] | fold4[2] | fold4[3];
-    __syncthreads();
-    return __builtin_amdgcn_readfirstlane(any) != 0;
-}
-
-// Bit 0: a holds in some thread of the workgroup; bit 1: b does. As
-// workgroup_any, one barrier to publish and one to free fold4.
-__device__ __forceinline__ int workgroup_any2(bool a, bool b, int* fold4) {
-    const int wave_any = (__ballot(a) != 0 ? 1 : 0) | (__ballot(b) != 0 ? 2 : 0);
-    if ((threadIdx.x & 63) == 0) fold4[threadIdx.x >> 6] = wave_any;
-    __syncthreads();
-    const int any = fold4[0] | fold4[1] | fold4[2] | fold4[3];
-    __syncthreads();
-    return __builtin_amdgcn_readfirstlane(any);
-}
-
-// One row, its pointers taken from the descriptor (a wave-uniform load), not
-// from the LDS copy used for the overlap tests.
-template <typename T, bool POS>
-__device__ __forceinline__ void spread_row(const rmsn_desc& dj, uint64_t pos, const PosArgs& pa,
-                                           float eps, float* lds4) {
-    const T* x;
-    const T* w;
-    T* y;
-    persistent_ptrs<T, POS>(dj, pos, pa, x, w, y);
-    persistent_row<T>(x, w, y, dj.n, eps, lds4);
-}
-
-// Which rows meet another one (rows_meet), found without testing every pair
-// when the outputs are disjoint: the outputs are put in order of start
-// address, and they are disjoint exactly when each one ends at or before the
-// next one starts. Their ends are then in order as well, so for each x or w
-// range the first output ending past its start is found by binary search, and
-// the outputs meeting the range are that one and those after it that start
-// before the range ends; both rows of every such pair (the row's own output,
-// in place, aside) are bound. With disjoint outputs no other pair meets. The
-// order is a rank sort: the key start * 2^16 + row is unique, and each lane
-// counts the keys below its own, reading them as LDS broadcasts with no
-// barrier between steps. Returns kNoneBound, kBoundMarked (bound[j] is 1
-// exactly for the bound rows), or kBoundUnknown when outputs overlap or lie
-// past 2^48 (beyond the key): the all-pairs test then decides.
-// mine[r] is row threadIdx.x + 256 r. Every thread gets the same answer.
-constexpr int kNoneBound = 0, kBoundMarked = 1, kBoundUnknown = 2;
-
-template <int RE, int R>
-__device__ __forceinline__ void key_ranks(const uint64_t* o_key, int32_t count,
-                                          const uint64_t (&key)[R], int32_t (&rank)[R]) {
-#pragma unroll 8
-    for (int32_t k = 0; k < count; ++k) {
-        const uint64_t kk = o_key[k];  // the same word in every lane
-#pragma unroll
-        for (int r = 0; r < RE; ++r) rank[r] += kk < key[r] ? 1 : 0;
-    }
-}
-
-template <int R>
-__device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t count,
-                                               uint8_t* bound, int* fold4) {
-    __shared__ uint64_t o_key[kSpanRows], o_start[kSpanRows], o_end[kSpanRows];
-    __shared__ uint16_t o_row[kSpanRows];
-    constexpr uint64_t kNoOutput = 0xFFFFFFFFFFFFull;  // the key's start for an empty row
-    int32_t m = 2;
-    while (m < count) m <<= 1;
-    uint64_t key[R];
-    int32_t rank[R];
-    bool high = false;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int32_t j = threadIdx.x + 256 * r;
-        const bool out = j < count && mine[r].len != 0;  // an empty row writes nothing
-        high |= out && ((uint64_t)(mine[r].y + mine[r].len) >> 48) != 0;
-        key[r] = ((out ? (uint64_t)mine[r].y : kNoOutput) << 16) | (uint64_t)j;
-        rank[r] = 0;
-        if (j < count) o_key[j] = key[r];
-    }
-    __syncthreads();  // o_key published
-    switch ((count + 255) >> 8) {
-        case 1: key_ranks<1>(o_key, count, key, rank); break;
-        case 2: key_ranks<2>(o_key, count, key, rank); break;
-        case 3: key_ranks<3>(o_key, count, key, rank); break;
-        default: key_ranks<4>(o_key, count, key, rank); break;
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int32_t j = threadIdx.x + 256 * r;
-        if (j >= m) continue;
-        const bool out = j < count && mine[r].len != 0;
-        const int32_t p = j < count ? rank[r] : j;  // padding sorts after every row
-        o_start[p] = out ? (uint64_t)mine[r].y : ~0ull;
-        o_end[p] = out ? (uint64_t)(mine[r].y + mine[r].len) : ~0ull;
-        o_row[p] = (uint16_t)j;
-    }
-    for (int32_t j = threadIdx.x; j < count; j += 256) bound[j] = 0;
-    __syncthreads();
-    // keys past 2^48 or overlapping outputs leave the answer unknown; the
-    // searches below still stay in bounds (the ranks are a permutation), and
-    // the all-pairs marking then rewrites every mark they made
-    bool unknown = high;
-    for (int32_t i = threadIdx.x; i + 1 < m; i += 256)
-        unknown |= (o_start[i + 1] != ~0ull) & (o_end[i] > o_start[i + 1]);
-    // every lane's 2R searches side by side: a branch-free lower bound with
-    // the same log2(m) steps for all, so their LDS reads are in flight together
-    constexpr int NQ = 2 * R;
-    uint64_t lo[NQ], hi[NQ];
-    int32_t at[NQ];
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-        const RowSpan& rs = mine[i >> 1];
-        lo[i] = (i & 1) ? (uint64_t)rs.w : (uint64_t)rs.x;
-        hi[i] = lo[i] + rs.len;
-        at[i] = 0;  // every output before at[i] ends at or before lo[i]
-    }
-    for (int32_t step = m >> 1; step > 0; step >>= 1) {
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) at[i] += o_end[at[i] + step - 1] <= lo[i] ? step : 0;
-    }
-    bool meet = false;
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-        const int32_t j = threadIdx.x + 256 * (i >> 1);
-        if (j >= count || mine[i >> 1].len == 0) continue;
-        int32_t p = at[i] + (o_end[at[i]] <= lo[i] ? 1 : 0);  // first output ending past lo[i]
-        for (; p < m && o_start[p] < hi[i]; ++p) {
-            const int32_t o = o_row[p];
-            if (o == j) continue;
-            meet = true;
-            bound[j] = 1;  // every writer stores the same value
-            bound[o] = 1;
-        }
-    }
-    // the barriers inside also publish bound[]
-    const int any = workgroup_any2(unknown, meet, fold4);
-    return (any & 1) ? kBoundUnknown : (any & 2) ? kBoundMarked : kNoneBound;
-}
-
-// --- Dependency walk: the bound rows in table order on four wavefronts,
-// each row waiting only for the rows it depends on. Rows are the walk list
-// lst[0..nb) (table indices). For each, dep is the latest earlier row of the
-// list it meets (rows_meet: either reads what the other writes, or both write
-// the same memory), found among the kDagWindow rows before it; if none of
-// those meets it, every row before the window counts as a dependency. dep_w is
-// the same for the earlier outputs that meet its w alone. Wavefront v takes
-// list entries v, v + 4, ... in order, and next[v] is the entry it is on (past
-// its last one when done): all entries up to d are complete exactly when every
-// other wavefront's next is past d. A row issues its w loads once dep_w is
-// complete, its x loads once dep is complete, then sums, applies and stores,
-// waits for its stores and moves next[v] on. The wavefront holding the lowest
-// pending entry always finds its dependencies complete, so the walk never
-// stalls; every wait is still bounded by `cap` polls, after which the walk
-// stops waiting (abort), counts the timeout in g_walk_timeouts and finishes
-// its rows unordered. Every row is a whole number of 16-byte vectors, at most
-// 8192 elements, 16-byte aligned (the round walk's one-wavefront rows).
-constexpr int kDagWindow = 64;
-constexpr uint32_t kDagSpinCap = 1u << 22;
-
-__device__ unsigned int g_walk_timeouts;
-
-// Wait until every list entry up to dep is complete (see above); false when
-// the wait ran out of polls (the walk then aborts its ordering).
-__device__ __forceinline__ bool dag_wait(const int* next, int* abort, int wave, int dep,
-                                         uint32_t cap) {
-    if (dep < 0) return true;
-    for (uint32_t spin = 0;; ++spin) {
-        const bool ok = __hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
-        bool all = true;
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            all &= (v == wave) |
-                   (__hip_atomic_load(next + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) > dep);
-        if (__builtin_amdgcn_readfirstlane((int)(ok | all))) break;
-        if (spin >= cap) {
-            if ((threadIdx.x & 63) == 0) {
-                __hip_atomic_store(abort, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                __hip_atomic_fetch_add(&g_walk_timeouts, 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-            }
-            return false;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // the rows' stores before our loads
-    return true;
-}
-
-template <typename T, int U, bool EXACT>
-__device__ __forceinline__ void dag_row_slices(const T* x, const T* w, T* y, int n, float eps,
-                                               int lane, const int* next, int* abort, int wave,
-                                               int dep_w, int dep, uint32_t cap) {
-    const uint32_t nvec = (uint32_t)n * (uint32_t)sizeof(T) / 16u;
-    SplitPart<T, U, EXACT, false> part;
-    dag_wait(next, abort, wave, dep_w, cap);
-    part.load_w(scalar_gptr(reinterpret_cast<const char*>(w)), 0, lane, nvec);
-    dag_wait(next, abort, wave, dep, cap);
-    part.load_x(scalar_gptr(reinterpret_cast<const char*>(x)), 0, lane, nvec);
-    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    part.chains(p, nvec);
-    const float inv = inverse_rms(split_sumsq(p, lane, T()), n, eps);
-    part.apply(inv, scalar_gptr(reinterpret_cast<char*>(y)), 0, lane, nvec);
-}
-
-// One row of the dependency walk (the round walk's one-wavefront layout).
-template <typename T>
-__device__ __forceinline__ void dag_row(const T* x, const T* w, T* y, int n, float eps, int lane,
-                                        const int* next, int* abort, int wave, int dep_w,
-                                        int dep, uint32_t cap) {
-    const int bytes = n * (int)sizeof(T);
-    const int slices = (bytes + 1023) >> 10;
-#define RMSN_CASE(U)                                                                          \
-    if constexpr (U * 1024 <= 8192 * (int)sizeof(T)) {                                        \
-        if (slices <= U) {                                                                    \
-            if (bytes == U * 1024)                                                            \
-                dag_row_slices<T, U, true>(x, w, y, n, eps, lane, next, abort, wave, dep_w,   \
-                                           dep, cap);                                         \
-            else                                                                              \
-                dag_row_slices<T, U, false>(x, w, y, n, eps, lane, next, abort, wave, dep_w,  \
-                                            dep, cap);                                        \
-            return;                                                                           \
-        }                                                                                     \
-    }
-    RMSN_FOR_ROUND_SLICES(RMSN_CASE)
-#undef RMSN_CASE
-}
-
-template <typename T, bool POS, typename S>
-__device__ __forceinline__ void dag_walk(const S* span, const uint16_t* lst, int32_t nb,
-                                         const rmsn_desc* d, float eps, uint64_t pos,
-                                         const PosArgs& pa, uint32_t cap) {
-    __shared__ int16_t dep[kSpanRows], dep_w[kSpanRows];
-    __shared__ int next[4];
-    __shared__ int abort;
-    for (int32_t i = threadIdx.x; i < nb; i += blockDim.x) {
-        const S a = span[lst[i]];
-        const int32_t lo = max(0, i - kDagWindow);
-        int32_t da = -1, dw = -1;
-        for (int32_t k = i - 1; k >= lo; --k) {
-            const S b = span[lst[k]];
-            if (da < 0 && rows_meet(a, b)) da = k;
-            if (w_meets_output(a, b)) {
-                dw = k;  // meeting w is meeting: da is set too
-                break;
-            }
-        }
-        dep[i] = (int16_t)(da >= 0 ? da : lo - 1);
-        dep_w[i] = (int16_t)(dw >= 0 ? dw : lo - 1);
-    }
-    if (threadIdx.x < 4) next[threadIdx.x] = (int)threadIdx.x;
-    if (threadIdx.x == 0) abort = 0;
-    __syncthreads();
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int lane = threadIdx.x & 63;
-    for (int32_t i = wave; i < nb; i += 4) {
-        const rmsn_desc dd = d[lst[i]];
-        const T* x;
-        const T* w;
-        T* y;
-        persistent_ptrs<T, POS>(dd, pos, pa, x, w, y);
-        dag_row<T>(x, w, y, (int)dd.n, eps, lane, next, &abort, wave, dep_w[i], dep[i], cap);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // our stores before the mark
-        if (lane == 0)
-            __hip_atomic_store(next + wave, (int)(i + 4), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    if (lane == 0)
-        __hip_atomic_store(next + wave, 0x7FFFFFFF, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// Which rows meet another row, on spans of type S in LDS (RowSpan or
-// RowSpan32). Workers (blockIdx > 0) test their row against every row, 256 at
-// a time, and run it when it meets none. In workgroup 0 (unless the ordered
-// outputs already marked the bound rows: `marked`) wavefront v decides
-// rows v, v + 4, ...: its lanes test the row against 64 rows at a time and a
-// ballot gives the answer, so no lane writes inside the loop; then the marked
-// ("bound") rows run in table order, found 64 at a time by a ballot over the
-// marks. Returns as spread_rows does.
-template <typename T, bool POS, typename S>
-__device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const uint8_t* rvec,
-                                          bool marked, const rmsn_desc* d, int32_t count,
-                                          float eps, uint64_t pos, const PosArgs& pa, float* lds4,
-                                          int* fold4, uint32_t cap) {
-    if (blockIdx.x != 0) {
-        const int32_t workers = (int32_t)gridDim.x - 1;
-        for (int32_t j = (int32_t)blockIdx.x - 1; j < count; j += workers) {
-            const S sj = span[j];
-            bool meet = false;
-            for (int32_t k = threadIdx.x; k < count; k += blockDim.x)
-                meet |= (k != j) & rows_meet(sj, span[k]);
-            if (workgroup_any(meet, fold4)) continue;  // bound: workgroup 0 runs it in order
-            spread_row<T, POS>(d[j], pos, pa, eps, lds4);
-            __syncthreads();  // lds4 is reused by the next row
-        }
-        return true;
-    }
-    const int32_t wave = (int32_t)(threadIdx.x >> 6), lane = (int32_t)(threadIdx.x & 63);
-    for (int32_t j = marked ? count : wave; j < count; j += 4) {
-        const S sj = span[j];
-        bool meet = false;
-#pragma unroll 4
-        for (int32_t k = lane; k < count; k += 64) meet |= (k != j) & rows_meet(sj, span[k]);
-        const bool any = __ballot(meet) != 0;
-        if (lane == 0) bound[j] = any;
-    }
-    __syncthreads();
-    // every bound row in the one-wavefront layout: the dependency walk
-    bool not_vec = false;
-    for (int32_t j = threadIdx.x; j < count; j += blockDim.x) not_vec |= bound[j] && !rvec[j];
-    if (!workgroup_any(not_vec, fold4)) {
-        __shared__ uint16_t lst[kSpanRows];
-        __shared__ int32_t nb_shared;
-        if (wave == 0) {
-            // the bound rows in table order, 64 at a time by a ballot
-            int32_t nb = 0;
-            for (int32_t j0 = 0; j0 < count; j0 += 64) {
-                const bool b = j0 + lane < count && bound[j0 + lane] != 0;
-                const unsigned long long marks = __ballot(b);
-                if (b) lst[nb + __builtin_popcountll(marks & ((1ull << lane) - 1ull))] =
-                    (uint16_t)(j0 + lane);
-                nb += __builtin_popcountll(marks);
-            }
-            if (lane == 0) nb_shared = nb;
-        }
-        __syncthreads();
-        dag_walk<T, POS, S>(span, lst, nb_shared, d, eps, pos, pa, cap);
-        return true;
-    }
-    bool some_free = false;
-    for (int32_t j = threadIdx.x; j < count; j += blockDim.x) some_free = some_free || !bound[j];
-    if (!workgroup_any(some_free, fold4)) return false;
-    // the bound rows, row after row, in table order
-    for (int32_t j0 = 0; j0 < count; j0 += 64) {
-        unsigned long long marks = __ballot(j0 + lane < count && bound[j0 + lane] != 0);
-        while (marks) {
-            const int32_t j = j0 + __builtin_ctzll(marks);
-            marks &= marks - 1;
-            spread_row<T, POS>(d[j], pos, pa, eps, lds4);
-            __syncthreads();  // this row's stores before the next bound row's loads
-        }
-    }
-    return true;
-}
-
-// Returns true when this workgroup's part of the table is done, false (in
-// workgroup 0 only) when no row is free, so the ordered walk takes the whole
-// table. (No row writes into the table itself: the walks read descriptors as
-// they go, and this step reads them all first.)
-template <typename T, bool POS>
-__device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, float eps,
-                                            uint64_t pos, const PosArgs& pa, float* lds4,
-                                            int* fold4, uint32_t cap) {
-    __shared__ RowSpan span[kSpanRows];   // 64-bit spans, or RowSpan32 in the same bytes
-    __shared__ uint8_t bound[kSpanRows];
-    __shared__ uint8_t rvec[kSpanRows];   // the row fits the one-wavefront layout
-    __shared__ unsigned long long lo_hi[2];
-    if (threadIdx.x == 0) {
-        lo_hi[0] = ~0ull;
-        lo_hi[1] = 0ull;
-    }
-    __syncthreads();
-    constexpr int R = kSpanRows / 256;     // rows per thread (blockDim.x == 256)
-    RowSpan mine[R];
-    uint64_t lo = ~0ull, hi = 0ull;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int32_t j = threadIdx.x + 256 * r;
-        mine[r] = j < count ? row_span<T, POS>(d[j], pos, pa) : RowSpan{0, 0, 0, 0};
-        if (mine[r].len != 0) {
-            lo = min(lo, (uint64_t)min(mine[r].x, min(mine[r].w, mine[r].y)));
-            hi = max(hi, (uint64_t)max(mine[r].x, max(mine[r].w, mine[r].y)) + mine[r].len);
-        }
-    }
-    // no row meets another (the usual table): the workers run every row
-    int found = kBoundUnknown;
-    if (blockIdx.x == 0) {
-        found = find_bound_rows(mine, count, bound, fold4);
-        if (found == kNoneBound) return true;
-    }
-    // lowest and highest address: within the wavefront, then one LDS atomic each
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        lo = min(lo, (uint64_t)__shfl_xor((unsigned long long)lo, o, 64));
-        hi = max(hi, (uint64_t)__shfl_xor((unsigned long long)hi, o, 64));
-    }
-    if ((threadIdx.x & 63) == 0) {
-        atomicMin(&lo_hi[0], (unsigned long long)lo);
-        atomicMax(&lo_hi[1], (unsigned long long)hi);
-    }
-    __syncthreads();
-    const uintptr_t base = (uintptr_t)lo_hi[0];
-    const bool narrow = lo_hi[1] <= lo_hi[0] || lo_hi[1] - lo_hi[0] < 0xFFFFFFFFull;
-    RowSpan32* span32 = reinterpret_cast<RowSpan32*>(span);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int32_t j = threadIdx.x + 256 * r;
-        if (j >= count) continue;
-        const RowSpan& m = mine[r];
-        rvec[j] = m.len != 0 && m.len % 16 == 0 && m.len <= 8192 * sizeof(T) &&
-                  ((m.x | m.w | m.y) & 15) == 0;
-        if (narrow) span32[j] = row_span32(m, base);
-        else span[j] = m;
-    }
-    __syncthreads();
-    const bool marked = found == kBoundMarked;
-    return narrow ? spread_on<T, POS>(span32, bound, rvec, marked, d, count, eps, pos, pa, lds4,
-                                      fold4, cap)
-                  : spread_on<T, POS>(static_cast<const RowSpan*>(span), bound, rvec, marked, d,
-                                      count, eps, pos, pa, lds4, fold4, cap);
-}
-
-template <typename T, bool POS>
-__global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __restrict__ d,
-                                                             int32_t count, float eps,
-                                                             PosArgs pa, uint32_t cap) {
-    __shared__ float lds4[4];
-    __shared__ float lds8[2][4];
-    __shared__ int lds_fold[4];
-    uint64_t pos = 0;
-    if (POS) {
-        const uint64_t per = (uint64_t)pa.period;
-        const uint64_t raw = (uint64_t)*pa.d_pos;
-        pos = raw < per ? raw : raw % per;
-    }
-    // the launcher gives more than one workgroup only to tables of at most
-    // kSpanRows rows
-    if (gridDim.x > 1 && spread_rows<T, POS>(d, count, eps, pos, pa, lds4, lds_fold, cap)) return;
-    switch (walk_mode<T, POS>(d, count, pos, pa, lds_fold)) {
-        case kRoundWalk16: round_walk<T, POS, 4>(d, count, eps, pos, pa); break;
-        case kRoundWalk4: round_walk<T, POS, 1>(d, count, eps, pos, pa); break;
-#define RMSN_CASE(Q) \
-    case Q: pipelined_walk<T, POS, Q>(d, count, eps, pos, pa, lds8); break;
-        RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)
-#undef RMSN_CASE
-        default: serial_walk<T, POS>(d, count, eps, pos, pa, lds4); break;
-    }
-    // with more than one workgroup the launcher advances the position in a
-    // launch of its own, once every workgroup has read it
-    if (POS && gridDim.x == 1 && threadIdx.x == 0) {
-        const uint64_t per = (uint64_t)pa.period;
-        const_cast<int64_t*>(pa.d_pos)[0] = (int64_t)(pos + 1 == per ? 0 : pos + 1);
-    }
 }
 
 template <typename T, int NCH>
@@ -1881,45 +419,6 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
         return launch_stream_rows(p, x, xs, w, y, ys, rows, n, eps, stream);
     return p.dtype == RMSN_F32 ? launch_block_t<float>(p, x, xs, w, y, ys, n, eps, stream)
                                : launch_block_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
-}
-
-hipError_t launch_sequence_persistent(int dtype, const rmsn_desc* d, int32_t count, float eps,
-                                     const PosArgs* pos, hipStream_t stream) {
-    const PosArgs none{nullptr, 0, 0, 1};
-    // workgroup 0 plus one worker per row (at most kSpreadWorkers) for free rows
-    const bool spread = count > 1 && count <= kSpanRows && option_persistent_workgroups() == 0;
-    const dim3 grid(spread ? 1u + (unsigned)std::min(count, kSpreadWorkers) : 1u), block(kBlockThreads);
-    const int opt_cap = option_walk_spin_cap();
-    const uint32_t cap = opt_cap > 0 ? (uint32_t)opt_cap : kDagSpinCap;
-    if (dtype == RMSN_F32) {
-        if (pos)
-            hipLaunchKernelGGL((k_sequence_persistent<float, true>), grid, block, 0, stream, d,
-                               count, eps, *pos, cap);
-        else
-            hipLaunchKernelGGL((k_sequence_persistent<float, false>), grid, block, 0, stream, d,
-                               count, eps, none, cap);
-    } else {
-        if (pos)
-            hipLaunchKernelGGL((k_sequence_persistent<uint16_t, true>), grid, block, 0, stream, d,
-                               count, eps, *pos, cap);
-        else
-            hipLaunchKernelGGL((k_sequence_persistent<uint16_t, false>), grid, block, 0, stream,
-                               d, count, eps, none, cap);
-    }
-    const hipError_t e = hipGetLastError();
-    // the rows of every workgroup are taken at the position read when the
-    // kernel starts; it is advanced after all of them, by the next launch
-    if (e != hipSuccess || !spread || pos == nullptr) return e;
-    return launch_advance(const_cast<int64_t*>(pos->d_pos), pos->period, stream);
-}
-
-hipError_t walk_timeouts(uint32_t* out, bool reset) {
-    hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_walk_timeouts), sizeof(uint32_t), 0,
-                                       hipMemcpyDeviceToHost);
-    if (e != hipSuccess || !reset) return e;
-    const uint32_t zero = 0;
-    return hipMemcpyToSymbol(HIP_SYMBOL(g_walk_timeouts), &zero, sizeof zero, 0,
-                             hipMemcpyHostToDevice);
 }
 
 hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,

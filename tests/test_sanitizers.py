@@ -81,7 +81,8 @@ def test_library_host_code_under_sanitizer(tmp_path, sanitizer, runtime, options
     common = [str(csrc / f) for f in ("rmsn_aux.hip", "rmsn_api.hip", "rmsn_plan.cpp")]
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     subprocess.check_call([hipcc, *flags, "-o", str(pkg / "librmsnorm_amd.so"),
-                           str(csrc / "rmsn_kernels.hip"), *common])
+                           *[str(csrc / f) for f in ("rmsn_kernels.hip", "rmsn_persistent.hip",
+                                                     "rmsn_wide.hip")], *common])
     subprocess.check_call([hipcc, *flags, "-DRMSN_LANES=128", "-o",
                            str(pkg / "librmsnorm_amd_l128.so"),
                            str(csrc / "rmsn_kernels_l128.hip"), *common])
