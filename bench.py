@@ -52,7 +52,8 @@ ROTATE = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_8192x7168_traffic.json")
 # the sources the prefill kernel is compiled from (its traffic record is tied to them)
 KERNEL_SRCS = [os.path.join(ROOT, "row_wise_rmsnorm_amd", "csrc", f)
-               for f in ("rmsn_kernels.hip", "rmsn_common.h", "rmsn_group.h", "rmsn_launch.h")]
+               for f in ("rmsn_kernels.hip", "rmsn_rows.h", "rmsn_common.h", "rmsn_group.h",
+                         "rmsn_launch.h")]
 
 
 def log(msg):

@@ -481,6 +481,19 @@ int rmsnorm_diag_inverse(uint32_t first_bits, int64_t count, int64_t n, float ep
  * odd. */
 int rmsnorm_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out, void* stream);
 
+/* A plain streaming copy of `bytes` bytes from src to dst (DEVICE memory, not
+ * overlapping, both 16-byte aligned, bytes a positive multiple of 16) on
+ * `stream`: each lane loads and stores `vectors` 16-byte vectors (1, 2 or 4)
+ * with non-temporal hints, in workgroups of `block` threads (a multiple of
+ * 64, at most 1024), workgroup b taking the next vectors * block vectors.
+ * It moves the same bytes as a norm of rows of that size and does nothing
+ * else, so its time bounds what a row kernel's access pattern can reach on
+ * this memory system (Lecture 04 section 3.1: compare the measured time with
+ * the floor the bytes set). RMSN_EINVAL for a null, misaligned or
+ * overlapping pointer, a bad size, vector count or block. */
+int rmsnorm_diag_copy(const void* src, void* dst, int64_t bytes, int vectors, int block,
+                      void* stream);
+
 /* Waits of rmsnorm_sequence_persistent's ordered walk that ran out of polls
  * (RMSN_OPT_WALK_SPIN_CAP) on the current device since the last reset: *out
  * (host). A launch in which a wait timed out stops ordering its rows, so its

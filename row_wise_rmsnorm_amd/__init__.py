@@ -83,6 +83,7 @@ def bind(path):
         "rmsnorm_batched_rows_ws": [c_int, vp, i64, vp, vp, i64, i64, i64, f, vp, i64, vp],
         "rmsnorm_batched_rows_noalloc": [c_int, vp, i64, vp, vp, i64, i64, i64, f, vp],
         "rmsnorm_diag_walk_timeouts": [ctypes.POINTER(u32), c_int],
+        "rmsnorm_diag_copy": [vp, vp, i64, c_int, c_int, vp],
         "rmsnorm_workspace_query": [c_int, i64, i64, c_int, ctypes.POINTER(_PlanInfo),
                                     ctypes.POINTER(i64)],
         "rmsnorm_sequence_eager": [c_int, vp, vp, i32, f, vp],
@@ -124,7 +125,7 @@ EXPORTED = ("rmsnorm_f32", "rmsnorm_bf16", "rmsnorm_batched_rows", "rmsnorm_sequ
             "rmsnorm_sequence_graph_create_positioned", "rmsnorm_sequence_graph_update",
             "rmsnorm_association_lanes", "rmsnorm_sequence_persistent",
             "rmsnorm_batched_rows_ws", "rmsnorm_workspace_query",
-            "rmsnorm_batched_rows_noalloc", "rmsnorm_diag_walk_timeouts")
+            "rmsnorm_batched_rows_noalloc", "rmsnorm_diag_walk_timeouts", "rmsnorm_diag_copy")
 
 
 def lib():
@@ -502,6 +503,23 @@ def diag_bf16(first_bits, count, out, stream=None):
         _check(_lib.rmsnorm_diag_bf16(int(first_bits), int(count),
                                       ctypes.c_void_p(out.data_ptr()),
                                       _stream_ptr(stream, out.device)))
+
+
+def diag_copy(src, dst, vectors=1, block=64, stream=None):
+    """Streaming copy of src's bytes into dst (contiguous device tensors of
+    equal byte size, a multiple of 16): `vectors` 16-byte vectors per lane,
+    `block` threads per workgroup (diagnostic: the copy-pattern ceiling)."""
+    for name, t in (("src", src), ("dst", dst)):
+        _device_tensor(t, name)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or src.device != dst.device:
+        raise ValueError("src and dst must hold the same number of bytes on one device")
+    with _on(src.device):
+        _check(_lib.rmsnorm_diag_copy(ctypes.c_void_p(src.data_ptr()),
+                                      ctypes.c_void_p(dst.data_ptr()), nbytes, int(vectors),
+                                      int(block), _stream_ptr(stream, src.device)))
 
 
 def diag_walk_timeouts(reset=False, device=None):

@@ -637,6 +637,33 @@ int rmsnorm_get_option(int key, int* value) {
     return get_option(key, value);
 }
 
+int rmsnorm_diag_copy(const void* src, void* dst, int64_t bytes, int vectors, int block,
+                      void* stream) {
+    clear_error();
+    const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+    if (!src || !dst || (a | b) % 16) {
+        set_error("src and dst must be non-null and 16-byte aligned (src=%p dst=%p)", src, dst);
+        return RMSN_EINVAL;
+    }
+    if (bytes <= 0 || bytes % 16) {
+        set_error("bytes must be a positive multiple of 16, got %lld", (long long)bytes);
+        return RMSN_EINVAL;
+    }
+    if (a < b + (uint64_t)bytes && b < a + (uint64_t)bytes) {
+        set_error("src and dst overlap");
+        return RMSN_EINVAL;
+    }
+    if ((vectors != 1 && vectors != 2 && vectors != 4) || block < 64 || block > 1024 ||
+        block % 64) {
+        set_error("vectors must be 1, 2 or 4 and block a multiple of 64 up to 1024 (got %d, %d)",
+                  vectors, block);
+        return RMSN_EINVAL;
+    }
+    const hipError_t e = launch_diag_copy(src, dst, bytes, vectors, block,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? RMSN_OK : hip_fail("diagnostic copy launch", e);
+}
+
 int rmsnorm_diag_walk_timeouts(uint32_t* out, int reset) {
     clear_error();
     if (!out) {

@@ -1,6 +1,8 @@
 // rmsn_aux.hip -- the small kernels every build of the library carries: the
-// position update of a positioned sequence and the diagnostics that run the
-// row kernels' own steps 4-7 and bf16 narrowing over bit-pattern ranges.
+// position update of a positioned sequence, the diagnostics that run the
+// row kernels' own steps 4-7 and bf16 narrowing over bit-pattern ranges, and
+// a plain streaming copy that measures what the memory system gives a pure
+// copy of the same bytes (the ceiling the row kernels are compared with).
 #include "rmsn_common.h"
 
 namespace rmsn {
@@ -43,7 +45,46 @@ __global__ __launch_bounds__(256) void k_diag_inverse(uint32_t first, int64_t co
     inv_out[i] = reciprocal(r);
 }
 
+// Copy of nvec 16-byte vectors: workgroup b takes V * blockDim.x consecutive
+// vectors, lane t vectors t, t + blockDim.x, ... of them; non-temporal loads
+// and stores (the streaming hints the prefill kernel uses).
+template <int V>
+__global__ void k_diag_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                            uint64_t nvec) {
+    const uint64_t base = (uint64_t)blockIdx.x * blockDim.x * V + threadIdx.x;
+    u32x4 v[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const uint64_t i = base + (uint64_t)k * blockDim.x;
+        if (i < nvec) v[k] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        const uint64_t i = base + (uint64_t)k * blockDim.x;
+        if (i < nvec) __builtin_nontemporal_store(v[k], dst + i);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_diag_copy(const void* src, void* dst, int64_t bytes, int vectors, int block,
+                            hipStream_t stream) {
+    const uint64_t nvec = (uint64_t)bytes / 16u;
+    const uint64_t per = (uint64_t)block * (uint64_t)vectors;
+    const uint64_t groups = (nvec + per - 1) / per;
+    if (groups > 0x7FFFFFFFull || groups * (uint64_t)block > 0xFFFFFFFFull)
+        return hipErrorInvalidConfiguration;
+    const u32x4* a = static_cast<const u32x4*>(src);
+    u32x4* b = static_cast<u32x4*>(dst);
+    const dim3 grid((unsigned)groups), blk((unsigned)block);
+    switch (vectors) {
+        case 1: hipLaunchKernelGGL(k_diag_copy<1>, grid, blk, 0, stream, a, b, nvec); break;
+        case 2: hipLaunchKernelGGL(k_diag_copy<2>, grid, blk, 0, stream, a, b, nvec); break;
+        case 4: hipLaunchKernelGGL(k_diag_copy<4>, grid, blk, 0, stream, a, b, nvec); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_advance(int64_t* d_pos, int64_t period, hipStream_t stream) {
     hipLaunchKernelGGL(k_advance, dim3(1), dim3(64), 0, stream, d_pos, period);

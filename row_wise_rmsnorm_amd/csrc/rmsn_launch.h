@@ -56,6 +56,11 @@ hipError_t walk_timeouts(uint32_t* out, bool reset);
 // update of a positioned sequence).
 hipError_t launch_advance(int64_t* d_pos, int64_t period, hipStream_t stream);
 
+// A streaming copy of `bytes` (a multiple of 16) with `vectors` 16-byte
+// vectors per lane in workgroups of `block` threads (diagnostic).
+hipError_t launch_diag_copy(const void* src, void* dst, int64_t bytes, int vectors, int block,
+                            hipStream_t stream);
+
 // Step 8's bf16 narrowing over consecutive bit patterns (diagnostic).
 hipError_t launch_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out,
                             hipStream_t stream);

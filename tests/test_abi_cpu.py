@@ -596,3 +596,33 @@ def test_replica_plan(rn):
         rn.set_option(rn.OPT_PATH, rn.PATH_AUTO)
         rn.set_option(rn.OPT_REPLICA_PARTS, 0)
     assert rn.plan_query(rn.F32, 1, 7168)["path"] == rn.PATH_GROUP
+
+
+def test_walk_spin_cap_option_and_diagnostics_reject(rn):
+    """The ordered walk's spin cap: 0 (default) or 1..2^30, round-trips;
+    the timeout counter needs an output; the diagnostic copy refuses bad
+    pointers, sizes, vector counts and blocks before any HIP call."""
+    assert rn.get_option(rn.OPT_WALK_SPIN_CAP) == 0
+    try:
+        for v in (1, 1000, 1 << 30):
+            rn.set_option(rn.OPT_WALK_SPIN_CAP, v)
+            assert rn.get_option(rn.OPT_WALK_SPIN_CAP) == v
+        for bad in (-1, (1 << 30) + 1):
+            with pytest.raises(rn.RmsnormError):
+                rn.set_option(rn.OPT_WALK_SPIN_CAP, bad)
+    finally:
+        rn.set_option(rn.OPT_WALK_SPIN_CAP, 0)
+    L = rn.lib()
+    assert L.rmsnorm_diag_walk_timeouts(None, 0) == rn.RMSN_EINVAL
+    S, D = 0x100000, 0x900000
+    good = dict(src=S, dst=D, nbytes=1 << 20, v=1, b=64)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return L.rmsnorm_diag_copy(a["src"], a["dst"], a["nbytes"], a["v"], a["b"], None)
+
+    for kw in (dict(src=0), dict(dst=0), dict(src=S + 8), dict(dst=D + 4), dict(nbytes=0),
+               dict(nbytes=100), dict(nbytes=-16), dict(dst=S + 4096), dict(v=3), dict(v=0),
+               dict(b=32), dict(b=96), dict(b=2048)):
+        assert call(**kw) == rn.RMSN_EINVAL, kw
+    assert call() != rn.RMSN_EINVAL          # valid: without a GPU the launch itself fails
