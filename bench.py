@@ -32,6 +32,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D]
        python bench.py --profile-kernels     (short run for rocprofv3 counters)
        python bench.py --profile-decode      (the same, decode step: eager + persistent)
        python bench.py --profile-persistent spread|one|chained   (one persistent arm)
+       python bench.py --profile-copy        (prefill kernel beside the copy-pattern ceilings)
 """
 import argparse
 import hashlib
@@ -49,6 +50,8 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak, 8 TB/s
 METRIC = ("RMSNorm achieved HBM GB/s (% of peak) + µs per 327-norm decode step "
           "(graph vs eager)")
 ROTATE = 4
+# (16-byte vectors per lane, threads per workgroup) of the copy-pattern ceilings
+COPY_PATTERNS = ((1, 64), (2, 448), (1, 1024))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_8192x7168_traffic.json")
 # the sources the prefill kernel is compiled from (its traffic record is tied to them)
 KERNEL_SRCS = [os.path.join(ROOT, "row_wise_rmsnorm_amd", "csrc", f)
@@ -155,6 +158,16 @@ def bench_prefill(rn, torch, np, wl, steps, warmup):
     # a plain device copy of the same bytes (x read, y written), rotated the
     # same way: the practical bandwidth ceiling of this traffic pattern
     copy_us = 1000.0 * elapsed_ms(lambda i: ys[i % ROTATE].copy_(xs[i % ROTATE]), steps) / steps
+    # the library's streaming copy of the same bytes in three granularities:
+    # 1 KB per 64-thread workgroup (the fastest pattern measured), the
+    # prefill kernel's own 14 KB per workgroup of 448 threads (two 16-byte
+    # vectors per lane) and 16 KB per 1024-thread workgroup
+    copy_patterns = {}
+    for v, b in COPY_PATTERNS:
+        fn = lambda i, v=v, b=b: rn.diag_copy(xs[i % ROTATE], ys[i % ROTATE], v, b)
+        for i in range(20):
+            fn(i)
+        copy_patterns[f"{v}x16B_per_lane_{b}_threads"] = 1000.0 * elapsed_ms(fn, steps) / steps
     # the timed kernel (automatic plan) and the WAVE kernel, another layout,
     # give the same bytes (parity with the oracle is the tests' job); the copy
     # above overwrote the output buffers, so both run once more
@@ -173,6 +186,7 @@ def bench_prefill(rn, torch, np, wl, steps, warmup):
         "warm_gbs": algo_bytes / (warm * 1e-6) / 1e9,
         "warm_cached_us": warm_cached, "rotated_cached_us": rot_cached,
         "copy_us": copy_us, "copy_gbs": (rows * n * 4) / (copy_us * 1e-6) / 1e9,
+        "copy_patterns_us": copy_patterns,
         "wave_path_us": wave_us, "wave_path_plan": wave_plan,
         "rows_per_s": rows / (us * 1e-6), "bit_exact_vs_wave_layout": parity,
         "host": (xb, wb),
@@ -733,8 +747,9 @@ def cpu_baseline(np, wl, host):
 
 def profile_kernels(rn, torch, np, wl):
     """Short run for counter collection: 5 prefill launches, 5 launches each
-    of the 64-row bf16 batch and of the single binary32 row, and 5 copies of
-    a 1 GiB buffer (a plain copy of known size to scale the counters)."""
+    of the 64-row bf16 batch and of the single binary32 row, 5 of each of the
+    first two copy patterns on the prefill's buffers, and 5 copies of a 1 GiB
+    buffer (a plain copy of known size to scale the counters)."""
     rows, n = wl.PREFILL_SHAPE
     dev = torch.device("cuda", 0)
     g = torch.Generator(device=dev)
@@ -752,6 +767,9 @@ def profile_kernels(rn, torch, np, wl):
     y1 = torch.empty_like(x1)
     for _ in range(5):
         rn.rmsnorm_f32(x1, w1, float(wl.EPS), out=y1)
+    for v, b in COPY_PATTERNS[:2]:
+        for _ in range(5):
+            rn.diag_copy(x, y, v, b)
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(5):
@@ -776,6 +794,31 @@ def profile_decode(rn, torch, np, wl):
     torch.cuda.synchronize()
     print(json.dumps({"profile_decode": "done", "eager_launches": len(widths),
                       "persistent_launches": 3}), flush=True)
+
+
+def profile_copy(rn, torch, np, wl, launches=200):
+    """A short run for a kernel trace of the prefill kernel beside the
+    copy-pattern ceilings on the same rotated buffers: 300 warm-up launches,
+    then `launches` of the prefill kernel and of each pattern of
+    COPY_PATTERNS (told apart in the trace by their workgroup size)."""
+    rows, n = wl.PREFILL_SHAPE
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    xs = [torch.randn(rows, n, device=dev, generator=g).to(torch.bfloat16) for _ in range(ROTATE)]
+    w = (1.0 + 0.1 * torch.randn(n, device=dev, generator=g)).to(torch.bfloat16)
+    ys = [torch.empty_like(xs[0]) for _ in range(ROTATE)]
+    eps = float(wl.EPS)
+    pre = lambda i: rn.rmsnorm_batched_rows(xs[i % ROTATE], w, eps, out=ys[i % ROTATE])
+    for i in range(300):
+        pre(i)
+    out = {"prefill_us": 1000.0 * elapsed_ms(pre, launches) / launches}
+    for v, b in COPY_PATTERNS:
+        fn = lambda i, v=v, b=b: rn.diag_copy(xs[i % ROTATE], ys[i % ROTATE], v, b)
+        for i in range(50):
+            fn(i)
+        out[f"copy_{v}x16B_{b}_threads_us"] = 1000.0 * elapsed_ms(fn, launches) / launches
+    print(json.dumps({"profile_copy": out, "launches": launches}), flush=True)
 
 
 def profile_persistent(rn, torch, np, wl, arm, launches=200):
@@ -821,6 +864,8 @@ def main():
                     help="short decode-step run for counter collection")
     ap.add_argument("--profile-wide", action="store_true",
                     help="a short run of the wide-row shapes for a kernel trace")
+    ap.add_argument("--profile-copy", action="store_true",
+                    help="prefill kernel and copy-pattern ceilings on the same buffers (trace)")
     ap.add_argument("--profile-persistent", choices=["spread", "one", "chained"],
                     help="200 launches of one persistent arm of the decode step (kernel trace)")
     ap.add_argument("--sections", default="prefill,single,batch64,decode",
@@ -849,6 +894,9 @@ def main():
         return
     if args.profile_wide:
         profile_wide(rn, torch, np, wl)
+        return
+    if args.profile_copy:
+        profile_copy(rn, torch, np, wl)
         return
     if args.profile_persistent:
         profile_persistent(rn, torch, np, wl, args.profile_persistent)
@@ -952,6 +1000,11 @@ def main():
             "wave_path_gbs": round(pre["algo_bytes"] / (pre["wave_path_us"] * 1e-6) / 1e9, 1),
             "wave_path_plan": pre["wave_path_plan"],
             "copy_reference_us": round(pre["copy_us"], 3),
+            "copy_patterns_us": {k: round(v, 3) for k, v in pre["copy_patterns_us"].items()},
+            "copy_patterns_note": ("rmsnorm_diag_copy of the same bytes (x read, y written), "
+                                   "rotated like the timed launches: the ceiling a pure copy of "
+                                   "each granularity reaches; 2x16B_per_lane_448_threads moves "
+                                   "one prefill row per workgroup"),
             "copy_reference_gbs": round(pre["copy_gbs"], 1),
             "fraction_of_copy": round(pre["copy_us"] / pre["us_per_launch"], 4),
             "bit_exact_vs_wave_layout": pre["bit_exact_vs_wave_layout"],

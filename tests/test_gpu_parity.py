@@ -521,3 +521,18 @@ def test_mean_division_sampled(rn):
         i_ref = np.float32(1.0) / r_ref
         assert np.array_equal(f32_host(r_d).view(np.uint32), r_ref.view(np.uint32)), (n, eps)
         assert np.array_equal(f32_host(i_d).view(np.uint32), i_ref.view(np.uint32)), (n, eps)
+
+
+@pytest.mark.parametrize("vectors,block", [(1, 64), (2, 448), (4, 256), (1, 1024)])
+def test_diag_copy(rn, vectors, block):
+    """The diagnostic streaming copy moves exactly the requested bytes: sizes
+    that are and are not a whole number of workgroups, nothing written past
+    the end."""
+    for nbytes in (16, 16 * 64 * vectors * 3, 16 * (64 * vectors * 7 + 5), 1 << 20):
+        say(f"diag copy {vectors} x 16 B, {block} threads, {nbytes} bytes")
+        src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev())
+        dst = torch.full((nbytes // 4 + 64,), 0x5A5A5A5A, dtype=torch.int32, device=dev())
+        rn.diag_copy(src, dst[:nbytes // 4], vectors, block)
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:nbytes // 4], src)
+        assert (dst[nbytes // 4:] == 0x5A5A5A5A).all()
