@@ -31,7 +31,7 @@ cache defeated by rotating over 4 buffer sets (940 MB). Also reported:
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps D]
        python bench.py --profile-kernels     (short run for rocprofv3 counters)
        python bench.py --profile-decode      (the same, decode step: eager + persistent)
-       python bench.py --profile-persistent spread|one|chained   (one persistent arm)
+       python bench.py --profile-persistent spread|one|chained|chained_offset   (one persistent arm)
        python bench.py --profile-copy        (prefill kernel beside the copy-pattern ceilings)
 """
 import argparse
@@ -404,7 +404,9 @@ def geometry_audit(single, b64, dec, nodes, pre, plan_prefill):
     gdev = dec["persistent_graph_captured_us_per_step"]
     for key, name, grid in (("spread", "spread over workgroups", 256),
                             ("one_workgroup", "one workgroup", 1),
-                            ("chained_table", "chained table (every row bound)", 256)):
+                            ("chained_table", "chained table (every row bound, run walk)", 256),
+                            ("chained_offset_table",
+                             "chained table read 8 elements off (dependency walk)", 256)):
         add("decode step, persistent (graph-timed)", f"k_sequence_persistent, {name}", grid, 256,
             1, gdev[key]["mean"], gdev[key]["sd"], step_bytes)
     rows.sort(key=lambda r: -r["above_floor_us_per_step"])
@@ -555,6 +557,20 @@ def bench_decode(rn, torch, np, wl, decode_steps):
     torch.cuda.synchronize()
     ok_c = all(np.array_equal(a, t.cpu().numpy().view(np.uint32)) for a, t in zip(want, ys))
     chained_us = stats([rep(chained) for _ in range(4)])
+    # the same chains with each x 8 elements past the output it reads: the
+    # rows meet at other than the same addresses, so the dependency walk
+    # orders them instead of the run walk
+    otable = offset_chained_table(rn, torch, xs, ws, widths)
+    for t in otable[1]:
+        t.fill_(float("nan"))
+    rn.rmsnorm_sequence_eager(otable[0], widths, eps, rn.F32)
+    torch.cuda.synchronize()
+    want_o = [t.cpu().numpy().view(np.uint32).copy() for t in otable[1]]
+    for t in otable[1]:
+        t.fill_(float("nan"))
+    rn.rmsnorm_sequence_persistent(otable[0], len(widths), eps, rn.F32)
+    torch.cuda.synchronize()
+    ok_o = all(np.array_equal(a, t.cpu().numpy().view(np.uint32)) for a, t in zip(want_o, otable[1]))
     # the same three arms captured in a graph (no host in the loop): the
     # persistent kernel's own time on the device
     pers_s = lambda tbl: (lambda st: rn.rmsnorm_sequence_persistent(tbl, len(widths), eps, rn.F32,
@@ -566,6 +582,7 @@ def bench_decode(rn, torch, np, wl, decode_steps):
     finally:
         rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 0)
     dev_chained = graph_us_per_launch(torch, pers_s(ctable), per_graph=10, replays=5, reps=5)
+    dev_offset = graph_us_per_launch(torch, pers_s(otable[0]), per_graph=10, replays=5, reps=5)
     timeouts = rn.diag_walk_timeouts(reset=True)
     algo = sum(n * 12 for n in widths)
     nodes = g.node_count()
@@ -579,13 +596,18 @@ def bench_decode(rn, torch, np, wl, decode_steps):
         "persistent_one_workgroup_us_per_step": one_wg,
         "persistent_chained_table_us_per_step": chained_us,
         "persistent_graph_captured_us_per_step": {"spread": dev_spread, "one_workgroup": dev_one,
-                                                  "chained_table": dev_chained},
+                                                  "chained_table": dev_chained,
+                                                  "chained_offset_table": dev_offset},
         "persistent_walk_timeouts": timeouts,
         "bit_exact_chained_persistent_eq_eager": bool(ok_c),
+        "bit_exact_chained_offset_persistent_eq_eager": bool(ok_o),
         "persistent_note": ("the step's norms share no memory, so the persistent launch runs them "
                             "on up to 256 workgroups; one_workgroup: the whole table walked by one "
                             "workgroup; chained_table: the same widths with norm j reading the "
-                            "previous same-width norm's output, so every row keeps table order; "
+                            "previous same-width norm's output, so every row keeps table order "
+                            "(run walk: the rows meet at the same addresses); "
+                            "chained_offset_table: the same chains read 8 elements past each "
+                            "output (dependency walk); "
                             "the *_us_per_step figures are host calls timed back to back, the "
                             "graph_captured ones the same launches replayed from a graph "
                             "(device time, no host in the loop)"),
@@ -821,11 +843,28 @@ def profile_copy(rn, torch, np, wl, launches=200):
     print(json.dumps({"profile_copy": out, "launches": launches}), flush=True)
 
 
+def offset_chained_table(rn, torch, xs, ws, widths, shift=8):
+    """The decode step's widths with norm j reading the output of the previous
+    norm of its width `shift` elements on (outputs padded by `shift`): every
+    row bound to table order, the rows meeting at other than the same
+    addresses. Returns the table and the padded outputs' row views."""
+    pads = [torch.empty(n + shift, dtype=torch.float32, device=xs[0].device) for n in widths]
+    ys = [p[:n] for p, n in zip(pads, widths)]
+    last, cx = {}, []
+    for j, n in enumerate(widths):
+        cx.append(pads[last[n]][shift:shift + n] if n in last else xs[j])
+        last[n] = j
+    table, _ = rn.make_table(list(zip(cx, ws, ys)))
+    return table, ys, pads
+
+
 def profile_persistent(rn, torch, np, wl, arm, launches=200):
     """A short run of one persistent arm of the decode step, so a kernel trace
     has one row per arm: 'spread' (the step's independent rows over up to 256
     workgroups), 'one' (the whole table in one workgroup), 'chained' (each norm
-    reading the previous same-width norm's output: every row in table order)."""
+    reading the previous same-width norm's output: every row in table order,
+    the run walk), 'chained_offset' (the same chains read 8 elements past each
+    output: the dependency walk)."""
     rows = wl.decode()
     dev = torch.device("cuda", 0)
     xs = [torch.from_numpy(x).to(dev) for x, _ in rows]
@@ -838,6 +877,8 @@ def profile_persistent(rn, torch, np, wl, arm, launches=200):
             cx.append(ys[last[n]] if n in last else xs[j])
             last[n] = j
         table, _ = rn.make_table(list(zip(cx, ws, ys)))
+    elif arm == "chained_offset":
+        table, ys, pads = offset_chained_table(rn, torch, xs, ws, widths)
     else:
         table, _ = rn.make_table(list(zip(xs, ws, ys)))
     rn.set_option(rn.OPT_PERSISTENT_WORKGROUPS, 1 if arm == "one" else 0)
@@ -866,7 +907,7 @@ def main():
                     help="a short run of the wide-row shapes for a kernel trace")
     ap.add_argument("--profile-copy", action="store_true",
                     help="prefill kernel and copy-pattern ceilings on the same buffers (trace)")
-    ap.add_argument("--profile-persistent", choices=["spread", "one", "chained"],
+    ap.add_argument("--profile-persistent", choices=["spread", "one", "chained", "chained_offset"],
                     help="200 launches of one persistent arm of the decode step (kernel trace)")
     ap.add_argument("--sections", default="prefill,single,batch64,decode",
                     help="comma list of prefill,single,batch64,decode,positioned,wide (for "
@@ -936,7 +977,8 @@ def main():
     dec = bench_decode(rn, torch, np, wl, args.decode_steps)
     gd = dec["persistent_graph_captured_us_per_step"]
     log(f"persistent, graph-timed: spread {gd['spread']['mean']:.2f} us, one workgroup "
-        f"{gd['one_workgroup']['mean']:.1f} us, chained {gd['chained_table']['mean']:.1f} us; "
+        f"{gd['one_workgroup']['mean']:.1f} us, chained {gd['chained_table']['mean']:.1f} us, "
+        f"chained 8 elements off {gd['chained_offset_table']['mean']:.1f} us; "
         f"walk timeouts {dec['persistent_walk_timeouts']}")
     log(f"decode eager {dec['eager_us_per_step']['mean']:.1f} us  "
         f"graph {dec['graph_us_per_step']['mean']:.1f} us  "

@@ -255,20 +255,28 @@ int rmsnorm_sequence_graph_update(rmsn_graph* g, const int64_t* h_widths, int32_
  * kernel as the endpoint of capturing many); the bits equal
  * rmsnorm_sequence_eager's. Rows that share no memory with any other row
  * (their reads and output meet no other row's output, their output no other
- * row's reads) cannot observe the order and run in parallel over up to 255
- * more workgroups. The others ("bound") keep table order in the first
- * workgroup, so a table in which a later x is an earlier y (y_i == x_j,
- * i < j) computes exactly what the launch sequence computes. When every bound
- * row is a whole number of 16-byte vectors, 16-byte aligned and at most 8192
- * elements, the four wavefronts of that workgroup take one bound row each and
- * a row starts only once every earlier bound row it shares memory with has
- * finished (its stores complete), found among the 64 bound rows before it;
- * independent bound rows overlap. Otherwise each bound row is finished --
- * its stores ordered before the next row's loads by a workgroup barrier --
- * before the next starts. The waits are bounded (RMSN_OPT_WALK_SPIN_CAP); a
- * wait that runs out is counted (rmsnorm_diag_walk_timeouts). Tables of more
- * than 1024 rows, and RMSN_OPT_PERSISTENT_WORKGROUPS = 1, keep every row in
- * one workgroup.
+ * row's reads) cannot observe the order and run in parallel over up to 252
+ * workgroups. The others ("bound") keep table order, so a table in which a
+ * later x is an earlier y (y_i == x_j, i < j) computes exactly what the
+ * launch sequence computes. They fall into components (rows that share
+ * memory directly or through other bound rows); the first four workgroups
+ * each take whole components, in table order within each:
+ *  - when every row of a workgroup's components is at most 8192 elements, a
+ *    multiple of 4, quad-aligned, and its rows share memory only at ranges
+ *    a multiple of 1024 elements apart, the workgroup's four wavefronts share
+ *    each row in a fixed mapping (every address is then read and written by
+ *    one thread) and the next rows' loads are issued early; a row whose x is
+ *    exactly the previous row's output takes it from registers;
+ *  - else, when every such row is a whole number of 16-byte vectors,
+ *    16-byte aligned and at most 8192 elements, the four wavefronts take one
+ *    row each and a row starts only once every earlier row it shares memory
+ *    with has finished (its stores complete), found among the 64 rows before
+ *    it; these waits are bounded (RMSN_OPT_WALK_SPIN_CAP), and a wait that
+ *    runs out is counted (rmsnorm_diag_walk_timeouts);
+ *  - otherwise row after row, each row's stores ordered before the next
+ *    row's loads by a workgroup barrier.
+ * Tables of more than 1024 rows, and RMSN_OPT_PERSISTENT_WORKGROUPS = 1,
+ * keep every row in one workgroup.
  * Widths come from the table (any n in [1, 2^24], any element alignment); no
  * host widths are needed. No row may write into the descriptor table itself.
  * pos: NULL, or the rows are taken at the position as in

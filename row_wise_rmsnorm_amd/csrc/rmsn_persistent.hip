@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "rmsn_common.h"
 #include "rmsn_group.h"
@@ -284,9 +285,12 @@ __device__ __forceinline__ void round_walk(const rmsn_desc* d, int32_t count, fl
 constexpr int kRoundWalk4 = 100;
 constexpr int kRoundWalk16 = 101;
 constexpr int kSpanRows = 1024;  // output ranges published in LDS (16 KB)
-// Worker workgroups for free rows: with workgroup 0, one wave of workgroups on
-// the 256 CUs (the kernel's registers allow one workgroup per CU).
-constexpr int kSpreadWorkers = 255;
+// Workgroups of the spread launch: kWalkers "walkers" that take the rows bound
+// to table order (each walks whole components of them, see spread_on), then
+// workers for the free rows -- one wave of workgroups on the 256 CUs (the
+// kernel's registers allow one workgroup per CU).
+constexpr int kWalkers = 4;
+constexpr int kSpreadWorkers = 256 - kWalkers;
 
 __device__ __forceinline__ bool ranges_meet(uintptr_t a, uintptr_t la, uintptr_t b, uintptr_t lb) {
     return a < b + lb && b < a + la;
@@ -480,10 +484,15 @@ __device__ __forceinline__ void serial_walk(const rmsn_desc* d, int32_t count, f
 // other row's output, and whose output meets no other row's reads, can run at
 // any time, in any workgroup: the order of the table cannot be observed on it.
 // With more than one workgroup launched (tables of at most kSpanRows rows; a
-// positioned table's rows taken at its position), workgroups 1..G-1 take such
-// "free" rows (row j in workgroup 1 + j mod (G-1)) while workgroup 0 runs the
-// others ("bound" rows) in table order. Both sides decide freeness from the same descriptors by the same
-// rule, so every row is run exactly once; no workgroup waits for another.
+// positioned table's rows taken at its position), workgroups W..G-1 take such
+// "free" rows (row j in workgroup W + j mod (G-W)), while the first W
+// workgroups (the walkers) run the others ("bound" rows) in table order. The
+// bound rows fall into components, groups of rows that meet one another
+// directly or through other rows; rows of different components share no
+// memory, so each component only needs its own order, and the walkers take
+// whole components each. Every workgroup decides from the same descriptors
+// by the same rules, so every row is run exactly once; no workgroup waits for
+// another.
 
 struct RowSpan {
     uintptr_t x, w, y, len;  // addresses and byte length; 0 for a width the kernels skip
@@ -543,6 +552,71 @@ __device__ __forceinline__ bool rows_meet(const RowSpan32& a, const RowSpan32& b
            ((b.w < a.ye) & (a.y < b.we));
 }
 
+// Whether two ranges that meet start a multiple of the run walk's period
+// apart (1024 elements: `pmask` is its byte length less one), so that each
+// address of both is taken by the same thread of that walk.
+__device__ __forceinline__ bool off_period(uintptr_t a, uintptr_t b, uint32_t pmask) {
+    return ((uint32_t)(a - b) & pmask) != 0;
+}
+
+// Rows a and b meet (rows_meet) at some pair of ranges whose starts are not a
+// multiple of the period apart.
+__device__ __forceinline__ bool rows_meet_off(const RowSpan& a, const RowSpan& b, uint32_t pmask) {
+    const uintptr_t ae = a.len, be = b.len;
+    const bool xb = (a.x < b.y + be) & (b.y < a.x + ae) & off_period(a.x, b.y, pmask);
+    const bool wb = (a.w < b.y + be) & (b.y < a.w + ae) & off_period(a.w, b.y, pmask);
+    const bool yy = (a.y < b.y + be) & (b.y < a.y + ae) & off_period(a.y, b.y, pmask);
+    const bool xa = (b.x < a.y + ae) & (a.y < b.x + be) & off_period(b.x, a.y, pmask);
+    const bool wa = (b.w < a.y + ae) & (a.y < b.w + be) & off_period(b.w, a.y, pmask);
+    return (ae != 0) & (be != 0) & (xb | wb | yy | xa | wa);
+}
+__device__ __forceinline__ bool rows_meet_off(const RowSpan32& a, const RowSpan32& b,
+                                              uint32_t pmask) {
+    const bool xb = (a.x < b.ye) & (b.y < a.xe) & off_period(a.x, b.y, pmask);
+    const bool wb = (a.w < b.ye) & (b.y < a.we) & off_period(a.w, b.y, pmask);
+    const bool yy = (a.y < b.ye) & (b.y < a.ye) & off_period(a.y, b.y, pmask);
+    const bool xa = (b.x < a.ye) & (a.y < b.xe) & off_period(b.x, a.y, pmask);
+    const bool wa = (b.w < a.ye) & (a.y < b.we) & off_period(b.w, a.y, pmask);
+    return xb | wb | yy | xa | wa;
+}
+
+// What the run walk reads of a span: byte length, addresses (the 32-bit
+// offsets are from `base`), and the tests it makes against the row before.
+__device__ __forceinline__ uint32_t span_bytes(const RowSpan& s) { return (uint32_t)s.len; }
+__device__ __forceinline__ uint32_t span_bytes(const RowSpan32& s) { return s.xe - s.x; }
+__device__ __forceinline__ void span_addrs(const RowSpan& s, uintptr_t, uintptr_t& x,
+                                           uintptr_t& w, uintptr_t& y) {
+    x = s.x;
+    w = s.w;
+    y = s.y;
+}
+__device__ __forceinline__ void span_addrs(const RowSpan32& s, uintptr_t base, uintptr_t& x,
+                                           uintptr_t& w, uintptr_t& y) {
+    x = base + s.x;
+    w = base + s.w;
+    y = base + s.y;
+}
+__device__ __forceinline__ bool x_meets_output(const RowSpan& a, const RowSpan& b) {
+    return (a.len != 0) & (b.len != 0) & (a.x < b.y + b.len) & (b.y < a.x + a.len);
+}
+__device__ __forceinline__ bool x_meets_output(const RowSpan32& a, const RowSpan32& b) {
+    return (a.x < b.ye) & (b.y < a.xe);
+}
+// a's x is exactly b's output
+__device__ __forceinline__ bool x_is_output(const RowSpan& a, const RowSpan& b) {
+    return a.len != 0 && a.x == b.y && a.len == b.len;
+}
+__device__ __forceinline__ bool x_is_output(const RowSpan32& a, const RowSpan32& b) {
+    return a.x == b.y && a.xe == b.ye;
+}
+// a's w meets its own output at other than the same addresses
+__device__ __forceinline__ bool w_off_own(const RowSpan& a, uint32_t pmask) {
+    return (a.len != 0) & (a.w < a.y + a.len) & (a.y < a.w + a.len) & off_period(a.w, a.y, pmask);
+}
+__device__ __forceinline__ bool w_off_own(const RowSpan32& a, uint32_t pmask) {
+    return (a.w < a.ye) & (a.y < a.we) & off_period(a.w, a.y, pmask);
+}
+
 // True in every thread when p holds in any thread of the workgroup (a ballot
 // per wavefront, one LDS word each, one barrier; the answer is read into a
 // scalar register). fold4 is free again when it returns.
@@ -592,6 +666,9 @@ __device__ __forceinline__ void spread_row(const rmsn_desc& dj, uint64_t pos, co
 // exactly for the bound rows), or kBoundUnknown when outputs overlap or lie
 // past 2^48 (beyond the key): the all-pairs test then decides.
 // mine[r] is row threadIdx.x + 256 r. Every thread gets the same answer.
+// Each meeting pair found is added to the edge list, and both its rows are
+// marked in el.off when the ranges' starts are not a multiple of the run
+// walk's period apart (off_period).
 constexpr int kNoneBound = 0, kBoundMarked = 1, kBoundUnknown = 2;
 
 template <int RE, int R>
@@ -605,9 +682,25 @@ __device__ __forceinline__ void key_ranks(const uint64_t* o_key, int32_t count,
     }
 }
 
+// Pairs of rows that meet, for the components of the bound rows: (j << 16) | k,
+// at most kMaxEdges of them (a count past it means the list is incomplete).
+constexpr int kMaxEdges = 2048;
+
+struct EdgeList {
+    uint32_t* e;
+    uint32_t* n;  // pairs appended (may pass kMaxEdges)
+    uint8_t* off; // off[j]: row j meets a row at ranges whose starts are not a period apart
+};
+
+__device__ __forceinline__ void add_edge(const EdgeList& el, int32_t j, int32_t k) {
+    const uint32_t at = atomicAdd(el.n, 1u);
+    if (at < (uint32_t)kMaxEdges) el.e[at] = ((uint32_t)j << 16) | (uint32_t)k;
+}
+
 template <int R>
 __device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t count,
-                                               uint8_t* bound, int* fold4) {
+                                               uint8_t* bound, int* fold4, uint32_t pmask,
+                                               const EdgeList& el) {
     __shared__ uint64_t o_key[kSpanRows], o_start[kSpanRows], o_end[kSpanRows];
     __shared__ uint16_t o_row[kSpanRows];
     constexpr uint64_t kNoOutput = 0xFFFFFFFFFFFFull;  // the key's start for an empty row
@@ -642,7 +735,8 @@ __device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t
         o_end[p] = out ? (uint64_t)(mine[r].y + mine[r].len) : ~0ull;
         o_row[p] = (uint16_t)j;
     }
-    for (int32_t j = threadIdx.x; j < count; j += 256) bound[j] = 0;
+    for (int32_t j = threadIdx.x; j < count; j += 256) bound[j] = el.off[j] = 0;
+    if (threadIdx.x == 0) *el.n = 0u;
     __syncthreads();
     // keys past 2^48 or overlapping outputs leave the answer unknown; the
     // searches below still stay in bounds (the ranks are a permutation), and
@@ -678,9 +772,11 @@ __device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t
             meet = true;
             bound[j] = 1;  // every writer stores the same value
             bound[o] = 1;
+            add_edge(el, j, o);
+            if (off_period(lo[i], o_start[p], pmask)) el.off[j] = el.off[o] = 1;
         }
     }
-    // the barriers inside also publish bound[]
+    // the barriers inside also publish bound[], the pairs and the marks
     const int any = workgroup_any2(unknown, meet, fold4);
     return (any & 1) ? kBoundUnknown : (any & 2) ? kBoundMarked : kNoneBound;
 }
@@ -816,76 +912,436 @@ __device__ __forceinline__ void dag_walk(const S* span, const uint16_t* lst, int
         __hip_atomic_store(next + wave, 0x7FFFFFFF, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Which rows meet another row, on spans of type S in LDS (RowSpan or
-// RowSpan32). Workers (blockIdx > 0) test their row against every row, 256 at
-// a time, and run it when it meets none. In workgroup 0 (unless the ordered
-// outputs already marked the bound rows: `marked`) wavefront v decides
-// rows v, v + 4, ...: its lanes test the row against 64 rows at a time and a
-// ballot gives the answer, so no lane writes inside the loop; then the marked
-// ("bound") rows run in table order, found 64 at a time by a ballot over the
-// marks. Returns as spread_rows does.
+// --- Run walk: the bound rows in table order, each one shared by the four
+// wavefronts in the pipelined walk's mapping, so that element e of every row
+// is taken by the same thread (the one for e mod 1024). It is chosen when
+// every pair of rows that meet, meets at ranges whose starts are a multiple
+// of 1024 elements apart: each address is then read and written by one
+// thread only, whichever row touches it, and a thread's own loads and stores
+// to one address take effect in program order, so the table's order holds
+// with no wait between threads. For the same reason a row's own w may meet
+// its output only at the same addresses; its x may meet it anywhere (every
+// thread has its x before the row's barrier, and the stores come after it).
+//  - Each row's stored values stay in registers until the next row is done.
+//    When entry j's x is exactly entry j - 1's output (same range), those
+//    values are its x ("forwarded") and x is not loaded.
+//  - Entry j is "ahead" when its w, and its x unless forwarded, meet none of
+//    the outputs of the kRunDepth entries before it: its loads may be issued
+//    before those entries store.
+//  - A run is a stretch of entries each ahead but the first. At the start of
+//    a run (after every store before it) the loads of its first kRunDepth
+//    entries are issued; while entry i is reduced, entry i + kRunDepth's loads
+//    are in flight, issued before entry i + 1 stores. An entry that is not
+//    ahead starts a new run.
+//  - A stretch of at least kFwdRun consecutive entries, each ahead and
+//    forwarded from the entry just before, is a run of its own (a "forward
+//    run", as a chain of rows each reading the one before): it loads w only.
+//    Other runs issue x and w loads for every entry (x over an empty range
+//    when forwarded), so that each loop issues the same instructions on
+//    every pass and the compiler's waits stay exact.
+// A later row's stores over what an earlier row c reads are ordered by the
+// rows' barriers: every thread has used its loads of row c before it
+// reaches row c + 1's barrier, and each row stores after its own barrier.
+// Every row has the walk's block count QM (lanes past the row take empty
+// ranges, as in the pipelined walk), 1 <= n <= 8192, n a multiple of 4,
+// pointers quad-aligned. No thread waits for a flag: the only waits are the
+// rows' barriers, which every thread reaches in the same order.
+constexpr int kRunDepth = 2;  // entries whose loads are in flight beyond the one reduced
+constexpr int kFwdRun = 4;    // shortest forward run
+// entry flags: ahead, deep (loads kRunDepth entries early), forwarded, in a
+// forward run, continues the run of the entry before
+constexpr uint8_t kRunAhead = 1, kRunDeep = 2, kRunFwd = 4, kRunFwdRun = 16, kRunCont = 32;
+
+// Buffer resources of list entry i (the last entry's bases with empty ranges
+// past the end); x and w get their range only when `what` asks for them
+// (bit 0: x, bit 1: w).
+template <typename T, typename S>
+__device__ __forceinline__ PipeRow run_row(const S* span, const uint16_t* lst, int32_t i,
+                                           int32_t nb, uintptr_t base, unsigned what) {
+    const bool real = i < nb;
+    const S s = span[lst[real ? i : nb - 1]];
+    uintptr_t x, w, y;
+    span_addrs(s, base, x, w, y);
+    const uint32_t bytes = real ? __builtin_amdgcn_readfirstlane(span_bytes(s)) : 0u;
+    // the addresses come from LDS: wave-uniform values, taken into scalar registers
+    const auto sp = [](uintptr_t p) {
+        return reinterpret_cast<const void*>(
+            reinterpret_cast<uint64_t>(scalar_gptr(reinterpret_cast<const void*>(p))));
+    };
+    return PipeRow{row_rsrc(sp(x), (what & 1u) ? bytes : 0u), row_rsrc(sp(w), (what & 2u) ? bytes : 0u),
+                   row_rsrc(sp(y), bytes), (int)(bytes / (uint32_t)sizeof(T))};
+}
+
+// The loads entry i takes (w, and x unless forwarded), or none when `issue`
+// is false or the list has ended.
+__device__ __forceinline__ unsigned run_loads(const uint8_t* flag, int32_t i, int32_t nb,
+                                              bool issue) {
+    if (!issue || i >= nb) return 0u;
+    return (flag[i] & kRunFwd) ? 2u : 3u;
+}
+
+template <typename T, int QM>
+struct RunPrev {
+    typename PipeQuad<T>::raw v[QM];  // the stored values of the row just done
+};
+
+// Row r: x from buffer b, or the stored values of the row just before when
+// forwarded (FWD: always, and b holds w only); reduce, apply, store; prev
+// then holds this row's stored values.
+template <bool FWD, typename T, int QM>
+__device__ __forceinline__ void run_compute(PipeBuf<T, QM>& b, const PipeRow& r, bool fwd,
+                                            RunPrev<T, QM>& prev, uint32_t lane_off, float eps,
+                                            float* lds4, int g, int lane) {
+    typedef typename PipeQuad<T>::raw raw;
+    raw x[QM];
+    if (FWD || fwd) {
+        const uint32_t bytes = (uint32_t)r.n * (uint32_t)sizeof(T);
+#pragma unroll
+        for (int m = 0; m < QM; ++m)  // lanes past the row load zeros
+            x[m] = pipe_off<T>(lane_off, m) < bytes ? prev.v[m] : raw{};
+    } else {
+#pragma unroll
+        for (int m = 0; m < QM; ++m) x[m] = b.x[m];
+    }
+    float p = 0.0f;
+#pragma unroll
+    for (int m = 0; m < QM; ++m) {
+        float v[4];
+        PipeQuad<T>::unpack(x[m], v);
+        transpose4(v);
+        p = fmaf(v[0], v[0], p);  // chunks 4m .. 4m+3 of chain 64g + 4t + q
+        p = fmaf(v[1], v[1], p);
+        p = fmaf(v[2], v[2], p);
+        p = fmaf(v[3], v[3], p);
+    }
+    const float gt = group_sumsq(p);
+    if (lane == 0) lds4[g] = gt;
+    lds_barrier();
+    const float inv = inverse_rms((lds4[0] + lds4[2]) + (lds4[1] + lds4[3]), r.n, eps);
+#pragma unroll
+    for (int m = 0; m < QM; ++m) {
+        prev.v[m] = PipeQuad<T>::apply(x[m], b.w[m], inv);
+        PipeQuad<T>::store(prev.v[m], r.y, pipe_off<T>(lane_off, m));
+    }
+}
+
+// Steps P, P + 1, ... NB - 1 of the unrolled run loop, each with its buffer
+// index fixed at compile time; false as soon as one ends the run.
+template <int P, int NB>
+struct RunSteps {
+    template <typename F>
+    __device__ __forceinline__ static bool go(F& step) {
+        return step(std::integral_constant<int, P>{}) && RunSteps<P + 1, NB>::go(step);
+    }
+};
+template <int NB>
+struct RunSteps<NB, NB> {
+    template <typename F>
+    __device__ __forceinline__ static bool go(F&) { return true; }
+};
+
+// This entry's loads into b: x (unless FWD) and w.
+template <bool FWD, typename T, int QM>
+__device__ __forceinline__ void run_issue(PipeBuf<T, QM>& b, const PipeRow& r, uint32_t lane_off) {
+    if (!FWD) {
+#pragma unroll
+        for (int m = 0; m < QM; ++m) b.x[m] = PipeQuad<T>::load(r.x, pipe_off<T>(lane_off, m));
+    }
+#pragma unroll
+    for (int m = 0; m < QM; ++m) b.w[m] = PipeQuad<T>::load(r.w, pipe_off<T>(lane_off, m));
+}
+
+// One run from entry i (its first entry), leaving i at the next run's first.
+template <bool FWD, typename T, int QM, typename S>
+__device__ __forceinline__ void run_one(const S* span, const uint16_t* lst, const uint8_t* flag,
+                                        int32_t nb, uintptr_t base, float eps, float (*lds8)[4],
+                                        RunPrev<T, QM>& prev, int32_t& i, uint32_t lane_off, int g,
+                                        int lane) {
+    constexpr int NB = kRunDepth + 1;  // entries i .. i + kRunDepth
+    PipeBuf<T, QM> buf[NB];
+    // the run's first kRunDepth entries load now (after every store before
+    // them). Each entry's loads are followed by QM stores to an empty range,
+    // as on the loop's back edge each entry's loads are followed by a row's
+    // stores: the compiler's waits for an entry then cover that entry's loads
+    // only, at the loop's entry as on its back edge.
+    const PipeRow none = run_row<T, S>(span, lst, nb, nb, base, 0u);
+    bool chain = true;
+#pragma unroll
+    for (int m = 0; m < kRunDepth; ++m) {
+        chain = chain && (m == 0 || (i + m < nb && (flag[i + m] & kRunCont)));
+        const unsigned what = FWD ? (chain && i + m < nb ? 2u : 0u) : run_loads(flag, i + m, nb, chain);
+        run_issue<FWD, T, QM>(buf[m], run_row<T, S>(span, lst, i + m, nb, base, what), lane_off);
+#pragma unroll
+        for (int q = 0; q < QM; ++q)
+            PipeQuad<T>::store(typename PipeQuad<T>::raw{}, none.y, pipe_off<T>(lane_off, q));
+    }
+    // entry i is in buf[p]; entry i + kRunDepth's loads go into the buffer
+    // entry i - 1 used, when every entry up to it continues the run
+    auto step = [&](auto pc) -> bool {
+        constexpr int p = decltype(pc)::value;
+        const uint8_t fi = __builtin_amdgcn_readfirstlane(flag[i]);
+        const int32_t j = i + kRunDepth;
+        const bool deep = j < nb && (flag[j] & kRunDeep);
+        const unsigned what = FWD ? (deep ? 2u : 0u) : run_loads(flag, j, nb, deep);
+        run_issue<FWD, T, QM>(buf[(p + kRunDepth) % NB], run_row<T, S>(span, lst, j, nb, base, what),
+                              lane_off);
+        const PipeRow cur = run_row<T, S>(span, lst, i, nb, base, 0u);
+        __builtin_amdgcn_sched_barrier(0);
+        run_compute<FWD, T, QM>(buf[p], cur, (fi & kRunFwd) != 0, prev, lane_off, eps,
+                                lds8[i & 1], g, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        ++i;
+        return i < nb && (__builtin_amdgcn_readfirstlane(flag[i]) & kRunCont);
+    };
+    while (RunSteps<0, NB>::go(step)) {
+    }
+}
+
+template <typename T, int QM, typename S>
+__device__ __forceinline__ void run_walk(const S* span, const uint16_t* lst, const uint8_t* flag,
+                                         int32_t nb, uintptr_t base, float eps,
+                                         float (*lds8)[4]) {
+    const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const uint32_t lane_off =
+        (uint32_t)((lane >> 4) * 256 + g * 64 + (lane & 15) * 4) * (uint32_t)sizeof(T);
+    RunPrev<T, QM> prev;
+#pragma unroll
+    for (int m = 0; m < QM; ++m) prev.v[m] = {};
+    for (int32_t i = 0; i < nb;) {
+        if (__builtin_amdgcn_readfirstlane(flag[i]) & kRunFwdRun)
+            run_one<true, T, QM, S>(span, lst, flag, nb, base, eps, lds8, prev, i, lane_off, g,
+                                    lane);
+        else
+            run_one<false, T, QM, S>(span, lst, flag, nb, base, eps, lds8, prev, i, lane_off, g,
+                                     lane);
+    }
+}
+
+// Components of the bound rows under rows_meet, from the edge list: label[j]
+// ends as the least row of j's component (rows in different components share
+// no memory, so their order cannot be observed). Each round hooks, for every
+// pair whose labels differ, the greater label to the lesser (labels only
+// decrease and label[j] <= j, so they form a forest whose roots are the
+// least rows), then every row follows its labels to their root; the rounds
+// end when no pair has two labels. False when the edge list overflowed or
+// kMaxRounds rounds did not settle it: the caller then keeps every bound row
+// in one walk.
+constexpr int kMaxRounds = 24;
+
+__device__ __forceinline__ bool components(const EdgeList& el, int32_t count, uint32_t* label,
+                                           int* fold4) {
+    const uint32_t ne = *el.n;  // published by a barrier before: the same in every thread
+    if (ne > (uint32_t)kMaxEdges) return false;
+    for (int32_t j = threadIdx.x; j < count; j += blockDim.x) label[j] = (uint32_t)j;
+    __syncthreads();
+    for (int round = 0; round < kMaxRounds; ++round) {
+        bool hooked = false;
+        for (uint32_t e = threadIdx.x; e < ne; e += blockDim.x) {
+            const uint32_t a = el.e[e] >> 16, b = el.e[e] & 0xFFFFu;
+            const uint32_t la = label[a], lb = label[b];
+            if (la != lb) {
+                atomicMin(&label[max(la, lb)], min(la, lb));
+                hooked = true;
+            }
+        }
+        if (!workgroup_any(hooked, fold4)) return true;
+        // each row follows its labels to their root; the other threads' writes
+        // only shorten the way (every label is an ancestor, and decreases)
+        for (int32_t j = threadIdx.x; j < count; j += blockDim.x) {
+            uint32_t r = label[j];
+            while (label[r] != r) r = label[r];
+            label[j] = r;
+        }
+        __syncthreads();
+    }
+    return false;
+}
+
+// The free rows and the bound rows of a spread launch, on spans of type S in
+// LDS (RowSpan or RowSpan32).
+//  - Workers (blockIdx >= walkers) test their rows against every row, 256 at
+//    a time, and run those that meet none.
+//  - Every walker finds the same bound rows (marked from the ordered outputs,
+//    `marked`, else by testing all pairs: wavefront v decides rows v, v + 4,
+//    ..., its lanes test 64 rows at a time and a ballot gives the answer), the
+//    meeting pairs among them, and from those the components. Components, in
+//    order of their least row, go round-robin to the walkers; each walker
+//    walks its components' rows in table order: by the run walk when they fit
+//    its mapping and meet only a multiple of its period apart (no row marked
+//    in el.off, no row's w meeting its own output elsewhere), else by the
+//    dependency walk when every row fits the one-wavefront layout, else row
+//    after row.
+// Returns as spread_rows does.
+constexpr uint8_t kFitVec = 1, kFitGroup = 2;  // row fits: one-wavefront layout, GROUP mapping
+
 template <typename T, bool POS, typename S>
-__device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const uint8_t* rvec,
-                                          bool marked, const rmsn_desc* d, int32_t count,
-                                          float eps, uint64_t pos, const PosArgs& pa, float* lds4,
-                                          int* fold4, uint32_t cap) {
-    if (blockIdx.x != 0) {
-        const int32_t workers = (int32_t)gridDim.x - 1;
-        for (int32_t j = (int32_t)blockIdx.x - 1; j < count; j += workers) {
+__device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const uint8_t* rfit,
+                                          bool marked, const EdgeList& el, uintptr_t base,
+                                          const rmsn_desc* d, int32_t count, float eps,
+                                          uint64_t pos, const PosArgs& pa, float* lds4,
+                                          float (*lds8)[4], int* fold4, uint32_t cap) {
+    const int32_t walkers = min(kWalkers, (int32_t)gridDim.x - 1);
+    if ((int32_t)blockIdx.x >= walkers) {
+        const int32_t workers = (int32_t)gridDim.x - walkers;
+        for (int32_t j = (int32_t)blockIdx.x - walkers; j < count; j += workers) {
             const S sj = span[j];
             bool meet = false;
             for (int32_t k = threadIdx.x; k < count; k += blockDim.x)
                 meet |= (k != j) & rows_meet(sj, span[k]);
-            if (workgroup_any(meet, fold4)) continue;  // bound: workgroup 0 runs it in order
+            if (workgroup_any(meet, fold4)) continue;  // bound: a walker runs it in order
             spread_row<T, POS>(d[j], pos, pa, eps, lds4);
             __syncthreads();  // lds4 is reused by the next row
         }
         return true;
     }
+    constexpr uint32_t pmask = 1024u * (uint32_t)sizeof(T) - 1u;
     const int32_t wave = (int32_t)(threadIdx.x >> 6), lane = (int32_t)(threadIdx.x & 63);
     for (int32_t j = marked ? count : wave; j < count; j += 4) {
         const S sj = span[j];
-        bool meet = false;
+        bool meet = false, off = false;
 #pragma unroll 4
-        for (int32_t k = lane; k < count; k += 64) meet |= (k != j) & rows_meet(sj, span[k]);
+        for (int32_t k = lane; k < count; k += 64) {
+            const S sk = span[k];
+            const bool m = (k != j) & rows_meet(sj, sk);
+            meet |= m;
+            off |= m & rows_meet_off(sj, sk, pmask);
+            if (m & (k < j)) add_edge(el, j, k);
+        }
         const bool any = __ballot(meet) != 0;
-        if (lane == 0) bound[j] = any;
+        const bool any_off = __ballot(off) != 0;
+        if (lane == 0) {
+            bound[j] = any;
+            if (any_off) el.off[j] = 1;  // the pair's other row marks itself in its turn
+        }
     }
     __syncthreads();
-    // every bound row in the one-wavefront layout: the dependency walk
-    bool not_vec = false;
-    for (int32_t j = threadIdx.x; j < count; j += blockDim.x) not_vec |= bound[j] && !rvec[j];
-    if (!workgroup_any(not_vec, fold4)) {
-        __shared__ uint16_t lst[kSpanRows];
-        __shared__ int32_t nb_shared;
-        if (wave == 0) {
-            // the bound rows in table order, 64 at a time by a ballot
-            int32_t nb = 0;
-            for (int32_t j0 = 0; j0 < count; j0 += 64) {
-                const bool b = j0 + lane < count && bound[j0 + lane] != 0;
-                const unsigned long long marks = __ballot(b);
-                if (b) lst[nb + __builtin_popcountll(marks & ((1ull << lane) - 1ull))] =
-                    (uint16_t)(j0 + lane);
-                nb += __builtin_popcountll(marks);
+    // components, and the walker of each: rank of its least row among the
+    // components' least rows, modulo the walkers
+    __shared__ uint32_t label[kSpanRows];
+    __shared__ uint16_t crank[kSpanRows];
+    const bool split = components(el, count, label, fold4);
+    if (wave == 0) {
+        int32_t nc = 0;
+        for (int32_t j0 = 0; j0 < count; j0 += 64) {
+            const int32_t j = j0 + lane;
+            const bool root = j < count && bound[j] != 0 && label[j] == (uint32_t)j;
+            const unsigned long long roots = __ballot(root);
+            if (root) crank[j] = (uint16_t)(nc + __builtin_popcountll(roots & ((1ull << lane) - 1ull)));
+            nc += __builtin_popcountll(roots);
+        }
+    }
+    __syncthreads();
+    const auto mine = [&](int32_t j) {
+        return bound[j] != 0 &&
+               (split ? (int32_t)crank[label[j]] % walkers : 0) == (int32_t)blockIdx.x;
+    };
+    // this walker's rows in table order, 64 at a time by a ballot
+    __shared__ uint16_t lst[kSpanRows];
+    __shared__ uint8_t flag[kSpanRows], flag2[kSpanRows];
+    __shared__ int32_t nb_shared;
+    if (wave == 0) {
+        int32_t nb = 0;
+        for (int32_t j0 = 0; j0 < count; j0 += 64) {
+            const bool b = j0 + lane < count && mine(j0 + lane);
+            const unsigned long long marks = __ballot(b);
+            if (b) lst[nb + __builtin_popcountll(marks & ((1ull << lane) - 1ull))] =
+                (uint16_t)(j0 + lane);
+            nb += __builtin_popcountll(marks);
+        }
+        if (lane == 0) nb_shared = nb;
+    }
+    __syncthreads();
+    const int32_t nb = nb_shared;
+    // which walk takes them, and the run walk's block count
+    __shared__ int qm4[4];
+    bool not_vec = false, not_group = false;
+    int blocks = 1;
+    for (int32_t i = threadIdx.x; i < nb; i += blockDim.x) {
+        const int32_t j = lst[i];
+        const S sj = span[j];
+        not_vec |= !(rfit[j] & kFitVec);
+        not_group |= !(rfit[j] & kFitGroup) || el.off[j] || w_off_own(sj, pmask);
+        blocks = max(blocks, (int)((span_bytes(sj) / (uint32_t)sizeof(T) + 1023u) >> 10));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) blocks = max(blocks, __shfl_xor(blocks, o, 64));
+    if (lane == 0) qm4[wave] = blocks;
+    const int fits = workgroup_any2(not_vec, not_group, fold4);  // its barriers publish qm4
+    if (nb == 0) return true;
+    if (!(fits & 2)) {
+        // each entry against the kRunDepth before it: forwarded (its x is
+        // exactly the output of the entry just before), ahead (w, and x
+        // unless forwarded, meet none of their outputs); entry 0 starts the
+        // first run
+        for (int32_t i = threadIdx.x; i < nb; i += blockDim.x) {
+            const S a = span[lst[i]];
+            bool fwd = false, xnear = false, wnear = false;
+#pragma unroll
+            for (int k = 1; k <= kRunDepth; ++k) {
+                if (i - k < 0) break;
+                const S b = span[lst[i - k]];
+                if (k == 1) fwd = x_is_output(a, b);
+                xnear |= x_meets_output(a, b);
+                wnear |= w_meets_output(a, b);
             }
-            if (lane == 0) nb_shared = nb;
+            // a forwarded x is not loaded: whatever earlier outputs wrote
+            // under it, the output just before has overwritten all of it
+            xnear = fwd ? false : xnear;
+            const bool ahead = i > 0 && !wnear && !xnear;
+            flag[i] = (uint8_t)((ahead ? kRunAhead : 0) | (fwd ? kRunFwd : 0));
         }
         __syncthreads();
-        dag_walk<T, POS, S>(span, lst, nb_shared, d, eps, pos, pa, cap);
+        // forward runs: stretches of at least kFwdRun entries each ahead and
+        // forwarded from the entry just before (counted up to kFwdRun - 1 on
+        // each side of the entry)
+        const auto chained = [&](int32_t k) {
+            return k > 0 && k < nb && (flag[k] & kRunAhead) && (flag[k] & kRunFwd);
+        };
+        for (int32_t i = threadIdx.x; i < nb; i += blockDim.x) {
+            int len = 0;
+            if (chained(i)) {
+                len = 1;
+                for (int k = 1; k < kFwdRun && chained(i - k); ++k) ++len;
+                for (int k = 1; k < kFwdRun && chained(i + k); ++k) ++len;
+            }
+            flag2[i] = flag[i] | (len >= kFwdRun ? kRunFwdRun : 0);
+        }
+        __syncthreads();
+        // cont: ahead and of the same kind of run as the entry before; deep:
+        // this entry and the kRunDepth - 1 before it all continue the run
+        const auto cont = [&](int32_t k) {
+            return k > 0 && (flag2[k] & kRunAhead) &&
+                   ((flag2[k] ^ flag2[k - 1]) & kRunFwdRun) == 0;
+        };
+        for (int32_t i = threadIdx.x; i < nb; i += blockDim.x) {
+            bool deep = i >= kRunDepth;
+#pragma unroll
+            for (int k = 0; k < kRunDepth; ++k) deep = deep && cont(i - k);
+            flag[i] = flag2[i] | (cont(i) ? kRunCont : 0) | (deep ? kRunDeep : 0);
+        }
+        __syncthreads();
+        const int qm = max(max(qm4[0], qm4[1]), max(qm4[2], qm4[3]));
+        switch (qm) {
+#define RMSN_CASE(Q) \
+    case Q: run_walk<T, Q, S>(span, lst, flag, nb, base, eps, lds8); break;
+            RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)
+#undef RMSN_CASE
+            default: break;
+        }
         return true;
     }
-    bool some_free = false;
-    for (int32_t j = threadIdx.x; j < count; j += blockDim.x) some_free = some_free || !bound[j];
-    if (!workgroup_any(some_free, fold4)) return false;
-    // the bound rows, row after row, in table order
-    for (int32_t j0 = 0; j0 < count; j0 += 64) {
-        unsigned long long marks = __ballot(j0 + lane < count && bound[j0 + lane] != 0);
-        while (marks) {
-            const int32_t j = j0 + __builtin_ctzll(marks);
-            marks &= marks - 1;
-            spread_row<T, POS>(d[j], pos, pa, eps, lds4);
-            __syncthreads();  // this row's stores before the next bound row's loads
-        }
+    if (!(fits & 1)) {
+        dag_walk<T, POS, S>(span, lst, nb, d, eps, pos, pa, cap);
+        return true;
+    }
+    // every bound row in this walker and no row free: the ordered walks of
+    // the whole table (workgroup 0 only; it is then the only walker with rows)
+    if (blockIdx.x == 0 && nb == count) return false;
+    // row after row, in table order
+    for (int32_t i = 0; i < nb; ++i) {
+        spread_row<T, POS>(d[lst[i]], pos, pa, eps, lds4);
+        __syncthreads();  // this row's stores before the next row's loads
     }
     return true;
 }
@@ -897,10 +1353,10 @@ __device__ __forceinline__ bool spread_on(const S* span, uint8_t* bound, const u
 template <typename T, bool POS>
 __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, float eps,
                                             uint64_t pos, const PosArgs& pa, float* lds4,
-                                            int* fold4, uint32_t cap) {
+                                            float (*lds8)[4], int* fold4, uint32_t cap) {
     __shared__ RowSpan span[kSpanRows];   // 64-bit spans, or RowSpan32 in the same bytes
     __shared__ uint8_t bound[kSpanRows];
-    __shared__ uint8_t rvec[kSpanRows];   // the row fits the one-wavefront layout
+    __shared__ uint8_t rfit[kSpanRows];   // the layouts the row fits (kFitVec, kFitGroup)
     __shared__ unsigned long long lo_hi[2];
     if (threadIdx.x == 0) {
         lo_hi[0] = ~0ull;
@@ -920,9 +1376,12 @@ __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, f
         }
     }
     // no row meets another (the usual table): the workers run every row
+    __shared__ uint32_t edges[kMaxEdges], n_edges;
+    __shared__ uint8_t off[kSpanRows];
+    const EdgeList el{edges, &n_edges, off};
     int found = kBoundUnknown;
-    if (blockIdx.x == 0) {
-        found = find_bound_rows(mine, count, bound, fold4);
+    if ((int32_t)blockIdx.x < min(kWalkers, (int32_t)gridDim.x - 1)) {
+        found = find_bound_rows(mine, count, bound, fold4, 1024u * (uint32_t)sizeof(T) - 1u, el);
         if (found == kNoneBound) return true;
     }
     // lowest and highest address: within the wavefront, then one LDS atomic each
@@ -944,17 +1403,20 @@ __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, f
         const int32_t j = threadIdx.x + 256 * r;
         if (j >= count) continue;
         const RowSpan& m = mine[r];
-        rvec[j] = m.len != 0 && m.len % 16 == 0 && m.len <= 8192 * sizeof(T) &&
-                  ((m.x | m.w | m.y) & 15) == 0;
+        const bool in = m.len != 0 && m.len <= 8192 * sizeof(T);
+        const bool vec = in && m.len % 16 == 0 && ((m.x | m.w | m.y) & 15) == 0;
+        const bool quad = in && m.len % (4 * sizeof(T)) == 0 &&
+                          ((m.x | m.w | m.y) & (4 * sizeof(T) - 1)) == 0;
+        rfit[j] = (vec ? kFitVec : 0) | (quad ? kFitGroup : 0);
         if (narrow) span32[j] = row_span32(m, base);
         else span[j] = m;
     }
     __syncthreads();
     const bool marked = found == kBoundMarked;
-    return narrow ? spread_on<T, POS>(span32, bound, rvec, marked, d, count, eps, pos, pa, lds4,
-                                      fold4, cap)
-                  : spread_on<T, POS>(static_cast<const RowSpan*>(span), bound, rvec, marked, d,
-                                      count, eps, pos, pa, lds4, fold4, cap);
+    return narrow ? spread_on<T, POS>(span32, bound, rfit, marked, el, base, d, count, eps, pos,
+                                      pa, lds4, lds8, fold4, cap)
+                  : spread_on<T, POS>(static_cast<const RowSpan*>(span), bound, rfit, marked, el,
+                                      base, d, count, eps, pos, pa, lds4, lds8, fold4, cap);
 }
 
 template <typename T, bool POS>
@@ -972,7 +1434,7 @@ __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __
     }
     // the launcher gives more than one workgroup only to tables of at most
     // kSpanRows rows
-    if (gridDim.x > 1 && spread_rows<T, POS>(d, count, eps, pos, pa, lds4, lds_fold, cap)) return;
+    if (gridDim.x > 1 && spread_rows<T, POS>(d, count, eps, pos, pa, lds4, lds8, lds_fold, cap)) return;
     switch (walk_mode<T, POS>(d, count, pos, pa, lds_fold)) {
         case kRoundWalk16: round_walk<T, POS, 4>(d, count, eps, pos, pa); break;
         case kRoundWalk4: round_walk<T, POS, 1>(d, count, eps, pos, pa); break;
@@ -995,9 +1457,10 @@ __global__ __launch_bounds__(256) void k_sequence_persistent(const rmsn_desc* __
 hipError_t launch_sequence_persistent(int dtype, const rmsn_desc* d, int32_t count, float eps,
                                      const PosArgs* pos, hipStream_t stream) {
     const PosArgs none{nullptr, 0, 0, 1};
-    // workgroup 0 plus one worker per row (at most kSpreadWorkers) for free rows
+    // the walkers plus one worker per row (at most kSpreadWorkers) for free rows
     const bool spread = count > 1 && count <= kSpanRows && option_persistent_workgroups() == 0;
-    const dim3 grid(spread ? 1u + (unsigned)std::min(count, kSpreadWorkers) : 1u), block(kBlockThreads);
+    const dim3 grid(spread ? (unsigned)(kWalkers + std::min(count, kSpreadWorkers)) : 1u),
+        block(kBlockThreads);
     const int opt_cap = option_walk_spin_cap();
     const uint32_t cap = opt_cap > 0 ? (uint32_t)opt_cap : kDagSpinCap;
     if (dtype == RMSN_F32) {

@@ -17,8 +17,12 @@ Every buffer is compared whole after the persistent launch (free rows spread
 over workgroups, then the whole table in one workgroup) and after the eager
 launch sequence. The decode step's widths chained (each norm reading the
 previous same-width norm's output, every row bound) run through the first
-workgroup's dependency walk, replayed three times; forcing its ordered waits
-to time out (a spin cap of one poll) must end the launch and be counted.
+workgroup's run walk (rows meeting only at the same addresses); the same
+chains read 8 elements past each output take its dependency walk instead.
+Both are replayed three times. A table of every kind of dependency at
+addresses a multiple of 1024 elements apart, with quad-only widths, takes the
+run walk too. Forcing the dependency walk's ordered waits to time out (a spin
+cap of one poll) must end the launch and be counted.
 """
 import numpy as np
 import pytest
@@ -277,27 +281,36 @@ def test_rows_more_than_4gb_apart(rn, kind):
     torch.cuda.empty_cache()
 
 
-def _chained_decode(kind):
+def _chained_decode(kind, shift=0):
     """The decode step's widths, each norm reading the previous norm of its
     width's output (every row bound to table order): three chains, of 7168,
-    1536 and 512 wide rows, interleaved as in the step."""
+    1536 and 512 wide rows, interleaved as in the step. With `shift` each x
+    starts that many elements past the output it reads (into the output
+    buffer's padding)."""
     widths = wl.decode_widths()
     t = Table()
     last = {}
     for n in widths:
-        x = t.rows[last[n]][2] if n in last else t.fresh(n)
-        t.add(x, t.fresh(n), t.fresh(n))
+        if n in last:
+            yb, yo, _ = t.rows[last[n]][2]
+            x = (yb, yo + shift, n)
+        else:
+            x = t.fresh(n)
+        t.add(x, t.fresh(n), (t.buf(n + shift + 3), 0, n))
         last[n] = len(t.rows) - 1
     return t
 
 
+@pytest.mark.parametrize("shift", [0, 8])
 @pytest.mark.parametrize("kind", ["f32", "bf16"])
-def test_chained_decode_table(rn, kind):
-    """Every row bound, chains at distances 1 to 8: the first workgroup's
-    dependency walk (all rows whole 16-byte vectors) against the rows applied
-    in order; no ordered wait may time out."""
-    t = _chained_decode(kind)
-    say(f"persistent chained decode table {kind}: {len(t.rows)} rows")
+def test_chained_decode_table(rn, kind, shift):
+    """Every row bound, chains at distances 1 to 8, against the rows applied
+    in order. Unshifted, every row meets others only at the same addresses
+    (the run walk, 7168-wide rows forwarded in registers); shifted by 8
+    elements (whole 16-byte vectors, other addresses) the dependency walk
+    takes them. No ordered wait may time out."""
+    t = _chained_decode(kind, shift)
+    say(f"persistent chained decode table {kind} shift {shift}: {len(t.rows)} rows")
     host = _host_buffers(t, kind, 6_000_000)
     want = _in_order(t, host, kind)
     todev, tohost, bits = _codec(kind)
@@ -320,11 +333,12 @@ def test_chained_decode_table(rn, kind):
 
 
 def test_walk_timeout_is_counted(rn):
-    """A spin cap of one poll makes the ordered waits of a chained table time
-    out: the launch still ends, and the device counter reports it (the rows'
-    outputs are then not ordered and are not checked). With the default cap
-    the same table is exact again and nothing is counted."""
-    t = _chained_decode("f32")
+    """A spin cap of one poll makes the ordered waits of a chained table (the
+    dependency walk: chains 8 elements off) time out: the launch still ends,
+    and the device counter reports it (the rows' outputs are then not ordered
+    and are not checked). With the default cap the same table is exact again
+    and nothing is counted."""
+    t = _chained_decode("f32", shift=8)
     host = _host_buffers(t, "f32", 6_100_000)
     todev, tohost, bits = _codec("f32")
     bufs = [todev(h) for h in host]
@@ -348,3 +362,104 @@ def test_walk_timeout_is_counted(rn):
     for b, buf in enumerate(bufs):
         assert (tohost(buf).view(bits) == want[b].view(bits)).all(), b
     assert rn.diag_walk_timeouts() == 0
+
+
+def _aligned_block(t, n, period):
+    """Rows of width n with every kind of dependency, every pair of them
+    meeting at addresses a multiple of `period` elements apart: a chain read
+    at the same addresses, a row reading the second period of a two-period
+    output, the same output written twice, a row overwriting an earlier read,
+    an in-place row, a row whose w is its output, a row whose output is one
+    period into an earlier output."""
+    big = lambda: (t.buf(n + 2 * period + 3), 0, n)
+    a = big()
+    t.add(t.fresh(n), t.fresh(n), a)
+    t.add(a, t.fresh(n), big())                              # forwarded: x is the output before
+    t.add(t.rows[-1][2], t.fresh(n), t.fresh(n))             # forwarded again
+    t.free_row(n)
+    t.add((a[0], period, n), t.fresh(n), t.fresh(n))         # a period into an earlier output
+    shared = big()
+    t.add(t.fresh(n), t.fresh(n), shared)
+    t.add(t.fresh(n), t.fresh(n), shared)                    # the same output, twice in a row
+    war = t.fresh(n)
+    t.add(war, t.fresh(n), t.fresh(n))
+    t.add(t.fresh(n), t.fresh(n), war)                       # overwrites the read before
+    ip = t.fresh(n)
+    t.add(ip, t.fresh(n), ip)                                # in place
+    wy = t.fresh(n)
+    t.add(t.fresh(n), wy, wy)                                # w is the output
+    t.add(t.fresh(n), t.fresh(n), (shared[0], period, n))    # output a period into another
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_run_walk_aligned_dependencies(rn, kind):
+    """Blocks of aligned dependencies (every meeting a multiple of 1024
+    elements apart) at widths 4, 12, 1028, 4100 (quads, not whole 16-byte
+    vectors in bf16) and 8192, among free rows: the run walk, against the
+    rows applied in order, replayed three times."""
+    t = Table()
+    for n in (4, 12, 1028, 4100, 8192, 7168):
+        t.free_row(n)
+        _aligned_block(t, n, 1024)
+    say(f"persistent aligned dependencies {kind}: {len(t.rows)} rows")
+    host = _host_buffers(t, kind, 6_200_000)
+    todev, tohost, bits = _codec(kind)
+    dtype = rn.BF16 if kind == "bf16" else rn.F32
+    rn.diag_walk_timeouts(reset=True)
+    bufs = [todev(h) for h in host]
+    table, widths = rn.make_table([(bufs[xb][xo:xo + n], bufs[wb][wo:wo + n], bufs[yb][yo:yo + n])
+                                   for (xb, xo, n), (wb, wo, _), (yb, yo, _) in t.rows])
+    prev = [h.copy() for h in host]
+    for rep in range(3):
+        _launch(rn, "persistent", table, widths, len(t.rows), dtype)
+        exp = _in_order(t, prev, kind)
+        for b, buf in enumerate(bufs):
+            same = tohost(buf).view(bits) == exp[b].view(bits)
+            assert same.all(), (f"replay {rep}: aligned {kind} buffer {b}: first difference at "
+                                f"{int(np.argmin(same))} of {len(same)}")
+        prev = [tohost(b) for b in bufs]
+    assert rn.diag_walk_timeouts() == 0
+
+
+@pytest.mark.parametrize("shift", [0, 8])
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_many_components(rn, kind, shift):
+    """Forty chains of six rows (each row reading the one before's output,
+    `shift` elements on), interleaved in the table with free rows: forty
+    components, more than the launch's walkers, each walker taking every
+    fourth of them in order of their first row; widths 8 to 7168. Against the
+    rows applied in order, replayed twice."""
+    g = np.random.Generator(np.random.PCG64(0x40C))
+    t = Table()
+    chains = 40
+    widths = [int(g.choice([8, 64, 512, 1536, 4096, 7168])) for _ in range(chains)]
+    last = [None] * chains
+    order = [c for c in range(chains) for _ in range(6)]
+    g.shuffle(order)
+    for c in order:
+        n = widths[c]
+        if last[c] is None:
+            x = t.fresh(n)
+        else:
+            yb, yo, _ = t.rows[last[c]][2]
+            x = (yb, yo + shift, n)
+        t.add(x, t.fresh(n), (t.buf(n + shift + 3), 0, n))
+        last[c] = len(t.rows) - 1
+        if g.random() < 0.3:
+            t.free_row(int(g.choice([256, 1024, 7168])))
+    say(f"persistent many components {kind} shift {shift}: {len(t.rows)} rows, {chains} chains")
+    host = _host_buffers(t, kind, 6_300_000 + shift)
+    todev, tohost, bits = _codec(kind)
+    dtype = rn.BF16 if kind == "bf16" else rn.F32
+    bufs = [todev(h) for h in host]
+    table, widths_t = rn.make_table([(bufs[xb][xo:xo + n], bufs[wb][wo:wo + n], bufs[yb][yo:yo + n])
+                                     for (xb, xo, n), (wb, wo, _), (yb, yo, _) in t.rows])
+    prev = [h.copy() for h in host]
+    for rep in range(2):
+        _launch(rn, "persistent", table, widths_t, len(t.rows), dtype)
+        exp = _in_order(t, prev, kind)
+        for b, buf in enumerate(bufs):
+            same = tohost(buf).view(bits) == exp[b].view(bits)
+            assert same.all(), (f"replay {rep}: {kind} shift {shift} buffer {b}: first "
+                                f"difference at {int(np.argmin(same))} of {len(same)}")
+        prev = [tohost(b) for b in bufs]
