@@ -660,9 +660,9 @@ __device__ __forceinline__ void spread_row(const rmsn_desc& dj, uint64_t pos, co
 // the outputs meeting the range are that one and those after it that start
 // before the range ends; both rows of every such pair (the row's own output,
 // in place, aside) are bound. With disjoint outputs no other pair meets. The
-// order is a rank sort: the key start * 2^16 + row is unique, and each lane
-// counts the keys below its own, reading them as LDS broadcasts with no
-// barrier between steps. Returns kNoneBound, kBoundMarked (bound[j] is 1
+// order is a rank sort of the unique keys start * 2^16 + row (quarter_ranks:
+// each quarter ranked within itself, then merged by binary searches).
+// Returns kNoneBound, kBoundMarked (bound[j] is 1
 // exactly for the bound rows), or kBoundUnknown when outputs overlap or lie
 // past 2^48 (beyond the key): the all-pairs test then decides.
 // mine[r] is row threadIdx.x + 256 r. Every thread gets the same answer.
@@ -671,15 +671,53 @@ __device__ __forceinline__ void spread_row(const rmsn_desc& dj, uint64_t pos, co
 // walk's period apart (off_period).
 constexpr int kNoneBound = 0, kBoundMarked = 1, kBoundUnknown = 2;
 
-template <int RE, int R>
-__device__ __forceinline__ void key_ranks(const uint64_t* o_key, int32_t count,
-                                          const uint64_t (&key)[R], int32_t (&rank)[R]) {
-#pragma unroll 8
-    for (int32_t k = 0; k < count; ++k) {
-        const uint64_t kk = o_key[k];  // the same word in every lane
+// Ranks of the keys o_key[0..count) (unique), in two steps so that no lane
+// compares its keys with all count of them: wavefront v ranks the keys of
+// rows [v q, v q + n_v) (q = ceil(count / 4)) among themselves, each lane
+// holding RE of them and reading the others as LDS broadcasts, and writes them
+// in order into its quarter of `sorted` (P slots, the rest padded with the
+// largest key); after a barrier each key's rank is the sum over the four
+// quarters of the keys below it, found by four branch-free binary searches
+// side by side. rank_of[j] is row j's rank. P is a power of two, at least q.
+template <int RE>
+__device__ __forceinline__ void quarter_ranks(const uint64_t* o_key, int32_t count, int32_t q,
+                                              int32_t P, uint64_t* sorted, uint16_t* rank_of) {
+    const int32_t v = (int32_t)(threadIdx.x >> 6), lane = (int32_t)(threadIdx.x & 63);
+    const int32_t q0 = v * q, qn = max(0, min(q, count - q0));
+    uint64_t key[RE];
+    int32_t rank[RE];
 #pragma unroll
-        for (int r = 0; r < RE; ++r) rank[r] += kk < key[r] ? 1 : 0;
+    for (int i = 0; i < RE; ++i) {
+        key[i] = lane + 64 * i < qn ? o_key[q0 + lane + 64 * i] : ~0ull;
+        rank[i] = 0;
     }
+#pragma unroll 8
+    for (int32_t t = 0; t < qn; ++t) {
+        const uint64_t kk = o_key[q0 + t];  // the same word in every lane
+#pragma unroll
+        for (int i = 0; i < RE; ++i) rank[i] += kk < key[i] ? 1 : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < RE; ++i) {
+        const int32_t idx = lane + 64 * i;
+        if (idx < qn) sorted[v * P + rank[i]] = key[i];
+        else if (idx < P) sorted[v * P + idx] = ~0ull;  // padding sorts after every key
+    }
+    for (int32_t idx = lane + 64 * RE; idx < P; idx += 64) sorted[v * P + idx] = ~0ull;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RE; ++i) {
+        int32_t at[4] = {0, 0, 0, 0};  // keys below key[i] in quarter u, before the last step
+        for (int32_t step = P >> 1; step > 0; step >>= 1) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) at[u] += sorted[u * P + at[u] + step - 1] < key[i] ? step : 0;
+        }
+        int32_t total = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) total += at[u] + (sorted[u * P + at[u]] < key[i] ? 1 : 0);
+        if (lane + 64 * i < qn) rank_of[q0 + lane + 64 * i] = (uint16_t)total;
+    }
+    __syncthreads();
 }
 
 // Pairs of rows that meet, for the components of the bound rows: (j << 16) | k,
@@ -719,11 +757,24 @@ __device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t
         if (j < count) o_key[j] = key[r];
     }
     __syncthreads();  // o_key published
-    switch ((count + 255) >> 8) {
-        case 1: key_ranks<1>(o_key, count, key, rank); break;
-        case 2: key_ranks<2>(o_key, count, key, rank); break;
-        case 3: key_ranks<3>(o_key, count, key, rank); break;
-        default: key_ranks<4>(o_key, count, key, rank); break;
+    {
+        // the quarters' sorted keys go where the ordered starts are written
+        // next (their last reads come before quarter_ranks' last barrier)
+        __shared__ uint16_t rank_of[kSpanRows];
+        const int32_t q = (count + 3) >> 2;
+        int32_t P = 1;
+        while (P < q) P <<= 1;
+        switch ((q + 63) >> 6) {
+            case 1: quarter_ranks<1>(o_key, count, q, P, o_start, rank_of); break;
+            case 2: quarter_ranks<2>(o_key, count, q, P, o_start, rank_of); break;
+            case 3: quarter_ranks<3>(o_key, count, q, P, o_start, rank_of); break;
+            default: quarter_ranks<4>(o_key, count, q, P, o_start, rank_of); break;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int32_t j = threadIdx.x + 256 * r;
+            rank[r] = j < count ? (int32_t)rank_of[j] : 0;
+        }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
