@@ -676,9 +676,10 @@ constexpr int kNoneBound = 0, kBoundMarked = 1, kBoundUnknown = 2;
 // rows [v q, v q + n_v) (q = ceil(count / 4)) among themselves, each lane
 // holding RE of them and reading the others as LDS broadcasts, and writes them
 // in order into its quarter of `sorted` (P slots, the rest padded with the
-// largest key); after a barrier each key's rank is the sum over the four
-// quarters of the keys below it, found by four branch-free binary searches
-// side by side. rank_of[j] is row j's rank. P is a power of two, at least q.
+// largest key); after a barrier each key's rank is its rank in its own
+// quarter plus the keys below it in each other quarter, found by three
+// branch-free binary searches side by side. rank_of[j] is row j's rank. P is
+// a power of two, at least q.
 template <int RE>
 __device__ __forceinline__ void quarter_ranks(const uint64_t* o_key, int32_t count, int32_t q,
                                               int32_t P, uint64_t* sorted, uint16_t* rank_of) {
@@ -707,14 +708,19 @@ __device__ __forceinline__ void quarter_ranks(const uint64_t* o_key, int32_t cou
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < RE; ++i) {
-        int32_t at[4] = {0, 0, 0, 0};  // keys below key[i] in quarter u, before the last step
+        // the other three quarters (this one's count is rank[i] already)
+        int32_t at[3] = {0, 0, 0};  // keys below key[i] in each, before the last step
         for (int32_t step = P >> 1; step > 0; step >>= 1) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) at[u] += sorted[u * P + at[u] + step - 1] < key[i] ? step : 0;
+            for (int u = 0; u < 3; ++u) {
+                const int32_t b = ((v + 1 + u) & 3) * P;
+                at[u] += sorted[b + at[u] + step - 1] < key[i] ? step : 0;
+            }
         }
-        int32_t total = 0;
+        int32_t total = rank[i];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) total += at[u] + (sorted[u * P + at[u]] < key[i] ? 1 : 0);
+        for (int u = 0; u < 3; ++u)
+            total += at[u] + (sorted[((v + 1 + u) & 3) * P + at[u]] < key[i] ? 1 : 0);
         if (lane + 64 * i < qn) rank_of[q0 + lane + 64 * i] = (uint16_t)total;
     }
     __syncthreads();
@@ -733,6 +739,54 @@ struct EdgeList {
 __device__ __forceinline__ void add_edge(const EdgeList& el, int32_t j, int32_t k) {
     const uint32_t at = atomicAdd(el.n, 1u);
     if (at < (uint32_t)kMaxEdges) el.e[at] = ((uint32_t)j << 16) | (uint32_t)k;
+}
+
+// The outputs that the x and w ranges of this thread's first RA rows meet,
+// from the outputs in order of start (o_start, o_end, o_row: m slots, past
+// count padded): every lane's 2 RA searches side by side, a branch-free lower
+// bound with the same log2(m) steps for all, so their LDS reads are in flight
+// together; then the outputs from the first one ending past the range's
+// start to the last one starting before its end. Marks both rows of every
+// such pair bound (the row's own output, in place, aside), adds the pair to
+// the edge list and marks it in el.off when the starts are not a period
+// apart. True when this thread found a pair.
+template <int RA, int R>
+__device__ __forceinline__ bool ranges_meeting_outputs(const RowSpan (&mine)[R], int32_t count,
+                                                       int32_t m, const uint64_t* o_start,
+                                                       const uint64_t* o_end,
+                                                       const uint16_t* o_row, uint8_t* bound,
+                                                       uint32_t pmask, const EdgeList& el) {
+    constexpr int NQ = 2 * RA;
+    uint64_t lo[NQ], hi[NQ];
+    int32_t at[NQ];
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const RowSpan& rs = mine[i >> 1];
+        lo[i] = (i & 1) ? (uint64_t)rs.w : (uint64_t)rs.x;
+        hi[i] = lo[i] + rs.len;
+        at[i] = 0;  // every output before at[i] ends at or before lo[i]
+    }
+    for (int32_t step = m >> 1; step > 0; step >>= 1) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) at[i] += o_end[at[i] + step - 1] <= lo[i] ? step : 0;
+    }
+    bool meet = false;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+        const int32_t j = threadIdx.x + 256 * (i >> 1);
+        if (j >= count || mine[i >> 1].len == 0) continue;
+        int32_t p = at[i] + (o_end[at[i]] <= lo[i] ? 1 : 0);  // first output ending past lo[i]
+        for (; p < m && o_start[p] < hi[i]; ++p) {
+            const int32_t o = o_row[p];
+            if (o == j) continue;
+            meet = true;
+            bound[j] = 1;  // every writer stores the same value
+            bound[o] = 1;
+            add_edge(el, j, o);
+            if (off_period(lo[i], o_start[p], pmask)) el.off[j] = el.off[o] = 1;
+        }
+    }
+    return meet;
 }
 
 template <int R>
@@ -795,37 +849,12 @@ __device__ __forceinline__ int find_bound_rows(const RowSpan (&mine)[R], int32_t
     bool unknown = high;
     for (int32_t i = threadIdx.x; i + 1 < m; i += 256)
         unknown |= (o_start[i + 1] != ~0ull) & (o_end[i] > o_start[i + 1]);
-    // every lane's 2R searches side by side: a branch-free lower bound with
-    // the same log2(m) steps for all, so their LDS reads are in flight together
-    constexpr int NQ = 2 * R;
-    uint64_t lo[NQ], hi[NQ];
-    int32_t at[NQ];
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-        const RowSpan& rs = mine[i >> 1];
-        lo[i] = (i & 1) ? (uint64_t)rs.w : (uint64_t)rs.x;
-        hi[i] = lo[i] + rs.len;
-        at[i] = 0;  // every output before at[i] ends at or before lo[i]
-    }
-    for (int32_t step = m >> 1; step > 0; step >>= 1) {
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) at[i] += o_end[at[i] + step - 1] <= lo[i] ? step : 0;
-    }
     bool meet = false;
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-        const int32_t j = threadIdx.x + 256 * (i >> 1);
-        if (j >= count || mine[i >> 1].len == 0) continue;
-        int32_t p = at[i] + (o_end[at[i]] <= lo[i] ? 1 : 0);  // first output ending past lo[i]
-        for (; p < m && o_start[p] < hi[i]; ++p) {
-            const int32_t o = o_row[p];
-            if (o == j) continue;
-            meet = true;
-            bound[j] = 1;  // every writer stores the same value
-            bound[o] = 1;
-            add_edge(el, j, o);
-            if (off_period(lo[i], o_start[p], pmask)) el.off[j] = el.off[o] = 1;
-        }
+    switch ((count + 255) >> 8) {
+        case 1: meet = ranges_meeting_outputs<1>(mine, count, m, o_start, o_end, o_row, bound, pmask, el); break;
+        case 2: meet = ranges_meeting_outputs<2>(mine, count, m, o_start, o_end, o_row, bound, pmask, el); break;
+        case 3: meet = ranges_meeting_outputs<3>(mine, count, m, o_start, o_end, o_row, bound, pmask, el); break;
+        default: meet = ranges_meeting_outputs<4>(mine, count, m, o_start, o_end, o_row, bound, pmask, el); break;
     }
     // the barriers inside also publish bound[], the pairs and the marks
     const int any = workgroup_any2(unknown, meet, fold4);
@@ -1409,11 +1438,6 @@ __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, f
     __shared__ uint8_t bound[kSpanRows];
     __shared__ uint8_t rfit[kSpanRows];   // the layouts the row fits (kFitVec, kFitGroup)
     __shared__ unsigned long long lo_hi[2];
-    if (threadIdx.x == 0) {
-        lo_hi[0] = ~0ull;
-        lo_hi[1] = 0ull;
-    }
-    __syncthreads();
     constexpr int R = kSpanRows / 256;     // rows per thread (blockDim.x == 256)
     RowSpan mine[R];
     uint64_t lo = ~0ull, hi = 0ull;
@@ -1426,15 +1450,28 @@ __device__ __forceinline__ bool spread_rows(const rmsn_desc* d, int32_t count, f
             hi = max(hi, (uint64_t)max(mine[r].x, max(mine[r].w, mine[r].y)) + mine[r].len);
         }
     }
-    // no row meets another (the usual table): the workers run every row
     __shared__ uint32_t edges[kMaxEdges], n_edges;
     __shared__ uint8_t off[kSpanRows];
     const EdgeList el{edges, &n_edges, off};
-    int found = kBoundUnknown;
-    if ((int32_t)blockIdx.x < min(kWalkers, (int32_t)gridDim.x - 1)) {
-        found = find_bound_rows(mine, count, bound, fold4, 1024u * (uint32_t)sizeof(T) - 1u, el);
-        if (found == kNoneBound) return true;
+    if ((int32_t)blockIdx.x >= min(kWalkers, (int32_t)gridDim.x - 1)) {
+        // a worker tests each of its rows against every row on the 64-bit spans
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int32_t j = threadIdx.x + 256 * r;
+            if (j < count) span[j] = mine[r];
+        }
+        __syncthreads();
+        return spread_on<T, POS>(static_cast<const RowSpan*>(span), bound, rfit, false, el, 0, d,
+                                 count, eps, pos, pa, lds4, lds8, fold4, cap);
     }
+    // no row meets another (the usual table): the workers run every row
+    if (threadIdx.x == 0) {
+        lo_hi[0] = ~0ull;  // published by the barriers of the search
+        lo_hi[1] = 0ull;
+    }
+    const int found =
+        find_bound_rows(mine, count, bound, fold4, 1024u * (uint32_t)sizeof(T) - 1u, el);
+    if (found == kNoneBound) return true;
     // lowest and highest address: within the wavefront, then one LDS atomic each
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {

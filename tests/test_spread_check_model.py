@@ -8,10 +8,10 @@ rank among all keys is found in two steps (quarter_ranks):
   wavefront v ranks the keys of its quarter among themselves and writes them
   in that order into slots [v P, v P + n_v) of a sorted array, padding the
   rest of its P slots (P a power of two, at least q) with the largest key;
-* each key's rank is the sum over the four quarters of the number of keys
-  below it, found by a branch-free binary search: steps P/2, P/4, ..., 1 each
-  add the step when the slot before the candidate holds a smaller key, and
-  a last comparison adds one.
+* each key's rank is its rank within its own quarter plus the number of keys
+  below it in each other quarter, found by a branch-free binary search:
+  steps P/2, P/4, ..., 1 each add the step when the slot before the
+  candidate holds a smaller key, and a last comparison adds one.
 
 The model restates those steps and checks that the ranks are exactly the
 positions of the keys in sorted order, at every count from 1 to 40, around
@@ -41,9 +41,13 @@ def quarter_ranks(keys):
         for idx, k in enumerate(own):
             sorted_[v * P + sum(1 for kk in own if kk < k)] = k
     ranks = []
-    for k in keys:
-        total = 0
+    for j, k in enumerate(keys):
+        v = j // q
+        own = keys[v * q:v * q + q]
+        total = sum(1 for kk in own if kk < k)
         for u in range(WAVES):
+            if u == v:
+                continue
             at, step = 0, P // 2
             while step > 0:
                 at += step if sorted_[u * P + at + step - 1] < k else 0
