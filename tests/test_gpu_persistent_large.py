@@ -421,14 +421,15 @@ def test_run_walk_aligned_dependencies(rn, kind):
     assert rn.diag_walk_timeouts() == 0
 
 
-@pytest.mark.parametrize("shift", [0, 8])
+@pytest.mark.parametrize("shift", [0, 8, "mixed"])
 @pytest.mark.parametrize("kind", ["f32", "bf16"])
 def test_many_components(rn, kind, shift):
     """Forty chains of six rows (each row reading the one before's output,
-    `shift` elements on), interleaved in the table with free rows: forty
-    components, more than the launch's walkers, each walker taking every
-    fourth of them in order of their first row; widths 8 to 7168. Against the
-    rows applied in order, replayed twice."""
+    `shift` elements on; "mixed": 8 on every other chain, so a walker's rows
+    mix components of both kinds), interleaved in the table with free rows:
+    forty components, more than the launch's walkers, each walker taking
+    every fourth of them in order of their first row; widths 8 to 7168.
+    Against the rows applied in order, replayed twice."""
     g = np.random.Generator(np.random.PCG64(0x40C))
     t = Table()
     chains = 40
@@ -438,17 +439,18 @@ def test_many_components(rn, kind, shift):
     g.shuffle(order)
     for c in order:
         n = widths[c]
+        sh = (8 if c % 2 else 0) if shift == "mixed" else shift
         if last[c] is None:
             x = t.fresh(n)
         else:
             yb, yo, _ = t.rows[last[c]][2]
-            x = (yb, yo + shift, n)
-        t.add(x, t.fresh(n), (t.buf(n + shift + 3), 0, n))
+            x = (yb, yo + sh, n)
+        t.add(x, t.fresh(n), (t.buf(n + sh + 3), 0, n))
         last[c] = len(t.rows) - 1
         if g.random() < 0.3:
             t.free_row(int(g.choice([256, 1024, 7168])))
     say(f"persistent many components {kind} shift {shift}: {len(t.rows)} rows, {chains} chains")
-    host = _host_buffers(t, kind, 6_300_000 + shift)
+    host = _host_buffers(t, kind, 6_300_000 + (9 if shift == "mixed" else shift))
     todev, tohost, bits = _codec(kind)
     dtype = rn.BF16 if kind == "bf16" else rn.F32
     bufs = [todev(h) for h in host]
@@ -463,3 +465,37 @@ def test_many_components(rn, kind, shift):
             assert same.all(), (f"replay {rep}: {kind} shift {shift} buffer {b}: first "
                                 f"difference at {int(np.argmin(same))} of {len(same)}")
         prev = [tohost(b) for b in bufs]
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_more_meeting_pairs_than_the_edge_list_holds(rn, kind):
+    """Eighty rows writing the same output (every pair meets: 3160 pairs,
+    more than the walkers' list of 2048), among free rows and a separate
+    chain: the walkers cannot tell the components apart and keep every bound
+    row in the first walker, in table order. The last writer's row must win,
+    and the chain must be exact."""
+    t = Table()
+    n = 1024
+    shared = t.fresh(n)
+    for i in range(80):
+        t.add(t.fresh(n), t.fresh(n), shared)
+        if i % 7 == 0:
+            t.free_row(512)
+    t.free_row(n)
+    for _ in range(5):
+        t.add(t.rows[-1][2], t.fresh(n), t.fresh(n))
+    say(f"persistent edge-list overflow {kind}: {len(t.rows)} rows")
+    host = _host_buffers(t, kind, 6_400_000)
+    want = _in_order(t, host, kind)
+    todev, tohost, bits = _codec(kind)
+    dtype = rn.BF16 if kind == "bf16" else rn.F32
+    for arm in ARMS:
+        bufs = [todev(h) for h in host]
+        table, widths = rn.make_table([(bufs[xb][xo:xo + n_], bufs[wb][wo:wo + n_],
+                                        bufs[yb][yo:yo + n_])
+                                       for (xb, xo, n_), (wb, wo, _), (yb, yo, _) in t.rows])
+        _launch(rn, arm, table, widths, len(t.rows), dtype)
+        for b, buf in enumerate(bufs):
+            same = tohost(buf).view(bits) == want[b].view(bits)
+            assert same.all(), (f"{arm}: {kind} buffer {b}: first difference at "
+                                f"{int(np.argmin(same))} of {len(same)}")
