@@ -1030,7 +1030,7 @@ constexpr int kRunDepth = 2;  // entries whose loads are in flight beyond the on
 constexpr int kFwdRun = 4;    // shortest forward run
 // entry flags: ahead, deep (loads kRunDepth entries early), forwarded, in a
 // forward run, continues the run of the entry before
-constexpr uint8_t kRunAhead = 1, kRunDeep = 2, kRunFwd = 4, kRunFwdRun = 16, kRunCont = 32;
+constexpr uint8_t kRunAhead = 1, kRunDeep = 2, kRunFwd = 4, kRunFwdRun = 8, kRunCont = 16;
 
 // Buffer resources of list entry i (the last entry's bases with empty ranges
 // past the end); x and w get their range only when `what` asks for them
