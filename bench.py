@@ -59,7 +59,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_8192x7168_traffic.js
 # the sources the prefill kernel is compiled from (its traffic record is tied to them)
 KERNEL_SRCS = [os.path.join(ROOT, "row_wise_rmsnorm_amd", "csrc", f)
                for f in ("rmsn_kernels.hip", "rmsn_rows.h", "rmsn_common.h", "rmsn_group.h",
-                         "rmsn_launch.h")]
+                         "rmsn_launch.h")] + [
+    os.path.join(ROOT, "row_wise_rmsnorm_amd", "build.py")]  # the compiler flags
 
 
 def log(msg):

@@ -7,7 +7,9 @@
 hipcc cross-compiles for gfx950 without a GPU present. Floating point:
 contraction off (-ffp-contract=off), no fast-math, HIP's default correctly
 rounded binary32 division and square root; packed-FP32 instructions are
-disabled for the device code.
+disabled for the device code. Kernel arguments are preloaded into SGPRs by
+the dispatcher (the first 16 arguments), so a kernel's first loads do not wait
+for a scalar load of its argument segment.
 """
 import os
 import subprocess
@@ -29,6 +31,7 @@ FLAGS = [
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
     "-I", os.path.join(HERE, "csrc"),
 ]
