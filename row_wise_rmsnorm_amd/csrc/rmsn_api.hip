@@ -177,7 +177,7 @@ int plan_sequence(int dtype, const int64_t* widths, int32_t count, std::vector<P
 int enqueue_sequence(const std::vector<Plan>& plans, const rmsn_desc* table, float eps,
                      const PosArgs* pos, hipStream_t s) {
     for (size_t i = 0; i < plans.size(); ++i) {
-        const hipError_t e = launch_desc(plans[i], table + i, eps, pos, s);
+        const hipError_t e = launch_desc_eager(plans[i], table + i, eps, pos, s);
         if (e != hipSuccess) return hip_fail("sequence kernel launch", e);
     }
     if (pos) {
@@ -215,7 +215,8 @@ int check_position(int dtype, const rmsn_position* pos, PosArgs* out) {
     return RMSN_OK;
 }
 
-// Run every distinct kernel variant of the sequence once on a private 1-element
+// Run every distinct kernel variant the graph records (the preloaded-argument
+// build of the descriptor kernels) once on a private 1-element
 // row (and, for a positioned sequence, a private position), so module loading
 // and any other first-use work happen before capture. The caller's rows and
 // position are not touched.
@@ -247,7 +248,7 @@ int prewarm(const std::vector<Plan>& plans, int dtype, float eps, bool positione
         for (int c : seen) dup = dup || c == key;
         if (dup) continue;
         seen.push_back(key);
-        e = launch_desc(plans[i], reinterpret_cast<const rmsn_desc*>(base), eps,
+        e = launch_desc_graph(plans[i], reinterpret_cast<const rmsn_desc*>(base), eps,
                         positioned ? &own : nullptr, s);
         if (e != hipSuccess) st = hip_fail("pre-warm launch", e);
     }
@@ -276,7 +277,7 @@ int capture(rmsn_graph* g, hipStream_t s) {
     int st = RMSN_OK;
     const PosArgs* pos = g->positioned ? &g->pos : nullptr;
     for (size_t i = 0; i < g->plans.size() && st == RMSN_OK; ++i) {
-        e = launch_desc(g->plans[i], g->table + i, g->eps, pos, s);
+        e = launch_desc_graph(g->plans[i], g->table + i, g->eps, pos, s);
         if (e != hipSuccess) st = hip_fail("captured launch", e);
         // Test hook: a synchronisation is not allowed while capturing, which
         // makes the capture fail the way a forgotten lazy initialisation would.

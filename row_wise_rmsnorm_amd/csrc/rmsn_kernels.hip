@@ -42,10 +42,9 @@
 //          left them (1 KB of LDS, one barrier per hand-off), and the last
 //          wavefront runs the group trees. Every wavefront issues all of its
 //          loads at once, so the whole row is in flight from the start.
-// Descriptor kernels run one row read from a device table (BLOCK or GROUP
-// layout, optionally at a device-resident position). The layouts' device code
-// is in rmsn_rows.h; the persistent launch, which walks a whole table in one
-// kernel, is in rmsn_persistent.hip.
+// The descriptor kernels, which run one row read from a device table, are in
+// rmsn_desc.hip. The layouts' device code is in rmsn_rows.h; the persistent
+// launch, which walks a whole table in one kernel, is in rmsn_persistent.hip.
 //
 // Floating point: contraction is off for this file; the one fused operation
 // of the association is written as fmaf. '/' and sqrtf are the correctly
@@ -161,29 +160,6 @@ __global__ __launch_bounds__(256) void k_rows_replica(const T* x, int64_t xs,
     row_group<T, Q>(x + r * xs, w, y + r * ys, n, eps, lds4, m0, m1);
 }
 
-// GROUP-layout descriptor row: the captured instance Q is used when the row
-// read at run time fits it (width in (1024 (Q-1), 1024 Q], a multiple of 4,
-// quad-aligned pointers); any other row is streamed with BLOCK's mapping.
-template <typename T, int Q, bool POS>
-__global__ __launch_bounds__(256) void k_desc_group(const rmsn_desc* __restrict__ d, float eps,
-                                                    PosArgs pa) {
-    __shared__ float lds4[4];
-    uint64_t pos;
-    const rmsn_desc dd = desc_load<POS>(d, pa, &pos);
-    const int64_t n = dd.n;
-    if (n < 1 || n > RMSN_MAX_N) return;
-    const T* x;
-    T* y;
-    desc_row<T, POS>(dd, pos, pa, x, y);
-    const T* w = static_cast<const T*>(dd.w);
-    const uintptr_t a = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w) |
-                        reinterpret_cast<uintptr_t>(y);
-    if ((n & 3) == 0 && n > 1024 * (Q - 1) && n <= 1024 * Q && a % (4 * sizeof(T)) == 0)
-        row_group<T, Q>(x, w, y, (int)n, eps, lds4);
-    else
-        row_block<T, 0>(x, w, y, (int)n, eps, lds4);
-}
-
 template <typename T, int NCH>
 __global__ __launch_bounds__(256) void k_rows_block(const T* x, int64_t xs,
                                                     const T* __restrict__ w, T* y, int64_t ys,
@@ -193,28 +169,8 @@ __global__ __launch_bounds__(256) void k_rows_block(const T* x, int64_t xs,
     row_block<T, NCH>(x + r * xs, w, y + r * ys, n, eps, lds4);
 }
 
-// One row whose pointers and width are read from device memory when the
-// kernel runs (Lecture 08 "Graph-resident decode", section 2: a value used
-// only as a loop bound can live in device memory; the launch geometry comes
-// from the capture-time width).
-template <typename T, int NCH, bool POS>
-__global__ __launch_bounds__(256) void k_desc_block(const rmsn_desc* __restrict__ d, float eps,
-                                                    PosArgs pa) {
-    __shared__ float lds4[4];
-    uint64_t pos;
-    const rmsn_desc dd = desc_load<POS>(d, pa, &pos);
-    const int64_t n = dd.n;
-    if (n < 1 || n > RMSN_MAX_N) return;
-    const T* x;
-    T* y;
-    desc_row<T, POS>(dd, pos, pa, x, y);
-    row_block<T, NCH>(x, static_cast<const T*>(dd.w), y, (int)n, eps, lds4);
-}
-
 // ---------------------------------------------------------------------------
-// Instance selection. The bucket list matches kChunkBuckets in rmsn_plan.h.
-
-#define RMSN_FOR_BUCKETS(X) X(1) X(2) X(4) X(6) X(8) X(12) X(16) X(20) X(24) X(28) X(32)
+// Instance selection (the bucket lists are in rmsn_rows.h).
 
 template <typename T>
 hipError_t launch_wave_t(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
@@ -345,34 +301,6 @@ hipError_t launch_block_t(const Plan& p, const void* x, int64_t xs, const void* 
     return hipGetLastError();
 }
 
-template <typename T, bool POS>
-hipError_t launch_desc_t(const Plan& p, const rmsn_desc* d, float eps, const PosArgs& pa,
-                         hipStream_t s) {
-    if (p.path == RMSN_PATH_GROUP) {
-#define RMSN_CASE(Q)                                                                          \
-    case Q:                                                                                   \
-        hipLaunchKernelGGL((k_desc_group<T, Q, POS>), dim3(1), dim3(256), 0, s, d, eps, pa);  \
-        break;
-        switch (p.loads) {
-            RMSN_FOR_GROUP_BLOCKS(RMSN_CASE)
-            default: return hipErrorInvalidValue;
-        }
-#undef RMSN_CASE
-        return hipGetLastError();
-    }
-#define RMSN_CASE(C)                                                                          \
-    case C:                                                                                   \
-        hipLaunchKernelGGL((k_desc_block<T, C, POS>), dim3(1), dim3(256), 0, s, d, eps, pa);  \
-        break;
-    switch (p.chunks) {
-        RMSN_CASE(0)
-        RMSN_FOR_BUCKETS(RMSN_CASE)
-        default: return hipErrorInvalidValue;
-    }
-#undef RMSN_CASE
-    return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, void* y,
@@ -419,18 +347,6 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
         return launch_stream_rows(p, x, xs, w, y, ys, rows, n, eps, stream);
     return p.dtype == RMSN_F32 ? launch_block_t<float>(p, x, xs, w, y, ys, n, eps, stream)
                                : launch_block_t<uint16_t>(p, x, xs, w, y, ys, n, eps, stream);
-}
-
-hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
-                       hipStream_t stream) {
-    if (p.path == RMSN_PATH_WAVE || p.path == RMSN_PATH_SPLIT)
-        return hipErrorInvalidValue;  // descriptors use GROUP, BLOCK or STREAM
-    if (pos)
-        return p.dtype == RMSN_F32 ? launch_desc_t<float, true>(p, d, eps, *pos, stream)
-                                   : launch_desc_t<uint16_t, true>(p, d, eps, *pos, stream);
-    const PosArgs none{nullptr, 0, 0, 1};
-    return p.dtype == RMSN_F32 ? launch_desc_t<float, false>(p, d, eps, none, stream)
-                               : launch_desc_t<uint16_t, false>(p, d, eps, none, stream);
 }
 
 }  // namespace rmsn

@@ -146,8 +146,10 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
     return hipGetLastError();
 }
 
-hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
-                       hipStream_t stream) {
+// One build of the descriptor kernel here: eager launches and the launches a
+// graph records share it.
+hipError_t launch_desc_eager(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
+                             hipStream_t stream) {
     if (!narrow_block(p)) return hipErrorInvalidValue;
     const dim3 block((unsigned)p.block);
     const PosArgs none{nullptr, 0, 0, 1};
@@ -159,6 +161,11 @@ hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosAr
         else hipLaunchKernelGGL((k_desc_narrow<uint16_t, false>), dim3(1), block, 0, stream, d, eps, none);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_desc_graph(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
+                             hipStream_t stream) {
+    return launch_desc_eager(p, d, eps, pos, stream);
 }
 
 // The WIDE path splits R256's four groups over workgroups; this build's plan

@@ -1,5 +1,5 @@
 // rmsn_launch.h -- host-side launchers of the gfx950 kernels (rmsn_kernels.hip,
-// rmsn_wide.hip, rmsn_aux.hip).
+// rmsn_desc.hip, rmsn_persistent.hip, rmsn_wide.hip, rmsn_aux.hip).
 // Each enqueues on `stream` and returns the launch's hipError_t; none
 // allocates or synchronises.
 #pragma once
@@ -38,9 +38,14 @@ struct PosArgs {
 
 // One row described by the device-resident descriptor `d` (read when the
 // kernel runs); plan `p` was made for the capture-time width. pos: NULL, or
-// the row is taken at the sequence's device-resident position.
-hipError_t launch_desc(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
-                       hipStream_t stream);
+// the row is taken at the sequence's device-resident position. Two builds of
+// the same kernels: launch_desc_eager for launches enqueued one by one (the
+// kernel loads its arguments), launch_desc_graph for the launches a sequence
+// graph records (arguments preloaded into SGPRs by the dispatcher).
+hipError_t launch_desc_eager(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
+                             hipStream_t stream);
+hipError_t launch_desc_graph(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
+                             hipStream_t stream);
 
 // All `count` rows of a descriptor table, in order, in one launch of one
 // workgroup; pos: NULL, or the rows are taken at the device-resident position

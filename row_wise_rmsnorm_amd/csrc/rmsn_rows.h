@@ -344,6 +344,10 @@ struct SplitPart {
     }
 };
 
+// Register buckets of the WAVE and BLOCK instances (chunks of 256 elements per
+// lane); the list matches kChunkBuckets in rmsn_plan.h.
+#define RMSN_FOR_BUCKETS(X) X(1) X(2) X(4) X(6) X(8) X(12) X(16) X(20) X(24) X(28) X(32)
+
 // ---------------------------------------------------------------------------
 // GROUP layout: 256 threads per row; wavefront g owns association group g.
 // Instances: Q = 1..8 blocks of 1024 elements (rows up to 8192).
