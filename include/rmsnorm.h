@@ -158,7 +158,10 @@ int rmsnorm_batched_rows_noalloc(int dtype, const void* x, int64_t x_row_stride,
 /* The norms of a decode step, in order, issued as `count` dependent launches
  * on `stream` (the eager arm). d_table: DEVICE array of count descriptors.
  * h_widths: HOST array of count widths that size each launch (the same plan
- * function sizes graph nodes, so both arms launch identical kernels).
+ * function sizes graph nodes, so both arms launch the same kernels; the
+ * graph's are a build with their arguments preloaded into SGPRs, these load
+ * their own, which is faster for launches enqueued one by one: same device
+ * code, same bits).
  * Lecture 08 "Graph-resident decode", section 1: the eager decode step pays
  * one host submission per kernel, the launch bill the graph removes; section
  * 4: the eager result is what every replay is compared against. Lecture 04
