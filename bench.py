@@ -850,6 +850,40 @@ def profile_copy(rn, torch, np, wl, launches=200):
     print(json.dumps({"profile_copy": out, "launches": launches}), flush=True)
 
 
+COPY_SWEEP = tuple((v, b) for v in (1, 2, 4) for b in (64, 128, 256, 448, 512, 768, 1024))
+
+
+def profile_copy_sweep(rn, torch, np, wl, launches=200):
+    """The prefill kernel beside the library's streaming copy of the same
+    bytes at every geometry of COPY_SWEEP (16-byte vectors per lane x threads
+    per workgroup), on the same rotated buffers, HIP-event timed, two reps in
+    opposite orders: how a plain copy's time depends on the vectors each lane
+    holds before its first store and on the workgroup's size."""
+    rows, n = wl.PREFILL_SHAPE
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    xs = [torch.randn(rows, n, device=dev, generator=g).to(torch.bfloat16) for _ in range(ROTATE)]
+    w = (1.0 + 0.1 * torch.randn(n, device=dev, generator=g)).to(torch.bfloat16)
+    ys = [torch.empty_like(xs[0]) for _ in range(ROTATE)]
+    eps = float(wl.EPS)
+    pre = lambda i: rn.rmsnorm_batched_rows(xs[i % ROTATE], w, eps, out=ys[i % ROTATE])
+    for i in range(400):
+        pre(i)
+    res = {}
+    for rep in range(2):
+        res.setdefault("prefill", []).append(1000.0 * elapsed_ms(pre, launches) / launches)
+        for v, b in (COPY_SWEEP if rep == 0 else COPY_SWEEP[::-1]):
+            fn = lambda i, v=v, b=b: rn.diag_copy(xs[i % ROTATE], ys[i % ROTATE], v, b)
+            for i in range(30):
+                fn(i)
+            res.setdefault(f"copy_{v}x16B_{b}_threads", []).append(
+                1000.0 * elapsed_ms(fn, launches) / launches)
+        log(f"copy sweep rep {rep} done")
+    print(json.dumps({"profile_copy_sweep": {k: sum(v) / len(v) for k, v in res.items()},
+                      "reps_us": res, "launches": launches}), flush=True)
+
+
 def offset_chained_table(rn, torch, xs, ws, widths, shift=8):
     """The decode step's widths with norm j reading the output of the previous
     norm of its width `shift` elements on (outputs padded by `shift`): every
@@ -912,6 +946,8 @@ def main():
                     help="short decode-step run for counter collection")
     ap.add_argument("--profile-wide", action="store_true",
                     help="a short run of the wide-row shapes for a kernel trace")
+    ap.add_argument("--profile-copy-sweep", action="store_true",
+                    help="prefill kernel beside the streaming copy at 21 geometries (HIP events)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="prefill kernel and copy-pattern ceilings on the same buffers (trace)")
     ap.add_argument("--profile-persistent", choices=["spread", "one", "chained", "chained_offset"],
@@ -945,6 +981,9 @@ def main():
         return
     if args.profile_copy:
         profile_copy(rn, torch, np, wl)
+        return
+    if args.profile_copy_sweep:
+        profile_copy_sweep(rn, torch, np, wl)
         return
     if args.profile_persistent:
         profile_persistent(rn, torch, np, wl, args.profile_persistent)
