@@ -11,6 +11,7 @@
 Everything happens in a scratch copy; the repository's builds are not touched.
 """
 import glob
+import importlib.util
 import os
 import shutil
 import subprocess
@@ -70,21 +71,31 @@ def test_library_host_code_under_sanitizer(tmp_path, sanitizer, runtime, options
     dst = tmp_path / "copy"
     dst.mkdir()
     _copy(dst, ["row_wise_rmsnorm_amd", "include", "oracle", "tests", "workloads", "pytest.ini",
-                "bench.py"])
+                "bench.py", "__graft_entry__.py"])
     pkg = dst / "row_wise_rmsnorm_amd"
     csrc = pkg / "csrc"
-    flags = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
+    flags = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC",
              "-ffp-contract=off", "-fno-fast-math", "-Xclang", "-target-feature", "-Xclang",
              "-packed-fp32-ops", "-Wno-unused-command-line-argument",
              "-I", str(dst / "include"), "-I", str(csrc),
              "-Xarch_host", f"-fsanitize={sanitizer}"]
-    common = [str(csrc / f) for f in ("rmsn_aux.hip", "rmsn_api.hip", "rmsn_plan.cpp")]
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    subprocess.check_call([hipcc, *flags, "-o", str(pkg / "librmsnorm_amd.so"),
-                           *[str(csrc / f) for f in ("rmsn_kernels.hip", "rmsn_persistent.hip",
-                                                     "rmsn_wide.hip")], *common])
-    subprocess.check_call([hipcc, *flags, "-DRMSN_LANES=128", "-o",
-                           str(pkg / "librmsnorm_amd_l128.so"),
-                           str(csrc / "rmsn_kernels_l128.hip"), *common])
+    # the library's own list of objects and their per-object flags
+    spec = importlib.util.spec_from_file_location("rmsn_build_copy", str(pkg / "build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
+
+    def link(out, units):
+        objs = []
+        for i, (src, extra) in enumerate(units):
+            obj = str(tmp_path / f"{out}.{i}.o")
+            subprocess.check_call([hipcc, *flags, *extra, "-c", "-o", obj, str(csrc / src)])
+            objs.append(obj)
+        subprocess.check_call([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC",
+                               "-Xarch_host", f"-fsanitize={sanitizer}", "-o", str(pkg / out),
+                               *objs])
+
+    link("librmsnorm_amd.so", build.UNITS)
+    link("librmsnorm_amd_l128.so", build.UNITS128)
     r = _pytest(dst, "tests/test_abi_cpu.py", {"LD_PRELOAD": rt, **options})
     assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
