@@ -160,8 +160,10 @@ int rmsnorm_batched_rows_noalloc(int dtype, const void* x, int64_t x_row_stride,
  * h_widths: HOST array of count widths that size each launch (the same plan
  * function sizes graph nodes, so both arms launch the same kernels; the
  * graph's are a build with their arguments preloaded into SGPRs, these load
- * their own, which is faster for launches enqueued one by one: same device
- * code, same bits).
+ * their own, which is faster for launches enqueued one by one while the HIP
+ * runtime keeps their arguments in device memory (its default; with
+ * HIP_FORCE_DEV_KERNARG=0 in the environment they take the preloaded build
+ * too): same device code, same bits).
  * Lecture 08 "Graph-resident decode", section 1: the eager decode step pays
  * one host submission per kernel, the launch bill the graph removes; section
  * 4: the eager result is what every replay is compared against. Lecture 04

@@ -5,14 +5,16 @@
 //
 // This file is compiled twice, with the same device code:
 //   RMSN_DESC_PRELOADED=1  kernel arguments preloaded into SGPRs by the
-//                          dispatcher (launch_desc_graph: the launches a
-//                          sequence graph records);
+//                          dispatcher (launch_desc_preloaded);
 //   RMSN_DESC_PRELOADED=0  the kernel loads its arguments itself
-//                          (launch_desc_eager: launches enqueued one by one).
+//                          (launch_desc_plain).
 // Measured on MI355X (327-norm decode step): preloading takes about 0.15 us
-// off each graph node (the first scalar load of the kernel is gone) but adds
-// about 0.17 us to each eager launch with the runtime's default placement of
-// kernel arguments in device memory; the bits are the same either way.
+// off each node of a captured graph (the kernel's first scalar load is gone)
+// but adds about 0.17 us to each launch enqueued one by one while the HIP
+// runtime keeps those launches' arguments in device memory (its default
+// here); with the arguments in host memory (HIP_FORCE_DEV_KERNARG=0) the
+// preloaded build is the faster one for those launches too. The bits are the
+// same either way.
 //
 // Floating point as in rmsn_kernels.hip: contraction off, the one fused
 // operation written as fmaf, correctly rounded '/' and sqrtf.
@@ -31,10 +33,10 @@
 #endif
 #if RMSN_DESC_PRELOADED
 #define RMSN_DESC_NS desc_preloaded
-#define RMSN_DESC_LAUNCH launch_desc_graph
+#define RMSN_DESC_LAUNCH launch_desc_preloaded
 #else
 #define RMSN_DESC_NS desc_loaded
-#define RMSN_DESC_LAUNCH launch_desc_eager
+#define RMSN_DESC_LAUNCH launch_desc_plain
 #endif
 
 namespace rmsn {

@@ -148,7 +148,7 @@ hipError_t launch_rows(const Plan& p, const void* x, int64_t xs, const void* w, 
 
 // One build of the descriptor kernel here: eager launches and the launches a
 // graph records share it.
-hipError_t launch_desc_eager(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
+hipError_t launch_desc_plain(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
                              hipStream_t stream) {
     if (!narrow_block(p)) return hipErrorInvalidValue;
     const dim3 block((unsigned)p.block);
@@ -163,9 +163,9 @@ hipError_t launch_desc_eager(const Plan& p, const rmsn_desc* d, float eps, const
     return hipGetLastError();
 }
 
-hipError_t launch_desc_graph(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
+hipError_t launch_desc_preloaded(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
                              hipStream_t stream) {
-    return launch_desc_eager(p, d, eps, pos, stream);
+    return launch_desc_plain(p, d, eps, pos, stream);
 }
 
 // The WIDE path splits R256's four groups over workgroups; this build's plan

@@ -39,13 +39,15 @@ struct PosArgs {
 // One row described by the device-resident descriptor `d` (read when the
 // kernel runs); plan `p` was made for the capture-time width. pos: NULL, or
 // the row is taken at the sequence's device-resident position. Two builds of
-// the same kernels: launch_desc_eager for launches enqueued one by one (the
-// kernel loads its arguments), launch_desc_graph for the launches a sequence
-// graph records (arguments preloaded into SGPRs by the dispatcher).
-hipError_t launch_desc_eager(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
+// the same kernels (rmsn_desc.hip): launch_desc_preloaded, arguments
+// preloaded into SGPRs by the dispatcher (the launches a sequence graph
+// records), and launch_desc_plain, where the kernel loads its arguments
+// (eager launches, unless the runtime keeps their arguments in host memory;
+// rmsn_api.hip).
+hipError_t launch_desc_plain(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
                              hipStream_t stream);
-hipError_t launch_desc_graph(const Plan& p, const rmsn_desc* d, float eps, const PosArgs* pos,
-                             hipStream_t stream);
+hipError_t launch_desc_preloaded(const Plan& p, const rmsn_desc* d, float eps,
+                                 const PosArgs* pos, hipStream_t stream);
 
 // All `count` rows of a descriptor table, in order, in one launch of one
 // workgroup; pos: NULL, or the rows are taken at the device-resident position
