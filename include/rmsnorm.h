@@ -223,7 +223,9 @@ typedef struct rmsn_position {
  * position, then the position update, all on `stream`. Arguments as for
  * rmsnorm_sequence_eager; RMSN_EINVAL also for a null position, d_pos null or
  * not 8-byte aligned, period < 1, negative or misaligned pitches, or
- * period * pitch overflowing. */
+ * period * pitch overflowing. Lecture 08 "Graph-resident decode", section 2:
+ * a value that changes from one step to the next (here the position) lives in
+ * device memory and the sequence itself updates it. */
 int rmsnorm_sequence_eager_positioned(int dtype, const rmsn_desc* d_table,
                                       const int64_t* h_widths, int32_t count, float eps,
                                       const rmsn_position* pos, void* stream);
@@ -233,7 +235,10 @@ int rmsnorm_sequence_eager_positioned(int dtype, const rmsn_desc* d_table,
  * update included, on a private row and a private position: neither the
  * caller's rows nor *d_pos change before the first launch. Otherwise as
  * rmsnorm_sequence_graph_create (a capture failure leaves *d_pos untouched
- * and the handle replays eagerly, position update included). */
+ * and the handle replays eagerly, position update included). Lecture 08
+ * "Graph-resident decode", section 2 (the state update captured inside the
+ * graph, so replays differ with no host work) and section 3 (warm every
+ * variant before capture; degrade to eager, do not fail). */
 int rmsnorm_sequence_graph_create_positioned(int dtype, const rmsn_desc* d_table,
                                              const int64_t* h_widths, int32_t count, float eps,
                                              const rmsn_position* pos, rmsn_graph** out);
@@ -399,12 +404,16 @@ typedef struct rmsn_plan_info {
  * of two dividing it counts, up to 16; 0 or anything below the element size
  * means element alignment only; -1 plans a descriptor row of a sequence,
  * whose pointers the kernel checks when it runs). Same function the launches
- * use. Returns RMSN_EINVAL for an invalid dtype, rows or n. */
+ * use (Lecture 08 "Graph-resident decode", section 2: the capture-time check
+ * and the launcher call one plan function; Lecture 04 section 1: the grid and
+ * block a launch gets). Returns RMSN_EINVAL for an invalid dtype, rows or n. */
 int rmsnorm_plan_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_info* out);
 
 /* The plan rmsnorm_batched_rows_ws would use for `rows` rows of width n at
  * alignment `align` (as rmsnorm_plan_query), and in *bytes the workspace it
- * needs (16 bytes per row on RMSN_PATH_WIDE, else 0). plan may be NULL. */
+ * needs (16 bytes per row on RMSN_PATH_WIDE, else 0). plan may be NULL.
+ * Lecture 04 section 1: a few rows on a chip of 256 CUs leave most of it idle
+ * unless a row is split over several of them. */
 int rmsnorm_workspace_query(int dtype, int64_t rows, int64_t n, int align, rmsn_plan_info* plan,
                             int64_t* bytes);
 
@@ -482,7 +491,9 @@ int rmsnorm_association_lanes(void);
  * calls) on count consecutive binary32 bit patterns starting at first_bits,
  * taken as ss, with the given n and eps: r_out[i] = sqrtf(ss/(float)n + eps),
  * inv_out[i] = 1.0f / r_out[i]. Device output arrays of count floats. Used to
- * check the device square root and division against a CPU exhaustively. */
+ * check the device square root and division against a CPU exhaustively: the
+ * epilogue of Lecture 04 section 2.1 (mean, eps, root, inverse), computed here
+ * with a correctly rounded root and a correctly rounded division. */
 int rmsnorm_diag_inverse(uint32_t first_bits, int64_t count, int64_t n, float eps, float* r_out,
                          float* inv_out, void* stream);
 
@@ -491,7 +502,8 @@ int rmsnorm_diag_inverse(uint32_t first_bits, int64_t count, int64_t n, float ep
  * at first_bits: out[i] = bf16(pattern first_bits + i), a DEVICE array of count
  * uint16. Used to check the hardware conversion against a CPU for every
  * binary32 pattern. RMSN_EINVAL if the range leaves 32 bits or out is null or
- * odd. */
+ * odd. The bf16 output format is this library's (see rmsnorm_bf16), not the
+ * pages'. */
 int rmsnorm_diag_bf16(uint32_t first_bits, int64_t count, uint16_t* out, void* stream);
 
 /* A plain streaming copy of `bytes` bytes from src to dst (DEVICE memory, not
