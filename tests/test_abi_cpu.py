@@ -541,6 +541,31 @@ def test_build_scripts_load_without_the_package():
     assert r.returncode == 0, r.stderr
 
 
+def test_descriptor_kernels_built_both_ways():
+    """The descriptor kernels are compiled twice (rmsn_desc.hip): with their
+    arguments preloaded into SGPRs (the launches a sequence graph records) and
+    loading their own (eager launches); the build lists both objects, and the
+    built library carries both kernel families. Every other object is built
+    with preloading except the host-only plan code."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "rmsn_build_check", os.path.join(ROOT, "row_wise_rmsnorm_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    desc = [extra for src, extra in b.UNITS if src == "rmsn_desc.hip"]
+    assert len(desc) == 2
+    assert sorted("-DRMSN_DESC_PRELOADED=1" in e for e in desc) == [False, True]
+    for e in desc:
+        assert ("-DRMSN_DESC_PRELOADED=1" in e) == all(f in e for f in b.PRELOAD)
+    for src, extra in b.UNITS:
+        if src.endswith(".hip") and src != "rmsn_desc.hip":
+            assert all(f in extra for f in b.PRELOAD), src
+    with open(os.path.join(ROOT, "row_wise_rmsnorm_amd", "librmsnorm_amd.so"), "rb") as f:
+        blob = f.read()
+    # the kernels' mangled names: namespace rmsn::desc_preloaded / rmsn::desc_loaded
+    assert b"14desc_preloaded" in blob and b"11desc_loaded" in blob
+
+
 def test_noalloc_rejects(rn):
     """The allocation-free entry point checks its arguments as the plain one
     does, and refuses a launch whose group totals would not fit the library's
